@@ -1,0 +1,180 @@
+"""Python binding of libqmm (quantized GEMV / GEMM with inline dequantization
+for AMD MI355X, gfx950).
+
+The functions here carry the C ABI's names (``include/qmm.h``) and only
+marshal arguments: every step of the computation runs in the HIP kernels of
+``libqmm.so``.  PyTorch supplies device memory and streams.  There is no
+fallback: if the library is missing or fails to load, every call raises.
+
+Arguments that are device buffers may be given as torch tensors (their
+``data_ptr()`` is passed) or as raw integer addresses.  ``stream`` defaults to
+torch's current stream on the current device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "QmmError", "library_path", "load",
+    "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
+    "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
+    "QMM_OK", "QMM_ERR_INVALID_ARGUMENT", "QMM_ERR_UNSUPPORTED", "QMM_ERR_MISALIGNED",
+    "QMM_ERR_DEVICE", "EXPORTED_SYMBOLS",
+]
+
+QMM_OK = 0
+QMM_ERR_INVALID_ARGUMENT = 1
+QMM_ERR_UNSUPPORTED = 2
+QMM_ERR_MISALIGNED = 3
+QMM_ERR_DEVICE = 4
+
+EXPORTED_SYMBOLS = (
+    "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
+    "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libqmm.so"
+_lib = None
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__("%s failed with status %d: %s" % (func, status, detail))
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [
+        ("variant", ctypes.c_int32),
+        ("lanes_per_row", ctypes.c_int32),
+        ("units_per_lane", ctypes.c_int32),
+        ("rows_per_iter", ctypes.c_int32),
+        ("unit_codes", ctypes.c_int32),
+        ("split_k", ctypes.c_int32),
+        ("tile_m", ctypes.c_int32),
+        ("tile_n", ctypes.c_int32),
+        ("grid", ctypes.c_int64),
+        ("block", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 5),
+    ]
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load():
+    """Load libqmm.so (built in-tree by ``python -m gemm_qmm_gemv_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libqmm.so is not built (%s); run `python -m gemm_qmm_gemv_amd.build`" % path)
+    try:
+        # torch first: its HIP runtime is then the one the library binds to.
+        import torch  # noqa: F401
+    except Exception:
+        pass
+    lib = ctypes.CDLL(path)
+    p, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.qmm_gemv.argtypes = [p, p, p, p, p, i64, i64, ci, ci, p]
+    lib.qmm_gemm.argtypes = [p, p, p, p, p, i64, i64, i64, ci, ci, p, sz, p]
+    lib.qmm_gemm_workspace_bytes.argtypes = [i64, i64, i64, ci, ci]
+    lib.qmm_gemm_workspace_bytes.restype = sz
+    lib.qmm_moe_gemm.argtypes = [p, p, p, p, p, i64, p, p, i64, i64, i64, i64, ci, ci, p]
+    lib.qmm_unpack.argtypes = [p, p, i64, i64, ci, p]
+    lib.qmm_get_plan.argtypes = [ci, i64, i64, i64, ci, ci, ci, sz, ctypes.POINTER(_Plan)]
+    for f in ("qmm_gemv", "qmm_gemm", "qmm_moe_gemm", "qmm_unpack", "qmm_get_plan"):
+        getattr(lib, f).restype = ci
+    lib.qmm_status_string.argtypes = [ci]
+    lib.qmm_status_string.restype = ctypes.c_char_p
+    lib.qmm_last_error.restype = ctypes.c_char_p
+    lib.qmm_abi_version.restype = ci
+    _lib = lib
+    return lib
+
+
+def _addr(v):
+    if v is None:
+        return None
+    if isinstance(v, int):
+        return v
+    return v.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, func: str) -> None:
+    if status != QMM_OK:
+        detail = load().qmm_last_error().decode()
+        raise QmmError(status, func, detail)
+
+
+def qmm_status_string(status: int) -> str:
+    return load().qmm_status_string(int(status)).decode()
+
+
+def qmm_last_error() -> str:
+    return load().qmm_last_error().decode()
+
+
+def qmm_abi_version() -> int:
+    return load().qmm_abi_version()
+
+
+def qmm_gemv(w_packed, scales, mins, x, y, n, k, bits, group_size, stream=None) -> None:
+    """y[n] = sum_k (s*q + m)[n][k] x[k] (fp16 x, fp32 y); asynchronous."""
+    _check(load().qmm_gemv(_addr(w_packed), _addr(scales), _addr(mins), _addr(x), _addr(y),
+                           int(n), int(k), int(bits), int(group_size), _stream(stream)),
+           "qmm_gemv")
+
+
+def qmm_gemm(w_packed, scales, mins, x, y, m, n, k, bits, group_size, workspace=None,
+             workspace_bytes=0, stream=None) -> None:
+    """y[m][n] = sum_k (s*q + m)[n][k] x[m][k]; asynchronous."""
+    _check(load().qmm_gemm(_addr(w_packed), _addr(scales), _addr(mins), _addr(x), _addr(y),
+                           int(m), int(n), int(k), int(bits), int(group_size), _addr(workspace),
+                           int(workspace_bytes), _stream(stream)),
+           "qmm_gemm")
+
+
+def qmm_gemm_workspace_bytes(m, n, k, bits, group_size) -> int:
+    return int(load().qmm_gemm_workspace_bytes(int(m), int(n), int(k), int(bits), int(group_size)))
+
+
+def qmm_moe_gemm(w_packed, scales, mins, x, x_rows, x_rows_count, expert_offsets, y, p_rows,
+                 n_experts, n, k, bits, group_size, stream=None) -> None:
+    """Expert-grouped rows: y[p] = W_{e(p)} x[x_rows[p]]; asynchronous."""
+    _check(load().qmm_moe_gemm(_addr(w_packed), _addr(scales), _addr(mins), _addr(x),
+                               _addr(x_rows), int(x_rows_count), _addr(expert_offsets), _addr(y),
+                               int(p_rows), int(n_experts), int(n), int(k), int(bits),
+                               int(group_size), _stream(stream)),
+           "qmm_moe_gemm")
+
+
+def qmm_unpack(w_packed, codes, n, k, bits, stream=None) -> None:
+    """codes[n][k] (uint8) = the packed codes; asynchronous."""
+    _check(load().qmm_unpack(_addr(w_packed), _addr(codes), int(n), int(k), int(bits),
+                             _stream(stream)),
+           "qmm_unpack")
+
+
+def qmm_get_plan(op, m, n, k, bits, group_size, cu_count=0, workspace_bytes=0) -> dict:
+    """The launch plan the library would use (op 0 gemv, 1 gemm, 2 moe)."""
+    plan = _Plan()
+    _check(load().qmm_get_plan(int(op), int(m), int(n), int(k), int(bits), int(group_size),
+                               int(cu_count), int(workspace_bytes), ctypes.byref(plan)),
+           "qmm_get_plan")
+    return {f: getattr(plan, f) for f, _ in _Plan._fields_ if f != "reserved"} | {
+        "multipass": bool(plan.reserved[0])}

@@ -1,0 +1,66 @@
+"""Build libqmm.so (HIP, gfx950) in-tree with hipcc.
+
+Usage: ``python -m gemm_qmm_gemv_amd.build``.  Every call compiles; the
+library is written next to this file so it travels with the source tree.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libqmm.so")
+SOURCES = ["qmm_api.hip", "gemv.hip", "gemm.hip", "unpack.hip"]
+ARCH = os.environ.get("QMM_OFFLOAD_ARCH", "gfx950")
+
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=" + ARCH,
+    # Keep the compiler from forming packed fp32 instructions.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fvisibility=hidden",
+    "-Wall", "-Wno-unused-function",
+    "-I" + os.path.join(ROOT, "include"),
+]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (proc.stdout + proc.stderr).splitlines() if noise not in ln]
+    if proc.returncode != 0:
+        sys.stderr.write("\n".join(msgs) + "\n")
+        raise RuntimeError("hipcc failed: %s" % " ".join(cmd[-3:]))
+    if verbose and msgs:
+        print("\n".join(msgs))
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel) and link libqmm.so.  Always rebuilds."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(ROOT, "_build", "qmm")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        jobs.append(([hipcc] + compile_flags + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "8"))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose), jobs))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH] + [o for _, o in jobs] + ["-o", tmp],
+         verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

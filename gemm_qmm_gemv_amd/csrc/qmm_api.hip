@@ -1,0 +1,398 @@
+// qmm_api.hip -- the C ABI of libqmm: argument checks, launch planning and
+// kernel launches.  Declarations and the contract are in include/qmm.h.
+//
+// Launch planning follows the pages' note that kernel choice and work-group
+// sizes are tuned per chip and per GPU-core count ("BaseRT: Best-in-Class
+// LLM Inference on Apple Silicon via Native Metal", section "Metodologia"):
+// here the inputs are the shape, the bit width and the device's compute-unit
+// count.  Everything is decided on the host from integers; no allocation,
+// no synchronization, no per-call state.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/qmm.h"
+#include "qmm_kernels.h"
+
+using namespace qmm;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qmm_status fail(qmm_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+qmm_status ok() {
+    g_err[0] = '\0';
+    return QMM_OK;
+}
+
+bool bits_supported(int bits) {
+    return bits == 2 || bits == 3 || bits == 4 || bits == 6 || bits == 8;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t INT_LIMIT = 0x7fffffff;
+
+qmm_status check_format(int64_t n, int64_t k, int bits, int group) {
+    if (bits < 2 || bits > 8) return fail(QMM_ERR_INVALID_ARGUMENT, "bits=%d outside 2..8", bits);
+    if (!bits_supported(bits))
+        return fail(QMM_ERR_UNSUPPORTED, "bits=%d not built (supported: 2, 3, 4, 6, 8)", bits);
+    if (group <= 0 || group % 32)
+        return fail(QMM_ERR_INVALID_ARGUMENT, "group_size=%d must be a positive multiple of 32", group);
+    if (k < 32 || k % group)
+        return fail(QMM_ERR_INVALID_ARGUMENT, "k=%lld must be >= 32 and a multiple of group_size=%d",
+                    (long long)k, group);
+    if (n < 0) return fail(QMM_ERR_INVALID_ARGUMENT, "n=%lld is negative", (long long)n);
+    if (n > INT_LIMIT || k > INT_LIMIT)
+        return fail(QMM_ERR_INVALID_ARGUMENT, "n or k above 2^31-1");
+    return QMM_OK;
+}
+
+qmm_status check_weight_ptrs(const void* w, const void* s, const void* m) {
+    if (!w || !s || !m) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL weight, scale or min pointer");
+    if (!aligned(w, 16)) return fail(QMM_ERR_MISALIGNED, "w_packed not 16-byte aligned");
+    if (!aligned(s, 2) || !aligned(m, 2)) return fail(QMM_ERR_MISALIGNED, "scales/mins not 2-byte aligned");
+    return QMM_OK;
+}
+
+// Compute units of the current device, cached per device id.
+std::atomic<int> g_cu_cache[64];
+
+qmm_status device_cus(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(QMM_ERR_DEVICE, "no HIP device available");
+    }
+    if (dev >= 0 && dev < 64) {
+        const int c = g_cu_cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cus = c;
+            return QMM_OK;
+        }
+    }
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) {
+        (void)hipGetLastError();
+        return fail(QMM_ERR_DEVICE, "cannot query compute units of device %d", dev);
+    }
+    if (dev >= 0 && dev < 64) g_cu_cache[dev].store(c, std::memory_order_relaxed);
+    *cus = c;
+    return QMM_OK;
+}
+
+int env_int(const char* name, int dflt) {
+    const char* v = getenv(name);
+    if (!v || !*v) return dflt;
+    return atoi(v);
+}
+
+// ---- planning ------------------------------------------------------------------
+
+struct LaneSplit {
+    int lpr, xc;
+    bool multipass;
+};
+
+// Lanes per row and units per lane: the single-pass split with the fewest idle
+// unit slots; ties prefer fewer units per lane (more lanes in flight).
+LaneSplit choose_split(int nu, int max_xc, bool (*supported)(int, int)) {
+    static const int cand[][2] = {{16, 1}, {32, 1}, {64, 1}, {8, 1}, {16, 2}, {32, 2},
+                                  {64, 2}, {8, 2},  {16, 3}};
+    LaneSplit best{64, max_xc >= 2 ? 2 : 1, true};
+    int best_waste = 1 << 30, best_xc = 99;
+    for (const auto& c : cand) {
+        const int lpr = c[0], xc = c[1];
+        if (xc > max_xc || !supported(lpr, xc)) continue;
+        const int cap = lpr * xc;
+        if (cap < nu) continue;
+        const int waste = cap - nu;
+        if (waste < best_waste || (waste == best_waste && xc < best_xc)) {
+            best = {lpr, xc, false};
+            best_waste = waste;
+            best_xc = xc;
+        }
+    }
+    return best;
+}
+
+bool gemv_split_ok(int lpr, int xc) { return gemv_shape_supported(lpr, xc, 1); }
+bool rows_split_ok(int lpr, int xc) { return rows_shape_supported(lpr, xc, xc == 1 ? 4 : 2); }
+
+GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
+    GemvShape sh{};
+    sh.unit = (group % 64 == 0) ? 64 : 32;
+    const int nu = (int)(k / sh.unit);
+    LaneSplit ls = choose_split(nu, 3, gemv_split_ok);
+    sh.lpr = ls.lpr;
+    sh.xc = ls.xc;
+    sh.multipass = ls.multipass;
+    const int slots = 64 / sh.lpr;
+    // Rows per slot per iteration: one when the row count alone fills the chip
+    // with single-iteration waves; otherwise enough to keep ~128 bytes of
+    // weights per lane in flight.
+    const int64_t waves_u1 = (n + slots - 1) / slots;
+    const int unit_bytes = sh.unit * bits / 8;
+    int u = 1;
+    if (waves_u1 > (int64_t)cus * 16) {
+        const int want = 128 / (unit_bytes * sh.xc);
+        u = want >= 4 ? 4 : want >= 2 ? 2 : 1;
+    }
+    while (u > 1 && !gemv_shape_supported(sh.lpr, sh.xc, u)) u /= 2;
+    const int ev = env_int("QMM_GEMV_U", 0);
+    if (ev > 0 && gemv_shape_supported(sh.lpr, sh.xc, ev)) u = ev;
+    sh.u = u;
+    const int64_t batches = (n + (int64_t)slots * u - 1) / ((int64_t)slots * u);
+    const int64_t max_waves = (int64_t)cus * env_int("QMM_GEMV_WAVES_PER_CU", 32);
+    const int64_t waves = batches < max_waves ? batches : max_waves;
+    sh.grid = (int)((waves + 3) / 4);
+    if (sh.grid < 1) sh.grid = 1;
+    return sh;
+}
+
+RowsShape plan_rows(int64_t rows_bound, int64_t n, int64_t k, int bits, int group, int cus,
+                    int64_t n_seg_active) {
+    (void)bits;
+    RowsShape sh{};
+    sh.unit = (group % 64 == 0) ? 64 : 32;
+    const int nu = (int)(k / sh.unit);
+    LaneSplit ls = choose_split(nu, 2, rows_split_ok);
+    sh.lpr = ls.lpr;
+    sh.xc = ls.xc;
+    sh.multipass = ls.multipass;
+    sh.mr = (sh.xc == 1 && rows_bound > 2) ? 4 : 2;
+    const int slots = 64 / sh.lpr;
+    const int64_t rows_per_block = 4 * slots;
+    int64_t gx = (n + rows_per_block - 1) / rows_per_block;
+    const int64_t cap = (int64_t)cus * 16;
+    if (gx * n_seg_active > cap) {
+        gx = cap / (n_seg_active > 0 ? n_seg_active : 1);
+        if (gx < 1) gx = 1;
+    }
+    sh.grid_x = (int)gx;
+    sh.grid_y = (int)(n_seg_active > 0 ? n_seg_active : 1);
+    return sh;
+}
+
+GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int cus, size_t ws_bytes, size_t* ws_need) {
+    GemmShape sh{};
+    sh.tile_m = m <= 64 ? 64 : 128;
+    sh.tile_n = 128;
+    sh.grid_m = (int)((m + sh.tile_m - 1) / sh.tile_m);
+    sh.grid_n = (int)((n + sh.tile_n - 1) / sh.tile_n);
+    const int k_tiles = (int)((k + GEMM_BK - 1) / GEMM_BK);
+    const int64_t tiles = (int64_t)sh.grid_m * sh.grid_n;
+    int split = 1;
+    if (tiles < cus) {
+        split = (int)((cus + tiles - 1) / tiles);
+        const int by_k = k_tiles / 4 > 1 ? k_tiles / 4 : 1;
+        if (split > by_k) split = by_k;
+        if (split > 16) split = 16;
+    }
+    const int es = env_int("QMM_GEMM_SPLIT", 0);
+    if (es > 0) split = es < k_tiles ? es : k_tiles;
+    const size_t per_split = (size_t)m * n * sizeof(float);
+    if (ws_need) *ws_need = split > 1 ? per_split * split : 0;
+    if (split > 1 && ws_bytes < per_split * split) {
+        split = per_split ? (int)(ws_bytes / per_split) : 1;
+        if (split < 2) split = 1;
+    }
+    sh.k_tiles_per_split = (k_tiles + split - 1) / split;
+    sh.split = (k_tiles + sh.k_tiles_per_split - 1) / sh.k_tiles_per_split;
+    return sh;
+}
+
+// m rows at or below this go to the multi-row GEMV kernel instead of MFMA.
+constexpr int64_t ROWS_KERNEL_MAX_M = 2;
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+qmm_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(QMM_ERR_DEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmm_abi_version(void) { return QMM_ABI_VERSION; }
+
+const char* qmm_last_error(void) { return g_err; }
+
+const char* qmm_status_string(qmm_status s) {
+    switch (s) {
+        case QMM_OK: return "QMM_OK";
+        case QMM_ERR_INVALID_ARGUMENT: return "QMM_ERR_INVALID_ARGUMENT";
+        case QMM_ERR_UNSUPPORTED: return "QMM_ERR_UNSUPPORTED";
+        case QMM_ERR_MISALIGNED: return "QMM_ERR_MISALIGNED";
+        case QMM_ERR_DEVICE: return "QMM_ERR_DEVICE";
+        default: return "QMM_ERR_UNKNOWN";
+    }
+}
+
+qmm_status qmm_gemv(const void* w_packed, const void* scales, const void* mins, const void* x,
+                    float* y, int64_t n, int64_t k, int bits, int group_size, void* stream) {
+    qmm_status st = check_format(n, k, bits, group_size);
+    if (st != QMM_OK) return st;
+    if (n == 0) return ok();
+    if ((st = check_weight_ptrs(w_packed, scales, mins)) != QMM_OK) return st;
+    if (!x || !y) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x or y");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(QMM_ERR_MISALIGNED, "x or y not 16-byte aligned");
+    int cus = 0;
+    if ((st = device_cus(&cus)) != QMM_OK) return st;
+    const GemvShape sh = plan_gemv(n, k, bits, group_size, cus);
+    GemvArgs a{static_cast<const uint32_t*>(w_packed), static_cast<const uint16_t*>(scales),
+               static_cast<const uint16_t*>(mins), static_cast<const uint16_t*>(x), y, (int)n, (int)k,
+               group_size, bits};
+    return launched(launch_gemv(a, sh, as_stream(stream)), "qmm_gemv");
+}
+
+size_t qmm_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits, int group_size) {
+    if (check_format(n, k, bits, group_size) != QMM_OK || m <= ROWS_KERNEL_MAX_M || n == 0) return 0;
+    int cus = 0;
+    if (device_cus(&cus) != QMM_OK) cus = 256;
+    size_t need = 0;
+    (void)plan_gemm(m, n, k, cus, (size_t)-1, &need);
+    return need;
+}
+
+qmm_status qmm_gemm(const void* w_packed, const void* scales, const void* mins, const void* x,
+                    float* y, int64_t m, int64_t n, int64_t k, int bits, int group_size,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    qmm_status st = check_format(n, k, bits, group_size);
+    if (st != QMM_OK) return st;
+    if (m < 0) return fail(QMM_ERR_INVALID_ARGUMENT, "m=%lld is negative", (long long)m);
+    if (m > INT_LIMIT || m * n > ((int64_t)1 << 40))
+        return fail(QMM_ERR_INVALID_ARGUMENT, "m too large");
+    if (m == 0 || n == 0) return ok();
+    if ((st = check_weight_ptrs(w_packed, scales, mins)) != QMM_OK) return st;
+    if (!x || !y) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x or y");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(QMM_ERR_MISALIGNED, "x or y not 16-byte aligned");
+    if (workspace_bytes && !workspace)
+        return fail(QMM_ERR_INVALID_ARGUMENT, "workspace_bytes > 0 with a NULL workspace");
+    if (workspace && !aligned(workspace, 16)) return fail(QMM_ERR_MISALIGNED, "workspace not 16-byte aligned");
+    int cus = 0;
+    if ((st = device_cus(&cus)) != QMM_OK) return st;
+    const uint32_t* w = static_cast<const uint32_t*>(w_packed);
+    const uint16_t* s = static_cast<const uint16_t*>(scales);
+    const uint16_t* mn = static_cast<const uint16_t*>(mins);
+    const uint16_t* xx = static_cast<const uint16_t*>(x);
+    if (m == 1) {
+        const GemvShape sh = plan_gemv(n, k, bits, group_size, cus);
+        GemvArgs a{w, s, mn, xx, y, (int)n, (int)k, group_size, bits};
+        return launched(launch_gemv(a, sh, as_stream(stream)), "qmm_gemm (gemv)");
+    }
+    if (m <= ROWS_KERNEL_MAX_M) {
+        const RowsShape sh = plan_rows(m, n, k, bits, group_size, cus, 1);
+        RowsArgs a{w, s, mn, xx, nullptr, (int)m, nullptr, 1, (int)m, y, (int)n, (int)k, group_size, bits};
+        return launched(launch_rows(a, sh, as_stream(stream)), "qmm_gemm (rows)");
+    }
+    const GemmShape sh = plan_gemm(m, n, k, cus, workspace ? workspace_bytes : 0, nullptr);
+    GemmArgs a{w, s, mn, xx, y, sh.split > 1 ? static_cast<float*>(workspace) : nullptr, (int)m, (int)n,
+               (int)k, group_size, bits};
+    return launched(launch_gemm(a, sh, as_stream(stream)), "qmm_gemm");
+}
+
+qmm_status qmm_moe_gemm(const void* w_packed, const void* scales, const void* mins, const void* x,
+                        const int32_t* x_rows, int64_t x_rows_count, const int32_t* expert_offsets,
+                        float* y, int64_t p_rows, int64_t n_experts, int64_t n, int64_t k, int bits,
+                        int group_size, void* stream) {
+    qmm_status st = check_format(n, k, bits, group_size);
+    if (st != QMM_OK) return st;
+    if (p_rows < 0 || n_experts < 0 || x_rows_count < 0)
+        return fail(QMM_ERR_INVALID_ARGUMENT, "negative p_rows, n_experts or x_rows_count");
+    if (p_rows > INT_LIMIT || n_experts > INT_LIMIT || x_rows_count > INT_LIMIT)
+        return fail(QMM_ERR_INVALID_ARGUMENT, "p_rows, n_experts or x_rows_count above 2^31-1");
+    if (p_rows == 0 || n == 0 || n_experts == 0) return ok();
+    if ((st = check_weight_ptrs(w_packed, scales, mins)) != QMM_OK) return st;
+    if (!x || !y || !expert_offsets) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x, y or expert_offsets");
+    if (!x_rows && x_rows_count < p_rows)
+        return fail(QMM_ERR_INVALID_ARGUMENT, "x_rows is NULL and x has fewer than p_rows rows");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(QMM_ERR_MISALIGNED, "x or y not 16-byte aligned");
+    if (!aligned(expert_offsets, 4) || (x_rows && !aligned(x_rows, 4)))
+        return fail(QMM_ERR_MISALIGNED, "index arrays not 4-byte aligned");
+    int cus = 0;
+    if ((st = device_cus(&cus)) != QMM_OK) return st;
+    const int64_t active = n_experts < p_rows ? n_experts : p_rows;
+    const RowsShape sh = plan_rows(p_rows, n, k, bits, group_size, cus, active);
+    RowsArgs a{static_cast<const uint32_t*>(w_packed), static_cast<const uint16_t*>(scales),
+               static_cast<const uint16_t*>(mins), static_cast<const uint16_t*>(x), x_rows,
+               (int)x_rows_count, expert_offsets, (int)n_experts, (int)p_rows, y, (int)n, (int)k,
+               group_size, bits};
+    return launched(launch_rows(a, sh, as_stream(stream)), "qmm_moe_gemm");
+}
+
+qmm_status qmm_unpack(const void* w_packed, uint8_t* codes, int64_t n, int64_t k, int bits,
+                      void* stream) {
+    qmm_status st = check_format(n, k, bits, 32);
+    if (st != QMM_OK) return st;
+    if (n == 0) return ok();
+    if (!w_packed || !codes) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL w_packed or codes");
+    if (!aligned(w_packed, 16) || !aligned(codes, 16))
+        return fail(QMM_ERR_MISALIGNED, "w_packed or codes not 16-byte aligned");
+    int cus = 0;
+    if ((st = device_cus(&cus)) != QMM_OK) return st;
+    return launched(launch_unpack(static_cast<const uint32_t*>(w_packed), codes, n, k, bits,
+                                  as_stream(stream)),
+                    "qmm_unpack");
+}
+
+qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits, int group_size,
+                        int cu_count, size_t workspace_bytes, qmm_plan* plan) {
+    if (!plan) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL plan");
+    memset(plan, 0, sizeof *plan);
+    qmm_status st = check_format(n, k, bits, group_size);
+    if (st != QMM_OK) return st;
+    if (m < 0) return fail(QMM_ERR_INVALID_ARGUMENT, "m is negative");
+    int cus = cu_count;
+    if (cus <= 0 && (st = device_cus(&cus)) != QMM_OK) return st;
+    plan->block = 256;
+    plan->split_k = 1;
+    if (op == 0 || (op == 1 && m == 1)) {
+        const GemvShape sh = plan_gemv(n, k, bits, group_size, cus);
+        plan->variant = 0;
+        plan->lanes_per_row = sh.lpr;
+        plan->units_per_lane = sh.xc;
+        plan->rows_per_iter = sh.u;
+        plan->unit_codes = sh.unit;
+        plan->grid = sh.grid;
+        plan->reserved[0] = sh.multipass;
+        return ok();
+    }
+    if (op == 2 || (op == 1 && m <= ROWS_KERNEL_MAX_M)) {
+        const RowsShape sh = plan_rows(m, n, k, bits, group_size, cus, 1);
+        plan->variant = 1;
+        plan->lanes_per_row = sh.lpr;
+        plan->units_per_lane = sh.xc;
+        plan->rows_per_iter = sh.mr;
+        plan->unit_codes = sh.unit;
+        plan->grid = (int64_t)sh.grid_x * sh.grid_y;
+        plan->reserved[0] = sh.multipass;
+        return ok();
+    }
+    if (op == 1) {
+        const GemmShape sh = plan_gemm(m, n, k, cus, workspace_bytes, nullptr);
+        plan->variant = 2;
+        plan->split_k = sh.split;
+        plan->tile_m = sh.tile_m;
+        plan->tile_n = sh.tile_n;
+        plan->grid = 8 * (((int64_t)sh.grid_m * sh.grid_n * sh.split + 7) / 8);
+        return ok();
+    }
+    return fail(QMM_ERR_INVALID_ARGUMENT, "op=%d unknown", op);
+}
+
+}  // extern "C"

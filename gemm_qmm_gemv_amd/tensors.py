@@ -1,0 +1,66 @@
+"""Torch-side plumbing around the C ABI: move numpy inputs to device memory
+and allocate outputs.  No arithmetic of the method happens here; every
+product is computed by the library's kernels.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (qmm_gemm, qmm_gemm_workspace_bytes, qmm_gemv, qmm_moe_gemm, qmm_unpack)
+
+
+def device_tensor(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """Copy a numpy array to the device, keeping its bits (uint32 -> int32,
+    float16 stays float16, uint16 -> int16 views)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    elif a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def upload_matrix(q: dict, device="cuda") -> dict:
+    """dict(w, scales, mins, n, k, bits, group) with device tensors."""
+    out = dict(q)
+    for key in ("w", "scales", "mins"):
+        out[key] = device_tensor(q[key], device)
+    return out
+
+
+def gemv(dq: dict, x: torch.Tensor, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    if y is None:
+        y = torch.empty(dq["n"], dtype=torch.float32, device=x.device)
+    qmm_gemv(dq["w"], dq["scales"], dq["mins"], x, y, dq["n"], dq["k"], dq["bits"], dq["group"],
+             stream=stream)
+    return y
+
+
+def gemm(dq: dict, x: torch.Tensor, y: torch.Tensor | None = None, workspace=None,
+         stream=None) -> torch.Tensor:
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, dq["n"]), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        need = qmm_gemm_workspace_bytes(m, dq["n"], dq["k"], dq["bits"], dq["group"])
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device) if need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    qmm_gemm(dq["w"], dq["scales"], dq["mins"], x, y, m, dq["n"], dq["k"], dq["bits"],
+             dq["group"], workspace=workspace, workspace_bytes=ws_bytes, stream=stream)
+    return y
+
+
+def moe(dst: dict, x: torch.Tensor, x_rows: torch.Tensor | None, offsets: torch.Tensor,
+        p_rows: int, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    if y is None:
+        y = torch.empty((p_rows, dst["n"]), dtype=torch.float32, device=x.device)
+    qmm_moe_gemm(dst["w"], dst["scales"], dst["mins"], x, x_rows, x.shape[0], offsets, y, p_rows,
+                 dst["n_experts"], dst["n"], dst["k"], dst["bits"], dst["group"], stream=stream)
+    return y
+
+
+def unpack(dq: dict, stream=None) -> torch.Tensor:
+    codes = torch.empty((dq["n"], dq["k"]), dtype=torch.uint8, device=dq["w"].device)
+    qmm_unpack(dq["w"], codes, dq["n"], dq["k"], dq["bits"], stream=stream)
+    return codes

@@ -1,0 +1,165 @@
+/*
+ * qmm.h -- quantized matrix products with inline dequantization, for AMD
+ * Instinct MI355X (gfx950).  Plain C ABI: no HIP, torch or C++ types.
+ *
+ * The operation (from the pages):
+ *   Weights are stored with affine quantization at 2 to 8 bits per weight
+ *   ("Apple Silicon 로컬 LLM 추론의 새 기준 BaseRT" (thakicloud.com), section
+ *   "BaseRT는 무엇인가").  Decode multiplies one activation row by the
+ *   weights with a dedicated GEMV (M = 1) and prefill several rows with a
+ *   GEMM (M > 1); dequantization happens inside the compute loop, so full
+ *   precision weights never go to memory and memory traffic scales with the
+ *   compressed size ("BaseRT claims fastest Apple Silicon inference"
+ *   (thetesserapress.com), section "What BaseRT does differently"; "BaseRT:
+ *   Best-in-Class LLM Inference on Apple Silicon via Native Metal"
+ *   (gist.science summary), section "Metodologia", per-format GEMV/GEMM
+ *   variants with dequantization in the inner loop).
+ *
+ * Format (the pages fix none of these details; this is the library's format):
+ *   W is N x K (output rows x reduction).  Codes are unsigned b-bit integers,
+ *   b in {2, 3, 4, 6, 8}.  Row n is a little-endian bitstream of K*b bits held
+ *   in K*b/32 uint32 words: code k occupies stream bits [k*b, k*b + b), and
+ *   stream bit i is bit (i mod 32) of word floor(i / 32) of the row.  Rows are
+ *   contiguous (row n starts at word n*K*b/32).
+ *   Each run of `group_size` consecutive k of a row shares one fp16 scale s
+ *   and one fp16 min m, stored as two arrays [N][K/group_size] row-major.
+ *   The weight is w[n][k] = s[n][k/group_size] * q[n][k] + m[n][k/group_size].
+ *   Activations x are fp16 [M][K] row-major; outputs y are fp32 [M][N]
+ *   row-major:  y[i][n] = sum_k w[n][k] * x[i][k].
+ *
+ * Requirements checked on the host before anything is launched:
+ *   bits in {2, 3, 4, 6, 8}; group_size a positive multiple of 32;
+ *   k >= 32 and k a multiple of group_size; n >= 0, m >= 0 (0 is a no-op);
+ *   weight, activation and output pointers 16-byte aligned; scale and min
+ *   pointers 2-byte aligned; non-NULL pointers wherever work is to be done.
+ *   A failed check returns a status, writes nothing and launches nothing;
+ *   qmm_last_error() then holds a one-line explanation (thread-local).
+ *
+ * Memory and streams:
+ *   Every pointer argument except those marked "host" is a device pointer,
+ *   owned by the caller.  The library allocates no device memory, frees none
+ *   and keeps no per-call state.  Calls are asynchronous on `stream`
+ *   (a hipStream_t passed as void*; NULL means the null stream); a kernel
+ *   fault shows up at the caller's next synchronization.  Results are
+ *   deterministic: no floating-point atomics; every output element is summed
+ *   in a fixed order that depends only on the shape.
+ *   QMM_ERR_DEVICE is returned when the HIP runtime reports an error at
+ *   launch time, or when no GPU is present.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMM_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define QMM_API __attribute__((visibility("default")))
+#else
+#define QMM_API
+#endif
+
+typedef enum qmm_status {
+    QMM_OK = 0,
+    QMM_ERR_INVALID_ARGUMENT = 1, /* shape, size or NULL pointer problem      */
+    QMM_ERR_UNSUPPORTED = 2,      /* valid request this build does not cover  */
+    QMM_ERR_MISALIGNED = 3,       /* pointer alignment below the requirement  */
+    QMM_ERR_DEVICE = 4            /* HIP runtime error at launch / no device  */
+} qmm_status;
+
+/* Decode GEMV (M = 1): y[n] = sum_k (s*q + m)[n][k] * x[k].
+ * Pages: "BaseRT claims fastest Apple Silicon inference", section "What
+ * BaseRT does differently" (dedicated GEMV kernels for decode where M = 1,
+ * dequantization inline in the compute loop).
+ *   w_packed  uint32 [n][k*bits/32]      scales, mins  fp16 [n][k/group_size]
+ *   x         fp16   [k]                 y             fp32 [n] (written)     */
+QMM_API qmm_status qmm_gemv(const void *w_packed, const void *scales, const void *mins,
+                    const void *x, float *y, int64_t n, int64_t k,
+                    int bits, int group_size, void *stream);
+
+/* Prefill GEMM (M >= 1): y[i][n] = sum_k (s*q + m)[n][k] * x[i][k].
+ * Pages: "BaseRT claims fastest Apple Silicon inference", section "What
+ * BaseRT does differently" (GEMM kernels for prefill where M > 1); "BaseRT:
+ * Best-in-Class LLM Inference on Apple Silicon via Native Metal", section
+ * "Metodologia" (tiled prefill GEMM on the GPU's matrix units).
+ * The weights are dequantized to fp16 tiles and multiplied on fp16 matrix
+ * cores with fp32 accumulation.  Small m is routed to the bandwidth-bound
+ * multi-row GEMV kernel.
+ *   x  fp16 [m][k]      y  fp32 [m][n] (written)
+ *   workspace: optional device scratch (may be NULL / 0 bytes).  When the
+ *   shape leaves the GPU under-filled, up to qmm_gemm_workspace_bytes() of it
+ *   is used to split the K loop; with less, the split shrinks to what fits
+ *   (no split with none).  Contents on return are unspecified.             */
+QMM_API qmm_status qmm_gemm(const void *w_packed, const void *scales, const void *mins,
+                    const void *x, float *y, int64_t m, int64_t n, int64_t k,
+                    int bits, int group_size, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace that let qmm_gemm use its preferred K split for this
+ * shape on the current device (0 when it would not split).  Host only.     */
+QMM_API size_t qmm_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits,
+                                int group_size);
+
+/* Mixture-of-experts projection over rows grouped by expert.
+ * Pages: "BaseRT claims fastest Apple Silicon inference", section "Where the
+ * wins land, and where they don't" (MoE decode and prefill; routing handled
+ * without branching in the hot path); "BaseRT: Best-in-Class LLM Inference on
+ * Apple Silicon via Native Metal", section "Resultados" (MoE prefill).
+ *   w_packed  uint32 [n_experts][n][k*bits/32]  (experts stacked)
+ *   scales, mins fp16 [n_experts][n][k/group_size]
+ *   expert_offsets int32 [n_experts + 1] (device): rows of expert e are
+ *     p in [expert_offsets[e], expert_offsets[e+1]); non-decreasing, from 0
+ *     to p_rows.
+ *   x fp16 [x_rows_count][k]; x_rows int32 [p_rows] (device) or NULL:
+ *     row p of the product reads activation row x_rows[p] (row p if NULL).
+ *   y fp32 [p_rows][n] (written): y[p][j] = sum_k w_e[j][k] * x[row(p)][k].
+ * Rows whose activation index is outside [0, x_rows_count) are written as
+ * NaN (nothing is read out of bounds); output rows that no expert range
+ * covers are left untouched.  Offsets are clamped to [0, p_rows].  Routing
+ * weights are not applied.                                                 */
+QMM_API qmm_status qmm_moe_gemm(const void *w_packed, const void *scales, const void *mins,
+                        const void *x, const int32_t *x_rows, int64_t x_rows_count,
+                        const int32_t *expert_offsets, float *y, int64_t p_rows,
+                        int64_t n_experts, int64_t n, int64_t k, int bits,
+                        int group_size, void *stream);
+
+/* Codes as bytes: codes[n][k] = q[n][k] (uint8).  Bit-exact view of the
+ * packed format, used to check the GPU's bit extraction.                   */
+QMM_API qmm_status qmm_unpack(const void *w_packed, uint8_t *codes, int64_t n, int64_t k,
+                      int bits, void *stream);
+
+/* Launch plan the library would use (host only, no device call): which
+ * kernel variant, grid and block.  `op` is 0 for qmm_gemv, 1 for qmm_gemm,
+ * 2 for qmm_moe_gemm (m = rows per expert bound).  cu_count <= 0 means
+ * "query the current device" (then this does call the runtime).            */
+typedef struct qmm_plan {
+    int32_t variant;       /* library-internal variant id                   */
+    int32_t lanes_per_row; /* GEMV: lanes cooperating on one output row     */
+    int32_t units_per_lane;/* GEMV: 64- or 32-code units per lane per pass  */
+    int32_t rows_per_iter; /* GEMV: rows per lane slot per loop iteration   */
+    int32_t unit_codes;    /* GEMV: codes per unit (64 or 32)               */
+    int32_t split_k;       /* GEMM: K split (1 = none)                      */
+    int32_t tile_m, tile_n;/* GEMM: block tile                              */
+    int64_t grid;          /* work-groups launched                          */
+    int32_t block;         /* threads per work-group                        */
+    int32_t reserved[5];
+} qmm_plan;
+
+QMM_API qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits,
+                        int group_size, int cu_count, size_t workspace_bytes,
+                        qmm_plan *plan /* host */);
+
+QMM_API const char *qmm_status_string(qmm_status s);
+QMM_API const char *qmm_last_error(void);   /* thread-local; "" when none */
+QMM_API int qmm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

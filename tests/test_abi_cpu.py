@@ -1,0 +1,176 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, rejects bad arguments before touching a device, and plans launches
+from integers alone."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemm_qmm_gemv_amd as qmm
+from gemm_qmm_gemv_amd import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+A16 = 0x10000  # a 16-byte aligned stand-in address; never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(qmm.library_path()):
+        from gemm_qmm_gemv_amd import build
+        build.build()
+    return qmm.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^QMM_API\s+[\w\s\*]+?\b(qmm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_python_surface():
+    assert sorted(qmm.EXPORTED_SYMBOLS) == header_functions()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+    assert qmm.qmm_abi_version() == 1
+
+
+def test_exports_are_only_the_abi(lib):
+    # nm -D lists the dynamic symbols; every qmm_ symbol must be declared.
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", qmm.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if " T qmm_" in ln})
+    assert exported == header_functions()
+
+
+def test_status_strings(lib):
+    assert qmm.qmm_status_string(0) == "QMM_OK"
+    assert qmm.qmm_status_string(3) == "QMM_ERR_MISALIGNED"
+    assert qmm.qmm_status_string(99) == "QMM_ERR_UNKNOWN"
+
+
+def _gemv(lib, w=A16, s=A16, m=A16, x=A16, y=A16, n=64, k=128, bits=4, g=64):
+    p = ctypes.c_void_p
+    return lib.qmm_gemv(p(w), p(s), p(m), p(x), p(y), n, k, bits, g, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(bits=5), qmm.QMM_ERR_UNSUPPORTED),
+    (dict(bits=7), qmm.QMM_ERR_UNSUPPORTED),
+    (dict(bits=1), qmm.QMM_ERR_INVALID_ARGUMENT),
+    (dict(bits=9), qmm.QMM_ERR_INVALID_ARGUMENT),
+    (dict(g=48), qmm.QMM_ERR_INVALID_ARGUMENT),
+    (dict(g=0), qmm.QMM_ERR_INVALID_ARGUMENT),
+    (dict(k=96, g=64), qmm.QMM_ERR_INVALID_ARGUMENT),
+    (dict(k=0), qmm.QMM_ERR_INVALID_ARGUMENT),
+    (dict(n=-1), qmm.QMM_ERR_INVALID_ARGUMENT),
+    (dict(w=0), qmm.QMM_ERR_INVALID_ARGUMENT),
+    (dict(x=0), qmm.QMM_ERR_INVALID_ARGUMENT),
+    (dict(w=A16 + 4), qmm.QMM_ERR_MISALIGNED),
+    (dict(x=A16 + 8), qmm.QMM_ERR_MISALIGNED),
+    (dict(y=A16 + 4), qmm.QMM_ERR_MISALIGNED),
+    (dict(s=A16 + 1), qmm.QMM_ERR_MISALIGNED),
+    (dict(n=0, w=0, x=0), qmm.QMM_OK),
+])
+def test_gemv_argument_checks(lib, kwargs, status):
+    assert _gemv(lib, **kwargs) == status
+    if status != qmm.QMM_OK:
+        assert qmm.qmm_last_error() != ""
+
+
+def test_valid_call_without_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _gemv(lib) == qmm.QMM_ERR_DEVICE
+    assert "device" in qmm.qmm_last_error()
+
+
+def test_gemm_and_moe_argument_checks(lib):
+    p = ctypes.c_void_p
+    g = lib.qmm_gemm
+    assert g(p(A16), p(A16), p(A16), p(A16), p(A16), -1, 64, 128, 4, 64, None, 0, None) == \
+        qmm.QMM_ERR_INVALID_ARGUMENT
+    assert g(p(A16), p(A16), p(A16), p(A16), p(A16), 0, 64, 128, 4, 64, None, 0, None) == qmm.QMM_OK
+    assert g(p(A16), p(A16), p(A16), p(A16), p(A16), 8, 64, 128, 4, 64, None, 64, None) == \
+        qmm.QMM_ERR_INVALID_ARGUMENT  # bytes without a buffer
+    assert g(p(A16), p(A16), p(A16), p(A16), p(A16), 8, 64, 128, 4, 64, p(A16 + 4), 64, None) == \
+        qmm.QMM_ERR_MISALIGNED
+    mo = lib.qmm_moe_gemm
+    assert mo(p(A16), p(A16), p(A16), p(A16), None, 4, p(A16), p(A16), 8, 2, 64, 128, 4, 64, None) == \
+        qmm.QMM_ERR_INVALID_ARGUMENT  # no index and too few x rows
+    assert mo(p(A16), p(A16), p(A16), p(A16), None, 8, None, p(A16), 8, 2, 64, 128, 4, 64, None) == \
+        qmm.QMM_ERR_INVALID_ARGUMENT  # no offsets
+    assert mo(p(A16), p(A16), p(A16), p(A16), None, 8, p(A16 + 2), p(A16), 8, 2, 64, 128, 4, 64,
+              None) == qmm.QMM_ERR_MISALIGNED
+    assert mo(p(A16), p(A16), p(A16), p(A16), None, 8, p(A16), p(A16), 0, 2, 64, 128, 4, 64, None) == \
+        qmm.QMM_OK
+    assert lib.qmm_unpack(p(A16), p(A16 + 8), 4, 64, 4, None) == qmm.QMM_ERR_MISALIGNED
+    assert lib.qmm_unpack(p(A16), p(A16), 4, 64, 5, None) == qmm.QMM_ERR_UNSUPPORTED
+
+
+# ---- launch planning (host integer logic) -----------------------------------------
+
+ALL_DECODE_SHAPES = sorted({(n, k) for _, n, k in configs.QWEN3_06B_PROJ + [configs.QWEN3_06B_LM_HEAD]}
+                           | {(n, k) for _, n, k in configs.LLAMA32_3B_PROJ}
+                           | {(configs.SINGLE_Q4["n"], configs.SINGLE_Q4["k"])}
+                           | {(n, k) for _, n, k in configs.MOE_PROJ})
+
+
+@pytest.mark.parametrize("bits", (2, 3, 4, 6, 8))
+@pytest.mark.parametrize("n,k", ALL_DECODE_SHAPES + [(5, 16384), (7, 96), (1, 64)])
+@pytest.mark.parametrize("group", (64, 32, 128))
+def test_gemv_plan_covers_the_row(lib, bits, n, k, group):
+    if k % group:
+        pytest.skip("k not a multiple of the group")
+    pl = qmm.qmm_get_plan(0, 1, n, k, bits, group, cu_count=256)
+    unit = pl["unit_codes"]
+    assert unit == (64 if group % 64 == 0 else 32)
+    assert pl["block"] == 256
+    cover = pl["lanes_per_row"] * pl["units_per_lane"] * unit
+    assert pl["multipass"] == (cover < k)
+    assert 64 % pl["lanes_per_row"] == 0
+    slots = 64 // pl["lanes_per_row"]
+    rows_per_block = 4 * slots * pl["rows_per_iter"]
+    # Enough work-groups to cover the rows, no more than the row batches need.
+    assert 1 <= pl["grid"] <= (n + rows_per_block - 1) // rows_per_block + 1
+    # Weight bytes in flight per lane per iteration stay modest.
+    assert pl["rows_per_iter"] * pl["units_per_lane"] * unit * bits // 8 <= 256
+
+
+def test_gemv_plan_small_vs_large(lib):
+    small = qmm.qmm_get_plan(0, 1, 3072, 1024, 4, 64, cu_count=256)
+    large = qmm.qmm_get_plan(0, 1, 151936, 1024, 4, 64, cu_count=256)
+    assert small["rows_per_iter"] == 1      # latency-bound: widest grid
+    assert large["rows_per_iter"] > 1       # bandwidth-bound: more bytes per lane
+    assert large["grid"] <= 256 * 32 // 4   # persistent-sized grid
+
+
+@pytest.mark.parametrize("m", (3, 64, 128, 512, 1000))
+@pytest.mark.parametrize("n,k", [(512, 2048), (2048, 2048), (8192, 2048), (2048, 8192)])
+def test_gemm_plan(lib, m, n, k):
+    unlimited = 1 << 40
+    pl = qmm.qmm_get_plan(1, m, n, k, 4, 64, cu_count=256, workspace_bytes=unlimited)
+    assert pl["variant"] == 2
+    assert pl["tile_m"] in (64, 128) and pl["tile_n"] == 128
+    tiles = -(-m // pl["tile_m"]) * -(-n // 128)
+    assert pl["grid"] >= tiles * pl["split_k"]
+    assert 1 <= pl["split_k"] <= 16
+    if tiles >= 256:
+        assert pl["split_k"] == 1
+    none = qmm.qmm_get_plan(1, m, n, k, 4, 64, cu_count=256, workspace_bytes=0)
+    assert none["split_k"] == 1
+
+
+def test_small_m_routes(lib):
+    assert qmm.qmm_get_plan(1, 1, 256, 1024, 4, 64, cu_count=256)["variant"] == 0
+    assert qmm.qmm_get_plan(1, 2, 256, 1024, 4, 64, cu_count=256)["variant"] == 1
+    assert qmm.qmm_get_plan(1, 3, 256, 1024, 4, 64, cu_count=256)["variant"] == 2
+    assert qmm.qmm_get_plan(2, 16, 768, 2048, 4, 64, cu_count=256)["variant"] == 1

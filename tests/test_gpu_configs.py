@@ -1,0 +1,69 @@
+"""Full-size decode workloads on the GPU, in the launch configuration the
+benchmark times, checked against the oracle on sampled outputs."""
+import numpy as np
+import pytest
+
+import oracle
+from gemm_qmm_gemv_amd import configs, inputs
+from tests.gpu_util import announce, assert_within
+
+pytestmark = pytest.mark.gpu
+
+
+def _gemv_device(q, x):
+    import torch
+    from gemm_qmm_gemv_amd import tensors
+    dq = tensors.upload_matrix(q)
+    y = tensors.gemv(dq, tensors.device_tensor(x))
+    torch.cuda.synchronize()
+    out = y.cpu().numpy()
+    del dq, y
+    return out
+
+
+def _sample_rows(n, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, n - 1, n // 2], rng.integers(0, n, count)]))
+    return rows.astype(np.int64)
+
+
+def _check(q, x, y, label, full_limit=4_000_000):
+    n, k, bits, group = q["n"], q["k"], q["bits"], q["group"]
+    if n * k <= full_limit:
+        y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, group)
+        assert_within(y, y_ref, a_ref, label)
+    else:
+        rn = _sample_rows(n, 384, n)
+        y_ref, a_ref = oracle.qmm_sample(q["w"], q["scales"], q["mins"], x, k, bits, group,
+                                         np.zeros_like(rn), rn)
+        assert_within(y[rn], y_ref, a_ref, label + " (sampled)")
+        assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("proj", list(range(len(configs.QWEN3_06B_PROJ))) + ["lm_head"])
+def test_qwen3_decode_projection(proj):
+    """Qwen3-0.6B-shaped decode projections (layer 0 and the LM head)."""
+    if proj == "lm_head":
+        layer, j = configs.QWEN3_06B_LAYERS, 0
+        name, n, k = configs.QWEN3_06B_LM_HEAD
+    else:
+        layer, j = 0, proj
+        name, n, k = configs.QWEN3_06B_PROJ[proj]
+    q = inputs.quantized_matrix(n, k, 4, configs.GROUP, key=(configs.CFG_DECODE_SET, layer, j, 4))
+    x = inputs.activation_rows(1, k, key=(configs.CFG_DECODE_SET, layer, j, 4))[0]
+    announce("decode-set", name, n, k)
+    y = _gemv_device(q, x)
+    _check(q, x, y, "qwen3 %s %dx%d" % (name, n, k))
+
+
+@pytest.mark.parametrize("bits", configs.SWEEP_BITS)
+@pytest.mark.parametrize("proj", [p[0] for p in configs.LLAMA32_3B_PROJ])
+def test_llama3b_sweep(bits, proj):
+    """Llama-3.2-3B-shaped GEMVs at every bit width."""
+    j = [p[0] for p in configs.LLAMA32_3B_PROJ].index(proj)
+    _, n, k = configs.LLAMA32_3B_PROJ[j]
+    q = inputs.quantized_matrix(n, k, bits, configs.GROUP, key=(configs.CFG_SWEEP, 0, j, bits))
+    x = inputs.activation_rows(1, k, key=(configs.CFG_SWEEP, 0, j, bits))[0]
+    announce("sweep", bits, proj, n, k)
+    y = _gemv_device(q, x)
+    _check(q, x, y, "llama3b b%d %s %dx%d" % (bits, proj, n, k), full_limit=1_000_000)

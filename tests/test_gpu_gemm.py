@@ -1,0 +1,123 @@
+"""Prefill GEMM (qmm_gemm) on the GPU vs the CPU oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from gemm_qmm_gemv_amd import configs, inputs
+from tests.gpu_util import announce, assert_within
+
+pytestmark = pytest.mark.gpu
+
+BITS = (2, 3, 4, 6, 8)
+
+
+def _run_gemm(q, x, workspace="auto"):
+    import torch
+    from gemm_qmm_gemv_amd import tensors
+    dq = tensors.upload_matrix(q)
+    xd = tensors.device_tensor(x)
+    ws = None if workspace == "auto" else workspace
+    if workspace is None:
+        ws = torch.empty(0, dtype=torch.uint8, device="cuda")
+    y = tensors.gemm(dq, xd, workspace=ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("m,n,k,group", [
+    (2, 130, 256, 64), (3, 64, 128, 64), (5, 200, 1024, 64), (64, 128, 512, 64),
+    (100, 300, 1024, 64), (128, 512, 2048, 64), (130, 257, 320, 64), (256, 640, 768, 32),
+    (17, 129, 4096, 128)])
+def test_gemm_parity(bits, m, n, k, group):
+    q = inputs.quantized_matrix(n, k, bits, group, key=(60, m, n, k, bits, group))
+    x = inputs.activation_rows(m, k, key=(60, m, n, k, bits, group))
+    announce("gemm", bits, m, n, k, group)
+    y = _run_gemm(q, x)
+    y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, group)
+    assert_within(y, y_ref, a_ref, "gemm b%d m%d %dx%d g%d" % (bits, m, n, k, group))
+
+
+@pytest.mark.parametrize("bits", (4, 8))
+def test_gemm_without_workspace_matches_split(bits):
+    # Same product with and without a K split: both within tolerance, and the
+    # unsplit result is deterministic run to run.
+    m, n, k = 128, 512, 4096
+    q = inputs.quantized_matrix(n, k, bits, 64, key=(61, bits))
+    x = inputs.activation_rows(m, k, key=(61, bits))
+    announce("gemm-split-vs-none", bits)
+    y_split = _run_gemm(q, x)
+    y_none = _run_gemm(q, x, workspace=None)
+    y_none2 = _run_gemm(q, x, workspace=None)
+    assert np.array_equal(y_none, y_none2)
+    y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, 64)
+    assert_within(y_split, y_ref, a_ref, "gemm split b%d" % bits)
+    assert_within(y_none, y_ref, a_ref, "gemm no-split b%d" % bits)
+
+
+def test_gemm_exact_integer():
+    # scale 1, min 0, integer x: fp16 weights are exact small integers, MFMA
+    # products and fp32 sums stay below 2^24 -> exact.
+    for bits in BITS:
+        m, n, k = 96, 160, 2048
+        rng = inputs.rng_for(62, bits)
+        w = inputs.packed_words(rng, n, k, bits)
+        s = np.ones((n, k // 64), dtype=np.float16)
+        mn = np.zeros((n, k // 64), dtype=np.float16)
+        x = rng.integers(-2, 3, size=(m, k)).astype(np.float16)
+        q = {"w": w, "scales": s, "mins": mn, "n": n, "k": k, "bits": bits, "group": 64}
+        announce("gemm-exact-int", bits)
+        y = _run_gemm(q, x)
+        y_ref, _ = oracle.qmm(w, s, mn, x, n, k, bits, 64)
+        assert np.array_equal(y.astype(np.float64), y_ref), bits
+
+
+def test_gemm_identity_activation_gives_fp16_weights():
+    # X = I: Y = fp16(s*q + m)^T, the dequantized tile exactly as staged.
+    k, n, bits = 128, 96, 4
+    q = inputs.quantized_matrix(n, k, bits, 64, key=(63,))
+    x = np.eye(k, dtype=np.float16)
+    announce("gemm-identity")
+    y = _run_gemm(q, x)
+    wd = oracle.dequant(q["w"], q["scales"], q["mins"], n, k, bits, 64)
+    assert np.array_equal(y, wd.T.astype(np.float16).astype(np.float32))
+
+
+def test_gemm_rows_match_gemv():
+    # Row i of a GEMM is the GEMV of x[i] (within tolerance of each other and
+    # of the oracle; different kernels, so not bit-identical).
+    import torch
+    from gemm_qmm_gemv_amd import tensors
+    m, n, k, bits = 4, 300, 1024, 4
+    q = inputs.quantized_matrix(n, k, bits, 64, key=(64,))
+    x = inputs.activation_rows(m, k, key=(64,))
+    announce("gemm-rows-vs-gemv")
+    dq = tensors.upload_matrix(q)
+    y = tensors.gemm(dq, tensors.device_tensor(x))
+    ys = [tensors.gemv(dq, tensors.device_tensor(x[i])) for i in range(m)]
+    torch.cuda.synchronize()
+    y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, 64)
+    for i in range(m):
+        assert_within(ys[i].cpu().numpy(), y_ref[i], a_ref[i], "gemv row %d" % i)
+    assert_within(y.cpu().numpy(), y_ref, a_ref, "gemm rows")
+
+
+@pytest.mark.parametrize("m", configs.PREFILL_M)
+@pytest.mark.parametrize("proj", configs.LLAMA32_1B_PROJ, ids=[p[0] for p in configs.LLAMA32_1B_PROJ])
+def test_gemm_prefill_config_sampled(m, proj):
+    """Llama-3.2-1B-shaped prefill at full size, in the launch configuration the
+    benchmark times; 256 sampled outputs checked against the oracle."""
+    name, n, k = proj
+    j = [p[0] for p in configs.LLAMA32_1B_PROJ].index(name)
+    q = inputs.quantized_matrix(n, k, 4, configs.GROUP, key=(configs.CFG_PREFILL, 0, j, 4))
+    x = inputs.activation_rows(m, k, key=(configs.CFG_PREFILL, 0, j, 4, m))
+    announce("gemm-prefill", m, name, n, k)
+    y = _run_gemm(q, x)
+    rng = np.random.default_rng(7)
+    rm = rng.integers(0, m, 256)
+    rn = rng.integers(0, n, 256)
+    rm[:4] = [0, m - 1, 0, m - 1]
+    rn[:4] = [0, 0, n - 1, n - 1]
+    y_ref, a_ref = oracle.qmm_sample(q["w"], q["scales"], q["mins"], x, k, 4, configs.GROUP, rm, rn)
+    assert_within(y[rm, rn], y_ref, a_ref, "prefill m%d %s" % (m, name))
+    assert np.all(np.isfinite(y))

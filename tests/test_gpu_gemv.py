@@ -1,0 +1,143 @@
+"""Decode GEMV (qmm_gemv) and code unpacking on the GPU vs the CPU oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from gemm_qmm_gemv_amd import configs, inputs
+from tests.gpu_util import announce, assert_within
+
+pytestmark = pytest.mark.gpu
+
+BITS = (2, 3, 4, 6, 8)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _run_gemv(q, x):
+    torch = _torch()
+    from gemm_qmm_gemv_amd import tensors
+    dq = tensors.upload_matrix(q)
+    xd = tensors.device_tensor(x)
+    y = tensors.gemv(dq, xd)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("n,k", [(1, 64), (3, 128), (17, 192), (1000, 1024), (257, 3072),
+                                 (64, 8192), (33, 16384), (5, 768)])
+def test_unpack_bit_exact(bits, n, k):
+    from gemm_qmm_gemv_amd import tensors
+    torch = _torch()
+    q = inputs.quantized_matrix(n, k, bits, 64, key=(50, n, k, bits))
+    announce("unpack", bits, n, k)
+    dq = tensors.upload_matrix(q)
+    codes = tensors.unpack(dq)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), oracle.unpack(q["w"], n, k, bits))
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("n,k,group", [
+    (1, 64, 64), (7, 64, 32), (17, 192, 64), (3072, 1024, 64), (1000, 3072, 64),
+    (300, 2048, 128), (129, 768, 64), (96, 8192, 64), (40, 16384, 64), (50, 96, 32),
+    (61, 4160, 64), (1031, 1024, 64)])
+def test_gemv_parity(bits, n, k, group):
+    q = inputs.quantized_matrix(n, k, bits, group, key=(51, n, k, bits, group))
+    x = inputs.activation_rows(1, k, key=(51, n, k, bits, group))[0]
+    announce("gemv", bits, n, k, group)
+    y = _run_gemv(q, x)
+    y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, group)
+    assert_within(y, y_ref, a_ref, "gemv b%d %dx%d g%d" % (bits, n, k, group))
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_gemv_exact_integer(bits):
+    # scale 1, min 0, integer x in [-2, 2]: every partial sum is an integer
+    # below 2^24, so the GPU result must equal the oracle exactly.
+    n, k = 300, 4096
+    rng = inputs.rng_for(52, bits)
+    w = inputs.packed_words(rng, n, k, bits)
+    s = np.ones((n, k // 64), dtype=np.float16)
+    mn = np.zeros((n, k // 64), dtype=np.float16)
+    x = rng.integers(-2, 3, size=k).astype(np.float16)
+    q = {"w": w, "scales": s, "mins": mn, "n": n, "k": k, "bits": bits, "group": 64}
+    announce("gemv-exact-int", bits)
+    y = _run_gemv(q, x)
+    y_ref, _ = oracle.qmm(w, s, mn, x, n, k, bits, 64)
+    assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_gemv_one_hot(bits):
+    # x = e_j: y[n] = s*q[n,j] + m, one rounding to fp32 of an exact value.
+    n, k = 200, 1024
+    q = inputs.quantized_matrix(n, k, bits, 64, key=(53, bits))
+    for j in (0, 1, 5, 31, 32, 63, 64, 500, 1023):
+        x = np.zeros(k, dtype=np.float16)
+        x[j] = 1.0
+        announce("gemv-one-hot", bits, j)
+        y = _run_gemv(q, x)
+        y_ref, _ = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, 64)
+        assert np.array_equal(y, y_ref.astype(np.float32)), (bits, j)
+
+
+@pytest.mark.parametrize("bits", (3, 4, 8))
+def test_gemv_exact_invariants_and_determinism(bits):
+    n, k = 500, 2048
+    q = inputs.quantized_matrix(n, k, bits, 64, key=(54, bits))
+    x = inputs.activation_rows(1, k, key=(54, bits))[0]
+    announce("gemv-invariants", bits)
+    y = _run_gemv(q, x)
+    y_again = _run_gemv(q, x)
+    assert np.array_equal(y, y_again)
+    q2 = dict(q)
+    q2["scales"] = (q["scales"].astype(np.float32) * 2).astype(np.float16)
+    q2["mins"] = (q["mins"].astype(np.float32) * 2).astype(np.float16)
+    assert np.array_equal(_run_gemv(q2, x), 2 * y)
+    assert np.array_equal(_run_gemv(q, -x), -y)
+
+
+def test_gemv_constant_codes_closed_form():
+    # Codes all equal c: y = sum_g (c s_g + m_g) sum_{k in g} x_k.
+    n, k, group = 64, 1024, 64
+    rng = inputs.rng_for(55)
+    s, mn = inputs.scales_mins(rng, n, k, group)
+    x = inputs.activations(rng, 1, k)[0]
+    xs = x.astype(np.float64).reshape(k // group, group).sum(axis=1)
+    for bits in BITS:
+        for c in (0, (1 << bits) - 1):
+            w = oracle.pack(np.full((n, k), c, dtype=np.uint8), bits)
+            q = {"w": w, "scales": s, "mins": mn, "n": n, "k": k, "bits": bits, "group": group}
+            announce("gemv-constant", bits, c)
+            y = _run_gemv(q, x)
+            y_cf = (c * s.astype(np.float64) + mn.astype(np.float64)) @ xs
+            a = np.abs(c * s.astype(np.float64) + mn.astype(np.float64)) @ np.abs(
+                x.astype(np.float64).reshape(k // group, group)).sum(axis=1)
+            assert_within(y, y_cf, a, "constant b%d c%d" % (bits, c))
+
+
+def test_gemv_single_q4_config():
+    """The single Q4 GEMV workload, full size, every output checked."""
+    c = configs.SINGLE_Q4
+    q = inputs.quantized_matrix(c["n"], c["k"], 4, configs.GROUP, key=(configs.CFG_SINGLE, 0, 0, 4))
+    x = inputs.activation_rows(1, c["k"], key=(configs.CFG_SINGLE, 0, 0, 4))[0]
+    announce("gemv-config-single", c)
+    y = _run_gemv(q, x)
+    y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, c["n"], c["k"], 4, configs.GROUP)
+    assert_within(y, y_ref, a_ref, "single q4 3072x1024")
+
+
+def test_gemv_zero_rows_is_noop():
+    torch = _torch()
+    from gemm_qmm_gemv_amd import qmm_gemv
+    y = torch.full((4,), 7.0, device="cuda")
+    x = torch.zeros(64, dtype=torch.float16, device="cuda")
+    w = torch.zeros(64, dtype=torch.int32, device="cuda")
+    s = torch.zeros(4, dtype=torch.float16, device="cuda")
+    qmm_gemv(w, s, s, x, y, 0, 64, 4, 64)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)

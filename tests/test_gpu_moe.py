@@ -1,0 +1,97 @@
+"""Mixture-of-experts projections (qmm_moe_gemm) on the GPU vs the CPU oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from gemm_qmm_gemv_amd import configs, inputs
+from tests.gpu_util import announce, assert_within
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_moe(st, x, x_rows, offsets, p_rows):
+    import torch
+    from gemm_qmm_gemv_amd import tensors
+    dst = tensors.upload_matrix(st)
+    xd = tensors.device_tensor(x)
+    xr = tensors.device_tensor(np.asarray(x_rows, dtype=np.int32)) if x_rows is not None else None
+    off = tensors.device_tensor(np.asarray(offsets, dtype=np.int32))
+    y = torch.full((p_rows, st["n"]), -7.0, dtype=torch.float32, device="cuda")
+    tensors.moe(dst, xd, xr, off, p_rows, y=y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("tokens", configs.MOE["tokens"])
+@pytest.mark.parametrize("proj", configs.MOE_PROJ, ids=[p[0] for p in configs.MOE_PROJ])
+def test_moe_config(tokens, proj):
+    """Qwen3-30B-A3B-shaped experts, top-8 of 128, full size, every output."""
+    name, n, k = proj
+    j = [p[0] for p in configs.MOE_PROJ].index(name)
+    e, top = configs.MOE["n_experts"], configs.MOE["top_k"]
+    st = inputs.stacked_experts(e, n, k, 4, configs.GROUP, key=(configs.CFG_MOE, j))
+    r = inputs.routing(tokens, e, top, key=(configs.CFG_MOE, tokens))
+    p = tokens * top
+    if name == "down_proj":
+        # The down projection reads one activation row per (token, expert) pair.
+        x = inputs.activation_rows(p, k, key=(configs.CFG_MOE, tokens, 9))
+        x_rows = None
+    else:
+        x = inputs.activation_rows(tokens, k, key=(configs.CFG_MOE, tokens))
+        x_rows = r["pair_token"]
+    announce("moe", tokens, name)
+    y = _run_moe(st, x, x_rows, r["offsets"], p)
+    y_ref, a_ref = oracle.moe(st["w"], st["scales"], st["mins"], x, x_rows, r["offsets"],
+                              e, n, k, 4, configs.GROUP)
+    assert_within(y, y_ref, a_ref, "moe T%d %s" % (tokens, name))
+
+
+@pytest.mark.parametrize("bits", (2, 3, 4, 6, 8))
+def test_moe_uneven_segments(bits):
+    # Experts with 0, 1, 2, 5 and 9 rows, ragged N, an out-of-range index.
+    e, n, k = 7, 70, 320
+    st = inputs.stacked_experts(e, n, k, bits, 64, key=(70, bits))
+    counts = [0, 1, 2, 0, 5, 9, 3]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    p = int(offsets[-1])
+    t = 6
+    x = inputs.activation_rows(t, k, key=(70, bits))
+    rng = inputs.rng_for(70, bits, 1)
+    x_rows = rng.integers(0, t, size=p).astype(np.int32)
+    announce("moe-uneven", bits)
+    y = _run_moe(st, x, x_rows, offsets, p)
+    y_ref, a_ref = oracle.moe(st["w"], st["scales"], st["mins"], x, x_rows, offsets, e, n, k, bits, 64)
+    assert_within(y, y_ref, a_ref, "moe uneven b%d" % bits)
+    # An activation index out of range gives a NaN row and nothing else changes.
+    bad = x_rows.copy()
+    bad[3] = t + 5
+    y_bad = _run_moe(st, x, bad, offsets, p)
+    assert np.all(np.isnan(y_bad[3]))
+    keep = np.ones(p, bool)
+    keep[3] = False
+    assert np.array_equal(y_bad[keep], y[keep])
+
+
+def test_moe_rows_equal_per_expert_gemv():
+    # Each MoE row equals qmm_gemv on that expert's matrix (same kernel family,
+    # both checked against the oracle).
+    import torch
+    from gemm_qmm_gemv_amd import tensors
+    e, n, k, tokens = 16, 256, 2048, 3
+    st = inputs.stacked_experts(e, n, k, 4, 64, key=(71,))
+    r = inputs.routing(tokens, e, 4, key=(71,))
+    x = inputs.activation_rows(tokens, k, key=(71,))
+    p = tokens * 4
+    announce("moe-vs-gemv")
+    y = _run_moe(st, x, r["pair_token"], r["offsets"], p)
+    y_ref, a_ref = oracle.moe(st["w"], st["scales"], st["mins"], x, r["pair_token"], r["offsets"],
+                              e, n, k, 4, 64)
+    assert_within(y, y_ref, a_ref, "moe small")
+    for pi in range(p):
+        ex = int(r["pair_expert"][pi])
+        q = {"w": st["w"][ex], "scales": st["scales"][ex], "mins": st["mins"][ex],
+             "n": n, "k": k, "bits": 4, "group": 64}
+        dq = tensors.upload_matrix(q)
+        yg = tensors.gemv(dq, tensors.device_tensor(x[r["pair_token"][pi]]))
+        torch.cuda.synchronize()
+        assert_within(yg.cpu().numpy(), y_ref[pi], a_ref[pi], "gemv expert %d" % ex)
