@@ -1,0 +1,419 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized GEMV / GEMM hot path on one MI355X.
+
+Headline workload: the Qwen3-0.6B-shaped Q4 decode projection set (28 layers
+x {q, k, v, o, gate, up, down} + the 151936 x 1024 LM head, group 64, M = 1,
+597 M weights, 337.8 MB of compressed weights), synthetic seeded inputs
+resident in HBM.  One step = every GEMV of the set once, issued as one
+batched launch per K (K = 2048, 1024, 3072).  The headline value is the
+set's algorithmic bytes (compressed weights + fp16 x + fp32 y) per second.
+
+Also measured (outside the timed region, reported in the same JSON line):
+  * the roofline of the dominant kernel (the K = 1024 batched launch), from
+    HIP events around every one of its launches inside the timed region;
+  * the same set as 197 separate qmm_gemv launches replayed from a HIP graph;
+  * the set in decode dependency order (per layer: q|k|v, o, gate|up, down;
+    then the LM head) replayed from a HIP graph: per-token projection time;
+  * the LM head alone with four rotating copies (steady state);
+  * the single 3072 x 1024 Q4 GEMV;
+  * the Llama-3.2-3B-shaped bit-width sweep (Q2/Q3/Q4/Q6/Q8);
+  * Llama-3.2-1B-shaped prefill GEMMs at M = 128 and 512: TFLOP/s, % MFMA;
+  * Qwen3-30B-A3B-shaped MoE expert projections at 1 and 16 tokens;
+  * the CPU oracle on the host cores over the same projection set.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_FP16_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense fp16 flop/clk/CU
+METRIC = "Q4 dequant-GEMV HBM GB/s (% of peak); prefill qGEMM TFLOP/s (% MFMA)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_batched_q4_qwen3_decode_set.txt")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources; ties stored counter readings to a build."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gemm_qmm_gemv_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when missing or taken on different kernel sources."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for ln in f:
+                if ":" in ln:
+                    k, v = ln.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("kernel_source_sha256") != kernel_source_digest():
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """Average milliseconds of fn() over reps, HIP events on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def __call__(self, fn, reps=20, warmup=3):
+        t = self.torch
+        for _ in range(warmup):
+            fn()
+        t.cuda.synchronize()
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        t.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="headline only (for profiler runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the work would shard by output rows with no exchange; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gemm_qmm_gemv_amd as qmm
+    from gemm_qmm_gemv_amd import configs, inputs, tensors
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    qmm.load()
+    torch.cuda.set_device(0)
+    timer = Timer(torch)
+    G = configs.GROUP
+
+    # ---- headline workload: the decode projection set --------------------------
+    t0 = time.time()
+    mats, xs, ys = [], [], []
+    for layer, j, name, n, k in configs.decode_set():
+        key = (configs.CFG_DECODE_SET, layer, j, 4)
+        q = inputs.quantized_matrix(n, k, 4, G, key=key)
+        dq = tensors.upload_matrix(q)
+        x = tensors.device_tensor(inputs.activation_rows(1, k, key=key)[0])
+        mats.append((layer, name, dq))
+        xs.append(x)
+        ys.append(torch.empty(n, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    log("decode set generated and uploaded in %.1f s" % (time.time() - t0))
+    set_bytes = sum(configs.gemv_bytes(dq["n"], dq["k"], 4) for _, _, dq in mats)
+    set_weight_bytes = sum(configs.weight_bytes(dq["n"], dq["k"], 4) for _, _, dq in mats)
+
+    by_k = {}
+    for (layer, name, dq), x, y in zip(mats, xs, ys):
+        by_k.setdefault(dq["k"], []).append((dq, x, y))
+    batches = {k: tensors.GemvBatch(items, 4, G) for k, items in by_k.items()}
+    dom_k = max(by_k, key=lambda k: sum(configs.gemv_bytes(d["n"], d["k"], 4) for d, _, _ in by_k[k]))
+    dom_bytes = sum(configs.gemv_bytes(d["n"], d["k"], 4) for d, _, _ in by_k[dom_k])
+    order = [k for k in sorted(by_k) if k != dom_k]
+    plan = qmm.qmm_get_plan(3, 1, sum(d["n"] for d, _, _ in by_k[dom_k]), dom_k, 4, G)
+
+    evs = []
+
+    def step(record=False):
+        for k in order[:1]:
+            batches[k]()
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            batches[dom_k]()
+            b.record()
+            evs.append((a, b))
+        else:
+            batches[dom_k]()
+        for k in order[1:]:
+            batches[k]()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step(record=True)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    value = set_bytes / (ms_per_step * 1e-3) / 1e9
+    dom_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+    log("step %.3f us (wall %.3f us), %.1f GB/s; dominant K=%d launch %.3f us, %.1f GB/s"
+        % (ms_per_step * 1e3, wall / args.steps * 1e6, value, dom_k, dom_ms * 1e3, dom_gbs))
+
+    traffic = stored_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4 weights, fp16 x, fp32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": "qwen3_0.6b_q4_decode_projection_set",
+            "gemvs": len(mats), "layers": configs.QWEN3_06B_LAYERS, "hidden": 1024,
+            "lm_head": "151936x1024", "bits": 4, "group": G, "m": 1,
+            "weight_bytes": set_weight_bytes, "algorithmic_bytes_per_step": set_bytes,
+            "launches_per_step": len(by_k), "parallelism": "none (1 GPU)",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "kernel": "gemv_batched_kernel<4,64,%d,%d,%d> (K=%d launch)" % (
+                plan["lanes_per_row"], plan["units_per_lane"], plan["rows_per_iter"], dom_k),
+            "bound": "hbm",
+            "achieved": round(dom_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dom_bytes,
+            "avg_launch_us": round(dom_ms * 1e3, 3),
+        },
+    }
+
+    if not args.quick:
+        result["extras"] = extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys,
+                                  batches, set_bytes)
+    if not args.no_cpu_baseline and not args.quick:
+        result["cpu_baseline"] = cpu_baseline(np, configs, inputs, set_bytes)
+    print(json.dumps(result), flush=True)
+
+
+def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, batches, set_bytes):
+    G = configs.GROUP
+    out = {}
+
+    # 197 separate launches, replayed from a HIP graph.
+    def per_call():
+        for (layer, name, dq), x, y in zip(mats, xs, ys):
+            tensors.gemv(dq, x, y)
+    per_call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        per_call()
+    ms = timer(g.replay, reps=20)
+    out["decode_set_per_call_graph"] = {"us": round(ms * 1e3, 2),
+                                        "GBps": round(set_bytes / ms / 1e6, 1)}
+    log("per-call graph: %.1f us" % (ms * 1e3))
+
+    # Decode dependency order: per layer q|k|v, o, gate|up, down; then LM head.
+    stage_batches = []
+    per_layer = len(configs.QWEN3_06B_PROJ)
+    for layer in range(configs.QWEN3_06B_LAYERS):
+        base = layer * per_layer
+        item = lambda i: (mats[base + i][2], xs[base + i], ys[base + i])
+        for group_ in ((0, 1, 2), (3,), (4, 5), (6,)):
+            stage_batches.append(tensors.GemvBatch([item(i) for i in group_], 4, G))
+    lm = (mats[-1][2], xs[-1], ys[-1])
+
+    def dependent():
+        for b in stage_batches:
+            b()
+        tensors.gemv(lm[0], lm[1], lm[2])
+    dependent()
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        dependent()
+    ms = timer(g2.replay, reps=20)
+    out["decode_dependent_stages_graph"] = {
+        "launches": len(stage_batches) + 1, "per_token_us": round(ms * 1e3, 2),
+        "GBps": round(set_bytes / ms / 1e6, 1), "projection_tok_per_s": round(1e3 / ms, 1)}
+    log("dependent-stage graph: %.1f us" % (ms * 1e3))
+
+    # LM head alone, four rotating copies (352 MB > the 256 MB last-level cache).
+    name, n, k = configs.QWEN3_06B_LM_HEAD
+    copies = [mats[-1][2]] + [tensors.upload_matrix(inputs.quantized_matrix(n, k, 4, G, key=(90, c)))
+                              for c in range(3)]
+    yl = torch.empty(n, dtype=torch.float32, device="cuda")
+    idx = [0]
+
+    def lm_call():
+        tensors.gemv(copies[idx[0] % 4], xs[-1], yl)
+        idx[0] += 1
+    ms = timer(lm_call, reps=40)
+    b = configs.gemv_bytes(n, k, 4)
+    out["lm_head_151936x1024_q4"] = {"us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1),
+                                     "pct_peak": round(100 * b / ms / 1e6 / HBM_PEAK_GBS, 1)}
+    del copies
+    log("lm head: %.1f us" % (ms * 1e3))
+
+    # Single 3072 x 1024 Q4 GEMV.
+    c = configs.SINGLE_Q4
+    q = inputs.quantized_matrix(c["n"], c["k"], 4, G, key=(configs.CFG_SINGLE, 0, 0, 4))
+    dq = tensors.upload_matrix(q)
+    x = tensors.device_tensor(inputs.activation_rows(1, c["k"], key=(configs.CFG_SINGLE, 0, 0, 4))[0])
+    y = torch.empty(c["n"], dtype=torch.float32, device="cuda")
+    ms = timer(lambda: tensors.gemv(dq, x, y), reps=100)
+    b = configs.gemv_bytes(c["n"], c["k"], 4)
+    out["single_3072x1024_q4"] = {"us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1)}
+
+    # Bit-width sweep on Llama-3.2-3B shapes (rotating 2 copies of each).
+    sweep = {}
+    for bits in configs.SWEEP_BITS:
+        row = {}
+        for j, (pname, n, k) in enumerate(configs.LLAMA32_3B_PROJ):
+            if pname in ("k_proj", "o_proj", "up_proj"):
+                continue  # same shapes as v, q and gate
+            cps = [tensors.upload_matrix(inputs.quantized_matrix(n, k, bits, G, key=(configs.CFG_SWEEP, r, j, bits)))
+                   for r in range(2 if pname == "lm_head" else 4)]
+            xv = tensors.device_tensor(inputs.activation_rows(1, k, key=(configs.CFG_SWEEP, 0, j, bits))[0])
+            yv = torch.empty(n, dtype=torch.float32, device="cuda")
+            ii = [0]
+
+            def call():
+                tensors.gemv(cps[ii[0] % len(cps)], xv, yv)
+                ii[0] += 1
+            ms = timer(call, reps=20)
+            b = configs.gemv_bytes(n, k, bits)
+            row[pname] = {"us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1)}
+            del cps
+        sweep["q%d" % bits] = row
+        log("sweep q%d: lm_head %.0f GB/s" % (bits, row["lm_head"]["GBps"]))
+    out["llama3.2_3b_bit_sweep"] = sweep
+
+    # Prefill GEMMs (Llama-3.2-1B shapes).
+    pre = {}
+    for m in configs.PREFILL_M:
+        tot_flops, tot_ms = 0.0, 0.0
+        row = {}
+        for j, (pname, n, k) in enumerate(configs.LLAMA32_1B_PROJ):
+            q = inputs.quantized_matrix(n, k, 4, G, key=(configs.CFG_PREFILL, 0, j, 4))
+            dq = tensors.upload_matrix(q)
+            xm = tensors.device_tensor(inputs.activation_rows(m, k, key=(configs.CFG_PREFILL, 0, j, 4, m)))
+            ym = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            need = qmm.qmm_gemm_workspace_bytes(m, n, k, 4, G)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+            ms = timer(lambda: tensors.gemm(dq, xm, ym, workspace=ws), reps=30)
+            fl = 2.0 * m * n * k
+            tf = fl / ms / 1e9
+            pl = qmm.qmm_get_plan(1, m, n, k, 4, G, workspace_bytes=ws.numel())
+            row[pname] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
+                          "pct_mfma": round(100 * tf / MFMA_FP16_PEAK_TFLOPS, 2),
+                          "split_k": pl["split_k"], "tile_m": pl["tile_m"]}
+            tot_flops += fl
+            tot_ms += ms
+        tf = tot_flops / tot_ms / 1e9
+        pre["m%d" % m] = {"layer_us": round(tot_ms * 1e3, 2), "TFLOPs": round(tf, 1),
+                          "pct_mfma": round(100 * tf / MFMA_FP16_PEAK_TFLOPS, 2), "shapes": row}
+        log("prefill m=%d: %.1f TFLOP/s" % (m, tf))
+    out["prefill_llama3.2_1b_q4"] = pre
+
+    # MoE expert projections (Qwen3-30B-A3B shapes).
+    moe = {}
+    e, top = configs.MOE["n_experts"], configs.MOE["top_k"]
+    stacks = {}
+    for j, (pname, n, k) in enumerate(configs.MOE_PROJ):
+        stacks[pname] = tensors.upload_matrix(inputs.stacked_experts(e, n, k, 4, G, key=(configs.CFG_MOE, j)))
+    for tokens in configs.MOE["tokens"]:
+        r = inputs.routing(tokens, e, top, key=(configs.CFG_MOE, tokens))
+        p = tokens * top
+        distinct = int((np.diff(r["offsets"]) > 0).sum())
+        off = tensors.device_tensor(r["offsets"])
+        rows = tensors.device_tensor(r["pair_token"])
+        x_tok = tensors.device_tensor(inputs.activation_rows(tokens, 2048, key=(configs.CFG_MOE, tokens)))
+        x_pair = tensors.device_tensor(inputs.activation_rows(p, 768, key=(configs.CFG_MOE, tokens, 9)))
+        row = {}
+        tot_b, tot_ms = 0, 0.0
+        for pname, n, k in configs.MOE_PROJ:
+            st = stacks[pname]
+            yo = torch.empty((p, n), dtype=torch.float32, device="cuda")
+            if pname == "down_proj":
+                fn = lambda: tensors.moe(st, x_pair, None, off, p, y=yo)
+            else:
+                fn = lambda: tensors.moe(st, x_tok, rows, off, p, y=yo)
+            ms = timer(fn, reps=30)
+            b = distinct * configs.weight_bytes(n, k, 4) + 2 * p * k + 4 * p * n
+            row[pname] = {"us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1)}
+            tot_b += b
+            tot_ms += ms
+        moe["t%d" % tokens] = {"distinct_experts": distinct, "us": round(tot_ms * 1e3, 2),
+                               "GBps": round(tot_b / tot_ms / 1e6, 1), "proj": row}
+        log("moe T=%d: %.1f us" % (tokens, tot_ms * 1e3))
+    out["moe_qwen3_30b_a3b_q4"] = moe
+    return out
+
+
+def cpu_baseline(np, configs, inputs, set_bytes):
+    """The CPU oracle (C, fp64, OpenMP over rows) on the host cores, on a
+    bounded sample of the decode set: layer 0's seven projections and the
+    first 8192 rows of the LM head."""
+    import oracle
+    G = configs.GROUP
+    work = []
+    for j, (name, n, k) in enumerate(configs.QWEN3_06B_PROJ):
+        key = (configs.CFG_DECODE_SET, 0, j, 4)
+        work.append((inputs.quantized_matrix(n, k, 4, G, key=key), inputs.activation_rows(1, k, key=key)[0]))
+    name, n, k = configs.QWEN3_06B_LM_HEAD
+    key = (configs.CFG_DECODE_SET, configs.QWEN3_06B_LAYERS, 0, 4)
+    q = inputs.quantized_matrix(n, k, 4, G, key=key)
+    rows = 8192
+    q = dict(q, w=q["w"][:rows], scales=q["scales"][:rows], mins=q["mins"][:rows], n=rows)
+    work.append((q, inputs.activation_rows(1, k, key=key)[0]))
+    b = sum(configs.gemv_bytes(q["n"], q["k"], 4) for q, _ in work)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for q, x in work:
+            oracle.qmm(q["w"], q["scales"], q["mins"], x, q["n"], q["k"], 4, G)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 50:
+            break
+    gbs = reps * b / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "layer 0's 7 Q4 projections + LM head rows 0..8191 (%d bytes), %d passes in %.1f s"
+                      % (b, reps, el),
+            "seconds_per_decode_set": round(set_bytes / (gbs * 1e9), 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -18,6 +18,7 @@ import os
 __all__ = [
     "QmmError", "library_path", "load",
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
+    "qmm_gemv_batch_prepare", "qmm_gemv_batched", "GemvDesc",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
     "QMM_OK", "QMM_ERR_INVALID_ARGUMENT", "QMM_ERR_UNSUPPORTED", "QMM_ERR_MISALIGNED",
     "QMM_ERR_DEVICE", "EXPORTED_SYMBOLS",
@@ -31,6 +32,7 @@ QMM_ERR_DEVICE = 4
 
 EXPORTED_SYMBOLS = (
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
+    "qmm_gemv_batch_prepare", "qmm_gemv_batched",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
 )
 
@@ -61,6 +63,23 @@ class _Plan(ctypes.Structure):
     ]
 
 
+class GemvDesc(ctypes.Structure):
+    """qmm_gemv_desc: one GEMV of a batched launch (64 bytes)."""
+    _fields_ = [
+        ("w_packed", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("mins", ctypes.c_void_p),
+        ("x", ctypes.c_void_p),
+        ("y", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+        ("first_item", ctypes.c_int64),
+    ]
+
+
+assert ctypes.sizeof(GemvDesc) == 64
+
+
 def library_path() -> str:
     return os.path.join(_HERE, _LIB_NAME)
 
@@ -87,8 +106,11 @@ def load():
     lib.qmm_gemm_workspace_bytes.restype = sz
     lib.qmm_moe_gemm.argtypes = [p, p, p, p, p, i64, p, p, i64, i64, i64, i64, ci, ci, p]
     lib.qmm_unpack.argtypes = [p, p, i64, i64, ci, p]
+    lib.qmm_gemv_batch_prepare.argtypes = [p, i64, ci, ci]
+    lib.qmm_gemv_batched.argtypes = [p, p, i64, ci, ci, p]
     lib.qmm_get_plan.argtypes = [ci, i64, i64, i64, ci, ci, ci, sz, ctypes.POINTER(_Plan)]
-    for f in ("qmm_gemv", "qmm_gemm", "qmm_moe_gemm", "qmm_unpack", "qmm_get_plan"):
+    for f in ("qmm_gemv", "qmm_gemm", "qmm_moe_gemm", "qmm_unpack", "qmm_get_plan",
+              "qmm_gemv_batch_prepare", "qmm_gemv_batched"):
         getattr(lib, f).restype = ci
     lib.qmm_status_string.argtypes = [ci]
     lib.qmm_status_string.restype = ctypes.c_char_p
@@ -170,8 +192,25 @@ def qmm_unpack(w_packed, codes, n, k, bits, stream=None) -> None:
            "qmm_unpack")
 
 
+def qmm_gemv_batch_prepare(descs, bits, group_size) -> None:
+    """Fill the library-owned fields of a ``GemvDesc`` array (host memory)."""
+    _check(load().qmm_gemv_batch_prepare(ctypes.addressof(descs), len(descs), int(bits),
+                                         int(group_size)),
+           "qmm_gemv_batch_prepare")
+
+
+def qmm_gemv_batched(descs_device, descs_host, bits, group_size, stream=None) -> None:
+    """One launch over every GEMV of a prepared descriptor array.
+    ``descs_device``: device copy (tensor or address); ``descs_host``: the
+    ``GemvDesc`` array it was copied from."""
+    _check(load().qmm_gemv_batched(_addr(descs_device), ctypes.addressof(descs_host),
+                                   len(descs_host), int(bits), int(group_size), _stream(stream)),
+           "qmm_gemv_batched")
+
+
 def qmm_get_plan(op, m, n, k, bits, group_size, cu_count=0, workspace_bytes=0) -> dict:
-    """The launch plan the library would use (op 0 gemv, 1 gemm, 2 moe)."""
+    """The launch plan the library would use (op 0 gemv, 1 gemm, 2 moe,
+    3 batched gemv with n = total rows and k = largest k)."""
     plan = _Plan()
     _check(load().qmm_get_plan(int(op), int(m), int(n), int(k), int(bits), int(group_size),
                                int(cu_count), int(workspace_bytes), ctypes.byref(plan)),

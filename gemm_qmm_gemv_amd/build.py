@@ -13,7 +13,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmm.so")
-SOURCES = ["qmm_api.hip", "gemv.hip", "gemm.hip", "unpack.hip"]
+# (source, extra defines, object name); gemv_bits.hip is built once per width.
+SOURCES = [("qmm_api.hip", [], "qmm_api.o"), ("gemm.hip", [], "gemm.o"),
+           ("unpack.hip", [], "unpack.o")] + [
+    ("gemv_bits.hip", ["-DQMM_BITS=%d" % b], "gemv_b%d.o" % b) for b in (2, 3, 4, 6, 8)]
 ARCH = os.environ.get("QMM_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -49,9 +52,9 @@ def build(verbose: bool = False) -> str:
     os.makedirs(objdir, exist_ok=True)
     compile_flags = [f for f in FLAGS if f != "-shared"]
     jobs = []
-    for src in SOURCES:
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        jobs.append(([hipcc] + compile_flags + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
+    for src, defs, oname in SOURCES:
+        obj = os.path.join(objdir, oname)
+        jobs.append(([hipcc] + compile_flags + defs + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "8"))))
     with ThreadPoolExecutor(max_workers=workers) as ex:
         list(ex.map(lambda j: _run(j[0], verbose), jobs))

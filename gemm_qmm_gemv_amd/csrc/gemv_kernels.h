@@ -1,4 +1,4 @@
-// gemv.hip -- bandwidth-bound quantized GEMV kernels (decode, M = 1) and the
+// gemv_kernels.h -- bandwidth-bound quantized GEMV kernels (decode, M = 1) and the
 // multi-row variant used for small M and for mixture-of-experts rows.
 //
 // Pages: "BaseRT claims fastest Apple Silicon inference" (thetesserapress.com),
@@ -17,6 +17,8 @@
 //   (pairs, offset constant, plain sum) is built once per wave and reused for
 //   every row the wave visits.  Partial sums are reduced across the LPR lanes
 //   with cross-lane shuffles; no atomics, so results are deterministic.
+#pragma once
+
 #include "qmm_device.h"
 #include "qmm_kernels.h"
 
@@ -240,62 +242,129 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
     }
 }
 
-// ---- host-side launch helpers -------------------------------------------------
+// Many independent GEMVs in one launch (same bit width and group size; every
+// K fits one pass).  The work list is the concatenation, descriptor by
+// descriptor, of each GEMV's row batches (SLOTS*U rows each); descriptor d's
+// batches start at item D[d].first.  Wave w takes the contiguous item range
+// [w*per, (w+1)*per), so it changes descriptor rarely; on every change it
+// rebuilds its activation units from the new x.
+template <int B, int UNIT, int LPR, int XC, int U>
+__global__ __launch_bounds__(256) void gemv_batched_kernel(const BatchDesc* __restrict__ D, int count,
+                                                           int64_t total, int group) {
+    constexpr int SLOTS = 64 / LPR;
+    constexpr int WPU = UNIT * B / 32;
+    constexpr int ALIGN = unit_align(B, UNIT);
+    constexpr int ROWS = SLOTS * U;
+    const int lane = threadIdx.x & 63;
+    const int slot = lane / LPR, j = lane % LPR;
+    const int waves_per_block = blockDim.x >> 6;
+    const int wave = blockIdx.x * waves_per_block + (threadIdx.x >> 6);
+    const int nwaves = gridDim.x * waves_per_block;
+    const int64_t per = (total + nwaves - 1) / nwaves;
+    const int64_t i0 = (int64_t)wave * per;
+    const int64_t i1 = i0 + per < total ? i0 + per : total;
+    if (i0 >= i1) return;
+
+    // Last descriptor whose first item is <= i0 (binary search, wave-uniform).
+    int lo = 0, hi = count - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (D[mid].first <= i0) lo = mid; else hi = mid - 1;
+    }
+    int d = __builtin_amdgcn_readfirstlane(lo);
+
+    BatchDesc cur;
+    XUnit<B, UNIT> xu[XC];
+    int gidx[XC];
+    bool uok[XC];
+    int64_t d_end = 0;
+    int nu = 0, wpr = 0, gpr = 0, n = 0;
+    auto enter = [&](int dd) {
+        cur = D[dd];
+        n = (int)cur.n;
+        const int k = (int)cur.k;
+        nu = k / UNIT;
+        wpr = k / 32 * B;
+        gpr = k / group;
+        d_end = cur.first + (cur.n + ROWS - 1) / ROWS;
+#pragma unroll
+        for (int c = 0; c < XC; ++c) {
+            const int u = c * LPR + j;
+            uok[c] = u < nu && n > 0;
+            gidx[c] = uok[c] ? (u * UNIT) / group : 0;
+            if (uok[c])
+                prep_xunit<B, UNIT>(cur.x + (size_t)u * UNIT, xu[c]);
+            else
+                zero_xunit<B, UNIT>(xu[c]);
+        }
+    };
+    enter(d);
+
+    for (int64_t i = i0; i < i1; ++i) {
+        while (i >= d_end) enter(++d);
+        const int rb = (int)(i - cur.first) * ROWS;
+        u32 wv[U][XC][WPU];
+        uint16_t sv[U][XC], mv[U][XC];
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            const int row = rb + r * SLOTS + slot;
+#pragma unroll
+            for (int c = 0; c < XC; ++c) {
+                const int u = c * LPR + j;
+                if (row < n && uok[c]) {
+                    load_words<WPU, ALIGN>(cur.w + (size_t)row * wpr + (size_t)u * WPU, wv[r][c]);
+                    sv[r][c] = cur.s[(size_t)row * gpr + gidx[c]];
+                    mv[r][c] = cur.m[(size_t)row * gpr + gidx[c]];
+                } else {
+#pragma unroll
+                    for (int t = 0; t < WPU; ++t) wv[r][c][t] = 0u;
+                    sv[r][c] = 0;
+                    mv[r][c] = 0;
+                }
+            }
+        }
+        float yacc[U];
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            yacc[r] = 0.f;
+#pragma unroll
+            for (int c = 0; c < XC; ++c) {
+                const float t = unit_qx<B, UNIT>(wv[r][c], xu[c]);
+                yacc[r] = __builtin_fmaf(half_bits_to_float(sv[r][c]), t,
+                                         __builtin_fmaf(half_bits_to_float(mv[r][c]), xu[c].xsum, yacc[r]));
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            const float v = group_sum<LPR>(yacc[r]);
+            const int row = rb + r * SLOTS + slot;
+            if (j == 0 && row < n) cur.y[row] = v;
+        }
+    }
+}
+
+// ---- launch templates (instantiated per bit width in gemv_bits.hip) -----------
 
 template <int B, int UNIT, int LPR, int XC, int U>
-static hipError_t launch_gemv_t(const GemvArgs& a, int grid, hipStream_t st, bool mp) {
-    if (mp)
-        hipLaunchKernelGGL((gemv_kernel<B, UNIT, LPR, XC, U, true>), dim3(grid), dim3(256), 0, st,
+hipError_t launch_gemv_t(const GemvArgs& a, const GemvShape& sh, hipStream_t st) {
+    if (sh.multipass)
+        hipLaunchKernelGGL((gemv_kernel<B, UNIT, LPR, XC, U, true>), dim3(sh.grid), dim3(256), 0, st,
                            a.w, a.s, a.m, a.x, a.y, a.n, a.k, a.group);
     else
-        hipLaunchKernelGGL((gemv_kernel<B, UNIT, LPR, XC, U, false>), dim3(grid), dim3(256), 0, st,
+        hipLaunchKernelGGL((gemv_kernel<B, UNIT, LPR, XC, U, false>), dim3(sh.grid), dim3(256), 0, st,
                            a.w, a.s, a.m, a.x, a.y, a.n, a.k, a.group);
     return hipGetLastError();
 }
 
-// The (LPR, XC, U) combinations instantiated for every bit width and unit.
-#define QMM_GEMV_SHAPES(X) \
-    X(16, 1, 1) X(16, 1, 2) X(16, 1, 4) \
-    X(32, 1, 1) X(32, 1, 2) X(32, 1, 4) \
-    X(64, 1, 1) X(64, 1, 2) X(64, 1, 4) \
-    X(16, 2, 1) X(16, 2, 2) \
-    X(32, 2, 1) X(32, 2, 2) \
-    X(64, 2, 1) X(64, 2, 2) \
-    X(16, 3, 1) X(16, 3, 2) \
-    X(8, 2, 1) X(8, 2, 2) X(8, 1, 2) X(8, 1, 4)
-
-template <int B, int UNIT>
-static hipError_t launch_gemv_b(const GemvArgs& a, const GemvShape& sh, hipStream_t st) {
-#define X(L, C, UU)                                                         \
-    if (sh.lpr == L && sh.xc == C && sh.u == UU)                            \
-        return launch_gemv_t<B, UNIT, L, C, UU>(a, sh.grid, st, sh.multipass);
-    QMM_GEMV_SHAPES(X)
-#undef X
-    return hipErrorInvalidValue;
-}
-
-bool gemv_shape_supported(int lpr, int xc, int u) {
-#define X(L, C, UU) \
-    if (lpr == L && xc == C && u == UU) return true;
-    QMM_GEMV_SHAPES(X)
-#undef X
-    return false;
-}
-
-hipError_t launch_gemv(const GemvArgs& a, const GemvShape& sh, hipStream_t st) {
-    const bool u64 = sh.unit == 64;
-    switch (a.bits) {
-        case 2: return u64 ? launch_gemv_b<2, 64>(a, sh, st) : launch_gemv_b<2, 32>(a, sh, st);
-        case 3: return u64 ? launch_gemv_b<3, 64>(a, sh, st) : launch_gemv_b<3, 32>(a, sh, st);
-        case 4: return u64 ? launch_gemv_b<4, 64>(a, sh, st) : launch_gemv_b<4, 32>(a, sh, st);
-        case 6: return u64 ? launch_gemv_b<6, 64>(a, sh, st) : launch_gemv_b<6, 32>(a, sh, st);
-        case 8: return u64 ? launch_gemv_b<8, 64>(a, sh, st) : launch_gemv_b<8, 32>(a, sh, st);
-        default: return hipErrorInvalidValue;
-    }
+template <int B, int UNIT, int LPR, int XC, int U>
+hipError_t launch_batched_t(const BatchArgs& a, const GemvShape& sh, hipStream_t st) {
+    hipLaunchKernelGGL((gemv_batched_kernel<B, UNIT, LPR, XC, U>), dim3(sh.grid), dim3(256), 0, st,
+                       a.descs, a.count, a.total_items, a.group);
+    return hipGetLastError();
 }
 
 template <int B, int UNIT, int LPR, int XC, int MR>
-static hipError_t launch_rows_t(const RowsArgs& a, const RowsShape& sh, hipStream_t st) {
+hipError_t launch_rows_t(const RowsArgs& a, const RowsShape& sh, hipStream_t st) {
     const dim3 grid(sh.grid_x, sh.grid_y);
     if (sh.multipass)
         hipLaunchKernelGGL((gemv_rows_kernel<B, UNIT, LPR, XC, MR, true>), grid, dim3(256), 0, st,
@@ -308,37 +377,31 @@ static hipError_t launch_rows_t(const RowsArgs& a, const RowsShape& sh, hipStrea
     return hipGetLastError();
 }
 
-#define QMM_ROWS_SHAPES(X) \
-    X(16, 1, 4) X(32, 1, 4) X(64, 1, 4) \
-    X(16, 1, 2) X(32, 1, 2) X(64, 1, 2) X(64, 2, 2) X(32, 2, 2) X(16, 2, 2)
+template <int B, int UNIT>
+hipError_t launch_gemv_unit(const GemvArgs& a, const GemvShape& sh, hipStream_t st) {
+#define X(L, C, UU) \
+    if (sh.lpr == L && sh.xc == C && sh.u == UU) return launch_gemv_t<B, UNIT, L, C, UU>(a, sh, st);
+    QMM_GEMV_SHAPES(X)
+#undef X
+    return hipErrorInvalidValue;
+}
 
 template <int B, int UNIT>
-static hipError_t launch_rows_b(const RowsArgs& a, const RowsShape& sh, hipStream_t st) {
+hipError_t launch_batched_unit(const BatchArgs& a, const GemvShape& sh, hipStream_t st) {
+#define X(L, C, UU) \
+    if (sh.lpr == L && sh.xc == C && sh.u == UU) return launch_batched_t<B, UNIT, L, C, UU>(a, sh, st);
+    QMM_BATCHED_SHAPES(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+template <int B, int UNIT>
+hipError_t launch_rows_unit(const RowsArgs& a, const RowsShape& sh, hipStream_t st) {
 #define X(L, C, R) \
     if (sh.lpr == L && sh.xc == C && sh.mr == R) return launch_rows_t<B, UNIT, L, C, R>(a, sh, st);
     QMM_ROWS_SHAPES(X)
 #undef X
     return hipErrorInvalidValue;
-}
-
-bool rows_shape_supported(int lpr, int xc, int mr) {
-#define X(L, C, R) \
-    if (lpr == L && xc == C && mr == R) return true;
-    QMM_ROWS_SHAPES(X)
-#undef X
-    return false;
-}
-
-hipError_t launch_rows(const RowsArgs& a, const RowsShape& sh, hipStream_t st) {
-    const bool u64 = sh.unit == 64;
-    switch (a.bits) {
-        case 2: return u64 ? launch_rows_b<2, 64>(a, sh, st) : launch_rows_b<2, 32>(a, sh, st);
-        case 3: return u64 ? launch_rows_b<3, 64>(a, sh, st) : launch_rows_b<3, 32>(a, sh, st);
-        case 4: return u64 ? launch_rows_b<4, 64>(a, sh, st) : launch_rows_b<4, 32>(a, sh, st);
-        case 6: return u64 ? launch_rows_b<6, 64>(a, sh, st) : launch_rows_b<6, 32>(a, sh, st);
-        case 8: return u64 ? launch_rows_b<8, 64>(a, sh, st) : launch_rows_b<8, 32>(a, sh, st);
-        default: return hipErrorInvalidValue;
-    }
 }
 
 }  // namespace qmm

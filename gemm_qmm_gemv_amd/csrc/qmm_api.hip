@@ -22,6 +22,26 @@ using namespace qmm;
 
 namespace {
 
+#define QMM_BITS_SWITCH(bits, FN, ...)                    \
+    switch (bits) {                                       \
+        case 2: return FN<2>(__VA_ARGS__);                \
+        case 3: return FN<3>(__VA_ARGS__);                \
+        case 4: return FN<4>(__VA_ARGS__);                \
+        case 6: return FN<6>(__VA_ARGS__);                \
+        case 8: return FN<8>(__VA_ARGS__);                \
+        default: return hipErrorInvalidValue;             \
+    }
+
+hipError_t launch_gemv(const GemvArgs& a, const GemvShape& sh, hipStream_t st) {
+    QMM_BITS_SWITCH(a.bits, launch_gemv_bits, a, sh, st)
+}
+hipError_t launch_batched(const BatchArgs& a, const GemvShape& sh, hipStream_t st) {
+    QMM_BITS_SWITCH(a.bits, launch_batched_bits, a, sh, st)
+}
+hipError_t launch_rows(const RowsArgs& a, const RowsShape& sh, hipStream_t st) {
+    QMM_BITS_SWITCH(a.bits, launch_rows_bits, a, sh, st)
+}
+
 thread_local char g_err[512] = "";
 
 qmm_status fail(qmm_status st, const char* fmt, ...) {
@@ -129,6 +149,7 @@ LaneSplit choose_split(int nu, int max_xc, bool (*supported)(int, int)) {
 }
 
 bool gemv_split_ok(int lpr, int xc) { return gemv_shape_supported(lpr, xc, 1); }
+bool batched_split_ok(int lpr, int xc) { return batched_shape_supported(lpr, xc, 1); }
 bool rows_split_ok(int lpr, int xc) { return rows_shape_supported(lpr, xc, xc == 1 ? 4 : 2); }
 
 GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
@@ -160,6 +181,34 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     sh.grid = (int)((waves + 3) / 4);
     if (sh.grid < 1) sh.grid = 1;
     return sh;
+}
+
+// Batched GEMVs: one kernel shape for every descriptor, chosen from the
+// largest K (which must fit a single pass) and the total row count.
+bool plan_batched(int64_t total_rows, int64_t kmax, int bits, int group, GemvShape* out) {
+    GemvShape sh{};
+    sh.unit = (group % 64 == 0) ? 64 : 32;
+    const int nu = (int)(kmax / sh.unit);
+    LaneSplit ls = choose_split(nu, 3, batched_split_ok);
+    if (ls.multipass) return false;
+    sh.lpr = ls.lpr;
+    sh.xc = ls.xc;
+    sh.multipass = false;
+    const int slots = 64 / sh.lpr;
+    const int unit_bytes = sh.unit * bits / 8;
+    int u = 1;
+    // The row count decides, not the device, so prepared descriptors stay
+    // valid on any GPU: big batches stream with several rows per lane.
+    if (total_rows > (int64_t)slots * 4096) {
+        const int want = 128 / (unit_bytes * sh.xc);
+        u = want >= 4 ? 4 : want >= 2 ? 2 : 1;
+    }
+    while (u > 1 && !batched_shape_supported(sh.lpr, sh.xc, u)) u /= 2;
+    const int ev = env_int("QMM_BATCH_U", 0);
+    if (ev > 0 && batched_shape_supported(sh.lpr, sh.xc, ev)) u = ev;
+    sh.u = u;
+    *out = sh;
+    return true;
 }
 
 RowsShape plan_rows(int64_t rows_bound, int64_t n, int64_t k, int bits, int group, int cus,
@@ -335,6 +384,74 @@ qmm_status qmm_moe_gemm(const void* w_packed, const void* scales, const void* mi
     return launched(launch_rows(a, sh, as_stream(stream)), "qmm_moe_gemm");
 }
 
+static qmm_status check_batch(const qmm_gemv_desc* d, int64_t count, int bits, int group,
+                              int64_t* total_rows, int64_t* kmax) {
+    if (count < 0 || count > INT_LIMIT) return fail(QMM_ERR_INVALID_ARGUMENT, "count=%lld out of range", (long long)count);
+    if (count > 0 && !d) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL descriptor array");
+    *total_rows = 0;
+    *kmax = 32;
+    char why[sizeof g_err];
+    for (int64_t i = 0; i < count; ++i) {
+        qmm_status st = check_format(d[i].n, d[i].k, bits, group);
+        if (st == QMM_OK && d[i].n > 0) st = check_weight_ptrs(d[i].w_packed, d[i].scales, d[i].mins);
+        if (st != QMM_OK) {
+            memcpy(why, g_err, sizeof why);
+            return fail(st, "descriptor %lld: %s", (long long)i, why);
+        }
+        if (d[i].n == 0) continue;
+        if (!d[i].x || !d[i].y) return fail(QMM_ERR_INVALID_ARGUMENT, "descriptor %lld: NULL x or y", (long long)i);
+        if (!aligned(d[i].x, 16) || !aligned(d[i].y, 16))
+            return fail(QMM_ERR_MISALIGNED, "descriptor %lld: x or y not 16-byte aligned", (long long)i);
+        *total_rows += d[i].n;
+        if (d[i].k > *kmax) *kmax = d[i].k;
+    }
+    return QMM_OK;
+}
+
+qmm_status qmm_gemv_batch_prepare(qmm_gemv_desc* descs, int64_t count, int bits, int group_size) {
+    int64_t rows = 0, kmax = 0;
+    qmm_status st = check_batch(descs, count, bits, group_size, &rows, &kmax);
+    if (st != QMM_OK) return st;
+    GemvShape sh{};
+    if (!plan_batched(rows, kmax, bits, group_size, &sh))
+        return fail(QMM_ERR_UNSUPPORTED, "largest k=%lld too large for a batched launch", (long long)kmax);
+    const int64_t per_item = (int64_t)(64 / sh.lpr) * sh.u;
+    int64_t first = 0;
+    for (int64_t i = 0; i < count; ++i) {
+        descs[i].first_item = first;
+        first += (descs[i].n + per_item - 1) / per_item;
+    }
+    return ok();
+}
+
+qmm_status qmm_gemv_batched(const qmm_gemv_desc* descs_device, const qmm_gemv_desc* descs_host,
+                            int64_t count, int bits, int group_size, void* stream) {
+    int64_t rows = 0, kmax = 0;
+    qmm_status st = check_batch(descs_host, count, bits, group_size, &rows, &kmax);
+    if (st != QMM_OK) return st;
+    if (rows == 0) return ok();
+    if (!descs_device || !aligned(descs_device, 8))
+        return fail(QMM_ERR_INVALID_ARGUMENT, "descs_device NULL or not 8-byte aligned");
+    GemvShape sh{};
+    if (!plan_batched(rows, kmax, bits, group_size, &sh))
+        return fail(QMM_ERR_UNSUPPORTED, "largest k=%lld too large for a batched launch", (long long)kmax);
+    const int64_t per_item = (int64_t)(64 / sh.lpr) * sh.u;
+    int64_t first = 0;
+    for (int64_t i = 0; i < count; ++i) {
+        if (descs_host[i].first_item != first)
+            return fail(QMM_ERR_INVALID_ARGUMENT,
+                        "descriptor %lld not prepared for this batch (call qmm_gemv_batch_prepare)", (long long)i);
+        first += (descs_host[i].n + per_item - 1) / per_item;
+    }
+    int cus = 0;
+    if ((st = device_cus(&cus)) != QMM_OK) return st;
+    const int64_t max_waves = (int64_t)cus * env_int("QMM_GEMV_WAVES_PER_CU", 32);
+    const int64_t waves = first < max_waves ? first : max_waves;
+    sh.grid = (int)((waves + 3) / 4);
+    BatchArgs a{reinterpret_cast<const BatchDesc*>(descs_device), (int)count, first, group_size, bits};
+    return launched(launch_batched(a, sh, as_stream(stream)), "qmm_gemv_batched");
+}
+
 qmm_status qmm_unpack(const void* w_packed, uint8_t* codes, int64_t n, int64_t k, int bits,
                       void* stream) {
     qmm_status st = check_format(n, k, bits, 32);
@@ -370,6 +487,20 @@ qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits, int g
         plan->unit_codes = sh.unit;
         plan->grid = sh.grid;
         plan->reserved[0] = sh.multipass;
+        return ok();
+    }
+    if (op == 3) {
+        GemvShape sh{};
+        if (!plan_batched(n, k, bits, group_size, &sh))
+            return fail(QMM_ERR_UNSUPPORTED, "k too large for a batched launch");
+        plan->variant = 3;
+        plan->lanes_per_row = sh.lpr;
+        plan->units_per_lane = sh.xc;
+        plan->rows_per_iter = sh.u;
+        plan->unit_codes = sh.unit;
+        const int64_t items = (n + (64 / sh.lpr) * sh.u - 1) / ((64 / sh.lpr) * sh.u);
+        const int64_t w = items < (int64_t)cus * 32 ? items : (int64_t)cus * 32;
+        plan->grid = (w + 3) / 4;
         return ok();
     }
     if (op == 2 || (op == 1 && m <= ROWS_KERNEL_MAX_M)) {

@@ -62,11 +62,82 @@ struct GemmShape {
     int grid_m, grid_n;
 };
 
-hipError_t launch_gemv(const GemvArgs& a, const GemvShape& sh, hipStream_t st);
-bool gemv_shape_supported(int lpr, int xc, int u);
+// One GEMV of a batched launch.  Same layout as qmm_gemv_desc in qmm.h.
+struct BatchDesc {
+    const uint32_t* w;
+    const uint16_t* s;
+    const uint16_t* m;
+    const uint16_t* x;
+    float* y;
+    int64_t n, k;
+    int64_t first;  // index of this GEMV's first row batch in the launch's work list
+};
+static_assert(sizeof(BatchDesc) == 64, "descriptor layout");
 
-hipError_t launch_rows(const RowsArgs& a, const RowsShape& sh, hipStream_t st);
-bool rows_shape_supported(int lpr, int xc, int mr);
+struct BatchArgs {
+    const BatchDesc* descs;  // device memory
+    int count;
+    int64_t total_items;
+    int group, bits;
+};
+
+// Kernel shapes compiled for each bit width and unit: (lanes per row, units
+// per lane, rows per slot) for the GEMV kernels, (lanes, units, activation
+// rows) for the multi-row kernel.
+#define QMM_GEMV_SHAPES(X) \
+    X(16, 1, 1) X(16, 1, 2) X(16, 1, 4) \
+    X(32, 1, 1) X(32, 1, 2) X(32, 1, 4) \
+    X(64, 1, 1) X(64, 1, 2) X(64, 1, 4) \
+    X(16, 2, 1) X(16, 2, 2) \
+    X(32, 2, 1) X(32, 2, 2) \
+    X(64, 2, 1) X(64, 2, 2) \
+    X(16, 3, 1) X(16, 3, 2) \
+    X(8, 2, 1) X(8, 2, 2) X(8, 1, 2) X(8, 1, 4)
+
+#define QMM_BATCHED_SHAPES(X) \
+    X(16, 1, 1) X(16, 1, 2) X(16, 1, 4) \
+    X(32, 1, 1) X(32, 1, 2) X(32, 1, 4) \
+    X(64, 1, 1) X(64, 1, 2) X(64, 1, 4) \
+    X(64, 2, 1) X(64, 2, 2) X(16, 3, 1) X(16, 3, 2)
+
+#define QMM_ROWS_SHAPES(X) \
+    X(16, 1, 4) X(32, 1, 4) X(64, 1, 4) \
+    X(16, 1, 2) X(32, 1, 2) X(64, 1, 2) X(64, 2, 2) X(32, 2, 2) X(16, 2, 2)
+
+constexpr bool gemv_shape_supported(int lpr, int xc, int u) {
+#define X(L, C, UU) if (lpr == L && xc == C && u == UU) return true;
+    QMM_GEMV_SHAPES(X)
+#undef X
+    return false;
+}
+constexpr bool batched_shape_supported(int lpr, int xc, int u) {
+#define X(L, C, UU) if (lpr == L && xc == C && u == UU) return true;
+    QMM_BATCHED_SHAPES(X)
+#undef X
+    return false;
+}
+constexpr bool rows_shape_supported(int lpr, int xc, int mr) {
+#define X(L, C, R) if (lpr == L && xc == C && mr == R) return true;
+    QMM_ROWS_SHAPES(X)
+#undef X
+    return false;
+}
+
+// Per-bit-width launchers, each defined in its own translation unit
+// (gemv_bits.hip built with -DQMM_BITS=b).
+template <int B> hipError_t launch_gemv_bits(const GemvArgs& a, const GemvShape& sh, hipStream_t st);
+template <int B> hipError_t launch_batched_bits(const BatchArgs& a, const GemvShape& sh, hipStream_t st);
+template <int B> hipError_t launch_rows_bits(const RowsArgs& a, const RowsShape& sh, hipStream_t st);
+#define QMM_DECLARE_BITS(B)                                                                      \
+    template <> hipError_t launch_gemv_bits<B>(const GemvArgs&, const GemvShape&, hipStream_t);  \
+    template <> hipError_t launch_batched_bits<B>(const BatchArgs&, const GemvShape&, hipStream_t); \
+    template <> hipError_t launch_rows_bits<B>(const RowsArgs&, const RowsShape&, hipStream_t);
+QMM_DECLARE_BITS(2)
+QMM_DECLARE_BITS(3)
+QMM_DECLARE_BITS(4)
+QMM_DECLARE_BITS(6)
+QMM_DECLARE_BITS(8)
+#undef QMM_DECLARE_BITS
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmShape& sh, hipStream_t st);
 constexpr int GEMM_BK = 64;  // K per main-loop step

@@ -7,7 +7,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (qmm_gemm, qmm_gemm_workspace_bytes, qmm_gemv, qmm_moe_gemm, qmm_unpack)
+from . import (GemvDesc, qmm_gemm, qmm_gemm_workspace_bytes, qmm_gemv, qmm_gemv_batch_prepare,
+               qmm_gemv_batched, qmm_moe_gemm, qmm_unpack)
 
 
 def device_tensor(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -64,3 +65,26 @@ def unpack(dq: dict, stream=None) -> torch.Tensor:
     codes = torch.empty((dq["n"], dq["k"]), dtype=torch.uint8, device=dq["w"].device)
     qmm_unpack(dq["w"], codes, dq["n"], dq["k"], dq["bits"], stream=stream)
     return codes
+
+
+class GemvBatch:
+    """A prepared batched launch: host descriptors plus their device copy.
+
+    items: list of (device matrix dict, x tensor [k], y tensor [n]); every
+    matrix must share bits and group size."""
+
+    def __init__(self, items, bits: int, group: int, device="cuda"):
+        self.bits, self.group = bits, group
+        self.host = (GemvDesc * len(items))()
+        for d, (dq, x, y) in zip(self.host, items):
+            assert dq["bits"] == bits and dq["group"] == group
+            d.w_packed, d.scales, d.mins = dq["w"].data_ptr(), dq["scales"].data_ptr(), dq["mins"].data_ptr()
+            d.x, d.y = x.data_ptr(), y.data_ptr()
+            d.n, d.k = dq["n"], dq["k"]
+        qmm_gemv_batch_prepare(self.host, bits, group)
+        raw = np.frombuffer(bytes(self.host), dtype=np.uint8).copy()
+        self.device = torch.from_numpy(raw).to(device)
+        self.keep = items  # the buffers must outlive the batch
+
+    def __call__(self, stream=None) -> None:
+        qmm_gemv_batched(self.device, self.host, self.bits, self.group, stream=stream)

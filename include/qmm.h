@@ -100,6 +100,36 @@ QMM_API qmm_status qmm_gemm(const void *w_packed, const void *scales, const void
                     int bits, int group_size, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/* Many independent decode GEMVs in one launch.
+ * Pages: "BaseRT claims fastest Apple Silicon inference", section "What
+ * BaseRT does differently" (operations other runtimes dispatch separately
+ * are combined, saving launches); "BaseRT: Best-in-Class LLM Inference on
+ * Apple Silicon via Native Metal", section "Metodologia" (low-overhead
+ * dispatch without per-operation scheduling).
+ * Every descriptor is one qmm_gemv (same bits and group_size for all; each
+ * k at most 64*3*64 codes for 64-multiple groups).  first_item is owned by
+ * the library: qmm_gemv_batch_prepare fills it in a host array, the caller
+ * copies the array to device memory (once; it can be reused for every
+ * later call with the same shapes and pointers) and passes both copies to
+ * qmm_gemv_batched, which checks the host copy and launches one kernel that
+ * reads the device copy.  The two copies must hold the same bytes.  Outputs
+ * of different descriptors must not overlap.                                */
+typedef struct qmm_gemv_desc {
+    const void *w_packed;   /* uint32 [n][k*bits/32]                          */
+    const void *scales;     /* fp16 [n][k/group_size]                         */
+    const void *mins;       /* fp16 [n][k/group_size]                         */
+    const void *x;          /* fp16 [k]                                       */
+    float *y;               /* fp32 [n] (written)                             */
+    int64_t n, k;
+    int64_t first_item;     /* library-owned, see qmm_gemv_batch_prepare      */
+} qmm_gemv_desc;
+
+QMM_API qmm_status qmm_gemv_batch_prepare(qmm_gemv_desc *descs /* host */, int64_t count,
+                                          int bits, int group_size);
+QMM_API qmm_status qmm_gemv_batched(const qmm_gemv_desc *descs_device,
+                                    const qmm_gemv_desc *descs_host, int64_t count,
+                                    int bits, int group_size, void *stream);
+
 /* Bytes of workspace that let qmm_gemm use its preferred K split for this
  * shape on the current device (0 when it would not split).  Host only.     */
 QMM_API size_t qmm_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits,
@@ -135,7 +165,8 @@ QMM_API qmm_status qmm_unpack(const void *w_packed, uint8_t *codes, int64_t n, i
 
 /* Launch plan the library would use (host only, no device call): which
  * kernel variant, grid and block.  `op` is 0 for qmm_gemv, 1 for qmm_gemm,
- * 2 for qmm_moe_gemm (m = rows per expert bound).  cu_count <= 0 means
+ * 2 for qmm_moe_gemm (m = rows per expert bound), 3 for qmm_gemv_batched
+ * (n = total rows of the batch, k = its largest k).  cu_count <= 0 means
  * "query the current device" (then this does call the runtime).            */
 typedef struct qmm_plan {
     int32_t variant;       /* library-internal variant id                   */
