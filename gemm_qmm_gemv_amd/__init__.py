@@ -81,7 +81,8 @@ assert ctypes.sizeof(GemvDesc) == 64
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, _LIB_NAME)
+    """In-tree libqmm.so, or the file named by $QMM_LIBRARY (tuning builds)."""
+    return os.environ.get("QMM_LIBRARY") or os.path.join(_HERE, _LIB_NAME)
 
 
 def load():

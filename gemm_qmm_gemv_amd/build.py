@@ -43,14 +43,17 @@ def _run(cmd, verbose):
         print("\n".join(msgs))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source (in parallel) and link libqmm.so.  Always rebuilds."""
+def build(verbose: bool = False, out: str | None = None, extra_flags=(), objdir: str | None = None) -> str:
+    """Compile every source (in parallel) and link libqmm.so.  Always rebuilds.
+    ``out``/``extra_flags``/``objdir`` produce variant builds (e.g. with a
+    -D switch) next to the default one."""
     from concurrent.futures import ThreadPoolExecutor
 
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    objdir = os.path.join(ROOT, "_build", "qmm")
+    objdir = objdir or os.path.join(ROOT, "_build", "qmm")
+    out = out or LIB
     os.makedirs(objdir, exist_ok=True)
-    compile_flags = [f for f in FLAGS if f != "-shared"]
+    compile_flags = [f for f in FLAGS if f != "-shared"] + list(extra_flags)
     jobs = []
     for src, defs, oname in SOURCES:
         obj = os.path.join(objdir, oname)
@@ -58,11 +61,11 @@ def build(verbose: bool = False) -> str:
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "8"))))
     with ThreadPoolExecutor(max_workers=workers) as ex:
         list(ex.map(lambda j: _run(j[0], verbose), jobs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     _run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH] + [o for _, o in jobs] + ["-o", tmp],
          verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

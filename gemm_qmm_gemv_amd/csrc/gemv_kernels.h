@@ -24,9 +24,126 @@
 
 namespace qmm {
 
-// K fits in one pass (k <= LPR*XC*UNIT): activations stay in registers for the
-// whole kernel.  Otherwise (MP) each row batch walks K in passes and rebuilds
-// the activation units per pass.
+// Weights of one row batch held in registers: U rows per slot, XC units per
+// lane, with each unit's scale and min (fp16 bits).  On the wide path the
+// scales and mins arrive instead as one 32-bit word per lane of the batch's
+// contiguous scale block (and min block) and are handed out to the lanes
+// that need them with cross-lane permutes.
+template <int B, int UNIT, int XC, int U>
+struct RowBatch {
+    static constexpr int WPU = UNIT * B / 32;
+    u32 w[U][XC][WPU];
+    u32 s[U][XC], m[U][XC];
+    u32 sblk, mblk;
+};
+
+// Scale/min loads: the rows of one iteration (rb .. rb + SLOTS*U - 1) are
+// consecutive, so their scales form one contiguous block of SLOTS*U*gpr fp16
+// values, and likewise their mins.  When that block fits one 32-bit word per
+// lane (and the arrays are 4-byte aligned with an even group count per row)
+// two dword loads per lane replace 2*U*XC two-byte loads: fewer memory
+// instructions and whole cache lines.
+template <int LPR, int U>
+__device__ __forceinline__ bool wide_scales_ok(const uint16_t* S, const uint16_t* Mn, int gpr) {
+    constexpr int SLOTS = 64 / LPR;
+    return ((reinterpret_cast<uintptr_t>(S) | reinterpret_cast<uintptr_t>(Mn)) & 3u) == 0 &&
+           (gpr & 1) == 0 && SLOTS * U * gpr <= 128;
+}
+
+// Buffer resources over one matrix: packed weights, scales, mins.
+struct MatRsrc {
+    rsrc_t w, s, m;
+};
+__device__ __forceinline__ MatRsrc mat_rsrc(const void* W, const void* S, const void* Mn, int n,
+                                            int wpr, int gpr) {
+    return {make_rsrc(W, (uint32_t)n * (uint32_t)wpr * 4u), make_rsrc(S, (uint32_t)n * (uint32_t)gpr * 2u),
+            make_rsrc(Mn, (uint32_t)n * (uint32_t)gpr * 2u)};
+}
+
+// Issue every load of a row batch (rows rb + r*SLOTS + slot, r < U).  Rows
+// past n read zeros (buffer range check); units past the row read nothing.
+template <int B, int UNIT, int LPR, int XC, int U>
+__device__ __forceinline__ void load_batch(RowBatch<B, UNIT, XC, U>& bt, const MatRsrc& mr, int rb,
+                                           int wpr, int gpr, int slot, const int (&unit)[XC],
+                                           const int (&gidx)[XC], int nu, bool wide, int lane) {
+    constexpr int SLOTS = 64 / LPR;
+    constexpr int WPU = UNIT * B / 32;
+    constexpr int ALIGN = unit_align(B, UNIT);
+    if (wide) {
+        const int words = SLOTS * U * gpr / 2;
+        const uint32_t off = ((uint32_t)rb * (uint32_t)gpr + 2u * (uint32_t)lane) * 2u;
+        bt.sblk = lane < words ? buffer_u32(mr.s, off) : 0u;
+        bt.mblk = lane < words ? buffer_u32(mr.m, off) : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < U; ++r) {
+        const uint32_t row = (uint32_t)(rb + r * SLOTS + slot);
+#pragma unroll
+        for (int c = 0; c < XC; ++c) {
+            bt.s[r][c] = 0u;
+            bt.m[r][c] = 0u;
+            if (unit[c] < nu) {
+                buffer_words<WPU, ALIGN>(mr.w, (row * (uint32_t)wpr + (uint32_t)(unit[c] * WPU)) * 4u,
+                                         bt.w[r][c]);
+                if (!wide) {
+                    const uint32_t so = (row * (uint32_t)gpr + (uint32_t)gidx[c]) * 2u;
+                    bt.s[r][c] = buffer_u16(mr.s, so);
+                    bt.m[r][c] = buffer_u16(mr.m, so);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < WPU; ++i) bt.w[r][c][i] = 0u;
+            }
+        }
+    }
+}
+
+// Partial dot products of a loaded batch, added into yacc[r].
+template <int B, int UNIT, int LPR, int XC, int U>
+__device__ __forceinline__ void accumulate_batch(const RowBatch<B, UNIT, XC, U>& bt,
+                                                 const XUnit<B, UNIT> (&xu)[XC], float (&yacc)[U],
+                                                 bool wide, int slot, int gpr, const int (&gidx)[XC]) {
+    constexpr int SLOTS = 64 / LPR;
+#pragma unroll
+    for (int r = 0; r < U; ++r)
+#pragma unroll
+        for (int c = 0; c < XC; ++c) {
+            u32 sb = bt.s[r][c], mb = bt.m[r][c];
+            if (wide) {
+                // fp16 value number off of the block lives in word off/2, half off%2.
+                const int off = (r * SLOTS + slot) * gpr + gidx[c];
+                const int src = (off >> 1) << 2;
+                const u32 sw = (u32)__builtin_amdgcn_ds_bpermute(src, (int)bt.sblk);
+                const u32 mw = (u32)__builtin_amdgcn_ds_bpermute(src, (int)bt.mblk);
+                const u32 sh = (off & 1) << 4;
+                sb = (sw >> sh) & 0xFFFFu;
+                mb = (mw >> sh) & 0xFFFFu;
+            }
+            const float t = unit_qx<B, UNIT>(bt.w[r][c], xu[c]);
+            yacc[r] = __builtin_fmaf(half_bits_to_float((uint16_t)sb), t,
+                                     __builtin_fmaf(half_bits_to_float((uint16_t)mb), xu[c].xsum, yacc[r]));
+        }
+}
+
+// Reduce the U row sums over the LPR lanes of each slot and store them.
+template <int LPR, int U>
+__device__ __forceinline__ void store_batch(float (&yacc)[U], float* __restrict__ Y, int rb, int n,
+                                            int slot, int j) {
+    constexpr int SLOTS = 64 / LPR;
+#pragma unroll
+    for (int r = 0; r < U; ++r) {
+        const float v = group_sum<LPR>(yacc[r]);
+        const int row = rb + r * SLOTS + slot;
+        if (j == 0 && row < n) Y[row] = v;
+    }
+}
+
+// Decode GEMV.  Single pass (k <= LPR*XC*UNIT): the activation units stay in
+// registers for the whole kernel, and the loop is software-pipelined -- the
+// next row batch's loads are issued before the current batch's arithmetic, and
+// the first batch's loads before the activation set-up, so memory latency
+// overlaps both.  Multi-pass (MP, larger k): each row batch walks k in passes
+// and rebuilds the activation units per pass (no pipelining).
 template <int B, int UNIT, int LPR, int XC, int U, bool MP>
 __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
                                                    const uint16_t* __restrict__ S,
@@ -34,8 +151,6 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
                                                    const uint16_t* __restrict__ X,
                                                    float* __restrict__ Y, int n, int k, int group) {
     constexpr int SLOTS = 64 / LPR;
-    constexpr int WPU = UNIT * B / 32;
-    constexpr int ALIGN = unit_align(B, UNIT);
     const int lane = threadIdx.x & 63;
     const int slot = lane / LPR, j = lane % LPR;
     const int waves_per_block = blockDim.x >> 6;
@@ -44,68 +159,70 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
     const int nu = k / UNIT;
     const int wpr = k / 32 * B;
     const int gpr = k / group;
-    const int passes = MP ? (nu + LPR * XC - 1) / (LPR * XC) : 1;
+    const int stride = nwaves * SLOTS * U;
+    const bool wide = wide_scales_ok<LPR, U>(S, Mn, gpr);
+    const MatRsrc mr = mat_rsrc(W, S, Mn, n, wpr, gpr);
+    const rsrc_t xr = make_rsrc(X, (uint32_t)k * 2u);
 
     XUnit<B, UNIT> xu[XC];
-    int gidx[XC];
-    bool uok[XC];
-
-    auto prep = [&](int pass) {
+    int unit[XC], gidx[XC];
+    auto units_of_pass = [&](int pass) {
 #pragma unroll
         for (int c = 0; c < XC; ++c) {
-            const int u = (pass * XC + c) * LPR + j;
-            uok[c] = u < nu;
-            gidx[c] = uok[c] ? (u * UNIT) / group : 0;
-            if (uok[c])
-                prep_xunit<B, UNIT>(X + (size_t)u * UNIT, xu[c]);
+            unit[c] = (pass * XC + c) * LPR + j;
+            gidx[c] = unit[c] < nu ? (unit[c] * UNIT) / group : 0;
+        }
+    };
+    auto prep = [&]() {
+#pragma unroll
+        for (int c = 0; c < XC; ++c) {
+            if (unit[c] < nu)
+                prep_xunit<B, UNIT>(xr, (uint32_t)(unit[c] * UNIT * 2), xu[c]);
             else
                 zero_xunit<B, UNIT>(xu[c]);
         }
     };
-    if constexpr (!MP) prep(0);
 
-    for (int rb = wave * SLOTS * U; rb < n; rb += nwaves * SLOTS * U) {
-        float yacc[U];
+    if constexpr (MP) {
+        const int passes = (nu + LPR * XC - 1) / (LPR * XC);
+        for (int rb = wave * SLOTS * U; rb < n; rb += stride) {
+            float yacc[U];
 #pragma unroll
-        for (int r = 0; r < U; ++r) yacc[r] = 0.f;
-        for (int pass = 0; pass < passes; ++pass) {
-            if constexpr (MP) prep(pass);
-            u32 wv[U][XC][WPU];
-            uint16_t sv[U][XC], mv[U][XC];
-#pragma unroll
-            for (int r = 0; r < U; ++r) {
-                const int row = rb + r * SLOTS + slot;
-#pragma unroll
-                for (int c = 0; c < XC; ++c) {
-                    const int u = (pass * XC + c) * LPR + j;
-                    if (row < n && uok[c]) {
-                        load_words<WPU, ALIGN>(W + (size_t)row * wpr + (size_t)u * WPU, wv[r][c]);
-                        sv[r][c] = S[(size_t)row * gpr + gidx[c]];
-                        mv[r][c] = Mn[(size_t)row * gpr + gidx[c]];
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < WPU; ++i) wv[r][c][i] = 0u;
-                        sv[r][c] = 0;
-                        mv[r][c] = 0;
-                    }
-                }
+            for (int r = 0; r < U; ++r) yacc[r] = 0.f;
+            for (int pass = 0; pass < passes; ++pass) {
+                units_of_pass(pass);
+                RowBatch<B, UNIT, XC, U> bt;
+                load_batch<B, UNIT, LPR, XC, U>(bt, mr, rb, wpr, gpr, slot, unit, gidx, nu, wide, lane);
+                prep();
+                accumulate_batch<B, UNIT, LPR, XC, U>(bt, xu, yacc, wide, slot, gpr, gidx);
             }
-#pragma unroll
-            for (int r = 0; r < U; ++r) {
-#pragma unroll
-                for (int c = 0; c < XC; ++c) {
-                    const float t = unit_qx<B, UNIT>(wv[r][c], xu[c]);
-                    const float s = half_bits_to_float(sv[r][c]);
-                    const float m = half_bits_to_float(mv[r][c]);
-                    yacc[r] = __builtin_fmaf(s, t, __builtin_fmaf(m, xu[c].xsum, yacc[r]));
-                }
-            }
+            store_batch<LPR, U>(yacc, Y, rb, n, slot, j);
         }
+    } else {
+        units_of_pass(0);
+        int rb = wave * SLOTS * U;
+        if (rb >= n) return;
+        RowBatch<B, UNIT, XC, U> ba, bb;
+        load_batch<B, UNIT, LPR, XC, U>(ba, mr, rb, wpr, gpr, slot, unit, gidx, nu, wide, lane);
+        prep();
+        while (true) {
+            float yacc[U];
+            int nxt = rb + stride;
+            if (nxt < n) load_batch<B, UNIT, LPR, XC, U>(bb, mr, nxt, wpr, gpr, slot, unit, gidx, nu, wide, lane);
 #pragma unroll
-        for (int r = 0; r < U; ++r) {
-            const float v = group_sum<LPR>(yacc[r]);
-            const int row = rb + r * SLOTS + slot;
-            if (j == 0 && row < n) Y[row] = v;
+            for (int r = 0; r < U; ++r) yacc[r] = 0.f;
+            accumulate_batch<B, UNIT, LPR, XC, U>(ba, xu, yacc, wide, slot, gpr, gidx);
+            store_batch<LPR, U>(yacc, Y, rb, n, slot, j);
+            rb = nxt;
+            if (rb >= n) break;
+            nxt = rb + stride;
+            if (nxt < n) load_batch<B, UNIT, LPR, XC, U>(ba, mr, nxt, wpr, gpr, slot, unit, gidx, nu, wide, lane);
+#pragma unroll
+            for (int r = 0; r < U; ++r) yacc[r] = 0.f;
+            accumulate_batch<B, UNIT, LPR, XC, U>(bb, xu, yacc, wide, slot, gpr, gidx);
+            store_batch<LPR, U>(yacc, Y, rb, n, slot, j);
+            rb = nxt;
+            if (rb >= n) break;
         }
     }
 }
@@ -170,9 +287,9 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
         }
     }
     if (e < 0 || p0 >= p1) return;
-    const u32* We = W + (size_t)e * n * wpr;
-    const uint16_t* Se = S + (size_t)e * n * gpr;
-    const uint16_t* Me = Mn + (size_t)e * n * gpr;
+    const MatRsrc mr = mat_rsrc(W + (size_t)e * n * wpr, S + (size_t)e * n * gpr,
+                                Mn + (size_t)e * n * gpr, n, wpr, gpr);
+    const rsrc_t xbuf = make_rsrc(X, (uint32_t)x_count * (uint32_t)k * 2u);
 
     for (int pb = p0; pb < p1; pb += MR) {
         int xr[MR];
@@ -192,7 +309,8 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
                 for (int c = 0; c < XC; ++c) {
                     const int u = (pass * XC + c) * LPR + j;
                     if (xr[r] >= 0 && u < nu)
-                        prep_xunit<B, UNIT>(X + (size_t)xr[r] * k + (size_t)u * UNIT, xu[r][c]);
+                        prep_xunit<B, UNIT>(xbuf, ((uint32_t)xr[r] * (uint32_t)k + (uint32_t)(u * UNIT)) * 2u,
+                                            xu[r][c]);
                     else
                         zero_xunit<B, UNIT>(xu[r][c]);
                 }
@@ -211,10 +329,11 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
                 for (int c = 0; c < XC; ++c) {
                     const int u = (pass * XC + c) * LPR + j;
                     if (row < n && u < nu) {
-                        load_words<WPU, ALIGN>(We + (size_t)row * wpr + (size_t)u * WPU, wv[c]);
-                        const int g = (u * UNIT) / group;
-                        sv[c] = Se[(size_t)row * gpr + g];
-                        mv[c] = Me[(size_t)row * gpr + g];
+                        buffer_words<WPU, ALIGN>(mr.w, ((uint32_t)row * (uint32_t)wpr + (uint32_t)(u * WPU)) * 4u,
+                                                 wv[c]);
+                        const uint32_t so = ((uint32_t)row * (uint32_t)gpr + (uint32_t)((u * UNIT) / group)) * 2u;
+                        sv[c] = (uint16_t)buffer_u16(mr.s, so);
+                        mv[c] = (uint16_t)buffer_u16(mr.m, so);
                     } else {
 #pragma unroll
                         for (int i = 0; i < WPU; ++i) wv[c][i] = 0u;
@@ -243,17 +362,16 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
 }
 
 // Many independent GEMVs in one launch (same bit width and group size; every
-// K fits one pass).  The work list is the concatenation, descriptor by
+// K fits in one pass).  The work list is the concatenation, descriptor by
 // descriptor, of each GEMV's row batches (SLOTS*U rows each); descriptor d's
 // batches start at item D[d].first.  Wave w takes the contiguous item range
 // [w*per, (w+1)*per), so it changes descriptor rarely; on every change it
-// rebuilds its activation units from the new x.
+// rebuilds its activation units from the new x.  Pipelined like gemv_kernel:
+// item i+1's loads are in flight while item i is reduced.
 template <int B, int UNIT, int LPR, int XC, int U>
 __global__ __launch_bounds__(256) void gemv_batched_kernel(const BatchDesc* __restrict__ D, int count,
                                                            int64_t total, int group) {
     constexpr int SLOTS = 64 / LPR;
-    constexpr int WPU = UNIT * B / 32;
-    constexpr int ALIGN = unit_align(B, UNIT);
     constexpr int ROWS = SLOTS * U;
     const int lane = threadIdx.x & 63;
     const int slot = lane / LPR, j = lane % LPR;
@@ -271,75 +389,100 @@ __global__ __launch_bounds__(256) void gemv_batched_kernel(const BatchDesc* __re
         const int mid = (lo + hi + 1) >> 1;
         if (D[mid].first <= i0) lo = mid; else hi = mid - 1;
     }
-    int d = __builtin_amdgcn_readfirstlane(lo);
 
-    BatchDesc cur;
-    XUnit<B, UNIT> xu[XC];
-    int gidx[XC];
-    bool uok[XC];
-    int64_t d_end = 0;
-    int nu = 0, wpr = 0, gpr = 0, n = 0;
-    auto enter = [&](int dd) {
-        cur = D[dd];
-        n = (int)cur.n;
-        const int k = (int)cur.k;
-        nu = k / UNIT;
-        wpr = k / 32 * B;
-        gpr = k / group;
-        d_end = cur.first + (cur.n + ROWS - 1) / ROWS;
+    // Lane geometry does not depend on the descriptor (all share the group).
+    int unit[XC], gidx[XC];
 #pragma unroll
-        for (int c = 0; c < XC; ++c) {
-            const int u = c * LPR + j;
-            uok[c] = u < nu && n > 0;
-            gidx[c] = uok[c] ? (u * UNIT) / group : 0;
-            if (uok[c])
-                prep_xunit<B, UNIT>(cur.x + (size_t)u * UNIT, xu[c]);
-            else
-                zero_xunit<B, UNIT>(xu[c]);
-        }
+    for (int c = 0; c < XC; ++c) {
+        unit[c] = c * LPR + j;
+        gidx[c] = (unit[c] * UNIT) / group;
+    }
+
+    // Item cursor: the descriptor an item belongs to, with its row geometry.
+    // Values derived from the descriptor are re-made wave-uniform where they
+    // feed a buffer resource (readfirstlane), so buffer accesses take their
+    // base straight from scalar registers.
+    struct Cursor {
+        int d, n, nu, wpr, gpr;
+        bool wide;
+        int64_t first, end;  // items [first, end) belong to descriptor d
+        const u32* w;
+        const uint16_t *s, *m, *x;
+        float* y;
     };
-    enter(d);
-
-    for (int64_t i = i0; i < i1; ++i) {
-        while (i >= d_end) enter(++d);
-        const int rb = (int)(i - cur.first) * ROWS;
-        u32 wv[U][XC][WPU];
-        uint16_t sv[U][XC], mv[U][XC];
-#pragma unroll
-        for (int r = 0; r < U; ++r) {
-            const int row = rb + r * SLOTS + slot;
-#pragma unroll
-            for (int c = 0; c < XC; ++c) {
-                const int u = c * LPR + j;
-                if (row < n && uok[c]) {
-                    load_words<WPU, ALIGN>(cur.w + (size_t)row * wpr + (size_t)u * WPU, wv[r][c]);
-                    sv[r][c] = cur.s[(size_t)row * gpr + gidx[c]];
-                    mv[r][c] = cur.m[(size_t)row * gpr + gidx[c]];
-                } else {
-#pragma unroll
-                    for (int t = 0; t < WPU; ++t) wv[r][c][t] = 0u;
-                    sv[r][c] = 0;
-                    mv[r][c] = 0;
-                }
-            }
-        }
-        float yacc[U];
-#pragma unroll
-        for (int r = 0; r < U; ++r) {
-            yacc[r] = 0.f;
-#pragma unroll
-            for (int c = 0; c < XC; ++c) {
-                const float t = unit_qx<B, UNIT>(wv[r][c], xu[c]);
-                yacc[r] = __builtin_fmaf(half_bits_to_float(sv[r][c]), t,
-                                         __builtin_fmaf(half_bits_to_float(mv[r][c]), xu[c].xsum, yacc[r]));
-            }
-        }
+    auto enter = [&](Cursor& cu, int dd) {
+        const BatchDesc& bd = D[dd];
+        cu.d = dd;
+        cu.n = (int)bd.n;
+        const int k = (int)bd.k;
+        cu.nu = cu.n > 0 ? k / UNIT : 0;
+        cu.wpr = k / 32 * B;
+        cu.gpr = k / group;
+        cu.first = bd.first;
+        cu.end = cu.first + (cu.n + ROWS - 1) / ROWS;
+        cu.w = bd.w;
+        cu.s = bd.s;
+        cu.m = bd.m;
+        cu.x = bd.x;
+        cu.y = bd.y;
+        cu.wide = wide_scales_ok<LPR, U>(cu.s, cu.m, cu.gpr);
+    };
+    auto load_item = [&](RowBatch<B, UNIT, XC, U>& bt, const Cursor& cu, int64_t i) {
+        const int n = uniform(cu.n), wpr = uniform(cu.wpr), gpr = uniform(cu.gpr);
+        const int rb = uniform((int)(i - cu.first) * ROWS);
+        const MatRsrc mr = mat_rsrc(uniform(cu.w), uniform(cu.s), uniform(cu.m), n, wpr, gpr);
+        load_batch<B, UNIT, LPR, XC, U>(bt, mr, rb, wpr, gpr, slot, unit, gidx, uniform(cu.nu),
+                                        uniform((int)cu.wide) != 0, lane);
+    };
+    auto store_item = [&](float (&yacc)[U], const Cursor& cu, int64_t i) {
+        const int n = uniform(cu.n);
+        const int rb = uniform((int)(i - cu.first) * ROWS);
+        const rsrc_t yr = make_rsrc(uniform(cu.y), (uint32_t)n * 4u);
 #pragma unroll
         for (int r = 0; r < U; ++r) {
             const float v = group_sum<LPR>(yacc[r]);
             const int row = rb + r * SLOTS + slot;
-            if (j == 0 && row < n) cur.y[row] = v;
+            if (j == 0 && row < n) buffer_store_f32(v, yr, (uint32_t)row * 4u);
         }
+    };
+
+    XUnit<B, UNIT> xu[XC];
+    int xu_desc = -1;  // descriptor whose activations xu holds
+    auto prep_for = [&](const Cursor& cu) {
+        if (cu.d == xu_desc) return;
+        xu_desc = cu.d;
+        const int nu = uniform(cu.nu);
+        const rsrc_t xr = make_rsrc(uniform(cu.x), (uint32_t)(nu * UNIT * 2));
+#pragma unroll
+        for (int c = 0; c < XC; ++c) {
+            if (unit[c] < nu)
+                prep_xunit<B, UNIT>(xr, (uint32_t)(unit[c] * UNIT * 2), xu[c]);
+            else
+                zero_xunit<B, UNIT>(xu[c]);
+        }
+    };
+
+    Cursor cur;
+    enter(cur, __builtin_amdgcn_readfirstlane(lo));
+    while (i0 >= cur.end) enter(cur, cur.d + 1);
+    RowBatch<B, UNIT, XC, U> bcur, bnxt;
+    load_item(bcur, cur, i0);
+    for (int64_t i = i0; i < i1; ++i) {
+        // Item i is loaded in bcur; fetch item i+1 before reducing item i.
+        Cursor nc = cur;
+        if (i + 1 < i1) {
+            while (i + 1 >= nc.end) enter(nc, nc.d + 1);
+            load_item(bnxt, nc, i + 1);
+        }
+        prep_for(cur);
+        float yacc[U];
+#pragma unroll
+        for (int r = 0; r < U; ++r) yacc[r] = 0.f;
+        accumulate_batch<B, UNIT, LPR, XC, U>(bcur, xu, yacc, uniform((int)cur.wide) != 0, slot,
+                                              uniform(cur.gpr), gidx);
+        store_item(yacc, cur, i);
+        bcur = bnxt;
+        cur = nc;
     }
 }
 
@@ -347,19 +490,23 @@ __global__ __launch_bounds__(256) void gemv_batched_kernel(const BatchDesc* __re
 
 template <int B, int UNIT, int LPR, int XC, int U>
 hipError_t launch_gemv_t(const GemvArgs& a, const GemvShape& sh, hipStream_t st) {
-    if (sh.multipass)
-        hipLaunchKernelGGL((gemv_kernel<B, UNIT, LPR, XC, U, true>), dim3(sh.grid), dim3(256), 0, st,
-                           a.w, a.s, a.m, a.x, a.y, a.n, a.k, a.group);
-    else
-        hipLaunchKernelGGL((gemv_kernel<B, UNIT, LPR, XC, U, false>), dim3(sh.grid), dim3(256), 0, st,
-                           a.w, a.s, a.m, a.x, a.y, a.n, a.k, a.group);
+    if (sh.multipass) {
+        constexpr auto kern = gemv_kernel<B, UNIT, LPR, XC, U, true>;
+        const int grid = persistent_grid(sh.work, sh.cus, blocks_per_cu<kern>(), sh.waves_per_cu);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, a.w, a.s, a.m, a.x, a.y, a.n, a.k, a.group);
+    } else {
+        constexpr auto kern = gemv_kernel<B, UNIT, LPR, XC, U, false>;
+        const int grid = persistent_grid(sh.work, sh.cus, blocks_per_cu<kern>(), sh.waves_per_cu);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, a.w, a.s, a.m, a.x, a.y, a.n, a.k, a.group);
+    }
     return hipGetLastError();
 }
 
 template <int B, int UNIT, int LPR, int XC, int U>
 hipError_t launch_batched_t(const BatchArgs& a, const GemvShape& sh, hipStream_t st) {
-    hipLaunchKernelGGL((gemv_batched_kernel<B, UNIT, LPR, XC, U>), dim3(sh.grid), dim3(256), 0, st,
-                       a.descs, a.count, a.total_items, a.group);
+    constexpr auto kern = gemv_batched_kernel<B, UNIT, LPR, XC, U>;
+    const int grid = persistent_grid(sh.work, sh.cus, blocks_per_cu<kern>(), sh.waves_per_cu);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, a.descs, a.count, a.total_items, a.group);
     return hipGetLastError();
 }
 

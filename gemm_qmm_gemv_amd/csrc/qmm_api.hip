@@ -126,26 +126,18 @@ struct LaneSplit {
     bool multipass;
 };
 
-// Lanes per row and units per lane: the single-pass split with the fewest idle
-// unit slots; ties prefer fewer units per lane (more lanes in flight).
+// Lanes per row and units per lane.  One unit per lane while a row has at
+// most 64 units (lanes = the next power of two: idle lanes cost less than a
+// second serial unit, which doubles the activation registers and the work
+// between a lane's loads); above that, 64 lanes with ceil(units/64) units each
+// up to max_xc, and multi-pass beyond.
 LaneSplit choose_split(int nu, int max_xc, bool (*supported)(int, int)) {
-    static const int cand[][2] = {{16, 1}, {32, 1}, {64, 1}, {8, 1}, {16, 2}, {32, 2},
-                                  {64, 2}, {8, 2},  {16, 3}};
-    LaneSplit best{64, max_xc >= 2 ? 2 : 1, true};
-    int best_waste = 1 << 30, best_xc = 99;
-    for (const auto& c : cand) {
-        const int lpr = c[0], xc = c[1];
-        if (xc > max_xc || !supported(lpr, xc)) continue;
-        const int cap = lpr * xc;
-        if (cap < nu) continue;
-        const int waste = cap - nu;
-        if (waste < best_waste || (waste == best_waste && xc < best_xc)) {
-            best = {lpr, xc, false};
-            best_waste = waste;
-            best_xc = xc;
-        }
-    }
-    return best;
+    int lpr = 16;
+    while (lpr < 64 && lpr < nu) lpr *= 2;
+    const int xc = (nu + lpr - 1) / lpr;
+    if (xc <= max_xc && supported(lpr, xc)) return {lpr, xc, false};
+    const int mxc = max_xc >= 2 ? 2 : 1;
+    return {64, mxc, true};
 }
 
 bool gemv_split_ok(int lpr, int xc) { return gemv_shape_supported(lpr, xc, 1); }
@@ -154,9 +146,11 @@ bool rows_split_ok(int lpr, int xc) { return rows_shape_supported(lpr, xc, xc ==
 
 GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     GemvShape sh{};
-    sh.unit = (group % 64 == 0) ? 64 : 32;
+    sh.unit = (group % 64 == 0 && env_int("QMM_UNIT", 64) != 32) ? 64 : 32;
     const int nu = (int)(k / sh.unit);
     LaneSplit ls = choose_split(nu, 3, gemv_split_ok);
+    const int el = env_int("QMM_GEMV_LPR", 0), ex = env_int("QMM_GEMV_XC", 0);
+    if (el > 0 && ex > 0 && gemv_split_ok(el, ex)) ls = {el, ex, el * ex < nu};
     sh.lpr = ls.lpr;
     sh.xc = ls.xc;
     sh.multipass = ls.multipass;
@@ -164,22 +158,23 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     // Rows per slot per iteration: one when the row count alone fills the chip
     // with single-iteration waves; otherwise enough to keep ~128 bytes of
     // weights per lane in flight.
+    // Rows per slot per iteration: one when the row count alone fills the
+    // chip with single-iteration waves; otherwise two (the kernel keeps the
+    // next iteration's loads in flight, so two rows per slot already hold
+    // 2-4 units of weights per lane in flight).
     const int64_t waves_u1 = (n + slots - 1) / slots;
-    const int unit_bytes = sh.unit * bits / 8;
-    int u = 1;
-    if (waves_u1 > (int64_t)cus * 16) {
-        const int want = 128 / (unit_bytes * sh.xc);
-        u = want >= 4 ? 4 : want >= 2 ? 2 : 1;
-    }
+    int u = (waves_u1 > (int64_t)cus * 16) ? 2 : 1;
     while (u > 1 && !gemv_shape_supported(sh.lpr, sh.xc, u)) u /= 2;
     const int ev = env_int("QMM_GEMV_U", 0);
     if (ev > 0 && gemv_shape_supported(sh.lpr, sh.xc, ev)) u = ev;
     sh.u = u;
     const int64_t batches = (n + (int64_t)slots * u - 1) / ((int64_t)slots * u);
-    const int64_t max_waves = (int64_t)cus * env_int("QMM_GEMV_WAVES_PER_CU", 32);
-    const int64_t waves = batches < max_waves ? batches : max_waves;
-    sh.grid = (int)((waves + 3) / 4);
-    if (sh.grid < 1) sh.grid = 1;
+    sh.work = batches;
+    sh.cus = cus;
+    sh.waves_per_cu = env_int("QMM_GEMV_WAVES_PER_CU", 0);
+    // Reported grid: the cap assumes 16 resident waves per CU; the launch
+    // uses the kernel's real occupancy.
+    sh.grid = persistent_grid(sh.work, cus, sh.waves_per_cu > 0 ? sh.waves_per_cu / 4 : 4, 0);
     return sh;
 }
 
@@ -187,22 +182,20 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
 // largest K (which must fit a single pass) and the total row count.
 bool plan_batched(int64_t total_rows, int64_t kmax, int bits, int group, GemvShape* out) {
     GemvShape sh{};
-    sh.unit = (group % 64 == 0) ? 64 : 32;
+    sh.unit = (group % 64 == 0 && env_int("QMM_UNIT", 64) != 32) ? 64 : 32;
     const int nu = (int)(kmax / sh.unit);
     LaneSplit ls = choose_split(nu, 3, batched_split_ok);
+    const int el = env_int("QMM_BATCH_LPR", 0), ex = env_int("QMM_BATCH_XC", 0);
+    if (el > 0 && ex > 0 && batched_split_ok(el, ex) && el * ex >= nu) ls = {el, ex, false};
     if (ls.multipass) return false;
     sh.lpr = ls.lpr;
     sh.xc = ls.xc;
     sh.multipass = false;
     const int slots = 64 / sh.lpr;
-    const int unit_bytes = sh.unit * bits / 8;
-    int u = 1;
+    (void)bits;
     // The row count decides, not the device, so prepared descriptors stay
-    // valid on any GPU: big batches stream with several rows per lane.
-    if (total_rows > (int64_t)slots * 4096) {
-        const int want = 128 / (unit_bytes * sh.xc);
-        u = want >= 4 ? 4 : want >= 2 ? 2 : 1;
-    }
+    // valid on any GPU: big batches stream two rows per slot per iteration.
+    int u = (total_rows > (int64_t)slots * 4096) ? 2 : 1;
     while (u > 1 && !batched_shape_supported(sh.lpr, sh.xc, u)) u /= 2;
     const int ev = env_int("QMM_BATCH_U", 0);
     if (ev > 0 && batched_shape_supported(sh.lpr, sh.xc, ev)) u = ev;
@@ -445,9 +438,9 @@ qmm_status qmm_gemv_batched(const qmm_gemv_desc* descs_device, const qmm_gemv_de
     }
     int cus = 0;
     if ((st = device_cus(&cus)) != QMM_OK) return st;
-    const int64_t max_waves = (int64_t)cus * env_int("QMM_GEMV_WAVES_PER_CU", 32);
-    const int64_t waves = first < max_waves ? first : max_waves;
-    sh.grid = (int)((waves + 3) / 4);
+    sh.work = first;
+    sh.cus = cus;
+    sh.waves_per_cu = env_int("QMM_GEMV_WAVES_PER_CU", 0);
     BatchArgs a{reinterpret_cast<const BatchDesc*>(descs_device), (int)count, first, group_size, bits};
     return launched(launch_batched(a, sh, as_stream(stream)), "qmm_gemv_batched");
 }
@@ -499,8 +492,7 @@ qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits, int g
         plan->rows_per_iter = sh.u;
         plan->unit_codes = sh.unit;
         const int64_t items = (n + (64 / sh.lpr) * sh.u - 1) / ((64 / sh.lpr) * sh.u);
-        const int64_t w = items < (int64_t)cus * 32 ? items : (int64_t)cus * 32;
-        plan->grid = (w + 3) / 4;
+        plan->grid = persistent_grid(items, cus, 4, 0);
         return ok();
     }
     if (op == 2 || (op == 1 && m <= ROWS_KERNEL_MAX_M)) {

@@ -58,6 +58,75 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t v) {
 __device__ __forceinline__ u32 funnel(u32 hi, u32 lo, u32 sh) {
     return __builtin_amdgcn_alignbit(hi, lo, sh);
 }
+// (v & mask) | 0x64006400 as one v_and_or_b32.  gfx9 VOP3 encodings take no
+// literal operands and at most one scalar register, so the mask comes from
+// an SGPR and the fp16 pair constant from a VGPR; left to itself the
+// compiler splits this into an AND and an OR with literals.
+__device__ __forceinline__ u32 mask_or_magic(u32 v, u32 mask) {
+    u32 r;
+    const u32 magic = MAGIC2;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(magic));
+    return r;
+}
+// Raw buffer resources.  A buffer load addresses memory as an SGPR base plus
+// a 32-bit VGPR byte offset, and returns zero for offsets at or past the
+// resource's size, so row and unit tails need no branches and the per-load
+// address arithmetic is one 32-bit multiply-add instead of 64-bit math.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Word 3 of the descriptor: 32-bit data format, the setting for raw
+// (untyped) buffer access on gfx9-family parts.
+constexpr int RSRC_WORD3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, RSRC_WORD3);
+}
+
+// NW consecutive words at byte offset off (aligned to A bytes).
+template <int NW, int A>
+__device__ __forceinline__ void buffer_words(rsrc_t r, uint32_t off, u32 (&w)[NW]) {
+    if constexpr (A == 16 && NW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < NW / 4; ++i) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0);
+            w[4 * i + 0] = v[0]; w[4 * i + 1] = v[1]; w[4 * i + 2] = v[2]; w[4 * i + 3] = v[3];
+        }
+    } else if constexpr (A >= 8 && NW % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < NW / 2; ++i) {
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 8 * i, 0, 0);
+            w[2 * i + 0] = v[0]; w[2 * i + 1] = v[1];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void buffer_store_f32(float v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, v), r, off, 0, 0);
+}
+
+// Values the whole wave agrees on, made explicitly scalar.  Loads from a
+// descriptor table that the kernel also writes through (outputs) cannot be
+// proven invariant, so the compiler would treat them as per-lane values and
+// wrap every buffer access in a loop over distinct values.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <class T>
+__device__ __forceinline__ T* uniform(T* p) {
+    return reinterpret_cast<T*>(uniform(reinterpret_cast<int64_t>(p)));
+}
+
+__device__ __forceinline__ u32 buffer_u16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ u32 buffer_u32(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
 // 24-bit field t (codes at bits 0..23) -> low 12 bits kept, bits 12..23 moved
 // to 16..27; bits 12..15 and 28..31 of the result are don't-care.
 __device__ __forceinline__ u32 spread12(u32 t) {
@@ -80,7 +149,7 @@ template <> struct PairFmt<2> {
             const u32 v = w[j], v8 = w[j] >> 8;
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                p[8 * j + t] = ((t < 4 ? v : v8) & (0x00030003u << (2 * (t % 4)))) | MAGIC2;
+                p[8 * j + t] = mask_or_magic(t < 4 ? v : v8, 0x00030003u << (2 * (t % 4)));
         }
     }
 };
@@ -99,10 +168,10 @@ template <> struct PairFmt<3> {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const u32 u = spread12(t[q]);
-            p[4 * q + 0] = (u & 0x00070007u) | MAGIC2;
-            p[4 * q + 1] = (u & 0x00380038u) | MAGIC2;
-            p[4 * q + 2] = (u & 0x01C001C0u) | MAGIC2;
-            p[4 * q + 3] = ((u >> 9) & 0x00070007u) | MAGIC2;
+            p[4 * q + 0] = mask_or_magic(u, 0x00070007u);
+            p[4 * q + 1] = mask_or_magic(u, 0x00380038u);
+            p[4 * q + 2] = mask_or_magic(u, 0x01C001C0u);
+            p[4 * q + 3] = mask_or_magic(u >> 9, 0x00070007u);
         }
     }
 };
@@ -119,10 +188,10 @@ template <> struct PairFmt<4> {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const u32 v = w[j], v8 = w[j] >> 8;
-            p[4 * j + 0] = (v & 0x000F000Fu) | MAGIC2;
-            p[4 * j + 1] = (v & 0x00F000F0u) | MAGIC2;
-            p[4 * j + 2] = (v8 & 0x000F000Fu) | MAGIC2;
-            p[4 * j + 3] = (v8 & 0x00F000F0u) | MAGIC2;
+            p[4 * j + 0] = mask_or_magic(v, 0x000F000Fu);
+            p[4 * j + 1] = mask_or_magic(v, 0x00F000F0u);
+            p[4 * j + 2] = mask_or_magic(v8, 0x000F000Fu);
+            p[4 * j + 3] = mask_or_magic(v8, 0x00F000F0u);
         }
     }
 };
@@ -142,8 +211,8 @@ template <> struct PairFmt<6> {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const u32 u = spread12(t[q]);
-            p[2 * q + 0] = (u & 0x003F003Fu) | MAGIC2;
-            p[2 * q + 1] = ((u >> 6) & 0x003F003Fu) | MAGIC2;
+            p[2 * q + 0] = mask_or_magic(u, 0x003F003Fu);
+            p[2 * q + 1] = mask_or_magic(u >> 6, 0x003F003Fu);
         }
     }
 };
@@ -158,8 +227,8 @@ template <> struct PairFmt<8> {
     __device__ static __forceinline__ void extract(const u32* w, u32* p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[2 * j + 0] = (w[j] & 0x00FF00FFu) | MAGIC2;
-            p[2 * j + 1] = ((w[j] >> 8) & 0x00FF00FFu) | MAGIC2;
+            p[2 * j + 0] = mask_or_magic(w[j], 0x00FF00FFu);
+            p[2 * j + 1] = mask_or_magic(w[j] >> 8, 0x00FF00FFu);
         }
     }
 };
@@ -204,13 +273,18 @@ struct XUnit {
     float xsum;  // sum of the UNIT activations
 };
 
-// Build an XUnit from UNIT fp16 activations at x (16-byte aligned).
+// Build an XUnit from the UNIT fp16 activations at byte offset off of the
+// activation buffer (16-byte aligned).
 template <int B, int UNIT>
-__device__ __forceinline__ void prep_xunit(const uint16_t* __restrict__ x, XUnit<B, UNIT>& xu) {
+__device__ __forceinline__ void prep_xunit(rsrc_t xr, uint32_t off, XUnit<B, UNIT>& xu) {
     using F = PairFmt<B>;
     u32 xw[UNIT / 2];
-    load_words<UNIT / 2, 16>(reinterpret_cast<const u32*>(x), xw);
+    buffer_words<UNIT / 2, 16>(xr, off, xw);
+    // Both constants come from packed dot products on the pairs themselves:
+    // corr += x_a * c + x_b * c with c = 1024 * 2^-f (exact in fp16), and
+    // xsum += x_a + x_b.  No per-element conversions, few live registers.
     float corr = 0.f, xsum = 0.f;
+    const f16x2 one2 = {(f16)1.0f, (f16)1.0f};
 #pragma unroll
     for (int c = 0; c < UNIT / 32; ++c) {
 #pragma unroll
@@ -218,15 +292,12 @@ __device__ __forceinline__ void prep_xunit(const uint16_t* __restrict__ x, XUnit
             const int a = 32 * c + F::ka(i), b = 32 * c + F::kb(i);
             const u32 lo = (xw[a / 2] >> (16 * (a % 2))) & 0xFFFFu;
             const u32 hi = (xw[b / 2] >> (16 * (b % 2))) & 0xFFFFu;
-            xu.xp[16 * c + i] = as_h2(lo | (hi << 16));
-            const float fa = half_bits_to_float((uint16_t)lo), fb = half_bits_to_float((uint16_t)hi);
-            corr += 1024.f * F::inv_factor(F::acc(i)) * (fa + fb);
+            const f16x2 pr = as_h2(lo | (hi << 16));
+            xu.xp[16 * c + i] = pr;
+            const f16 cf = (f16)(1024.0f * F::inv_factor(F::acc(i)));
+            corr = __builtin_amdgcn_fdot2(pr, f16x2{cf, cf}, corr, false);
+            xsum = __builtin_amdgcn_fdot2(pr, one2, xsum, false);
         }
-    }
-#pragma unroll
-    for (int i = 0; i < UNIT / 2; ++i) {
-        xsum += half_bits_to_float((uint16_t)(xw[i] & 0xFFFFu));
-        xsum += half_bits_to_float((uint16_t)(xw[i] >> 16));
     }
     xu.corr = corr;
     xu.xsum = xsum;

@@ -17,13 +17,44 @@ struct GemvArgs {
 };
 
 struct GemvShape {
-    int unit;       // codes per unit: 64 or 32
-    int lpr;        // lanes per row
-    int xc;         // units per lane per pass
-    int u;          // rows per slot per iteration
-    bool multipass; // k > lpr * xc * unit
-    int grid;       // work-groups of 256 threads
+    int unit;           // codes per unit: 64 or 32
+    int lpr;            // lanes per row
+    int xc;             // units per lane per pass
+    int u;              // rows per slot per iteration
+    bool multipass;     // k > lpr * xc * unit
+    int64_t work;       // row batches (waves that have work)
+    int cus;            // compute units of the device
+    int waves_per_cu;   // > 0: cap resident waves per CU; 0: the kernel's occupancy
+    int grid;           // work-groups of 256 threads (set at launch)
 };
+
+// Work-groups for a persistent launch: enough for the work, at most what the
+// device holds resident at once (blocks_per_cu from the kernel's occupancy),
+// so no wave waits for another to finish before it can start.
+inline int persistent_grid(int64_t work_waves, int cus, int blocks_per_cu, int waves_per_cu_override) {
+    const int64_t cap = waves_per_cu_override > 0 ? (int64_t)cus * waves_per_cu_override / 4
+                                                  : (int64_t)cus * blocks_per_cu;
+    int64_t g = (work_waves + 3) / 4;
+    if (g > cap) g = cap;
+    return g < 1 ? 1 : (int)g;
+}
+
+// Resident 256-thread work-groups per CU for a kernel (queried once per
+// kernel: the template parameter is the kernel itself).
+template <auto Kernel>
+inline int blocks_per_cu() {
+    static int cached = 0;
+    if (cached == 0) {
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(Kernel), 256, 0) !=
+                hipSuccess || nb <= 0) {
+            (void)hipGetLastError();
+            nb = 2;
+        }
+        cached = nb;
+    }
+    return cached;
+}
 
 struct RowsArgs {
     const uint32_t* w;
@@ -85,20 +116,12 @@ struct BatchArgs {
 // per lane, rows per slot) for the GEMV kernels, (lanes, units, activation
 // rows) for the multi-row kernel.
 #define QMM_GEMV_SHAPES(X) \
-    X(16, 1, 1) X(16, 1, 2) X(16, 1, 4) \
-    X(32, 1, 1) X(32, 1, 2) X(32, 1, 4) \
-    X(64, 1, 1) X(64, 1, 2) X(64, 1, 4) \
-    X(16, 2, 1) X(16, 2, 2) \
-    X(32, 2, 1) X(32, 2, 2) \
-    X(64, 2, 1) X(64, 2, 2) \
-    X(16, 3, 1) X(16, 3, 2) \
-    X(8, 2, 1) X(8, 2, 2) X(8, 1, 2) X(8, 1, 4)
+    X(16, 1, 1) X(16, 1, 2) \
+    X(32, 1, 1) X(32, 1, 2) \
+    X(64, 1, 1) X(64, 1, 2) \
+    X(64, 2, 1) X(64, 2, 2)
 
-#define QMM_BATCHED_SHAPES(X) \
-    X(16, 1, 1) X(16, 1, 2) X(16, 1, 4) \
-    X(32, 1, 1) X(32, 1, 2) X(32, 1, 4) \
-    X(64, 1, 1) X(64, 1, 2) X(64, 1, 4) \
-    X(64, 2, 1) X(64, 2, 2) X(16, 3, 1) X(16, 3, 2)
+#define QMM_BATCHED_SHAPES(X) QMM_GEMV_SHAPES(X)
 
 #define QMM_ROWS_SHAPES(X) \
     X(16, 1, 4) X(32, 1, 4) X(64, 1, 4) \
