@@ -50,14 +50,17 @@ __device__ __forceinline__ bool wide_scales_ok(const uint16_t* S, const uint16_t
            (gpr & 1) == 0 && SLOTS * U * gpr <= 128;
 }
 
-// Buffer resources over one matrix: packed weights, scales, mins.
+// Buffer resources over one matrix: packed weights, scales, mins, with their
+// byte sizes.  An offset equal to the size reads zeros, which is how lanes
+// with nothing to load are handled without branches.
 struct MatRsrc {
     rsrc_t w, s, m;
+    uint32_t wbytes, sbytes;
 };
 __device__ __forceinline__ MatRsrc mat_rsrc(const void* W, const void* S, const void* Mn, int n,
                                             int wpr, int gpr) {
-    return {make_rsrc(W, (uint32_t)n * (uint32_t)wpr * 4u), make_rsrc(S, (uint32_t)n * (uint32_t)gpr * 2u),
-            make_rsrc(Mn, (uint32_t)n * (uint32_t)gpr * 2u)};
+    const uint32_t wb = (uint32_t)n * (uint32_t)wpr * 4u, sb = (uint32_t)n * (uint32_t)gpr * 2u;
+    return {make_rsrc(W, wb), make_rsrc(S, sb), make_rsrc(Mn, sb), wb, sb};
 }
 
 // Issue every load of a row batch (rows rb + r*SLOTS + slot, r < U).  Rows
@@ -71,28 +74,22 @@ __device__ __forceinline__ void load_batch(RowBatch<B, UNIT, XC, U>& bt, const M
     constexpr int ALIGN = unit_align(B, UNIT);
     if (wide) {
         const int words = SLOTS * U * gpr / 2;
-        const uint32_t off = ((uint32_t)rb * (uint32_t)gpr + 2u * (uint32_t)lane) * 2u;
-        bt.sblk = lane < words ? buffer_u32(mr.s, off) : 0u;
-        bt.mblk = lane < words ? buffer_u32(mr.m, off) : 0u;
+        const uint32_t off = lane < words ? ((uint32_t)rb * (uint32_t)gpr + 2u * (uint32_t)lane) * 2u : mr.sbytes;
+        bt.sblk = buffer_u32(mr.s, off);
+        bt.mblk = buffer_u32(mr.m, off);
     }
 #pragma unroll
     for (int r = 0; r < U; ++r) {
         const uint32_t row = (uint32_t)(rb + r * SLOTS + slot);
 #pragma unroll
         for (int c = 0; c < XC; ++c) {
-            bt.s[r][c] = 0u;
-            bt.m[r][c] = 0u;
-            if (unit[c] < nu) {
-                buffer_words<WPU, ALIGN>(mr.w, (row * (uint32_t)wpr + (uint32_t)(unit[c] * WPU)) * 4u,
-                                         bt.w[r][c]);
-                if (!wide) {
-                    const uint32_t so = (row * (uint32_t)gpr + (uint32_t)gidx[c]) * 2u;
-                    bt.s[r][c] = buffer_u16(mr.s, so);
-                    bt.m[r][c] = buffer_u16(mr.m, so);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < WPU; ++i) bt.w[r][c][i] = 0u;
+            const bool live = unit[c] < nu;  // rows past n fall past the end by themselves
+            const uint32_t woff = live ? (row * (uint32_t)wpr + (uint32_t)(unit[c] * WPU)) * 4u : mr.wbytes;
+            buffer_words<WPU, ALIGN>(mr.w, woff, bt.w[r][c]);
+            if (!wide) {
+                const uint32_t so = live ? (row * (uint32_t)gpr + (uint32_t)gidx[c]) * 2u : mr.sbytes;
+                bt.s[r][c] = buffer_u16(mr.s, so);
+                bt.m[r][c] = buffer_u16(mr.m, so);
             }
         }
     }
@@ -361,26 +358,86 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
     }
 }
 
-// Many independent GEMVs in one launch (same bit width and group size; every
-// K fits in one pass).  The work list is the concatenation, descriptor by
-// descriptor, of each GEMV's row batches (SLOTS*U rows each); descriptor d's
-// batches start at item D[d].first.  Wave w takes the contiguous item range
-// [w*per, (w+1)*per), so it changes descriptor rarely; on every change it
-// rebuilds its activation units from the new x.  Pipelined like gemv_kernel:
-// item i+1's loads are in flight while item i is reduced.
+// Many independent GEMVs in one launch (same bit width and group size).
+// Each descriptor gets its own lane layout, chosen from its K exactly as
+// batched_lanes_per_row_host() does on the host: LPR lanes per row (16, 32 or
+// 64) with XC units each, so matrices of different K share one launch.  The
+// work list is the concatenation, descriptor by descriptor, of each GEMV's
+// row batches (64/LPR * U rows each); descriptor d's batches start at item
+// D[d].first.  Wave w takes the contiguous item range
+// [w*total/nwaves, (w+1)*total/nwaves) -- sizes differ by at most one -- and
+// walks it as runs, one per descriptor it touches.  A run is the same
+// pipelined loop as the single GEMV with the lane layout fixed at compile
+// time; between runs the wave rebuilds its activation units.
+template <int XC>
+__device__ __forceinline__ int batched_lanes_per_row(int nu) {
+    int lpr = 16;
+    while (lpr < 64 && lpr * XC < nu) lpr *= 2;
+    return lpr;
+}
+
+// Row batches [b0, b1) of one matrix (all arguments wave-uniform).
 template <int B, int UNIT, int LPR, int XC, int U>
-__global__ __launch_bounds__(256) void gemv_batched_kernel(const BatchDesc* __restrict__ D, int count,
-                                                           int64_t total, int group) {
+__device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const uint16_t* Mn,
+                                         const uint16_t* X, float* Y, int n, int k, int group, int b0,
+                                         int b1, int lane) {
     constexpr int SLOTS = 64 / LPR;
     constexpr int ROWS = SLOTS * U;
-    const int lane = threadIdx.x & 63;
     const int slot = lane / LPR, j = lane % LPR;
+    const int nu = k / UNIT;
+    const int wpr = k / 32 * B;
+    const int gpr = k / group;
+    const bool wide = wide_scales_ok<LPR, U>(S, Mn, gpr);
+    const MatRsrc mr = mat_rsrc(W, S, Mn, n, wpr, gpr);
+    const rsrc_t xr = make_rsrc(X, (uint32_t)k * 2u);
+    const rsrc_t yr = make_rsrc(Y, (uint32_t)n * 4u);
+    int unit[XC], gidx[XC];
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+        unit[c] = c * LPR + j;
+        gidx[c] = unit[c] < nu ? (unit[c] * UNIT) / group : 0;
+    }
+    RowBatch<B, UNIT, XC, U> ba, bb;
+    load_batch<B, UNIT, LPR, XC, U>(ba, mr, b0 * ROWS, wpr, gpr, slot, unit, gidx, nu, wide, lane);
+    XUnit<B, UNIT> xu[XC];
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+        if (unit[c] < nu)
+            prep_xunit<B, UNIT>(xr, (uint32_t)(unit[c] * UNIT * 2), xu[c]);
+        else
+            zero_xunit<B, UNIT>(xu[c]);
+    }
+    auto finish = [&](const RowBatch<B, UNIT, XC, U>& bt, int b) {
+        float yacc[U];
+#pragma unroll
+        for (int r = 0; r < U; ++r) yacc[r] = 0.f;
+        accumulate_batch<B, UNIT, LPR, XC, U>(bt, xu, yacc, wide, slot, gpr, gidx);
+        const int rb = b * ROWS;
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            const float v = group_sum<LPR>(yacc[r]);
+            const int row = rb + r * SLOTS + slot;
+            if (j == 0 && row < n) buffer_store_f32(v, yr, (uint32_t)row * 4u);
+        }
+    };
+    for (int b = b0; b < b1; b += 2) {
+        if (b + 1 < b1) load_batch<B, UNIT, LPR, XC, U>(bb, mr, (b + 1) * ROWS, wpr, gpr, slot, unit, gidx, nu, wide, lane);
+        finish(ba, b);
+        if (b + 1 >= b1) break;
+        if (b + 2 < b1) load_batch<B, UNIT, LPR, XC, U>(ba, mr, (b + 2) * ROWS, wpr, gpr, slot, unit, gidx, nu, wide, lane);
+        finish(bb, b + 1);
+    }
+}
+
+template <int B, int UNIT, int XC, int U>
+__global__ __launch_bounds__(256) void gemv_batched_kernel(const BatchDesc* __restrict__ D, int count,
+                                                           int64_t total, int group) {
+    const int lane = threadIdx.x & 63;
     const int waves_per_block = blockDim.x >> 6;
     const int wave = blockIdx.x * waves_per_block + (threadIdx.x >> 6);
     const int nwaves = gridDim.x * waves_per_block;
-    const int64_t per = (total + nwaves - 1) / nwaves;
-    const int64_t i0 = (int64_t)wave * per;
-    const int64_t i1 = i0 + per < total ? i0 + per : total;
+    const int64_t i0 = total * wave / nwaves;
+    const int64_t i1 = total * (wave + 1) / nwaves;
     if (i0 >= i1) return;
 
     // Last descriptor whose first item is <= i0 (binary search, wave-uniform).
@@ -389,100 +446,35 @@ __global__ __launch_bounds__(256) void gemv_batched_kernel(const BatchDesc* __re
         const int mid = (lo + hi + 1) >> 1;
         if (D[mid].first <= i0) lo = mid; else hi = mid - 1;
     }
-
-    // Lane geometry does not depend on the descriptor (all share the group).
-    int unit[XC], gidx[XC];
-#pragma unroll
-    for (int c = 0; c < XC; ++c) {
-        unit[c] = c * LPR + j;
-        gidx[c] = (unit[c] * UNIT) / group;
-    }
-
-    // Item cursor: the descriptor an item belongs to, with its row geometry.
-    // Values derived from the descriptor are re-made wave-uniform where they
-    // feed a buffer resource (readfirstlane), so buffer accesses take their
-    // base straight from scalar registers.
-    struct Cursor {
-        int d, n, nu, wpr, gpr;
-        bool wide;
-        int64_t first, end;  // items [first, end) belong to descriptor d
-        const u32* w;
-        const uint16_t *s, *m, *x;
-        float* y;
-    };
-    auto enter = [&](Cursor& cu, int dd) {
-        const BatchDesc& bd = D[dd];
-        cu.d = dd;
-        cu.n = (int)bd.n;
-        const int k = (int)bd.k;
-        cu.nu = cu.n > 0 ? k / UNIT : 0;
-        cu.wpr = k / 32 * B;
-        cu.gpr = k / group;
-        cu.first = bd.first;
-        cu.end = cu.first + (cu.n + ROWS - 1) / ROWS;
-        cu.w = bd.w;
-        cu.s = bd.s;
-        cu.m = bd.m;
-        cu.x = bd.x;
-        cu.y = bd.y;
-        cu.wide = wide_scales_ok<LPR, U>(cu.s, cu.m, cu.gpr);
-    };
-    auto load_item = [&](RowBatch<B, UNIT, XC, U>& bt, const Cursor& cu, int64_t i) {
-        const int n = uniform(cu.n), wpr = uniform(cu.wpr), gpr = uniform(cu.gpr);
-        const int rb = uniform((int)(i - cu.first) * ROWS);
-        const MatRsrc mr = mat_rsrc(uniform(cu.w), uniform(cu.s), uniform(cu.m), n, wpr, gpr);
-        load_batch<B, UNIT, LPR, XC, U>(bt, mr, rb, wpr, gpr, slot, unit, gidx, uniform(cu.nu),
-                                        uniform((int)cu.wide) != 0, lane);
-    };
-    auto store_item = [&](float (&yacc)[U], const Cursor& cu, int64_t i) {
-        const int n = uniform(cu.n);
-        const int rb = uniform((int)(i - cu.first) * ROWS);
-        const rsrc_t yr = make_rsrc(uniform(cu.y), (uint32_t)n * 4u);
-#pragma unroll
-        for (int r = 0; r < U; ++r) {
-            const float v = group_sum<LPR>(yacc[r]);
-            const int row = rb + r * SLOTS + slot;
-            if (j == 0 && row < n) buffer_store_f32(v, yr, (uint32_t)row * 4u);
-        }
-    };
-
-    XUnit<B, UNIT> xu[XC];
-    int xu_desc = -1;  // descriptor whose activations xu holds
-    auto prep_for = [&](const Cursor& cu) {
-        if (cu.d == xu_desc) return;
-        xu_desc = cu.d;
-        const int nu = uniform(cu.nu);
-        const rsrc_t xr = make_rsrc(uniform(cu.x), (uint32_t)(nu * UNIT * 2));
-#pragma unroll
-        for (int c = 0; c < XC; ++c) {
-            if (unit[c] < nu)
-                prep_xunit<B, UNIT>(xr, (uint32_t)(unit[c] * UNIT * 2), xu[c]);
+    int d = uniform(lo);
+    int64_t i = i0;
+    while (i < i1 && d < count) {
+        // Descriptor fields, made explicitly wave-uniform: the table is read
+        // through the vector path (the kernel writes memory), and the values
+        // feed buffer resources that must live in scalar registers.
+        const BatchDesc& bd = D[d];
+        const int n = uniform((int)bd.n), k = uniform((int)bd.k);
+        const int64_t first = uniform(bd.first);
+        const int lpr = batched_lanes_per_row<XC>(k / UNIT);
+        const int rows = (64 / lpr) * U;
+        const int64_t end = first + (n + rows - 1) / rows;
+        if (i < end) {
+            const int b0 = (int)(i - first);
+            const int b1 = (int)((i1 < end ? i1 : end) - first);
+            const u32* w = uniform(bd.w);
+            const uint16_t* sp = uniform(bd.s);
+            const uint16_t* mp = uniform(bd.m);
+            const uint16_t* xp = uniform(bd.x);
+            float* yp = uniform(bd.y);
+            if (lpr == 16)
+                gemv_run<B, UNIT, 16, XC, U>(w, sp, mp, xp, yp, n, k, group, b0, b1, lane);
+            else if (lpr == 32)
+                gemv_run<B, UNIT, 32, XC, U>(w, sp, mp, xp, yp, n, k, group, b0, b1, lane);
             else
-                zero_xunit<B, UNIT>(xu[c]);
+                gemv_run<B, UNIT, 64, XC, U>(w, sp, mp, xp, yp, n, k, group, b0, b1, lane);
+            i = first + b1;
         }
-    };
-
-    Cursor cur;
-    enter(cur, __builtin_amdgcn_readfirstlane(lo));
-    while (i0 >= cur.end) enter(cur, cur.d + 1);
-    RowBatch<B, UNIT, XC, U> bcur, bnxt;
-    load_item(bcur, cur, i0);
-    for (int64_t i = i0; i < i1; ++i) {
-        // Item i is loaded in bcur; fetch item i+1 before reducing item i.
-        Cursor nc = cur;
-        if (i + 1 < i1) {
-            while (i + 1 >= nc.end) enter(nc, nc.d + 1);
-            load_item(bnxt, nc, i + 1);
-        }
-        prep_for(cur);
-        float yacc[U];
-#pragma unroll
-        for (int r = 0; r < U; ++r) yacc[r] = 0.f;
-        accumulate_batch<B, UNIT, LPR, XC, U>(bcur, xu, yacc, uniform((int)cur.wide) != 0, slot,
-                                              uniform(cur.gpr), gidx);
-        store_item(yacc, cur, i);
-        bcur = bnxt;
-        cur = nc;
+        ++d;
     }
 }
 
@@ -502,9 +494,9 @@ hipError_t launch_gemv_t(const GemvArgs& a, const GemvShape& sh, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int B, int UNIT, int LPR, int XC, int U>
+template <int B, int UNIT, int XC, int U>
 hipError_t launch_batched_t(const BatchArgs& a, const GemvShape& sh, hipStream_t st) {
-    constexpr auto kern = gemv_batched_kernel<B, UNIT, LPR, XC, U>;
+    constexpr auto kern = gemv_batched_kernel<B, UNIT, XC, U>;
     const int grid = persistent_grid(sh.work, sh.cus, blocks_per_cu<kern>(), sh.waves_per_cu);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, a.descs, a.count, a.total_items, a.group);
     return hipGetLastError();
@@ -535,8 +527,8 @@ hipError_t launch_gemv_unit(const GemvArgs& a, const GemvShape& sh, hipStream_t 
 
 template <int B, int UNIT>
 hipError_t launch_batched_unit(const BatchArgs& a, const GemvShape& sh, hipStream_t st) {
-#define X(L, C, UU) \
-    if (sh.lpr == L && sh.xc == C && sh.u == UU) return launch_batched_t<B, UNIT, L, C, UU>(a, sh, st);
+#define X(C, UU) \
+    if (sh.xc == C && sh.u == UU) return launch_batched_t<B, UNIT, C, UU>(a, sh, st);
     QMM_BATCHED_SHAPES(X)
 #undef X
     return hipErrorInvalidValue;

@@ -141,7 +141,6 @@ LaneSplit choose_split(int nu, int max_xc, bool (*supported)(int, int)) {
 }
 
 bool gemv_split_ok(int lpr, int xc) { return gemv_shape_supported(lpr, xc, 1); }
-bool batched_split_ok(int lpr, int xc) { return batched_shape_supported(lpr, xc, 1); }
 bool rows_split_ok(int lpr, int xc) { return rows_shape_supported(lpr, xc, xc == 1 ? 4 : 2); }
 
 GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
@@ -163,7 +162,7 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     // next iteration's loads in flight, so two rows per slot already hold
     // 2-4 units of weights per lane in flight).
     const int64_t waves_u1 = (n + slots - 1) / slots;
-    int u = (waves_u1 > (int64_t)cus * 16) ? 2 : 1;
+    int u = (waves_u1 > (int64_t)cus * 16 && sh.xc == 1) ? 2 : 1;
     while (u > 1 && !gemv_shape_supported(sh.lpr, sh.xc, u)) u /= 2;
     const int ev = env_int("QMM_GEMV_U", 0);
     if (ev > 0 && gemv_shape_supported(sh.lpr, sh.xc, ev)) u = ev;
@@ -178,30 +177,35 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     return sh;
 }
 
-// Batched GEMVs: one kernel shape for every descriptor, chosen from the
-// largest K (which must fit a single pass) and the total row count.
+// Batched GEMVs: one compiled shape (units per lane, rows per slot) for the
+// launch, chosen from the largest K (at most 128 units per row) and the total
+// row count; lanes per row are chosen per descriptor from its own K.
 bool plan_batched(int64_t total_rows, int64_t kmax, int bits, int group, GemvShape* out) {
+    (void)bits;
     GemvShape sh{};
     sh.unit = (group % 64 == 0 && env_int("QMM_UNIT", 64) != 32) ? 64 : 32;
     const int nu = (int)(kmax / sh.unit);
-    LaneSplit ls = choose_split(nu, 3, batched_split_ok);
-    const int el = env_int("QMM_BATCH_LPR", 0), ex = env_int("QMM_BATCH_XC", 0);
-    if (el > 0 && ex > 0 && batched_split_ok(el, ex) && el * ex >= nu) ls = {el, ex, false};
-    if (ls.multipass) return false;
-    sh.lpr = ls.lpr;
-    sh.xc = ls.xc;
+    sh.xc = (nu + 63) / 64;
+    if (sh.xc > 2) return false;
+    sh.lpr = batched_lanes_per_row_host(nu, sh.xc);
     sh.multipass = false;
-    const int slots = 64 / sh.lpr;
-    (void)bits;
     // The row count decides, not the device, so prepared descriptors stay
     // valid on any GPU: big batches stream two rows per slot per iteration.
-    int u = (total_rows > (int64_t)slots * 4096) ? 2 : 1;
-    while (u > 1 && !batched_shape_supported(sh.lpr, sh.xc, u)) u /= 2;
+    // Two units per lane already double the registers; those keep one row.
+    int u = (total_rows > (int64_t)16 * 4096 && sh.xc == 1) ? 2 : 1;
     const int ev = env_int("QMM_BATCH_U", 0);
-    if (ev > 0 && batched_shape_supported(sh.lpr, sh.xc, ev)) u = ev;
+    if (ev > 0) u = ev;
+    if (!batched_shape_supported(sh.xc, u)) u = 1;
     sh.u = u;
     *out = sh;
     return true;
+}
+
+// Row batches of one descriptor in a batched launch planned as sh.
+int64_t batched_items(const GemvShape& sh, int64_t n, int64_t k) {
+    const int lpr = batched_lanes_per_row_host((int)(k / sh.unit), sh.xc);
+    const int64_t rows = (int64_t)(64 / lpr) * sh.u;
+    return (n + rows - 1) / rows;
 }
 
 RowsShape plan_rows(int64_t rows_bound, int64_t n, int64_t k, int bits, int group, int cus,
@@ -408,11 +412,10 @@ qmm_status qmm_gemv_batch_prepare(qmm_gemv_desc* descs, int64_t count, int bits,
     GemvShape sh{};
     if (!plan_batched(rows, kmax, bits, group_size, &sh))
         return fail(QMM_ERR_UNSUPPORTED, "largest k=%lld too large for a batched launch", (long long)kmax);
-    const int64_t per_item = (int64_t)(64 / sh.lpr) * sh.u;
     int64_t first = 0;
     for (int64_t i = 0; i < count; ++i) {
         descs[i].first_item = first;
-        first += (descs[i].n + per_item - 1) / per_item;
+        first += batched_items(sh, descs[i].n, descs[i].k);
     }
     return ok();
 }
@@ -428,13 +431,12 @@ qmm_status qmm_gemv_batched(const qmm_gemv_desc* descs_device, const qmm_gemv_de
     GemvShape sh{};
     if (!plan_batched(rows, kmax, bits, group_size, &sh))
         return fail(QMM_ERR_UNSUPPORTED, "largest k=%lld too large for a batched launch", (long long)kmax);
-    const int64_t per_item = (int64_t)(64 / sh.lpr) * sh.u;
     int64_t first = 0;
     for (int64_t i = 0; i < count; ++i) {
         if (descs_host[i].first_item != first)
             return fail(QMM_ERR_INVALID_ARGUMENT,
                         "descriptor %lld not prepared for this batch (call qmm_gemv_batch_prepare)", (long long)i);
-        first += (descs_host[i].n + per_item - 1) / per_item;
+        first += batched_items(sh, descs_host[i].n, descs_host[i].k);
     }
     int cus = 0;
     if ((st = device_cus(&cus)) != QMM_OK) return st;
@@ -491,8 +493,7 @@ qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits, int g
         plan->units_per_lane = sh.xc;
         plan->rows_per_iter = sh.u;
         plan->unit_codes = sh.unit;
-        const int64_t items = (n + (64 / sh.lpr) * sh.u - 1) / ((64 / sh.lpr) * sh.u);
-        plan->grid = persistent_grid(items, cus, 4, 0);
+        plan->grid = persistent_grid(batched_items(sh, n, k), cus, 4, 0);
         return ok();
     }
     if (op == 2 || (op == 1 && m <= ROWS_KERNEL_MAX_M)) {

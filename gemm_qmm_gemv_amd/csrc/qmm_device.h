@@ -332,12 +332,41 @@ __device__ __forceinline__ float unit_qx(const u32* w, const XUnit<B, UNIT>& xu)
     return t - xu.corr;
 }
 
-// Sum over aligned groups of L lanes (L a power of two <= 64); every lane of
-// the group gets the total.
+// Sum over aligned groups of L lanes (L = 16, 32 or 64); every lane of the
+// group gets the total.  Within a 16-lane row the butterfly runs on DPP
+// lane swizzles folded into the adds (xor 1, xor 2, then the half-row and
+// row mirrors, which pair each lane with one holding the complementary
+// partial sum); across rows one ds_swizzle (xor 16) and one cross-lane
+// permute (xor 32).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f32<0x141>(v);  // row_half_mirror
+    v += dpp_f32<0x140>(v);  // row_mirror
+    return v;
+}
+__device__ __forceinline__ float xor16_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+__device__ __forceinline__ float xor32_add(float v) { return v + __shfl_xor(v, 32, 64); }
+
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int off = L / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    static_assert(L == 16 || L == 32 || L == 64, "lanes per row");
+    v = row16_sum(v);
+    if constexpr (L >= 32) v = xor16_add(v);
+    if constexpr (L == 64) v = xor32_add(v);
+    return v;
+}
+// Same with a wave-uniform run-time width (16, 32 or 64).
+__device__ __forceinline__ float group_sum_rt(float v, int lanes) {
+    v = row16_sum(v);
+    if (lanes >= 32) v = xor16_add(v);
+    if (lanes == 64) v = xor32_add(v);
     return v;
 }
 

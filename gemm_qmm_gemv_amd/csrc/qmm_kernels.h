@@ -119,9 +119,11 @@ struct BatchArgs {
     X(16, 1, 1) X(16, 1, 2) \
     X(32, 1, 1) X(32, 1, 2) \
     X(64, 1, 1) X(64, 1, 2) \
-    X(64, 2, 1) X(64, 2, 2)
+    X(64, 2, 1)
 
-#define QMM_BATCHED_SHAPES(X) QMM_GEMV_SHAPES(X)
+// Batched launches choose the lanes per row per descriptor at run time;
+// compiled shapes are (units per lane, rows per slot).
+#define QMM_BATCHED_SHAPES(X) X(1, 1) X(1, 2) X(2, 1)
 
 #define QMM_ROWS_SHAPES(X) \
     X(16, 1, 4) X(32, 1, 4) X(64, 1, 4) \
@@ -133,11 +135,20 @@ constexpr bool gemv_shape_supported(int lpr, int xc, int u) {
 #undef X
     return false;
 }
-constexpr bool batched_shape_supported(int lpr, int xc, int u) {
-#define X(L, C, UU) if (lpr == L && xc == C && u == UU) return true;
+constexpr bool batched_shape_supported(int xc, int u) {
+#define X(C, UU) if (xc == C && u == UU) return true;
     QMM_BATCHED_SHAPES(X)
 #undef X
     return false;
+}
+
+// Lanes per row a batched launch gives a descriptor with nu units per row
+// (the kernel computes the same from K): the smallest of 16, 32, 64 whose
+// lanes cover the row with xc units each.
+constexpr int batched_lanes_per_row_host(int nu, int xc) {
+    int lpr = 16;
+    while (lpr < 64 && lpr * xc < nu) lpr *= 2;
+    return lpr;
 }
 constexpr bool rows_shape_supported(int lpr, int xc, int mr) {
 #define X(L, C, R) if (lpr == L && xc == C && mr == R) return true;

@@ -39,6 +39,19 @@ def test_batched_mixed_shapes(bits):
         assert_within(y[:n], y_ref, a_ref, "batched b%d %dx%d" % (bits, n, k))
 
 
+@pytest.mark.parametrize("bits", (2, 3, 4, 6, 8))
+def test_batched_mixed_k_one_launch(bits):
+    # Different K per descriptor in one launch: each gets its own lane layout
+    # (16, 32 or 64 lanes per row; two units per lane for K = 8192).
+    shapes = [(300, 1024), (129, 2048), (77, 3072), (1000, 1024), (5, 768), (40, 8192), (64, 4096),
+              (1, 64), (33, 2048)]
+    announce("batched-mixed-k", bits)
+    qs, ys = _run_batch(shapes, bits, 64, 4)
+    for (q, x), y, (n, k) in zip(qs, ys, shapes):
+        y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, 64)
+        assert_within(y[:n], y_ref, a_ref, "batched mixed-k b%d %dx%d" % (bits, n, k))
+
+
 @pytest.mark.parametrize("k", (2048, 3072))
 def test_batched_layer_like(k):
     # Many matrices of one K, as in one launch of the decode set.
