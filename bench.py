@@ -9,8 +9,9 @@ batched launch (each GEMV with its own lane layout for its K).  The headline val
 set's algorithmic bytes (compressed weights + fp16 x + fp32 y) per second.
 
 Also measured (outside the timed region, reported in the same JSON line):
-  * the roofline of the dominant kernel (that batched launch), from HIP
-    events around every one of its launches inside the timed region;
+  * the roofline of the dominant kernel (that batched launch, the only
+    kernel of a step): its average launch duration is the timed region's
+    HIP-event time over K;
   * the same set as 197 separate qmm_gemv launches replayed from a HIP graph;
   * the set in decode dependency order (per layer: q|k|v, o, gate|up, down;
     then the LM head) replayed from a HIP graph: per-token projection time;
@@ -64,7 +65,7 @@ def stored_traffic():
         fields = {}
         with open(TRAFFIC_FILE) as f:
             for ln in f:
-                if ":" in ln:
+                if ":" in ln and not ln.startswith("#"):
                     k, v = ln.split(":", 1)
                     fields[k.strip()] = v.strip()
         if fields.get("kernel_source_sha256") != kernel_source_digest():
@@ -157,32 +158,26 @@ def main():
     total_rows = sum(d["n"] for _, _, d in mats)
     plan = qmm.qmm_get_plan(3, 1, total_rows, max(d["k"] for _, _, d in mats), 4, G)
     st = torch.cuda.current_stream().cuda_stream
-    evs = []
-
-    def step(record=False):
-        if record:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            batch(stream=st)
-            b.record()
-            evs.append((a, b))
-        else:
-            batch(stream=st)
 
     for _ in range(args.warmup):
-        step()
+        batch(stream=st)
     torch.cuda.synchronize()
+    # Timed region: K steps back to back, bracketed by events and syncs.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     start.record()
     for _ in range(args.steps):
-        step(record=True)
+        batch(stream=st)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = start.elapsed_time(end) / args.steps
     value = set_bytes / (ms_per_step * 1e-3) / 1e9
-    dom_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    # The step is one launch of the dominant kernel, so its average launch
+    # duration is the timed region's event time over K (it includes the
+    # inter-launch gap of about a microsecond, so it slightly understates the
+    # kernel's own rate as a profiler's kernel trace reports it).
+    dom_ms = ms_per_step
     dom_bytes = set_bytes
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     log("step %.3f us (wall %.3f us), %.1f GB/s; batched launch %.3f us, %.1f GB/s"
