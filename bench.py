@@ -76,23 +76,50 @@ def stored_traffic():
 
 
 class Timer:
-    """Average milliseconds of fn() over reps, HIP events on the current stream."""
+    """Average milliseconds per call of fn(), measured on the GPU side.
+
+    `reps` calls are captured into one HIP graph (a caller that rotates
+    through several input copies bakes that rotation into the graph), the
+    graph is replayed `replays` times between two events, and the elapsed
+    time is divided by the number of calls.  Replaying a graph keeps the host
+    out of the measurement: each call costs its kernels plus the dispatch gap
+    between graph nodes, which is what a captured decode or prefill step pays.
+    """
 
     def __init__(self, torch):
         self.torch = torch
 
-    def __call__(self, fn, reps=20, warmup=3):
+    def __call__(self, fn, reps=20, warmup=3, replays=5):
         t = self.torch
         for _ in range(warmup):
             fn()
         t.cuda.synchronize()
+        g = t.cuda.CUDAGraph()
+        with t.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        t.cuda.synchronize()
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         a.record()
-        for _ in range(reps):
-            fn()
+        for _ in range(replays):
+            g.replay()
         b.record()
         t.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+        return a.elapsed_time(b) / (replays * reps)
+
+    def replay(self, g, replays=20):
+        """Average milliseconds per replay of an already captured graph."""
+        t = self.torch
+        g.replay()
+        t.cuda.synchronize()
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(replays):
+            g.replay()
+        b.record()
+        t.cuda.synchronize()
+        return a.elapsed_time(b) / replays
 
 
 def main():
@@ -240,7 +267,7 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         per_call()
-    ms = timer(g.replay, reps=20)
+    ms = timer.replay(g)
     out["decode_set_per_call_graph"] = {"us": round(ms * 1e3, 2),
                                         "GBps": round(set_bytes / ms / 1e6, 1)}
     log("per-call graph: %.1f us" % (ms * 1e3))
@@ -264,7 +291,7 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
     g2 = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g2):
         dependent()
-    ms = timer(g2.replay, reps=20)
+    ms = timer.replay(g2)
     out["decode_dependent_stages_graph"] = {
         "launches": len(stage_batches) + 1, "per_token_us": round(ms * 1e3, 2),
         "GBps": round(set_bytes / ms / 1e6, 1), "projection_tok_per_s": round(1e3 / ms, 1)}
@@ -332,14 +359,32 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
             xm = tensors.device_tensor(inputs.activation_rows(m, k, key=(configs.CFG_PREFILL, 0, j, 4, m)))
             ym = torch.empty((m, n), dtype=torch.float32, device="cuda")
             need = qmm.qmm_gemm_workspace_bytes(m, n, k, 4, G)
-            ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-            ms = timer(lambda: tensors.gemm(dq, xm, ym, workspace=ws), reps=30)
+            ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
+            # Device-side copies of the same matrix, rotated so that the
+            # weights come from HBM (total above twice the 256 MB last-level
+            # cache, at most 64 copies).
+            wb = configs.weight_bytes(n, k, 4)
+            ncp = max(4, min(64, -(-512 * 2**20 // wb)))
+            cps = [dq] + [{**dq, "w": dq["w"].clone(), "scales": dq["scales"].clone(),
+                           "mins": dq["mins"].clone()} for _ in range(ncp - 1)]
+            ii = [0]
+
+            def call():
+                tensors.gemm(cps[ii[0] % ncp], xm, ym, workspace=ws)
+                ii[0] += 1
+            ms = timer(call, reps=ncp)
             fl = 2.0 * m * n * k
             tf = fl / ms / 1e9
             pl = qmm.qmm_get_plan(1, m, n, k, 4, G, workspace_bytes=ws.numel())
+            # Context only: dense fp16 matmul of the same shape through the
+            # installed BLAS library (weights already dequantized, 4x the bytes).
+            wd = torch.randn((k, n), dtype=torch.float16, device="cuda")
+            ms_dense = timer(lambda: torch.matmul(xm, wd), reps=20)
             row[pname] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
                           "pct_mfma": round(100 * tf / MFMA_FP16_PEAK_TFLOPS, 2),
-                          "split_k": pl["split_k"], "tile_m": pl["tile_m"]}
+                          "split_k": pl["split_k"], "tile_m": pl["tile_m"], "copies": ncp,
+                          "dense_fp16_matmul_us": round(ms_dense * 1e3, 2)}
+            del cps, wd
             tot_flops += fl
             tot_ms += ms
         tf = tot_flops / tot_ms / 1e9

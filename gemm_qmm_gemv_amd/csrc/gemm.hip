@@ -6,78 +6,164 @@
 // Inference on Apple Silicon via Native Metal" (gist.science summary),
 // section "Metodologia" (tiled prefill GEMM on the GPU's matrix hardware).
 //
-// Y[M][N] = X[M][K] * W^T with W = s*q + m.  One work-group (4 waves) owns a
-// TILE_M x 128 tile of Y and walks its share of K in steps of 64:
-//   * the X tile (fp16) is copied to LDS;
-//   * the W tile is read packed (b/8 bytes per weight plus one scale and min
-//     per 64), dequantized in registers -- exact code, then one fused
-//     multiply-add s*q + m rounded once to fp16 -- and written to LDS;
-//   * each wave multiplies a (TILE_M/2) x 64 sub-tile with
-//     v_mfma_f32_32x32x16_f16, fp32 accumulation.
-// The next step's global loads are issued before the current step's matrix
-// work, so memory and MFMA overlap.  When the tile grid alone would leave
-// compute units idle, K is split across work-groups; partial sums go to a
-// caller-provided workspace and a second kernel adds them in split order
-// (deterministic, no atomics).  Work-group ids are remapped so that the tiles
-// sharing a W column block land on the same XCD (and its L2).
+// Y[M][N] = X[M][K] * W^T with W = s*q + m, on v_mfma_f32_32x32x16_f16.
+//
+// Work-group: 4 waves, tile TILE_M (= 32*MS) x 128 of Y, K in steps of 128.
+// Wave (wn, wk) owns 64 columns (two 32-column fragments) and one 64-wide
+// half of every K step; the two K-halves are added through LDS at the end.
+//
+//   * W never goes through LDS.  The matrix core's B operand for lane l is
+//     eight K values of column l%32, and lanes l and l+32 cover the two
+//     K-halves of a 16-deep step.  Each lane therefore loads one 32-code
+//     chunk of its own column straight into registers (b words), turns it
+//     into sixteen fp16 pairs -- exact code, then s*q + m with one rounding --
+//     and feeds four consecutive pairs to each of four MFMA steps.
+//   * The pairs come out of the bit tricks in a fixed, format-dependent order
+//     (for Q4: codes 0,4 / 1,5 / 2,6 / 3,7 of every eight).  A dot product
+//     does not care about the order of its terms, only that both operands use
+//     the same one, so X is written to LDS in that same order ("slot order")
+//     while it is staged; the W side needs no shuffles at all.
+//   * X (fp16) is the shared operand: the work-group copies its TILE_M x 128
+//     block to LDS once per step (double-buffered, one barrier per step) and
+//     every wave reads 32x16 A fragments from there.
+//   * The next step's X and W loads are issued before the current step's
+//     dequantization and matrix work, so memory, VALU and MFMA overlap.
+//
+// When the tile grid alone would leave compute units idle, K is split across
+// work-groups; partial sums go to a caller-provided workspace and a second
+// kernel adds them in split order (deterministic, no atomics).  Work-group ids
+// are remapped so that tiles sharing a W column block land on the same XCD
+// (and its L2).
 #include "qmm_device.h"
 #include "qmm_kernels.h"
 
+#include <type_traits>
+
 namespace qmm {
 
-constexpr int BK = GEMM_BK;   // K per step
-constexpr int BN = 128;       // N per work-group
-constexpr int PAD = 8;        // halves of padding per LDS row (conflict-free 16-byte reads)
-constexpr int LDS_ROW = BK + PAD;
+constexpr int BK = GEMM_BK;     // K per step (128)
+constexpr int BN = 128;         // columns per work-group
+constexpr int XPAD = 8;         // halves of padding per LDS row (conflict-free 16-byte reads)
+constexpr int XROW = BK + XPAD; // halves per LDS row
 
-// Dequantize one 32-code chunk (B words) to 32 fp16 values in k order.
+// Slot order of a 32-code chunk: slot 2i holds code ka(i) and slot 2i+1 code
+// kb(i) of the pair format, i.e. exactly the order in which the dequantized
+// pairs sit in registers.
 template <int B>
-__device__ __forceinline__ void dequant_chunk(const u32* w, uint16_t s_bits, uint16_t m_bits,
+constexpr int slot_k(int p) {
+    return (p & 1) ? PairFmt<B>::kb(p >> 1) : PairFmt<B>::ka(p >> 1);
+}
+
+// Halves of X reordered as one unit: every format keeps each aligned block
+// of XH slots inside the same XH codes, with the same pattern in every block
+// of a chunk (XH = 8 except for Q2, whose pairs span 16 codes).
+template <int B>
+constexpr int x_unit_halves() { return B == 2 ? 16 : 8; }
+
+template <int B>
+constexpr bool slot_blocks_ok() {
+    constexpr int XH = x_unit_halves<B>();
+    for (int p = 0; p < 32; ++p)
+        if (slot_k<B>(p) / XH != p / XH || slot_k<B>(p) % XH != slot_k<B>(p % XH)) return false;
+    return true;
+}
+static_assert(slot_blocks_ok<2>() && slot_blocks_ok<3>() && slot_blocks_ok<4>() &&
+                  slot_blocks_ok<6>() && slot_blocks_ok<8>(),
+              "slot order must stay within aligned blocks of x_unit_halves codes");
+
+// XH halves of X in natural k order -> slot order, one byte permute per
+// output dword.  v_perm_b32 selector bytes 0-3 pick bytes of its second
+// operand and 4-7 bytes of its first.
+template <int B>
+__device__ __forceinline__ void to_slot_order(const u32 (&in)[x_unit_halves<B>() / 2],
+                                              u32 (&out)[x_unit_halves<B>() / 2]) {
+#pragma unroll
+    for (int d = 0; d < x_unit_halves<B>() / 2; ++d) {
+        const int a = slot_k<B>(2 * d), b = slot_k<B>(2 * d + 1);
+        const u32 sel = (u32)(2 * (a & 1)) | (u32)(2 * (a & 1) + 1) << 8 |
+                        (u32)(4 + 2 * (b & 1)) << 16 | (u32)(4 + 2 * (b & 1) + 1) << 24;
+        out[d] = __builtin_amdgcn_perm(in[b >> 1], in[a >> 1], sel);
+    }
+}
+
+// One 32-code chunk (b words) -> 16 fp16 pairs s*q + m in slot order.
+template <int B>
+__device__ __forceinline__ void dequant_pairs(const u32 (&w)[B], u32 s_bits, u32 m_bits,
                                               f16x2 (&out)[16]) {
     using F = PairFmt<B>;
     u32 p[16];
     F::extract(w, p);
-    const f16 s = __builtin_bit_cast(f16, s_bits), m = __builtin_bit_cast(f16, m_bits);
+    const f16 s = __builtin_bit_cast(f16, (uint16_t)s_bits);
+    const f16 m = __builtin_bit_cast(f16, (uint16_t)m_bits);
     const f16x2 s2 = {s, s}, m2 = {m, m};
-    f16x2 wv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const f16 inv = (f16)F::inv_factor(F::acc(i));
-        const f16x2 inv2 = {inv, inv};
         const f16 off = (f16)(-1024.0f * F::inv_factor(F::acc(i)));
-        const f16x2 off2 = {off, off};
-        // (1024 + f q) * (1/f) - 1024/f == q exactly (f a power of two).
+        const f16x2 inv2 = {inv, inv}, off2 = {off, off};
+        // (1024 + f q) * (1/f) - 1024/f is exactly q (f a power of two).
         const f16x2 q2 = __builtin_elementwise_fma(as_h2(p[i]), inv2, off2);
-        // s*q + m with a single rounding to fp16.
-        wv[i] = __builtin_elementwise_fma(q2, s2, m2);
+        // s*q + m, fused: one rounding of the exact value to fp16.
+        out[i] = __builtin_elementwise_fma(q2, s2, m2);
     }
-    // Pairs 2t and 2t+1 hold codes (a, b) and (a+1, b+1): regroup to k order.
-    f16 h[32];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const int a = F::ka(2 * t), b = F::kb(2 * t);
-        h[a] = wv[2 * t][0];
-        h[a + 1] = wv[2 * t + 1][0];
-        h[b] = wv[2 * t][1];
-        h[b + 1] = wv[2 * t + 1][1];
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) out[i] = f16x2{h[2 * i], h[2 * i + 1]};
 }
 
-// TM: 32x32 fragments per wave along M (TILE_M = 64 * TM).
-template <int B, int TM>
-__global__ __launch_bounds__(256) void gemm_kernel(const u32* __restrict__ W,
+// Steps U..N-1 of one pass of the unrolled main loop, stopping at the end of
+// the range.
+template <int U, int N, class F>
+__device__ __forceinline__ void unrolled_steps(F& f, int st, int st1) {
+    if constexpr (U < N) {
+        if (st + U < st1) {
+            f(std::integral_constant<int, U>{}, st + U);
+            unrolled_steps<U + 1, N>(f, st, st1);
+        }
+    }
+}
+
+// Pipeline depths and the occupancy target (work-groups per CU the register
+// allocation must allow).
+#ifndef GEMM_WD
+#define GEMM_WD 1
+#endif
+#ifndef GEMM_XD
+#define GEMM_XD 1
+#endif
+#ifndef GEMM_MINB
+#define GEMM_MINB 2
+#endif
+constexpr int WD = GEMM_WD;
+constexpr int XD = GEMM_XD;
+
+// MS: 32-row fragments per wave along M (TILE_M = 32 * MS); WN: waves along
+// N (each with BN / WN columns, NS = BN / (32 WN) fragments); two waves
+// along K.  The work-group has 128 * WN threads.
+template <int B, int MS, int WN>
+__global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(const u32* __restrict__ W,
                                                    const uint16_t* __restrict__ S,
                                                    const uint16_t* __restrict__ Mn,
                                                    const uint16_t* __restrict__ X,
                                                    float* __restrict__ Y, float* __restrict__ P,
-                                                   int M, int N, int K, int group, int grid_m,
-                                                   int grid_n, int split, int kt_per_split) {
-    constexpr int TILE_M = 64 * TM;
-    constexpr int XH = TILE_M * BK / 256;  // halves of X per thread per step
-    __shared__ __attribute__((aligned(16))) f16 As[TILE_M * LDS_ROW];
-    __shared__ __attribute__((aligned(16))) f16 Bs[BN * LDS_ROW];
+                                                   int M, int N, int K, uint64_t gmul, int gsh,
+                                                   int grid_m, int grid_n, int split,
+                                                   int steps_per_split) {
+    constexpr int TILE_M = 32 * MS;
+    constexpr int THREADS = 128 * WN;
+    constexpr int NS = BN / (32 * WN);                   // 32-column fragments per wave
+    constexpr int NF = MS * NS;                          // fragments per wave
+    constexpr int XH = x_unit_halves<B>();               // halves per X unit
+    constexpr int XW = XH / 2;                           // dwords per X unit
+    constexpr int UPR = BK / XH;                         // X units per row and step
+    constexpr int XU = TILE_M * UPR / THREADS;           // X units per thread
+    static_assert(NS >= 1 && XU >= 1 && XU * THREADS == TILE_M * UPR, "tile shape");
+    constexpr int XBUF = TILE_M * XROW;                  // halves per X buffer
+    constexpr int X_BYTES = 2 * XBUF * 2;                // two buffers
+    // K-half exchange: every wave hands over half of its fragments (all of
+    // them when it has only one).
+    constexpr int GIVE = NF > 1 ? NF / 2 : 1;
+    constexpr int R_BYTES = 2 * WN * GIVE * 16 * 64 * 4;
+    constexpr int LDS_BYTES = X_BYTES > R_BYTES ? X_BYTES : R_BYTES;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
+    f16* xs = reinterpret_cast<f16*>(smem);
 
     // XCD-aware tile order: the 8 XCDs take contiguous tile ranges.
     const int tiles = grid_m * grid_n * split;
@@ -85,114 +171,199 @@ __global__ __launch_bounds__(256) void gemm_kernel(const u32* __restrict__ W,
     const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (t >= tiles) return;
     const int mt = t % grid_m;
-    const int ns = t / grid_m;
-    const int sk = ns % split;
-    const int nt = ns / split;
+    const int rest = t / grid_m;
+    const int sk = rest % split;
+    const int nt = rest / split;
     const int m0 = mt * TILE_M, n0 = nt * BN;
-    const int k_tiles = (K + BK - 1) / BK;
-    const int kt0 = sk * kt_per_split;
-    const int kt1 = min(k_tiles, kt0 + kt_per_split);
+    const int steps = (K + BK - 1) / BK;
+    const int st0 = sk * steps_per_split;
+    const int st1 = min(steps, st0 + steps_per_split);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int wpr = K / 32 * B;
-    const int gpr = K / group;
+    const int wn = wave % WN, wk = wave / WN;
+    const int col = lane & 31, kh = lane >> 5;
+    const uint32_t wpr = (uint32_t)K / 32 * B;  // words per W row
+    // K / group through the multiply-shift pair computed on the host (exact
+    // for every 31-bit dividend).
+    auto group_of = [&](uint32_t kk) { return (uint32_t)(((uint64_t)kk * gmul) >> gsh); };
+    const uint32_t gpr = group_of((uint32_t)K);
 
-    // X loader: thread -> (row, XH consecutive halves).
-    const int xrow = tid / (BK / XH);
-    const int xcol = (tid % (BK / XH)) * XH;
-    // W loader: thread -> (row, 32-code chunk).
-    const int wrow = tid >> 1;
-    const int wch = tid & 1;
+    const uint32_t w_bytes = (uint32_t)N * wpr * 4;
+    const uint32_t sm_bytes = (uint32_t)N * gpr * 2;
+    const uint32_t x_bytes = (uint32_t)M * (uint32_t)K * 2;
+    const rsrc_t wr = make_rsrc(W, w_bytes);
+    const rsrc_t sr = make_rsrc(S, sm_bytes);
+    const rsrc_t mr = make_rsrc(Mn, sm_bytes);
+    const rsrc_t xr = make_rsrc(X, x_bytes);
 
-    u32 xr[XH / 2];
-    u32 wr[B];
-    uint16_t sr = 0, mr = 0;
-
-    auto load_step = [&](int kt) {
-        const int kx = kt * BK + xcol;
-        const bool xok = (m0 + xrow) < M && kx < K;
-        if (xok) {
-            load_words<XH / 2, 16>(reinterpret_cast<const u32*>(X + (size_t)(m0 + xrow) * K + kx), xr);
-        } else {
+    // W side: this lane's NS columns; OOB columns read as zero.
+    uint32_t w_row[NS], s_row[NS];
+    bool n_ok[NS];
 #pragma unroll
-            for (int i = 0; i < XH / 2; ++i) xr[i] = 0u;
+    for (int ns = 0; ns < NS; ++ns) {
+        const int n = n0 + 32 * NS * wn + 32 * ns + col;
+        n_ok[ns] = n < N;
+        w_row[ns] = (uint32_t)n * wpr * 4;
+        s_row[ns] = (uint32_t)n * gpr * 2;
+    }
+    // X side: this thread stages XU units of XH halves per step; the
+    // threads of a row read it contiguously.
+    const int xcu = tid % UPR;
+    uint32_t x_row[XU];
+    bool m_ok[XU];
+#pragma unroll
+    for (int r = 0; r < XU; ++r) {
+        const int row = tid / UPR + (THREADS / UPR) * r;
+        m_ok[r] = m0 + row < M;
+        x_row[r] = (uint32_t)(m0 + row) * (uint32_t)K * 2;
+    }
+
+    // Register rings: W (codes, scale, min) runs WD steps ahead of the
+    // matrix work; X is loaded XD steps ahead (XD = 2: one step in
+    // registers while the previous one sits in LDS).  The main loop is
+    // unrolled by the W ring length so every ring index is a compile-time
+    // constant.
+    constexpr int WR = WD + 1;
+    static_assert(XD == 1 || XD == 2, "X runs one or two steps ahead");
+    static_assert(WR % XD == 0, "the X ring must divide the W ring");
+    u32 xq[XD][XU][XW];
+    u32 wq[WR][NS][B];
+    u32 sq[WR][NS], mq[WR][NS];
+
+    // Loads are unconditional: a step past this split's range, like a row
+    // or column past the matrix, reads zeros through the buffer range check.
+    // Branch-free step bodies let the compiler count outstanding loads
+    // exactly instead of draining the memory queue at every join.
+    auto load_x = [&](int st, u32 (&dst)[XU][XW]) {
+        const int kx = st * BK + XH * xcu;
+        const bool live = st < st1 && kx < K;
+#pragma unroll
+        for (int r = 0; r < XU; ++r) {
+            const uint32_t off = (m_ok[r] && live) ? x_row[r] + (uint32_t)kx * 2 : x_bytes;
+#pragma unroll
+            for (int h = 0; h < XW / 4; ++h) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16 * h, 0, 0);
+                dst[r][4 * h] = v[0]; dst[r][4 * h + 1] = v[1]; dst[r][4 * h + 2] = v[2]; dst[r][4 * h + 3] = v[3];
+            }
         }
-        const int kw = kt * BK + wch * 32;
-        const bool wok = (n0 + wrow) < N && kw < K;
-        if (wok) {
-            load_words<B, unit_align(B, 32)>(W + (size_t)(n0 + wrow) * wpr + (size_t)(kw / 32) * B, wr);
-            sr = S[(size_t)(n0 + wrow) * gpr + kw / group];
-            mr = Mn[(size_t)(n0 + wrow) * gpr + kw / group];
-        } else {
+    };
+    auto load_w = [&](int st, u32 (&w)[NS][B], u32 (&sv)[NS], u32 (&mv)[NS]) {
+        const int kc = st * BK + 64 * wk + 32 * kh;
+        const bool live = st < st1 && kc < K;
 #pragma unroll
-            for (int i = 0; i < B; ++i) wr[i] = 0u;
-            sr = 0;
-            mr = 0;
+        for (int ns = 0; ns < NS; ++ns) {
+            const bool ok = n_ok[ns] && live;
+            const uint32_t wo = ok ? w_row[ns] + (uint32_t)(kc / 32) * B * 4 : w_bytes;
+            buffer_words<B, unit_align(B, 32)>(wr, wo, w[ns]);
+            const uint32_t so = ok ? s_row[ns] + group_of((uint32_t)kc) * 2 : sm_bytes;
+            sv[ns] = buffer_u16(sr, so);
+            mv[ns] = buffer_u16(mr, so);
+        }
+    };
+    auto stage_x = [&](const u32 (&src)[XU][XW], int buf) {
+#pragma unroll
+        for (int r = 0; r < XU; ++r) {
+            u32 o[XW];
+            to_slot_order<B>(src[r], o);
+            const int row = tid / UPR + (THREADS / UPR) * r;
+            u32x4* dst = reinterpret_cast<u32x4*>(&xs[buf * XBUF + row * XROW + XH * xcu]);
+#pragma unroll
+            for (int h = 0; h < XW / 4; ++h) dst[h] = u32x4{o[4 * h], o[4 * h + 1], o[4 * h + 2], o[4 * h + 3]};
         }
     };
 
-    f32x16 acc[TM][2];
+    f32x16 acc[MS][NS];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < MS; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+            for (int v = 0; v < 16; ++v) acc[i][ns][v] = 0.f;
 
-    if (kt0 < kt1) load_step(kt0);
-    for (int kt = kt0; kt < kt1; ++kt) {
-        __syncthreads();  // previous step's fragment reads are done
-        {
-            u32x4* dst = reinterpret_cast<u32x4*>(&As[xrow * LDS_ROW + xcol]);
+    // Prologue: X for the first XD steps (the first one staged), W for the
+    // first WD steps.
 #pragma unroll
-            for (int i = 0; i < XH / 8; ++i)
-                dst[i] = u32x4{xr[4 * i], xr[4 * i + 1], xr[4 * i + 2], xr[4 * i + 3]};
-            f16x2 wh[16];
-            dequant_chunk<B>(wr, sr, mr, wh);
-            u32x4* wdst = reinterpret_cast<u32x4*>(&Bs[wrow * LDS_ROW + wch * 32]);
+    for (int d = 0; d < XD; ++d) load_x(st0 + d, xq[d]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                wdst[i] = u32x4{as_u32(wh[4 * i]), as_u32(wh[4 * i + 1]), as_u32(wh[4 * i + 2]),
-                                as_u32(wh[4 * i + 3])};
-        }
-        __syncthreads();
-        if (kt + 1 < kt1) load_step(kt + 1);
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int kofs = kk * 16 + 8 * (lane >> 5);
-            f16x8 a[TM], b[2];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                a[i] = *reinterpret_cast<const f16x8*>(
-                    &As[(wm * TM * 32 + i * 32 + (lane & 31)) * LDS_ROW + kofs]);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                b[j] = *reinterpret_cast<const f16x8*>(
-                    &Bs[(wn * 64 + j * 32 + (lane & 31)) * LDS_ROW + kofs]);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-    }
+    for (int d = 0; d < WD; ++d) load_w(st0 + d, wq[d], sq[d], mq[d]);
+    stage_x(xq[0], 0);
+    __syncthreads();
 
-    // Store: lane holds column (lane % 32) of each 32x32 fragment, rows
-    // 8*(v/4) + 4*(lane/32) + v%4.
-    float* out = (split == 1) ? Y : P + (size_t)sk * M * N;
+    // One step at ring position U (= (st - st0) mod WR); its X sits in LDS
+    // buffer U % 2 (WR is even).
+    static_assert(WR % 2 == 0, "LDS buffer parity must follow the ring position");
+    auto step = [&](auto u_c, int st) {
+        constexpr int U = decltype(u_c)::value;
+        constexpr int BUF = U % 2;
+        load_w(st + WD, wq[(U + WD) % WR], sq[(U + WD) % WR], mq[(U + WD) % WR]);
+        // XD = 2: slot U % 2 held X(st), staged a step ago; X(st + 1) waits
+        // in the other slot.  XD = 1: the single slot was staged a step ago.
+        load_x(st + XD, xq[U % XD]);
+        // Keep the loads at the top of the step: left alone, the scheduler
+        // sinks them towards their first use and the step then waits for
+        // their full latency.
+        __builtin_amdgcn_sched_barrier(0);
+        f16x2 wv[NS][16];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int ns = 0; ns < NS; ++ns) dequant_pairs<B>(wq[U][ns], sq[U][ns], mq[U][ns], wv[ns]);
+        const f16* xa = xs + BUF * XBUF + col * XROW + 64 * wk + 32 * kh;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+        for (int j = 0; j < 4; ++j) {
+            f16x8 a[MS];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = m0 + wm * TM * 32 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (row < M && col < N) out[(size_t)row * N + col] = acc[i][j][v];
+            for (int i = 0; i < MS; ++i) a[i] = *reinterpret_cast<const f16x8*>(xa + 32 * i * XROW + 8 * j);
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) {
+                const u32x4 bw = {as_u32(wv[ns][4 * j]), as_u32(wv[ns][4 * j + 1]),
+                                  as_u32(wv[ns][4 * j + 2]), as_u32(wv[ns][4 * j + 3])};
+                const f16x8 b = __builtin_bit_cast(f16x8, bw);
+#pragma unroll
+                for (int i = 0; i < MS; ++i)
+                    acc[i][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b, acc[i][ns], 0, 0, 0);
             }
         }
+        stage_x(xq[(U + 1) % XD], BUF ^ 1);
+        __syncthreads();
+    };
+    for (int st = st0; st < st1; st += WR) unrolled_steps<0, WR>(step, st, st1);
+
+    // Add the two K-halves.  Fragment f = i * NS + ns; wave (wn, wk) keeps
+    // the fragments with f % 2 == wk (all of them for wk == 0 when it has
+    // only one) and hands the others to its partner through LDS (the X
+    // buffers are free after the loop's last barrier).
+    float* red = reinterpret_cast<float*>(smem);
+    auto keeps = [&](int f) { return NF > 1 ? (f % 2) == wk : wk == 0; };
+    {
+        float* dst = red + ((wn * 2 + wk) * GIVE) * 16 * 64 + lane;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            if (keeps(f)) continue;
+            const int slot = NF > 1 ? f / 2 : 0;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dst[(slot * 16 + v) * 64] = acc[f / NS][f % NS][v];
+        }
+    }
+    __syncthreads();
+    {
+        const float* src = red + ((wn * 2 + (1 - wk)) * GIVE) * 16 * 64 + lane;
+        float* out = (split == 1) ? Y : P + (size_t)sk * M * N;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            if (!keeps(f)) continue;
+            const int slot = NF > 1 ? f / 2 : 0;
+            const int i = f / NS, ns = f % NS;
+            // Store: lane holds column (lane % 32) of each 32x32 fragment,
+            // rows 8*(v/4) + 4*(lane/32) + v%4.
+            const int c = n0 + 32 * NS * wn + 32 * ns + col;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float sum = acc[i][ns][v] + src[(slot * 16 + v) * 64];
+                const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * kh + (v & 3);
+                if (row < M && c < N) out[(size_t)row * N + c] = sum;
+            }
+        }
+    }
 }
 
 // y = sum over splits of the partial sums, in split order.
@@ -206,13 +377,28 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     Y[i] = v;
 }
 
-template <int B, int TM>
+// floor(n / d) = (n * mul) >> shift for every n < 2^31: shift = 31 + ceil(log2 d),
+// mul = ceil(2^shift / d) (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994, the N+1-bit multiplier case).
+struct DivMagic {
+    uint64_t mul;
+    int shift;
+};
+static DivMagic div_magic(int d) {
+    int l = 0;
+    while ((1LL << l) < d) ++l;
+    const int shift = 31 + l;
+    return {((1ULL << shift) + (uint64_t)d - 1) / (uint64_t)d, shift};
+}
+
+template <int B, int MS, int WN>
 static hipError_t launch_gemm_t(const GemmArgs& a, const GemmShape& sh, hipStream_t st) {
+    const DivMagic gm = div_magic(a.group);
     const int tiles = sh.grid_m * sh.grid_n * sh.split;
     const int grid = 8 * ((tiles + 7) / 8);
-    hipLaunchKernelGGL((gemm_kernel<B, TM>), dim3(grid), dim3(256), 0, st, a.w, a.s, a.m, a.x, a.y,
-                       a.partial, a.m_rows, a.n, a.k, a.group, sh.grid_m, sh.grid_n, sh.split,
-                       sh.k_tiles_per_split);
+    hipLaunchKernelGGL((gemm_kernel<B, MS, WN>), dim3(grid), dim3(128 * WN), 0, st, a.w, a.s, a.m, a.x, a.y,
+                       a.partial, a.m_rows, a.n, a.k, gm.mul, gm.shift, sh.grid_m, sh.grid_n,
+                       sh.split, sh.k_tiles_per_split);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || sh.split == 1) return err;
     const int64_t count = (int64_t)a.m_rows * a.n;
@@ -221,14 +407,23 @@ static hipError_t launch_gemm_t(const GemmArgs& a, const GemmShape& sh, hipStrea
     return hipGetLastError();
 }
 
+template <int B>
+static hipError_t launch_gemm_b(const GemmArgs& a, const GemmShape& sh, hipStream_t st) {
+    switch (sh.tile_m) {
+        case 32: return launch_gemm_t<B, 1, gemm_threads(32) / 128>(a, sh, st);
+        case 64: return launch_gemm_t<B, 2, gemm_threads(64) / 128>(a, sh, st);
+        case 128: return launch_gemm_t<B, 4, gemm_threads(128) / 128>(a, sh, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_gemm(const GemmArgs& a, const GemmShape& sh, hipStream_t st) {
-    const bool t2 = sh.tile_m == 128;
     switch (a.bits) {
-        case 2: return t2 ? launch_gemm_t<2, 2>(a, sh, st) : launch_gemm_t<2, 1>(a, sh, st);
-        case 3: return t2 ? launch_gemm_t<3, 2>(a, sh, st) : launch_gemm_t<3, 1>(a, sh, st);
-        case 4: return t2 ? launch_gemm_t<4, 2>(a, sh, st) : launch_gemm_t<4, 1>(a, sh, st);
-        case 6: return t2 ? launch_gemm_t<6, 2>(a, sh, st) : launch_gemm_t<6, 1>(a, sh, st);
-        case 8: return t2 ? launch_gemm_t<8, 2>(a, sh, st) : launch_gemm_t<8, 1>(a, sh, st);
+        case 2: return launch_gemm_b<2>(a, sh, st);
+        case 3: return launch_gemm_b<3>(a, sh, st);
+        case 4: return launch_gemm_b<4>(a, sh, st);
+        case 6: return launch_gemm_b<6>(a, sh, st);
+        case 8: return launch_gemm_b<8>(a, sh, st);
         default: return hipErrorInvalidValue;
     }
 }

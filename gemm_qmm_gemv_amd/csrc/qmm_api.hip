@@ -64,6 +64,7 @@ bool bits_supported(int bits) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr int64_t INT_LIMIT = 0x7fffffff;
+constexpr int64_t OFFSET_LIMIT = 0xffffffffLL;  // largest byte size a 32-bit offset covers
 
 qmm_status check_format(int64_t n, int64_t k, int bits, int group) {
     if (bits < 2 || bits > 8) return fail(QMM_ERR_INVALID_ARGUMENT, "bits=%d outside 2..8", bits);
@@ -77,6 +78,18 @@ qmm_status check_format(int64_t n, int64_t k, int bits, int group) {
     if (n < 0) return fail(QMM_ERR_INVALID_ARGUMENT, "n=%lld is negative", (long long)n);
     if (n > INT_LIMIT || k > INT_LIMIT)
         return fail(QMM_ERR_INVALID_ARGUMENT, "n or k above 2^31-1");
+    // The kernels address one matrix (and one activation block) with 32-bit
+    // buffer offsets.
+    if (n * (k / 32) * bits * 4 > OFFSET_LIMIT)
+        return fail(QMM_ERR_UNSUPPORTED, "packed matrix of %lld x %lld at %d bits is 4 GiB or more",
+                    (long long)n, (long long)k, bits);
+    return QMM_OK;
+}
+
+qmm_status check_activation_bytes(int64_t rows, int64_t k) {
+    if (rows * k * 2 > OFFSET_LIMIT)
+        return fail(QMM_ERR_UNSUPPORTED, "activation block of %lld x %lld fp16 is 4 GiB or more",
+                    (long long)rows, (long long)k);
     return QMM_OK;
 }
 
@@ -234,7 +247,7 @@ RowsShape plan_rows(int64_t rows_bound, int64_t n, int64_t k, int bits, int grou
 
 GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int cus, size_t ws_bytes, size_t* ws_need) {
     GemmShape sh{};
-    sh.tile_m = m <= 64 ? 64 : 128;
+    sh.tile_m = m <= 32 ? 32 : m <= 64 ? 64 : 128;
     sh.tile_n = 128;
     sh.grid_m = (int)((m + sh.tile_m - 1) / sh.tile_m);
     sh.grid_n = (int)((n + sh.tile_n - 1) / sh.tile_n);
@@ -243,7 +256,7 @@ GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int cus, size_t ws_bytes, s
     int split = 1;
     if (tiles < cus) {
         split = (int)((cus + tiles - 1) / tiles);
-        const int by_k = k_tiles / 4 > 1 ? k_tiles / 4 : 1;
+        const int by_k = k_tiles / 2 > 1 ? k_tiles / 2 : 1;
         if (split > by_k) split = by_k;
         if (split > 16) split = 16;
     }
@@ -324,6 +337,7 @@ qmm_status qmm_gemm(const void* w_packed, const void* scales, const void* mins, 
     if (m > INT_LIMIT || m * n > ((int64_t)1 << 40))
         return fail(QMM_ERR_INVALID_ARGUMENT, "m too large");
     if (m == 0 || n == 0) return ok();
+    if ((st = check_activation_bytes(m, k)) != QMM_OK) return st;
     if ((st = check_weight_ptrs(w_packed, scales, mins)) != QMM_OK) return st;
     if (!x || !y) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x or y");
     if (!aligned(x, 16) || !aligned(y, 16)) return fail(QMM_ERR_MISALIGNED, "x or y not 16-byte aligned");
@@ -363,6 +377,7 @@ qmm_status qmm_moe_gemm(const void* w_packed, const void* scales, const void* mi
     if (p_rows > INT_LIMIT || n_experts > INT_LIMIT || x_rows_count > INT_LIMIT)
         return fail(QMM_ERR_INVALID_ARGUMENT, "p_rows, n_experts or x_rows_count above 2^31-1");
     if (p_rows == 0 || n == 0 || n_experts == 0) return ok();
+    if ((st = check_activation_bytes(x_rows ? x_rows_count : p_rows, k)) != QMM_OK) return st;
     if ((st = check_weight_ptrs(w_packed, scales, mins)) != QMM_OK) return st;
     if (!x || !y || !expert_offsets) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x, y or expert_offsets");
     if (!x_rows && x_rows_count < p_rows)
@@ -510,6 +525,7 @@ qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits, int g
     if (op == 1) {
         const GemmShape sh = plan_gemm(m, n, k, cus, workspace_bytes, nullptr);
         plan->variant = 2;
+        plan->block = gemm_threads(sh.tile_m);
         plan->split_k = sh.split;
         plan->tile_m = sh.tile_m;
         plan->tile_n = sh.tile_n;

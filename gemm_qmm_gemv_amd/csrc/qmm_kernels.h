@@ -174,7 +174,13 @@ QMM_DECLARE_BITS(8)
 #undef QMM_DECLARE_BITS
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmShape& sh, hipStream_t st);
-constexpr int GEMM_BK = 64;  // K per main-loop step
+constexpr int GEMM_BK = 128;  // K per main-loop step
+// Threads per GEMM work-group: 128 per wave column along N (two waves along
+// K); tiles of 64 and 128 rows use GEMM_WN columns, 32-row tiles two.
+#ifndef GEMM_WN
+#define GEMM_WN 4
+#endif
+constexpr int gemm_threads(int tile_m) { return 128 * (tile_m == 32 ? 2 : GEMM_WN); }
 
 hipError_t launch_unpack(const uint32_t* w, uint8_t* codes, int64_t n, int64_t k, int bits,
                          hipStream_t st);

@@ -32,6 +32,9 @@
  *   k >= 32 and k a multiple of group_size; n >= 0, m >= 0 (0 is a no-op);
  *   weight, activation and output pointers 16-byte aligned; scale and min
  *   pointers 2-byte aligned; non-NULL pointers wherever work is to be done.
+ *   One packed matrix (one expert of a stack) and one activation block must
+ *   each stay below 4 GiB, else QMM_ERR_UNSUPPORTED (the kernels address
+ *   them with 32-bit offsets).
  *   A failed check returns a status, writes nothing and launches nothing;
  *   qmm_last_error() then holds a one-line explanation (thread-local).
  *

@@ -159,7 +159,8 @@ def test_gemm_plan(lib, m, n, k):
     unlimited = 1 << 40
     pl = qmm.qmm_get_plan(1, m, n, k, 4, 64, cu_count=256, workspace_bytes=unlimited)
     assert pl["variant"] == 2
-    assert pl["tile_m"] in (64, 128) and pl["tile_n"] == 128
+    assert pl["tile_m"] == (32 if m <= 32 else 64 if m <= 64 else 128) and pl["tile_n"] == 128
+    assert pl["block"] == (256 if pl["tile_m"] == 32 else 512)
     tiles = -(-m // pl["tile_m"]) * -(-n // 128)
     assert pl["grid"] >= tiles * pl["split_k"]
     assert 1 <= pl["split_k"] <= 16
@@ -174,3 +175,18 @@ def test_small_m_routes(lib):
     assert qmm.qmm_get_plan(1, 2, 256, 1024, 4, 64, cu_count=256)["variant"] == 1
     assert qmm.qmm_get_plan(1, 3, 256, 1024, 4, 64, cu_count=256)["variant"] == 2
     assert qmm.qmm_get_plan(2, 16, 768, 2048, 4, 64, cu_count=256)["variant"] == 1
+
+
+def test_sizes_beyond_32bit_offsets_are_rejected(lib):
+    # One packed matrix or one activation block of 4 GiB or more cannot be
+    # addressed with the kernels' 32-bit buffer offsets.
+    assert _gemv(lib, n=1 << 20, k=1 << 15) == qmm.QMM_ERR_UNSUPPORTED
+    assert "4 GiB" in qmm.qmm_last_error()
+    p = ctypes.c_void_p
+    assert lib.qmm_gemm(p(A16), p(A16), p(A16), p(A16), p(A16), 1 << 20, 64, 1 << 12, 4, 64,
+                        None, 0, None) == qmm.QMM_ERR_UNSUPPORTED
+    assert "activation" in qmm.qmm_last_error()
+    # Just below the limit the checks pass on to the device (none here).
+    import torch
+    if not torch.cuda.is_available():
+        assert _gemv(lib, n=(1 << 20) - 64, k=1 << 13) == qmm.QMM_ERR_DEVICE
