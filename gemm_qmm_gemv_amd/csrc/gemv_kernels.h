@@ -22,6 +22,8 @@
 #include "qmm_device.h"
 #include "qmm_kernels.h"
 
+#include <type_traits>
+
 namespace qmm {
 
 // Weights of one row batch held in registers: U rows per slot, XC units per
@@ -64,17 +66,25 @@ __device__ __forceinline__ MatRsrc mat_rsrc(const void* W, const void* S, const 
 }
 
 // Issue every load of a row batch (rows rb + r*SLOTS + slot, r < U).  Rows
-// past n read zeros (buffer range check); units past the row read nothing.
-template <int B, int UNIT, int LPR, int XC, int U>
+// past n read zeros (buffer range check); units past the row, and the whole
+// batch when `batch_live` is false, read nothing: their offsets point at the
+// end of the buffer.  The loads are unconditional and the scale layout is a
+// compile-time choice, so a pipelined loop has no branches around loads and
+// the compiler can wait for exactly the batch it is about to use (a load
+// issued on only one side of a branch makes it drain the whole queue).
+template <int B, int UNIT, int LPR, int XC, int U, bool WIDE>
 __device__ __forceinline__ void load_batch(RowBatch<B, UNIT, XC, U>& bt, const MatRsrc& mr, int rb,
-                                           int wpr, int gpr, int slot, const int (&unit)[XC],
-                                           const int (&gidx)[XC], int nu, bool wide, int lane) {
+                                           bool batch_live, int wpr, int gpr, int slot,
+                                           const int (&unit)[XC], const int (&gidx)[XC], int nu,
+                                           int lane) {
     constexpr int SLOTS = 64 / LPR;
     constexpr int WPU = UNIT * B / 32;
     constexpr int ALIGN = unit_align(B, UNIT);
-    if (wide) {
+    if constexpr (WIDE) {
         const int words = SLOTS * U * gpr / 2;
-        const uint32_t off = lane < words ? ((uint32_t)rb * (uint32_t)gpr + 2u * (uint32_t)lane) * 2u : mr.sbytes;
+        const uint32_t off = (batch_live && lane < words)
+                                 ? ((uint32_t)rb * (uint32_t)gpr + 2u * (uint32_t)lane) * 2u
+                                 : mr.sbytes;
         bt.sblk = buffer_u32(mr.s, off);
         bt.mblk = buffer_u32(mr.m, off);
     }
@@ -83,10 +93,10 @@ __device__ __forceinline__ void load_batch(RowBatch<B, UNIT, XC, U>& bt, const M
         const uint32_t row = (uint32_t)(rb + r * SLOTS + slot);
 #pragma unroll
         for (int c = 0; c < XC; ++c) {
-            const bool live = unit[c] < nu;  // rows past n fall past the end by themselves
+            const bool live = batch_live && unit[c] < nu;  // rows past n fall past the end by themselves
             const uint32_t woff = live ? (row * (uint32_t)wpr + (uint32_t)(unit[c] * WPU)) * 4u : mr.wbytes;
             buffer_words<WPU, ALIGN>(mr.w, woff, bt.w[r][c]);
-            if (!wide) {
+            if constexpr (!WIDE) {
                 const uint32_t so = live ? (row * (uint32_t)gpr + (uint32_t)gidx[c]) * 2u : mr.sbytes;
                 bt.s[r][c] = buffer_u16(mr.s, so);
                 bt.m[r][c] = buffer_u16(mr.m, so);
@@ -96,17 +106,20 @@ __device__ __forceinline__ void load_batch(RowBatch<B, UNIT, XC, U>& bt, const M
 }
 
 // Partial dot products of a loaded batch, added into yacc[r].
-template <int B, int UNIT, int LPR, int XC, int U>
+template <int B, int UNIT, int LPR, int XC, int U, bool WIDE>
 __device__ __forceinline__ void accumulate_batch(const RowBatch<B, UNIT, XC, U>& bt,
                                                  const XUnit<B, UNIT> (&xu)[XC], float (&yacc)[U],
-                                                 bool wide, int slot, int gpr, const int (&gidx)[XC]) {
+                                                 int slot, int gpr, const int (&gidx)[XC]) {
     constexpr int SLOTS = 64 / LPR;
 #pragma unroll
     for (int r = 0; r < U; ++r)
 #pragma unroll
         for (int c = 0; c < XC; ++c) {
-            u32 sb = bt.s[r][c], mb = bt.m[r][c];
-            if (wide) {
+            u32 sb, mb;
+            if constexpr (!WIDE) {
+                sb = bt.s[r][c];
+                mb = bt.m[r][c];
+            } else {
                 // fp16 value number off of the block lives in word off/2, half off%2.
                 const int off = (r * SLOTS + slot) * gpr + gidx[c];
                 const int src = (off >> 1) << 2;
@@ -122,16 +135,17 @@ __device__ __forceinline__ void accumulate_batch(const RowBatch<B, UNIT, XC, U>&
         }
 }
 
-// Reduce the U row sums over the LPR lanes of each slot and store them.
+// Reduce the U row sums over the LPR lanes of each slot and store them.  The
+// store is unconditional: lanes with nothing to write aim past the end of y.
 template <int LPR, int U>
-__device__ __forceinline__ void store_batch(float (&yacc)[U], float* __restrict__ Y, int rb, int n,
-                                            int slot, int j) {
+__device__ __forceinline__ void store_batch(float (&yacc)[U], rsrc_t yr, int rb, int n, int slot,
+                                            int j) {
     constexpr int SLOTS = 64 / LPR;
 #pragma unroll
     for (int r = 0; r < U; ++r) {
         const float v = group_sum<LPR>(yacc[r]);
         const int row = rb + r * SLOTS + slot;
-        if (j == 0 && row < n) Y[row] = v;
+        buffer_store_f32(v, yr, (j == 0 && row < n) ? (uint32_t)row * 4u : (uint32_t)n * 4u);
     }
 }
 
@@ -157,9 +171,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
     const int wpr = k / 32 * B;
     const int gpr = k / group;
     const int stride = nwaves * SLOTS * U;
-    const bool wide = wide_scales_ok<LPR, U>(S, Mn, gpr);
     const MatRsrc mr = mat_rsrc(W, S, Mn, n, wpr, gpr);
     const rsrc_t xr = make_rsrc(X, (uint32_t)k * 2u);
+    const rsrc_t yr = make_rsrc(Y, (uint32_t)n * 4u);
 
     XUnit<B, UNIT> xu[XC];
     int unit[XC], gidx[XC];
@@ -180,48 +194,57 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
         }
     };
 
-    if constexpr (MP) {
-        const int passes = (nu + LPR * XC - 1) / (LPR * XC);
-        for (int rb = wave * SLOTS * U; rb < n; rb += stride) {
-            float yacc[U];
+    // The scale layout is fixed for the whole launch; both variants are
+    // compiled and one is chosen here, outside every loop.
+    auto body = [&](auto wide_c) {
+        constexpr bool WIDE = decltype(wide_c)::value;
+        if constexpr (MP) {
+            const int passes = (nu + LPR * XC - 1) / (LPR * XC);
+            for (int rb = wave * SLOTS * U; rb < n; rb += stride) {
+                float yacc[U];
 #pragma unroll
-            for (int r = 0; r < U; ++r) yacc[r] = 0.f;
-            for (int pass = 0; pass < passes; ++pass) {
-                units_of_pass(pass);
-                RowBatch<B, UNIT, XC, U> bt;
-                load_batch<B, UNIT, LPR, XC, U>(bt, mr, rb, wpr, gpr, slot, unit, gidx, nu, wide, lane);
-                prep();
-                accumulate_batch<B, UNIT, LPR, XC, U>(bt, xu, yacc, wide, slot, gpr, gidx);
+                for (int r = 0; r < U; ++r) yacc[r] = 0.f;
+                for (int pass = 0; pass < passes; ++pass) {
+                    units_of_pass(pass);
+                    RowBatch<B, UNIT, XC, U> bt;
+                    load_batch<B, UNIT, LPR, XC, U, WIDE>(bt, mr, rb, true, wpr, gpr, slot, unit, gidx, nu, lane);
+                    prep();
+                    accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(bt, xu, yacc, slot, gpr, gidx);
+                }
+                store_batch<LPR, U>(yacc, yr, rb, n, slot, j);
             }
-            store_batch<LPR, U>(yacc, Y, rb, n, slot, j);
-        }
-    } else {
-        units_of_pass(0);
-        int rb = wave * SLOTS * U;
-        if (rb >= n) return;
-        RowBatch<B, UNIT, XC, U> ba, bb;
-        load_batch<B, UNIT, LPR, XC, U>(ba, mr, rb, wpr, gpr, slot, unit, gidx, nu, wide, lane);
-        prep();
-        while (true) {
-            float yacc[U];
-            int nxt = rb + stride;
-            if (nxt < n) load_batch<B, UNIT, LPR, XC, U>(bb, mr, nxt, wpr, gpr, slot, unit, gidx, nu, wide, lane);
+        } else {
+            units_of_pass(0);
+            int rb = wave * SLOTS * U;
+            if (rb >= n) return;
+            RowBatch<B, UNIT, XC, U> ba, bb;
+            load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, rb, true, wpr, gpr, slot, unit, gidx, nu, lane);
+            prep();
+            while (true) {
+                float yacc[U];
+                int nxt = rb + stride;
+                load_batch<B, UNIT, LPR, XC, U, WIDE>(bb, mr, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
 #pragma unroll
-            for (int r = 0; r < U; ++r) yacc[r] = 0.f;
-            accumulate_batch<B, UNIT, LPR, XC, U>(ba, xu, yacc, wide, slot, gpr, gidx);
-            store_batch<LPR, U>(yacc, Y, rb, n, slot, j);
-            rb = nxt;
-            if (rb >= n) break;
-            nxt = rb + stride;
-            if (nxt < n) load_batch<B, UNIT, LPR, XC, U>(ba, mr, nxt, wpr, gpr, slot, unit, gidx, nu, wide, lane);
+                for (int r = 0; r < U; ++r) yacc[r] = 0.f;
+                accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(ba, xu, yacc, slot, gpr, gidx);
+                store_batch<LPR, U>(yacc, yr, rb, n, slot, j);
+                rb = nxt;
+                if (rb >= n) break;
+                nxt = rb + stride;
+                load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
 #pragma unroll
-            for (int r = 0; r < U; ++r) yacc[r] = 0.f;
-            accumulate_batch<B, UNIT, LPR, XC, U>(bb, xu, yacc, wide, slot, gpr, gidx);
-            store_batch<LPR, U>(yacc, Y, rb, n, slot, j);
-            rb = nxt;
-            if (rb >= n) break;
+                for (int r = 0; r < U; ++r) yacc[r] = 0.f;
+                accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(bb, xu, yacc, slot, gpr, gidx);
+                store_batch<LPR, U>(yacc, yr, rb, n, slot, j);
+                rb = nxt;
+                if (rb >= n) break;
+            }
         }
-    }
+    };
+    if (wide_scales_ok<LPR, U>(S, Mn, gpr))
+        body(std::true_type{});
+    else
+        body(std::false_type{});
 }
 
 // Multi-row product over row segments.  Segment e covers activation rows
@@ -376,18 +399,18 @@ __device__ __forceinline__ int batched_lanes_per_row(int nu) {
     return lpr;
 }
 
-// Row batches [b0, b1) of one matrix (all arguments wave-uniform).
-template <int B, int UNIT, int LPR, int XC, int U>
-__device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const uint16_t* Mn,
-                                         const uint16_t* X, float* Y, int n, int k, int group, int b0,
-                                         int b1, int lane) {
+// Row batches [b0, b1) of one matrix (all arguments wave-uniform), with the
+// scale layout fixed at compile time.
+template <int B, int UNIT, int LPR, int XC, int U, bool WIDE>
+__device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, const uint16_t* Mn,
+                                           const uint16_t* X, float* Y, int n, int k, int group,
+                                           int b0, int b1, int lane) {
     constexpr int SLOTS = 64 / LPR;
     constexpr int ROWS = SLOTS * U;
     const int slot = lane / LPR, j = lane % LPR;
     const int nu = k / UNIT;
     const int wpr = k / 32 * B;
     const int gpr = k / group;
-    const bool wide = wide_scales_ok<LPR, U>(S, Mn, gpr);
     const MatRsrc mr = mat_rsrc(W, S, Mn, n, wpr, gpr);
     const rsrc_t xr = make_rsrc(X, (uint32_t)k * 2u);
     const rsrc_t yr = make_rsrc(Y, (uint32_t)n * 4u);
@@ -398,7 +421,7 @@ __device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const 
         gidx[c] = unit[c] < nu ? (unit[c] * UNIT) / group : 0;
     }
     RowBatch<B, UNIT, XC, U> ba, bb;
-    load_batch<B, UNIT, LPR, XC, U>(ba, mr, b0 * ROWS, wpr, gpr, slot, unit, gidx, nu, wide, lane);
+    load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, b0 * ROWS, true, wpr, gpr, slot, unit, gidx, nu, lane);
     XUnit<B, UNIT> xu[XC];
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
@@ -411,22 +434,26 @@ __device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const 
         float yacc[U];
 #pragma unroll
         for (int r = 0; r < U; ++r) yacc[r] = 0.f;
-        accumulate_batch<B, UNIT, LPR, XC, U>(bt, xu, yacc, wide, slot, gpr, gidx);
-        const int rb = b * ROWS;
-#pragma unroll
-        for (int r = 0; r < U; ++r) {
-            const float v = group_sum<LPR>(yacc[r]);
-            const int row = rb + r * SLOTS + slot;
-            if (j == 0 && row < n) buffer_store_f32(v, yr, (uint32_t)row * 4u);
-        }
+        accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(bt, xu, yacc, slot, gpr, gidx);
+        store_batch<LPR, U>(yacc, yr, b * ROWS, n, slot, j);
     };
     for (int b = b0; b < b1; b += 2) {
-        if (b + 1 < b1) load_batch<B, UNIT, LPR, XC, U>(bb, mr, (b + 1) * ROWS, wpr, gpr, slot, unit, gidx, nu, wide, lane);
+        load_batch<B, UNIT, LPR, XC, U, WIDE>(bb, mr, (b + 1) * ROWS, b + 1 < b1, wpr, gpr, slot, unit, gidx, nu, lane);
         finish(ba, b);
         if (b + 1 >= b1) break;
-        if (b + 2 < b1) load_batch<B, UNIT, LPR, XC, U>(ba, mr, (b + 2) * ROWS, wpr, gpr, slot, unit, gidx, nu, wide, lane);
+        load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, (b + 2) * ROWS, b + 2 < b1, wpr, gpr, slot, unit, gidx, nu, lane);
         finish(bb, b + 1);
     }
+}
+
+template <int B, int UNIT, int LPR, int XC, int U>
+__device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const uint16_t* Mn,
+                                         const uint16_t* X, float* Y, int n, int k, int group, int b0,
+                                         int b1, int lane) {
+    if (wide_scales_ok<LPR, U>(S, Mn, k / group))
+        gemv_run_w<B, UNIT, LPR, XC, U, true>(W, S, Mn, X, Y, n, k, group, b0, b1, lane);
+    else
+        gemv_run_w<B, UNIT, LPR, XC, U, false>(W, S, Mn, X, Y, n, k, group, b0, b1, lane);
 }
 
 template <int B, int UNIT, int XC, int U>
