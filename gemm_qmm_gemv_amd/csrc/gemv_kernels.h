@@ -184,14 +184,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
             gidx[c] = unit[c] < nu ? (unit[c] * UNIT) / group : 0;
         }
     };
+    // Units past the row read zeros (offset at the end of x), which gives the
+    // all-zero unit state without a branch around the loads.
     auto prep = [&]() {
 #pragma unroll
-        for (int c = 0; c < XC; ++c) {
-            if (unit[c] < nu)
-                prep_xunit<B, UNIT>(xr, (uint32_t)(unit[c] * UNIT * 2), xu[c]);
-            else
-                zero_xunit<B, UNIT>(xu[c]);
-        }
+        for (int c = 0; c < XC; ++c)
+            prep_xunit<B, UNIT>(xr, unit[c] < nu ? (uint32_t)(unit[c] * UNIT * 2) : (uint32_t)k * 2u, xu[c]);
     };
 
     // The scale layout is fixed for the whole launch; both variants are
@@ -219,6 +217,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
             if (rb >= n) return;
             RowBatch<B, UNIT, XC, U> ba, bb;
             load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, rb, true, wpr, gpr, slot, unit, gidx, nu, lane);
+            // The first batch's weight loads go out before the activation
+            // loads and their set-up arithmetic.
+            __builtin_amdgcn_sched_barrier(0);
             prep();
             while (true) {
                 float yacc[U];
@@ -422,14 +423,14 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
     }
     RowBatch<B, UNIT, XC, U> ba, bb;
     load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, b0 * ROWS, true, wpr, gpr, slot, unit, gidx, nu, lane);
+    // The first batch's weight loads go out before the activation loads and
+    // their set-up arithmetic, which the scheduler would otherwise hoist.
+    __builtin_amdgcn_sched_barrier(0);
+    // Units past the row read zeros: the all-zero unit state, branch-free.
     XUnit<B, UNIT> xu[XC];
 #pragma unroll
-    for (int c = 0; c < XC; ++c) {
-        if (unit[c] < nu)
-            prep_xunit<B, UNIT>(xr, (uint32_t)(unit[c] * UNIT * 2), xu[c]);
-        else
-            zero_xunit<B, UNIT>(xu[c]);
-    }
+    for (int c = 0; c < XC; ++c)
+        prep_xunit<B, UNIT>(xr, unit[c] < nu ? (uint32_t)(unit[c] * UNIT * 2) : (uint32_t)k * 2u, xu[c]);
     auto finish = [&](const RowBatch<B, UNIT, XC, U>& bt, int b) {
         float yacc[U];
 #pragma unroll
@@ -437,6 +438,10 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
         accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(bt, xu, yacc, slot, gpr, gidx);
         store_batch<LPR, U>(yacc, yr, b * ROWS, n, slot, j);
     };
+    // The batch range is wave-uniform; saying so keeps the loop a scalar loop
+    // (no per-lane exit masks).
+    b0 = uniform(b0);
+    b1 = uniform(b1);
     for (int b = b0; b < b1; b += 2) {
         load_batch<B, UNIT, LPR, XC, U, WIDE>(bb, mr, (b + 1) * ROWS, b + 1 < b1, wpr, gpr, slot, unit, gidx, nu, lane);
         finish(ba, b);
