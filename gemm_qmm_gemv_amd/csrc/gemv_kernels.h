@@ -253,10 +253,42 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
 // offsets is NULL) and multiplies them by weight matrix e of a stack
 // (W + e*n*wpr, S/Mn + e*n*gpr).  Only non-empty segments get work: blockIdx.y
 // is a rank among the non-empty segments, so the host can size the grid by
-// min(segments, rows) without reading the offsets.  blockIdx.x strides over
-// the weight rows.  Activations are taken MR rows at a time and their unit
-// state is built once per MR-batch; each weight unit loaded is then used for
-// all MR rows.  Rows whose activation index is out of range produce NaN.
+// min(segments, rows) without reading the offsets.  The waves of blockIdx.x
+// stride over the weight rows.  Activations are taken MR rows at a time and
+// their unit state is built once per MR-batch; each weight unit loaded is then
+// used for all MR rows.  Rows whose activation index is out of range produce
+// NaN.  Single pass (k <= LPR*XC*UNIT): the weight-row loop is pipelined like
+// the decode GEMV, and the first batch's weight loads go out as soon as the
+// segment is known, ahead of the activation lookups.
+template <int B, int UNIT, int LPR, int XC, int MR, bool WIDE>
+__device__ __forceinline__ void accumulate_rows(const RowBatch<B, UNIT, XC, 1>& bt,
+                                                const XUnit<B, UNIT> (&xu)[MR][XC],
+                                                float (&yacc)[MR], int slot, int gpr,
+                                                const int (&gidx)[XC]) {
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+        u32 sb, mb;
+        if constexpr (!WIDE) {
+            sb = bt.s[0][c];
+            mb = bt.m[0][c];
+        } else {
+            const int off = slot * gpr + gidx[c];
+            const int src = (off >> 1) << 2;
+            const u32 sw = (u32)__builtin_amdgcn_ds_bpermute(src, (int)bt.sblk);
+            const u32 mw = (u32)__builtin_amdgcn_ds_bpermute(src, (int)bt.mblk);
+            const u32 sh = (off & 1) << 4;
+            sb = (sw >> sh) & 0xFFFFu;
+            mb = (mw >> sh) & 0xFFFFu;
+        }
+        const float sf = half_bits_to_float((uint16_t)sb), mf = half_bits_to_float((uint16_t)mb);
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            const float t = unit_qx<B, UNIT>(bt.w[0][c], xu[r][c]);
+            yacc[r] = __builtin_fmaf(sf, t, __builtin_fmaf(mf, xu[r][c].xsum, yacc[r]));
+        }
+    }
+}
+
 template <int B, int UNIT, int LPR, int XC, int MR, bool MP>
 __global__ __launch_bounds__(256) void gemv_rows_kernel(
     const u32* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ Mn,
@@ -307,14 +339,23 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
             base += cnt;
         }
     }
+    e = uniform(e);
+    p0 = uniform(p0);
+    p1 = uniform(p1);
     if (e < 0 || p0 >= p1) return;
-    const MatRsrc mr = mat_rsrc(W + (size_t)e * n * wpr, S + (size_t)e * n * gpr,
-                                Mn + (size_t)e * n * gpr, n, wpr, gpr);
-    const rsrc_t xbuf = make_rsrc(X, (uint32_t)x_count * (uint32_t)k * 2u);
+    const u32* We = W + (size_t)e * n * wpr;
+    const uint16_t* Se = S + (size_t)e * n * gpr;
+    const uint16_t* Me = Mn + (size_t)e * n * gpr;
+    const MatRsrc mr = mat_rsrc(We, Se, Me, n, wpr, gpr);
+    const uint32_t x_bytes = (uint32_t)x_count * (uint32_t)k * 2u;
+    const rsrc_t xbuf = make_rsrc(X, x_bytes);
+    const uint32_t y_bytes = (uint32_t)m_total * (uint32_t)n * 4u;
+    const rsrc_t yr = make_rsrc(Y, y_bytes);
 
-    for (int pb = p0; pb < p1; pb += MR) {
-        int xr[MR];
-        bool bad[MR];
+    // Activation row indices of one MR-batch; out-of-range indices give NaN.
+    int xr[MR];
+    bool bad[MR];
+    auto rows_of = [&](int pb) {
 #pragma unroll
         for (int r = 0; r < MR; ++r) {
             const int p = pb + r;
@@ -322,63 +363,113 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
             bad[r] = (p < p1) && (idx < 0 || idx >= x_count);
             xr[r] = (p < p1 && !bad[r]) ? idx : -1;
         }
-        XUnit<B, UNIT> xu[MR][XC];
-        auto prep = [&](int pass) {
+    };
+    XUnit<B, UNIT> xu[MR][XC];
+    // Missing rows and units read zeros: the all-zero unit state, branch-free.
+    auto prep = [&](int pass) {
 #pragma unroll
-            for (int r = 0; r < MR; ++r)
+        for (int r = 0; r < MR; ++r)
 #pragma unroll
-                for (int c = 0; c < XC; ++c) {
-                    const int u = (pass * XC + c) * LPR + j;
-                    if (xr[r] >= 0 && u < nu)
-                        prep_xunit<B, UNIT>(xbuf, ((uint32_t)xr[r] * (uint32_t)k + (uint32_t)(u * UNIT)) * 2u,
-                                            xu[r][c]);
-                    else
-                        zero_xunit<B, UNIT>(xu[r][c]);
-                }
-        };
-        if constexpr (!MP) prep(0);
-        for (int rb = wave * SLOTS; rb < n; rb += nwaves * SLOTS) {
-            const int row = rb + slot;
-            float yacc[MR];
+            for (int c = 0; c < XC; ++c) {
+                const int u = (pass * XC + c) * LPR + j;
+                const uint32_t off = (xr[r] >= 0 && u < nu)
+                                         ? ((uint32_t)xr[r] * (uint32_t)k + (uint32_t)(u * UNIT)) * 2u
+                                         : x_bytes;
+                prep_xunit<B, UNIT>(xbuf, off, xu[r][c]);
+            }
+    };
+    auto store_rows = [&](float (&yacc)[MR], int pb, int row) {
 #pragma unroll
-            for (int r = 0; r < MR; ++r) yacc[r] = 0.f;
-            for (int pass = 0; pass < passes; ++pass) {
-                if constexpr (MP) prep(pass);
-                u32 wv[XC][WPU];
-                uint16_t sv[XC], mv[XC];
+        for (int r = 0; r < MR; ++r) {
+            const float v = group_sum<LPR>(yacc[r]);
+            const int p = pb + r;
+            const bool ok = j == 0 && row < n && p < p1;
+            buffer_store_f32(bad[r] ? __builtin_nanf("") : v, yr,
+                             ok ? ((uint32_t)p * (uint32_t)n + (uint32_t)row) * 4u : y_bytes);
+        }
+    };
+
+    if constexpr (MP) {
+        for (int pb = p0; pb < p1; pb += MR) {
+            rows_of(pb);
+            for (int rb = wave * SLOTS; rb < n; rb += nwaves * SLOTS) {
+                const int row = rb + slot;
+                float yacc[MR];
 #pragma unroll
-                for (int c = 0; c < XC; ++c) {
-                    const int u = (pass * XC + c) * LPR + j;
-                    if (row < n && u < nu) {
-                        buffer_words<WPU, ALIGN>(mr.w, ((uint32_t)row * (uint32_t)wpr + (uint32_t)(u * WPU)) * 4u,
-                                                 wv[c]);
-                        const uint32_t so = ((uint32_t)row * (uint32_t)gpr + (uint32_t)((u * UNIT) / group)) * 2u;
-                        sv[c] = (uint16_t)buffer_u16(mr.s, so);
-                        mv[c] = (uint16_t)buffer_u16(mr.m, so);
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < WPU; ++i) wv[c][i] = 0u;
-                        sv[c] = 0;
-                        mv[c] = 0;
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < MR; ++r)
+                for (int r = 0; r < MR; ++r) yacc[r] = 0.f;
+                for (int pass = 0; pass < passes; ++pass) {
+                    prep(pass);
+                    u32 wv[XC][WPU];
+                    u32 sv[XC], mv[XC];
 #pragma unroll
                     for (int c = 0; c < XC; ++c) {
-                        const float t = unit_qx<B, UNIT>(wv[c], xu[r][c]);
-                        yacc[r] = __builtin_fmaf(half_bits_to_float(sv[c]), t,
-                                                 __builtin_fmaf(half_bits_to_float(mv[c]), xu[r][c].xsum, yacc[r]));
+                        const int u = (pass * XC + c) * LPR + j;
+                        const bool live = row < n && u < nu;
+                        buffer_words<WPU, ALIGN>(mr.w,
+                                                 live ? ((uint32_t)row * (uint32_t)wpr + (uint32_t)(u * WPU)) * 4u
+                                                      : mr.wbytes,
+                                                 wv[c]);
+                        const uint32_t so = live ? ((uint32_t)row * (uint32_t)gpr + (uint32_t)((u * UNIT) / group)) * 2u
+                                                 : mr.sbytes;
+                        sv[c] = buffer_u16(mr.s, so);
+                        mv[c] = buffer_u16(mr.m, so);
                     }
-            }
 #pragma unroll
-            for (int r = 0; r < MR; ++r) {
-                const float v = group_sum<LPR>(yacc[r]);
-                const int p = pb + r;
-                if (j == 0 && row < n && p < p1)
-                    Y[(size_t)p * n + row] = bad[r] ? __builtin_nanf("") : v;
+                    for (int r = 0; r < MR; ++r)
+#pragma unroll
+                        for (int c = 0; c < XC; ++c) {
+                            const float t = unit_qx<B, UNIT>(wv[c], xu[r][c]);
+                            yacc[r] = __builtin_fmaf(half_bits_to_float((uint16_t)sv[c]), t,
+                                                     __builtin_fmaf(half_bits_to_float((uint16_t)mv[c]),
+                                                                    xu[r][c].xsum, yacc[r]));
+                        }
+                }
+                store_rows(yacc, pb, row);
             }
         }
+    } else {
+        int unit[XC], gidx[XC];
+#pragma unroll
+        for (int c = 0; c < XC; ++c) {
+            unit[c] = c * LPR + j;
+            gidx[c] = unit[c] < nu ? (unit[c] * UNIT) / group : 0;
+        }
+        const int stride = nwaves * SLOTS;
+        auto body = [&](auto wide_c) {
+            constexpr bool WIDE = decltype(wide_c)::value;
+            for (int pb = p0; pb < p1; pb += MR) {
+                int rb = wave * SLOTS;
+                if (rb >= n) return;
+                RowBatch<B, UNIT, XC, 1> ba, bb;
+                load_batch<B, UNIT, LPR, XC, 1, WIDE>(ba, mr, rb, true, wpr, gpr, slot, unit, gidx, nu, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                rows_of(pb);
+                prep(0);
+                while (true) {
+                    float yacc[MR];
+                    int nxt = rb + stride;
+                    load_batch<B, UNIT, LPR, XC, 1, WIDE>(bb, mr, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
+#pragma unroll
+                    for (int r = 0; r < MR; ++r) yacc[r] = 0.f;
+                    accumulate_rows<B, UNIT, LPR, XC, MR, WIDE>(ba, xu, yacc, slot, gpr, gidx);
+                    store_rows(yacc, pb, rb + slot);
+                    rb = nxt;
+                    if (rb >= n) break;
+                    nxt = rb + stride;
+                    load_batch<B, UNIT, LPR, XC, 1, WIDE>(ba, mr, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
+#pragma unroll
+                    for (int r = 0; r < MR; ++r) yacc[r] = 0.f;
+                    accumulate_rows<B, UNIT, LPR, XC, MR, WIDE>(bb, xu, yacc, slot, gpr, gidx);
+                    store_rows(yacc, pb, rb + slot);
+                    rb = nxt;
+                    if (rb >= n) break;
+                }
+            }
+        };
+        if (wide_scales_ok<LPR, 1>(Se, Me, gpr))
+            body(std::true_type{});
+        else
+            body(std::false_type{});
     }
 }
 
@@ -534,17 +625,29 @@ hipError_t launch_batched_t(const BatchArgs& a, const GemvShape& sh, hipStream_t
     return hipGetLastError();
 }
 
+// The grid is (row chunks, active segments); the row chunks of all segments
+// together are capped at what the GPU holds resident, so every wave starts at
+// once and loops over its rows instead of queueing behind other work-groups.
+template <auto Kernel>
+inline dim3 rows_grid(const RowsShape& sh) {
+    const int64_t resident = (int64_t)sh.cus * blocks_per_cu<Kernel>();
+    int64_t gx = resident / (sh.grid_y > 0 ? sh.grid_y : 1);
+    if (gx > sh.grid_x) gx = sh.grid_x;
+    if (gx < 1) gx = 1;
+    return dim3((unsigned)gx, (unsigned)sh.grid_y);
+}
+
 template <int B, int UNIT, int LPR, int XC, int MR>
 hipError_t launch_rows_t(const RowsArgs& a, const RowsShape& sh, hipStream_t st) {
-    const dim3 grid(sh.grid_x, sh.grid_y);
-    if (sh.multipass)
-        hipLaunchKernelGGL((gemv_rows_kernel<B, UNIT, LPR, XC, MR, true>), grid, dim3(256), 0, st,
-                           a.w, a.s, a.m, a.x, a.x_rows, a.x_count, a.offsets, a.n_seg, a.m_total,
-                           a.y, a.n, a.k, a.group);
-    else
-        hipLaunchKernelGGL((gemv_rows_kernel<B, UNIT, LPR, XC, MR, false>), grid, dim3(256), 0, st,
-                           a.w, a.s, a.m, a.x, a.x_rows, a.x_count, a.offsets, a.n_seg, a.m_total,
-                           a.y, a.n, a.k, a.group);
+    if (sh.multipass) {
+        constexpr auto kern = gemv_rows_kernel<B, UNIT, LPR, XC, MR, true>;
+        hipLaunchKernelGGL(kern, rows_grid<kern>(sh), dim3(256), 0, st, a.w, a.s, a.m, a.x, a.x_rows,
+                           a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group);
+    } else {
+        constexpr auto kern = gemv_rows_kernel<B, UNIT, LPR, XC, MR, false>;
+        hipLaunchKernelGGL(kern, rows_grid<kern>(sh), dim3(256), 0, st, a.w, a.s, a.m, a.x, a.x_rows,
+                           a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group);
+    }
     return hipGetLastError();
 }
 

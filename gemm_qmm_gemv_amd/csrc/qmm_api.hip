@@ -86,6 +86,13 @@ qmm_status check_format(int64_t n, int64_t k, int bits, int group) {
     return QMM_OK;
 }
 
+qmm_status check_output_bytes(int64_t rows, int64_t n) {
+    if (rows * n * 4 > OFFSET_LIMIT)
+        return fail(QMM_ERR_UNSUPPORTED, "output of %lld x %lld fp32 is 4 GiB or more",
+                    (long long)rows, (long long)n);
+    return QMM_OK;
+}
+
 qmm_status check_activation_bytes(int64_t rows, int64_t k) {
     if (rows * k * 2 > OFFSET_LIMIT)
         return fail(QMM_ERR_UNSUPPORTED, "activation block of %lld x %lld fp16 is 4 GiB or more",
@@ -231,17 +238,21 @@ RowsShape plan_rows(int64_t rows_bound, int64_t n, int64_t k, int bits, int grou
     sh.lpr = ls.lpr;
     sh.xc = ls.xc;
     sh.multipass = ls.multipass;
-    sh.mr = (sh.xc == 1 && rows_bound > 2) ? 4 : 2;
+    // Activation rows per MR-batch: what a segment is expected to hold
+    // (rows spread over the active segments), at most 4 (2 with two units
+    // per lane).
+    const int64_t segs = n_seg_active > 0 ? n_seg_active : 1;
+    const int64_t per_seg = (rows_bound + segs - 1) / segs;
+    const int mr_max = sh.xc == 1 ? 4 : 2;
+    sh.mr = per_seg <= 1 ? 1 : per_seg <= 2 ? 2 : mr_max;
+    const int em = env_int("QMM_ROWS_MR", 0);
+    if (em > 0 && rows_shape_supported(sh.lpr, sh.xc, em)) sh.mr = em;
     const int slots = 64 / sh.lpr;
     const int64_t rows_per_block = 4 * slots;
-    int64_t gx = (n + rows_per_block - 1) / rows_per_block;
-    const int64_t cap = (int64_t)cus * 16;
-    if (gx * n_seg_active > cap) {
-        gx = cap / (n_seg_active > 0 ? n_seg_active : 1);
-        if (gx < 1) gx = 1;
-    }
-    sh.grid_x = (int)gx;
-    sh.grid_y = (int)(n_seg_active > 0 ? n_seg_active : 1);
+    const int64_t gx = (n + rows_per_block - 1) / rows_per_block;
+    sh.grid_x = (int)(gx < INT_LIMIT ? gx : INT_LIMIT);
+    sh.grid_y = (int)segs;
+    sh.cus = cus;
     return sh;
 }
 
@@ -338,6 +349,7 @@ qmm_status qmm_gemm(const void* w_packed, const void* scales, const void* mins, 
         return fail(QMM_ERR_INVALID_ARGUMENT, "m too large");
     if (m == 0 || n == 0) return ok();
     if ((st = check_activation_bytes(m, k)) != QMM_OK) return st;
+    if ((st = check_output_bytes(m, n)) != QMM_OK) return st;
     if ((st = check_weight_ptrs(w_packed, scales, mins)) != QMM_OK) return st;
     if (!x || !y) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x or y");
     if (!aligned(x, 16) || !aligned(y, 16)) return fail(QMM_ERR_MISALIGNED, "x or y not 16-byte aligned");
@@ -378,6 +390,7 @@ qmm_status qmm_moe_gemm(const void* w_packed, const void* scales, const void* mi
         return fail(QMM_ERR_INVALID_ARGUMENT, "p_rows, n_experts or x_rows_count above 2^31-1");
     if (p_rows == 0 || n == 0 || n_experts == 0) return ok();
     if ((st = check_activation_bytes(x_rows ? x_rows_count : p_rows, k)) != QMM_OK) return st;
+    if ((st = check_output_bytes(p_rows, n)) != QMM_OK) return st;
     if ((st = check_weight_ptrs(w_packed, scales, mins)) != QMM_OK) return st;
     if (!x || !y || !expert_offsets) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x, y or expert_offsets");
     if (!x_rows && x_rows_count < p_rows)

@@ -73,7 +73,8 @@ struct RowsArgs {
 struct RowsShape {
     int unit, lpr, xc, mr;
     bool multipass;
-    int grid_x, grid_y;
+    int grid_x, grid_y;  // grid_x: row chunks wanted per segment (capped at launch)
+    int cus;
 };
 
 struct GemmArgs {
@@ -127,7 +128,8 @@ struct BatchArgs {
 
 #define QMM_ROWS_SHAPES(X) \
     X(16, 1, 4) X(32, 1, 4) X(64, 1, 4) \
-    X(16, 1, 2) X(32, 1, 2) X(64, 1, 2) X(64, 2, 2) X(32, 2, 2) X(16, 2, 2)
+    X(16, 1, 2) X(32, 1, 2) X(64, 1, 2) X(64, 2, 2) X(32, 2, 2) X(16, 2, 2) \
+    X(16, 1, 1) X(32, 1, 1) X(64, 1, 1) X(64, 2, 1) X(32, 2, 1) X(16, 2, 1)
 
 constexpr bool gemv_shape_supported(int lpr, int xc, int u) {
 #define X(L, C, UU) if (lpr == L && xc == C && u == UU) return true;

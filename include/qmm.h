@@ -34,7 +34,7 @@
  *   pointers 2-byte aligned; non-NULL pointers wherever work is to be done.
  *   One packed matrix (one expert of a stack) and one activation block must
  *   each stay below 4 GiB, else QMM_ERR_UNSUPPORTED (the kernels address
- *   them with 32-bit offsets).
+ *   them with 32-bit offsets); so must one output block.
  *   A failed check returns a status, writes nothing and launches nothing;
  *   qmm_last_error() then holds a one-line explanation (thread-local).
  *
