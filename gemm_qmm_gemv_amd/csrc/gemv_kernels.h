@@ -251,10 +251,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
 // Multi-row product over row segments.  Segment e covers activation rows
 // [offsets[e], offsets[e+1]) (clamped to [0, m_total]; [0, m_total) when
 // offsets is NULL) and multiplies them by weight matrix e of a stack
-// (W + e*n*wpr, S/Mn + e*n*gpr).  Only non-empty segments get work: blockIdx.y
-// is a rank among the non-empty segments, so the host can size the grid by
-// min(segments, rows) without reading the offsets.  The waves of blockIdx.x
-// stride over the weight rows.  Activations are taken MR rows at a time and
+// (W + e*n*wpr, S/Mn + e*n*gpr).  Only non-empty segments get work, one
+// work-group row (blockIdx.y) per batch of MR activation rows, so the host
+// can bound the grid by the row count without reading the offsets.  The waves
+// of blockIdx.x stride over the weight rows.  Activations are taken MR rows at a time and
 // their unit state is built once per MR-batch; each weight unit loaded is then
 // used for all MR rows.  Rows whose activation index is out of range produce
 // NaN.  Single pass (k <= LPR*XC*UNIT): the weight-row loop is pipelined like
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
     const u32* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ Mn,
     const uint16_t* __restrict__ X, const int32_t* __restrict__ x_rows, int x_count,
     const int32_t* __restrict__ offsets, int n_seg, int m_total, float* __restrict__ Y, int n,
-    int k, int group) {
+    int k, int group, int pair_bound) {
     constexpr int SLOTS = 64 / LPR;
     constexpr int WPU = UNIT * B / 32;
     constexpr int ALIGN = unit_align(B, UNIT);
@@ -308,12 +308,23 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
     const int gpr = k / group;
     const int passes = MP ? (nu + LPR * XC - 1) / (LPR * XC) : 1;
 
-    // Find the segment of rank blockIdx.y among the non-empty ones.
-    int e = -1, p0 = 0, p1 = 0;
-    if (!offsets) {
-        if (blockIdx.y == 0) { e = 0; p1 = m_total; }
-    } else {
-        const int target = blockIdx.y;
+    // A work-group row handles one (segment, MR-row batch) pair at a time:
+    // target is a rank among the pairs of the non-empty segments, in segment
+    // order, so segments with more rows get more work-groups instead of
+    // longer ones.  pair_bound is the host's upper bound on the number of
+    // pairs; when the grid's y extent is capped below it, each work-group row
+    // takes every gridDim.y-th pair.
+    auto find = [&](int target, int& e, int& p0, int& p1) {
+        e = -1;
+        p0 = p1 = 0;
+        if (!offsets) {
+            if (target * MR < m_total) {
+                e = 0;
+                p0 = target * MR;
+                p1 = min(m_total, p0 + MR);
+            }
+            return;
+        }
         int base = 0;
         for (int e0 = 0; e0 < n_seg && e < 0; e0 += 64) {
             const int ee = e0 + lane;
@@ -324,152 +335,161 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
                 a = a < 0 ? 0 : (a > m_total ? m_total : a);
                 b = b < a ? a : (b > m_total ? m_total : b);
             }
-            const bool ne = b > a;
-            const unsigned long long mask = __ballot(ne);
-            const int cnt = __popcll(mask);
-            if (target < base + cnt) {
-                const int before = __popcll(mask & ((1ull << lane) - 1ull));
-                const bool mine = ne && (before == target - base);
-                const unsigned long long who = __ballot(mine);
-                const int src = __ffsll((long long)who) - 1;
+            const int cnt = (b - a + MR - 1) / MR;
+            int incl = cnt;  // inclusive prefix sum over the lanes
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int t = __shfl_up(incl, d, 64);
+                if (lane >= d) incl += t;
+            }
+            const int total = __shfl(incl, 63, 64);
+            if (target < base + total) {
+                const unsigned long long past = __ballot(base + incl > target);
+                const int src = __ffsll((long long)past) - 1;
+                const int before = __shfl(incl - cnt, src, 64);
+                const int bi = target - base - before;
                 e = __shfl(ee, src, 64);
-                p0 = __shfl(a, src, 64);
-                p1 = __shfl(b, src, 64);
+                p0 = __shfl(a, src, 64) + bi * MR;
+                p1 = min(__shfl(b, src, 64), p0 + MR);
             }
-            base += cnt;
+            base += total;
         }
-    }
-    e = uniform(e);
-    p0 = uniform(p0);
-    p1 = uniform(p1);
-    if (e < 0 || p0 >= p1) return;
-    const u32* We = W + (size_t)e * n * wpr;
-    const uint16_t* Se = S + (size_t)e * n * gpr;
-    const uint16_t* Me = Mn + (size_t)e * n * gpr;
-    const MatRsrc mr = mat_rsrc(We, Se, Me, n, wpr, gpr);
-    const uint32_t x_bytes = (uint32_t)x_count * (uint32_t)k * 2u;
-    const rsrc_t xbuf = make_rsrc(X, x_bytes);
-    const uint32_t y_bytes = (uint32_t)m_total * (uint32_t)n * 4u;
-    const rsrc_t yr = make_rsrc(Y, y_bytes);
+    };
+    for (int target = blockIdx.y; target < pair_bound; target += gridDim.y) {
+        int e, p0, p1;
+        find(target, e, p0, p1);
+        e = uniform(e);
+        p0 = uniform(p0);
+        p1 = uniform(p1);
+        if (e < 0 || p0 >= p1) break;
+        const u32* We = W + (size_t)e * n * wpr;
+        const uint16_t* Se = S + (size_t)e * n * gpr;
+        const uint16_t* Me = Mn + (size_t)e * n * gpr;
+        const MatRsrc mr = mat_rsrc(We, Se, Me, n, wpr, gpr);
+        const uint32_t x_bytes = (uint32_t)x_count * (uint32_t)k * 2u;
+        const rsrc_t xbuf = make_rsrc(X, x_bytes);
+        const uint32_t y_bytes = (uint32_t)m_total * (uint32_t)n * 4u;
+        const rsrc_t yr = make_rsrc(Y, y_bytes);
 
-    // Activation row indices of one MR-batch; out-of-range indices give NaN.
-    int xr[MR];
-    bool bad[MR];
-    auto rows_of = [&](int pb) {
+        // Activation row indices of one MR-batch; out-of-range indices give NaN.
+        int xr[MR];
+        bool bad[MR];
+        auto rows_of = [&](int pb) {
 #pragma unroll
-        for (int r = 0; r < MR; ++r) {
-            const int p = pb + r;
-            const int idx = (p < p1) ? (x_rows ? x_rows[p] : p) : -1;
-            bad[r] = (p < p1) && (idx < 0 || idx >= x_count);
-            xr[r] = (p < p1 && !bad[r]) ? idx : -1;
-        }
-    };
-    XUnit<B, UNIT> xu[MR][XC];
-    // Missing rows and units read zeros: the all-zero unit state, branch-free.
-    auto prep = [&](int pass) {
-#pragma unroll
-        for (int r = 0; r < MR; ++r)
-#pragma unroll
-            for (int c = 0; c < XC; ++c) {
-                const int u = (pass * XC + c) * LPR + j;
-                const uint32_t off = (xr[r] >= 0 && u < nu)
-                                         ? ((uint32_t)xr[r] * (uint32_t)k + (uint32_t)(u * UNIT)) * 2u
-                                         : x_bytes;
-                prep_xunit<B, UNIT>(xbuf, off, xu[r][c]);
-            }
-    };
-    auto store_rows = [&](float (&yacc)[MR], int pb, int row) {
-#pragma unroll
-        for (int r = 0; r < MR; ++r) {
-            const float v = group_sum<LPR>(yacc[r]);
-            const int p = pb + r;
-            const bool ok = j == 0 && row < n && p < p1;
-            buffer_store_f32(bad[r] ? __builtin_nanf("") : v, yr,
-                             ok ? ((uint32_t)p * (uint32_t)n + (uint32_t)row) * 4u : y_bytes);
-        }
-    };
-
-    if constexpr (MP) {
-        for (int pb = p0; pb < p1; pb += MR) {
-            rows_of(pb);
-            for (int rb = wave * SLOTS; rb < n; rb += nwaves * SLOTS) {
-                const int row = rb + slot;
-                float yacc[MR];
-#pragma unroll
-                for (int r = 0; r < MR; ++r) yacc[r] = 0.f;
-                for (int pass = 0; pass < passes; ++pass) {
-                    prep(pass);
-                    u32 wv[XC][WPU];
-                    u32 sv[XC], mv[XC];
-#pragma unroll
-                    for (int c = 0; c < XC; ++c) {
-                        const int u = (pass * XC + c) * LPR + j;
-                        const bool live = row < n && u < nu;
-                        buffer_words<WPU, ALIGN>(mr.w,
-                                                 live ? ((uint32_t)row * (uint32_t)wpr + (uint32_t)(u * WPU)) * 4u
-                                                      : mr.wbytes,
-                                                 wv[c]);
-                        const uint32_t so = live ? ((uint32_t)row * (uint32_t)gpr + (uint32_t)((u * UNIT) / group)) * 2u
-                                                 : mr.sbytes;
-                        sv[c] = buffer_u16(mr.s, so);
-                        mv[c] = buffer_u16(mr.m, so);
-                    }
-#pragma unroll
-                    for (int r = 0; r < MR; ++r)
-#pragma unroll
-                        for (int c = 0; c < XC; ++c) {
-                            const float t = unit_qx<B, UNIT>(wv[c], xu[r][c]);
-                            yacc[r] = __builtin_fmaf(half_bits_to_float((uint16_t)sv[c]), t,
-                                                     __builtin_fmaf(half_bits_to_float((uint16_t)mv[c]),
-                                                                    xu[r][c].xsum, yacc[r]));
-                        }
-                }
-                store_rows(yacc, pb, row);
-            }
-        }
-    } else {
-        int unit[XC], gidx[XC];
-#pragma unroll
-        for (int c = 0; c < XC; ++c) {
-            unit[c] = c * LPR + j;
-            gidx[c] = unit[c] < nu ? (unit[c] * UNIT) / group : 0;
-        }
-        const int stride = nwaves * SLOTS;
-        auto body = [&](auto wide_c) {
-            constexpr bool WIDE = decltype(wide_c)::value;
-            for (int pb = p0; pb < p1; pb += MR) {
-                int rb = wave * SLOTS;
-                if (rb >= n) return;
-                RowBatch<B, UNIT, XC, 1> ba, bb;
-                load_batch<B, UNIT, LPR, XC, 1, WIDE>(ba, mr, rb, true, wpr, gpr, slot, unit, gidx, nu, lane);
-                __builtin_amdgcn_sched_barrier(0);
-                rows_of(pb);
-                prep(0);
-                while (true) {
-                    float yacc[MR];
-                    int nxt = rb + stride;
-                    load_batch<B, UNIT, LPR, XC, 1, WIDE>(bb, mr, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
-#pragma unroll
-                    for (int r = 0; r < MR; ++r) yacc[r] = 0.f;
-                    accumulate_rows<B, UNIT, LPR, XC, MR, WIDE>(ba, xu, yacc, slot, gpr, gidx);
-                    store_rows(yacc, pb, rb + slot);
-                    rb = nxt;
-                    if (rb >= n) break;
-                    nxt = rb + stride;
-                    load_batch<B, UNIT, LPR, XC, 1, WIDE>(ba, mr, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
-#pragma unroll
-                    for (int r = 0; r < MR; ++r) yacc[r] = 0.f;
-                    accumulate_rows<B, UNIT, LPR, XC, MR, WIDE>(bb, xu, yacc, slot, gpr, gidx);
-                    store_rows(yacc, pb, rb + slot);
-                    rb = nxt;
-                    if (rb >= n) break;
-                }
+            for (int r = 0; r < MR; ++r) {
+                const int p = pb + r;
+                const int idx = (p < p1) ? (x_rows ? x_rows[p] : p) : -1;
+                bad[r] = (p < p1) && (idx < 0 || idx >= x_count);
+                xr[r] = (p < p1 && !bad[r]) ? idx : -1;
             }
         };
-        if (wide_scales_ok<LPR, 1>(Se, Me, gpr))
-            body(std::true_type{});
-        else
-            body(std::false_type{});
+        XUnit<B, UNIT> xu[MR][XC];
+        // Missing rows and units read zeros: the all-zero unit state, branch-free.
+        auto prep = [&](int pass) {
+#pragma unroll
+            for (int r = 0; r < MR; ++r)
+#pragma unroll
+                for (int c = 0; c < XC; ++c) {
+                    const int u = (pass * XC + c) * LPR + j;
+                    const uint32_t off = (xr[r] >= 0 && u < nu)
+                                             ? ((uint32_t)xr[r] * (uint32_t)k + (uint32_t)(u * UNIT)) * 2u
+                                             : x_bytes;
+                    prep_xunit<B, UNIT>(xbuf, off, xu[r][c]);
+                }
+        };
+        auto store_rows = [&](float (&yacc)[MR], int pb, int row) {
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                const float v = group_sum<LPR>(yacc[r]);
+                const int p = pb + r;
+                const bool ok = j == 0 && row < n && p < p1;
+                buffer_store_f32(bad[r] ? __builtin_nanf("") : v, yr,
+                                 ok ? ((uint32_t)p * (uint32_t)n + (uint32_t)row) * 4u : y_bytes);
+            }
+        };
+
+        if constexpr (MP) {
+            for (int pb = p0; pb < p1; pb += MR) {
+                rows_of(pb);
+                for (int rb = wave * SLOTS; rb < n; rb += nwaves * SLOTS) {
+                    const int row = rb + slot;
+                    float yacc[MR];
+#pragma unroll
+                    for (int r = 0; r < MR; ++r) yacc[r] = 0.f;
+                    for (int pass = 0; pass < passes; ++pass) {
+                        prep(pass);
+                        u32 wv[XC][WPU];
+                        u32 sv[XC], mv[XC];
+#pragma unroll
+                        for (int c = 0; c < XC; ++c) {
+                            const int u = (pass * XC + c) * LPR + j;
+                            const bool live = row < n && u < nu;
+                            buffer_words<WPU, ALIGN>(mr.w,
+                                                     live ? ((uint32_t)row * (uint32_t)wpr + (uint32_t)(u * WPU)) * 4u
+                                                          : mr.wbytes,
+                                                     wv[c]);
+                            const uint32_t so = live ? ((uint32_t)row * (uint32_t)gpr + (uint32_t)((u * UNIT) / group)) * 2u
+                                                     : mr.sbytes;
+                            sv[c] = buffer_u16(mr.s, so);
+                            mv[c] = buffer_u16(mr.m, so);
+                        }
+#pragma unroll
+                        for (int r = 0; r < MR; ++r)
+#pragma unroll
+                            for (int c = 0; c < XC; ++c) {
+                                const float t = unit_qx<B, UNIT>(wv[c], xu[r][c]);
+                                yacc[r] = __builtin_fmaf(half_bits_to_float((uint16_t)sv[c]), t,
+                                                         __builtin_fmaf(half_bits_to_float((uint16_t)mv[c]),
+                                                                        xu[r][c].xsum, yacc[r]));
+                            }
+                    }
+                    store_rows(yacc, pb, row);
+                }
+            }
+        } else {
+            int unit[XC], gidx[XC];
+#pragma unroll
+            for (int c = 0; c < XC; ++c) {
+                unit[c] = c * LPR + j;
+                gidx[c] = unit[c] < nu ? (unit[c] * UNIT) / group : 0;
+            }
+            const int stride = nwaves * SLOTS;
+            auto body = [&](auto wide_c) {
+                constexpr bool WIDE = decltype(wide_c)::value;
+                for (int pb = p0; pb < p1; pb += MR) {
+                    int rb = wave * SLOTS;
+                    if (rb >= n) return;
+                    RowBatch<B, UNIT, XC, 1> ba, bb;
+                    load_batch<B, UNIT, LPR, XC, 1, WIDE>(ba, mr, rb, true, wpr, gpr, slot, unit, gidx, nu, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    rows_of(pb);
+                    prep(0);
+                    while (true) {
+                        float yacc[MR];
+                        int nxt = rb + stride;
+                        load_batch<B, UNIT, LPR, XC, 1, WIDE>(bb, mr, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
+#pragma unroll
+                        for (int r = 0; r < MR; ++r) yacc[r] = 0.f;
+                        accumulate_rows<B, UNIT, LPR, XC, MR, WIDE>(ba, xu, yacc, slot, gpr, gidx);
+                        store_rows(yacc, pb, rb + slot);
+                        rb = nxt;
+                        if (rb >= n) break;
+                        nxt = rb + stride;
+                        load_batch<B, UNIT, LPR, XC, 1, WIDE>(ba, mr, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
+#pragma unroll
+                        for (int r = 0; r < MR; ++r) yacc[r] = 0.f;
+                        accumulate_rows<B, UNIT, LPR, XC, MR, WIDE>(bb, xu, yacc, slot, gpr, gidx);
+                        store_rows(yacc, pb, rb + slot);
+                        rb = nxt;
+                        if (rb >= n) break;
+                    }
+                }
+            };
+            if (wide_scales_ok<LPR, 1>(Se, Me, gpr))
+                body(std::true_type{});
+            else
+                body(std::false_type{});
+        }
     }
 }
 
@@ -642,11 +662,11 @@ hipError_t launch_rows_t(const RowsArgs& a, const RowsShape& sh, hipStream_t st)
     if (sh.multipass) {
         constexpr auto kern = gemv_rows_kernel<B, UNIT, LPR, XC, MR, true>;
         hipLaunchKernelGGL(kern, rows_grid<kern>(sh), dim3(256), 0, st, a.w, a.s, a.m, a.x, a.x_rows,
-                           a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group);
+                           a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group, sh.pairs);
     } else {
         constexpr auto kern = gemv_rows_kernel<B, UNIT, LPR, XC, MR, false>;
         hipLaunchKernelGGL(kern, rows_grid<kern>(sh), dim3(256), 0, st, a.w, a.s, a.m, a.x, a.x_rows,
-                           a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group);
+                           a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group, sh.pairs);
     }
     return hipGetLastError();
 }

@@ -161,7 +161,7 @@ LaneSplit choose_split(int nu, int max_xc, bool (*supported)(int, int)) {
 }
 
 bool gemv_split_ok(int lpr, int xc) { return gemv_shape_supported(lpr, xc, 1); }
-bool rows_split_ok(int lpr, int xc) { return rows_shape_supported(lpr, xc, xc == 1 ? 4 : 2); }
+bool rows_split_ok(int lpr, int xc) { return rows_shape_supported(lpr, xc, 1); }
 
 GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     GemvShape sh{};
@@ -239,19 +239,22 @@ RowsShape plan_rows(int64_t rows_bound, int64_t n, int64_t k, int bits, int grou
     sh.xc = ls.xc;
     sh.multipass = ls.multipass;
     // Activation rows per MR-batch: what a segment is expected to hold
-    // (rows spread over the active segments), at most 4 (2 with two units
+    // (rows spread over the active segments), at most 2 (1 with two units
     // per lane).
     const int64_t segs = n_seg_active > 0 ? n_seg_active : 1;
     const int64_t per_seg = (rows_bound + segs - 1) / segs;
-    const int mr_max = sh.xc == 1 ? 4 : 2;
-    sh.mr = per_seg <= 1 ? 1 : per_seg <= 2 ? 2 : mr_max;
+    sh.mr = (per_seg <= 1 || sh.xc > 1) ? 1 : 2;
     const int em = env_int("QMM_ROWS_MR", 0);
     if (em > 0 && rows_shape_supported(sh.lpr, sh.xc, em)) sh.mr = em;
     const int slots = 64 / sh.lpr;
     const int64_t rows_per_block = 4 * slots;
     const int64_t gx = (n + rows_per_block - 1) / rows_per_block;
     sh.grid_x = (int)(gx < INT_LIMIT ? gx : INT_LIMIT);
-    sh.grid_y = (int)segs;
+    // One work-group row per (segment, MR-row batch): at most
+    // sum_e ceil(r_e / MR) <= (rows + (MR - 1) * segments) / MR of them.
+    const int64_t pairs = (rows_bound + (int64_t)(sh.mr - 1) * segs + sh.mr - 1) / sh.mr;
+    sh.pairs = (int)(pairs > 0 ? (pairs < INT_LIMIT ? pairs : INT_LIMIT) : 1);
+    sh.grid_y = sh.pairs < 65535 ? sh.pairs : 65535;
     sh.cus = cus;
     return sh;
 }

@@ -74,6 +74,7 @@ struct RowsShape {
     int unit, lpr, xc, mr;
     bool multipass;
     int grid_x, grid_y;  // grid_x: row chunks wanted per segment (capped at launch)
+    int pairs;           // upper bound on (segment, row batch) pairs; grid_y = min(pairs, 65535)
     int cus;
 };
 
@@ -126,9 +127,10 @@ struct BatchArgs {
 // compiled shapes are (units per lane, rows per slot).
 #define QMM_BATCHED_SHAPES(X) X(1, 1) X(1, 2) X(2, 1)
 
+// Multi-row kernel: at most two activation units per lane in flight (MR*XC
+// <= 2); beyond that the unit state no longer stays in registers.
 #define QMM_ROWS_SHAPES(X) \
-    X(16, 1, 4) X(32, 1, 4) X(64, 1, 4) \
-    X(16, 1, 2) X(32, 1, 2) X(64, 1, 2) X(64, 2, 2) X(32, 2, 2) X(16, 2, 2) \
+    X(16, 1, 2) X(32, 1, 2) X(64, 1, 2) \
     X(16, 1, 1) X(32, 1, 1) X(64, 1, 1) X(64, 2, 1) X(32, 2, 1) X(16, 2, 1)
 
 constexpr bool gemv_shape_supported(int lpr, int xc, int u) {

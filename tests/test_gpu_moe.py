@@ -95,3 +95,19 @@ def test_moe_rows_equal_per_expert_gemv():
         yg = tensors.gemv(dq, tensors.device_tensor(x[r["pair_token"][pi]]))
         torch.cuda.synchronize()
         assert_within(yg.cpu().numpy(), y_ref[pi], a_ref[pi], "gemv expert %d" % ex)
+
+
+def test_moe_more_row_batches_than_grid_rows():
+    # 140000 (token, expert) pairs over three experts: more row batches than
+    # one launch grid has work-group rows, so each row of work-groups takes
+    # several batches in turn.
+    e, n, k = 3, 16, 64
+    st = inputs.stacked_experts(e, n, k, 4, 64, key=(72,))
+    counts = [60000, 0, 80000]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    p = int(offsets[-1])
+    x = inputs.activation_rows(p, k, key=(72,))
+    announce("moe-many-pairs", p)
+    y = _run_moe(st, x, None, offsets, p)
+    y_ref, a_ref = oracle.moe(st["w"], st["scales"], st["mins"], x, None, offsets, e, n, k, 4, 64)
+    assert_within(y, y_ref, a_ref, "moe many pairs")
