@@ -41,7 +41,10 @@
 
 namespace qmm {
 
-constexpr int BK = GEMM_BK;     // K per step (128)
+constexpr int BK = GEMM_BK;     // K per step
+constexpr int HK = BK / 2;      // K per wave and step (one half of the step)
+constexpr int CH = HK / 64;     // 64-code chunks per wave and step (a lane holds half of each)
+static_assert(HK % 64 == 0, "each wave takes whole 64-code chunks");
 constexpr int BN = 128;         // columns per work-group
 constexpr int XPAD = 8;         // halves of padding per LDS row (conflict-free 16-byte reads)
 constexpr int XROW = BK + XPAD; // halves per LDS row
@@ -228,8 +231,8 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
     static_assert(XD == 1 || XD == 2, "X runs one or two steps ahead");
     static_assert(WR % XD == 0, "the X ring must divide the W ring");
     u32 xq[XD][XU][XW];
-    u32 wq[WR][NS][B];
-    u32 sq[WR][NS], mq[WR][NS];
+    u32 wq[WR][CH][NS][B];
+    u32 sq[WR][CH][NS], mq[WR][CH][NS];
 
     // Loads are unconditional: a step past this split's range, like a row
     // or column past the matrix, reads zeros through the buffer range check.
@@ -248,17 +251,20 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
             }
         }
     };
-    auto load_w = [&](int st, u32 (&w)[NS][B], u32 (&sv)[NS], u32 (&mv)[NS]) {
-        const int kc = st * BK + 64 * wk + 32 * kh;
-        const bool live = st < st1 && kc < K;
+    auto load_w = [&](int st, u32 (&w)[CH][NS][B], u32 (&sv)[CH][NS], u32 (&mv)[CH][NS]) {
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-            const bool ok = n_ok[ns] && live;
-            const uint32_t wo = ok ? w_row[ns] + (uint32_t)(kc / 32) * B * 4 : w_bytes;
-            buffer_words<B, unit_align(B, 32)>(wr, wo, w[ns]);
-            const uint32_t so = ok ? s_row[ns] + group_of((uint32_t)kc) * 2 : sm_bytes;
-            sv[ns] = buffer_u16(sr, so);
-            mv[ns] = buffer_u16(mr, so);
+        for (int c = 0; c < CH; ++c) {
+            const int kc = st * BK + HK * wk + 64 * c + 32 * kh;
+            const bool live = st < st1 && kc < K;
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) {
+                const bool ok = n_ok[ns] && live;
+                const uint32_t wo = ok ? w_row[ns] + (uint32_t)(kc / 32) * B * 4 : w_bytes;
+                buffer_words<B, unit_align(B, 32)>(wr, wo, w[c][ns]);
+                const uint32_t so = ok ? s_row[ns] + group_of((uint32_t)kc) * 2 : sm_bytes;
+                sv[c][ns] = buffer_u16(sr, so);
+                mv[c][ns] = buffer_u16(mr, so);
+            }
         }
     };
     auto stage_x = [&](const u32 (&src)[XU][XW], int buf) {
@@ -304,23 +310,26 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
         // sinks them towards their first use and the step then waits for
         // their full latency.
         __builtin_amdgcn_sched_barrier(0);
-        f16x2 wv[NS][16];
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) dequant_pairs<B>(wq[U][ns], sq[U][ns], mq[U][ns], wv[ns]);
-        const f16* xa = xs + BUF * XBUF + col * XROW + 64 * wk + 32 * kh;
+        for (int c = 0; c < CH; ++c) {
+            f16x2 wv[NS][16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f16x8 a[MS];
+            for (int ns = 0; ns < NS; ++ns) dequant_pairs<B>(wq[U][c][ns], sq[U][c][ns], mq[U][c][ns], wv[ns]);
+            const f16* xa = xs + BUF * XBUF + col * XROW + HK * wk + 64 * c + 32 * kh;
 #pragma unroll
-            for (int i = 0; i < MS; ++i) a[i] = *reinterpret_cast<const f16x8*>(xa + 32 * i * XROW + 8 * j);
+            for (int j = 0; j < 4; ++j) {
+                f16x8 a[MS];
 #pragma unroll
-            for (int ns = 0; ns < NS; ++ns) {
-                const u32x4 bw = {as_u32(wv[ns][4 * j]), as_u32(wv[ns][4 * j + 1]),
-                                  as_u32(wv[ns][4 * j + 2]), as_u32(wv[ns][4 * j + 3])};
-                const f16x8 b = __builtin_bit_cast(f16x8, bw);
+                for (int i = 0; i < MS; ++i) a[i] = *reinterpret_cast<const f16x8*>(xa + 32 * i * XROW + 8 * j);
 #pragma unroll
-                for (int i = 0; i < MS; ++i)
-                    acc[i][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b, acc[i][ns], 0, 0, 0);
+                for (int ns = 0; ns < NS; ++ns) {
+                    const u32x4 bw = {as_u32(wv[ns][4 * j]), as_u32(wv[ns][4 * j + 1]),
+                                      as_u32(wv[ns][4 * j + 2]), as_u32(wv[ns][4 * j + 3])};
+                    const f16x8 b = __builtin_bit_cast(f16x8, bw);
+#pragma unroll
+                    for (int i = 0; i < MS; ++i)
+                        acc[i][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b, acc[i][ns], 0, 0, 0);
+                }
             }
         }
         stage_x(xq[(U + 1) % XD], BUF ^ 1);

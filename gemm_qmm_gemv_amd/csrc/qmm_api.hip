@@ -221,6 +221,8 @@ bool plan_batched(int64_t total_rows, int64_t kmax, int bits, int group, GemvSha
     return true;
 }
 
+constexpr int BATCHED_WAVES_PER_CU = 8;
+
 // Row batches of one descriptor in a batched launch planned as sh.
 int64_t batched_items(const GemvShape& sh, int64_t n, int64_t k) {
     const int lpr = batched_lanes_per_row_host((int)(k / sh.unit), sh.xc);
@@ -473,7 +475,9 @@ qmm_status qmm_gemv_batched(const qmm_gemv_desc* descs_device, const qmm_gemv_de
     if ((st = device_cus(&cus)) != QMM_OK) return st;
     sh.work = first;
     sh.cus = cus;
-    sh.waves_per_cu = env_int("QMM_GEMV_WAVES_PER_CU", 0);
+    // Two 4-wave work-groups per CU: measured on the decode projection set,
+    // fewer concurrent streams than full occupancy read HBM faster.
+    sh.waves_per_cu = env_int("QMM_GEMV_WAVES_PER_CU", BATCHED_WAVES_PER_CU);
     BatchArgs a{reinterpret_cast<const BatchDesc*>(descs_device), (int)count, first, group_size, bits};
     return launched(launch_batched(a, sh, as_stream(stream)), "qmm_gemv_batched");
 }
@@ -524,7 +528,7 @@ qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits, int g
         plan->units_per_lane = sh.xc;
         plan->rows_per_iter = sh.u;
         plan->unit_codes = sh.unit;
-        plan->grid = persistent_grid(batched_items(sh, n, k), cus, 4, 0);
+        plan->grid = persistent_grid(batched_items(sh, n, k), cus, 4, BATCHED_WAVES_PER_CU);
         return ok();
     }
     if (op == 2 || (op == 1 && m <= ROWS_KERNEL_MAX_M)) {

@@ -178,7 +178,10 @@ QMM_DECLARE_BITS(8)
 #undef QMM_DECLARE_BITS
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmShape& sh, hipStream_t st);
-constexpr int GEMM_BK = 128;  // K per main-loop step
+#ifndef GEMM_BK_STEP
+#define GEMM_BK_STEP 128
+#endif
+constexpr int GEMM_BK = GEMM_BK_STEP;  // K per main-loop step
 // Threads per GEMM work-group: 128 per wave column along N (two waves along
 // K); tiles of 64 and 128 rows use GEMM_WN columns, 32-row tiles two.
 #ifndef GEMM_WN
