@@ -355,21 +355,29 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
     }
     __syncthreads();
     {
+        // Store: lane holds column (lane % 32) of each 32x32 fragment, rows
+        // 8*(v/4) + 4*(lane/32) + v%4.  Buffer stores, unconditional: an
+        // element outside the matrix gets an offset past its end and is
+        // dropped, so the epilogue has no branches (a branch per element
+        // would wait for each LDS read in turn).
         const float* src = red + ((wn * 2 + (1 - wk)) * GIVE) * 16 * 64 + lane;
         float* out = (split == 1) ? Y : P + (size_t)sk * M * N;
+        const uint32_t out_bytes = (uint32_t)M * (uint32_t)N * 4u;
+        const rsrc_t orr = make_rsrc(out, out_bytes);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
             if (!keeps(f)) continue;
             const int slot = NF > 1 ? f / 2 : 0;
             const int i = f / NS, ns = f % NS;
-            // Store: lane holds column (lane % 32) of each 32x32 fragment,
-            // rows 8*(v/4) + 4*(lane/32) + v%4.
             const int c = n0 + 32 * NS * wn + 32 * ns + col;
+            float part[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) part[v] = src[(slot * 16 + v) * 64];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float sum = acc[i][ns][v] + src[(slot * 16 + v) * 64];
                 const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * kh + (v & 3);
-                if (row < M && c < N) out[(size_t)row * N + c] = sum;
+                const uint32_t off = (row < M && c < N) ? ((uint32_t)row * (uint32_t)N + (uint32_t)c) * 4u : out_bytes;
+                buffer_store_f32(acc[i][ns][v] + part[v], orr, off);
             }
         }
     }
