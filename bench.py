@@ -134,8 +134,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the work would shard by output rows with no exchange; see DESIGN.md). "
+        print("bench.py measures one GPU only: there is no multi-GPU path here "
+              "(the projections would shard by output rows, with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
