@@ -511,12 +511,19 @@ __device__ __forceinline__ int batched_lanes_per_row(int nu) {
     return lpr;
 }
 
+// Output staging.  Stores and loads share one in-order completion counter on
+// this architecture, so a store issued inside the pipelined loop makes the
+// next wait for a load also wait for that store's write to complete.  The
+// row sums are therefore parked in LDS (a per-wave area of YSTAGE floats) and
+// written out with coalesced stores once per run, or when the area is full.
+constexpr int YSTAGE = 256;
+
 // Row batches [b0, b1) of one matrix (all arguments wave-uniform), with the
-// scale layout fixed at compile time.
+// scale layout fixed at compile time.  ystage: this wave's LDS area.
 template <int B, int UNIT, int LPR, int XC, int U, bool WIDE>
 __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, const uint16_t* Mn,
                                            const uint16_t* X, float* Y, int n, int k, int group,
-                                           int b0, int b1, int lane) {
+                                           int b0, int b1, int lane, float* ystage) {
     constexpr int SLOTS = 64 / LPR;
     constexpr int ROWS = SLOTS * U;
     const int slot = lane / LPR, j = lane % LPR;
@@ -542,43 +549,79 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
 #pragma unroll
     for (int c = 0; c < XC; ++c)
         prep_xunit<B, UNIT>(xr, unit[c] < nu ? (uint32_t)(unit[c] * UNIT * 2) : (uint32_t)k * 2u, xu[c]);
+    // The batch range is wave-uniform; saying so keeps the loop a scalar loop
+    // (no per-lane exit masks).
+    b0 = uniform(b0);
+    b1 = uniform(b1);
+    constexpr int CAP = YSTAGE / ROWS;  // batches the staging area holds
+    static_assert(CAP >= 2, "staging area too small");
+    int bf = b0;                        // first batch held in the staging area (uniform)
+    // Write batches [bf, be) out: lane l stores staged value l (+64 ...);
+    // rows past n get an offset past the end of y and are dropped.
+    auto flush = [&](int be) {
+        const int cnt = (be - bf) * ROWS;
+        for (int i0 = 0; i0 < cnt; i0 += 64) {
+            const int i = i0 + lane;
+            const int row = bf * ROWS + i;
+            const float v = ystage[i < YSTAGE ? i : 0];
+            buffer_store_f32(v, yr, (i < cnt && row < n) ? (uint32_t)row * 4u : (uint32_t)n * 4u);
+        }
+        bf = be;
+    };
+    // Every lane of a slot holds its row's sum, so all of them write it (the
+    // same value to the same word): no branch.
     auto finish = [&](const RowBatch<B, UNIT, XC, U>& bt, int b) {
         float yacc[U];
 #pragma unroll
         for (int r = 0; r < U; ++r) yacc[r] = 0.f;
         accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(bt, xu, yacc, slot, gpr, gidx);
-        store_batch<LPR, U>(yacc, yr, b * ROWS, n, slot, j);
+#pragma unroll
+        for (int r = 0; r < U; ++r) ystage[(b - bf) * ROWS + r * SLOTS + slot] = group_sum<LPR>(yacc[r]);
     };
-    // The batch range is wave-uniform; saying so keeps the loop a scalar loop
-    // (no per-lane exit masks).
-    b0 = uniform(b0);
-    b1 = uniform(b1);
-    for (int b = b0; b < b1; b += 2) {
-        load_batch<B, UNIT, LPR, XC, U, WIDE>(bb, mr, (b + 1) * ROWS, b + 1 < b1, wpr, gpr, slot, unit, gidx, nu, lane);
-        finish(ba, b);
-        if (b + 1 >= b1) break;
-        load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, (b + 2) * ROWS, b + 2 < b1, wpr, gpr, slot, unit, gidx, nu, lane);
-        finish(bb, b + 1);
+    // The run goes in chunks of CAP batches: a pipelined loop without any
+    // store, then one flush.  (A store inside the loop, even a conditional
+    // one, makes the compiler drain the memory queue at the top of every
+    // iteration.)  The scheduling barriers keep each batch's loads ahead of
+    // the previous batch's arithmetic; left alone, the scheduler moves them
+    // below it and only one batch is ever in flight.
+    for (int c0 = b0; c0 < b1; c0 += CAP) {
+        const int c1 = c0 + CAP < b1 ? c0 + CAP : b1;
+        // The chunk's first batch is in ba: loaded before the activation
+        // set-up for the first chunk, after the previous flush otherwise.
+        for (int b = c0; b < c1; b += 2) {
+            load_batch<B, UNIT, LPR, XC, U, WIDE>(bb, mr, (b + 1) * ROWS, b + 1 < c1, wpr, gpr, slot, unit, gidx, nu, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(ba, b);
+            if (b + 1 >= c1) break;
+            load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, (b + 2) * ROWS, b + 2 < c1, wpr, gpr, slot, unit, gidx, nu, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(bb, b + 1);
+        }
+        flush(c1);
+        // Next chunk's first batch, unconditionally (nothing past the run).
+        load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, c1 * ROWS, c1 < b1, wpr, gpr, slot, unit, gidx, nu, lane);
     }
 }
 
 template <int B, int UNIT, int LPR, int XC, int U>
 __device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const uint16_t* Mn,
                                          const uint16_t* X, float* Y, int n, int k, int group, int b0,
-                                         int b1, int lane) {
+                                         int b1, int lane, float* ystage) {
     if (wide_scales_ok<LPR, U>(S, Mn, k / group))
-        gemv_run_w<B, UNIT, LPR, XC, U, true>(W, S, Mn, X, Y, n, k, group, b0, b1, lane);
+        gemv_run_w<B, UNIT, LPR, XC, U, true>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage);
     else
-        gemv_run_w<B, UNIT, LPR, XC, U, false>(W, S, Mn, X, Y, n, k, group, b0, b1, lane);
+        gemv_run_w<B, UNIT, LPR, XC, U, false>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage);
 }
 
 template <int B, int UNIT, int XC, int U>
 __global__ __launch_bounds__(256) void gemv_batched_kernel(const BatchDesc* __restrict__ D, int count,
                                                            int64_t total, int group) {
+    __shared__ float ystage_all[4][YSTAGE];
     const int lane = threadIdx.x & 63;
     const int waves_per_block = blockDim.x >> 6;
     const int wave = blockIdx.x * waves_per_block + (threadIdx.x >> 6);
     const int nwaves = gridDim.x * waves_per_block;
+    float* ystage = ystage_all[threadIdx.x >> 6];
     const int64_t i0 = total * wave / nwaves;
     const int64_t i1 = total * (wave + 1) / nwaves;
     if (i0 >= i1) return;
@@ -610,11 +653,11 @@ __global__ __launch_bounds__(256) void gemv_batched_kernel(const BatchDesc* __re
             const uint16_t* xp = uniform(bd.x);
             float* yp = uniform(bd.y);
             if (lpr == 16)
-                gemv_run<B, UNIT, 16, XC, U>(w, sp, mp, xp, yp, n, k, group, b0, b1, lane);
+                gemv_run<B, UNIT, 16, XC, U>(w, sp, mp, xp, yp, n, k, group, b0, b1, lane, ystage);
             else if (lpr == 32)
-                gemv_run<B, UNIT, 32, XC, U>(w, sp, mp, xp, yp, n, k, group, b0, b1, lane);
+                gemv_run<B, UNIT, 32, XC, U>(w, sp, mp, xp, yp, n, k, group, b0, b1, lane, ystage);
             else
-                gemv_run<B, UNIT, 64, XC, U>(w, sp, mp, xp, yp, n, k, group, b0, b1, lane);
+                gemv_run<B, UNIT, 64, XC, U>(w, sp, mp, xp, yp, n, k, group, b0, b1, lane, ystage);
             i = first + b1;
         }
         ++d;
