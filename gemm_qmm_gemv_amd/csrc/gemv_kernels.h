@@ -553,7 +553,14 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
     // (no per-lane exit masks).
     b0 = uniform(b0);
     b1 = uniform(b1);
-    constexpr int CAP = YSTAGE / ROWS;  // batches the staging area holds
+    // Batches the staging area takes per flush: even, so that batches go
+    // through the loop in pairs with no early exit (an exit in mid-iteration
+    // joins the loop's back edge with the next batch's loads still pending,
+    // and the compiler then drains the memory queue at the top of every
+    // iteration).  For an odd count the pair's second batch lies past the run:
+    // it reads zeros, and its staging slot (still inside the area) is never
+    // flushed.
+    constexpr int CAP = (YSTAGE / ROWS) & ~1;
     static_assert(CAP >= 2, "staging area too small");
     int bf = b0;                        // first batch held in the staging area (uniform)
     // Write batches [bf, be) out: lane l stores staged value l (+64 ...);
@@ -583,23 +590,19 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
     // one, makes the compiler drain the memory queue at the top of every
     // iteration.)  The scheduling barriers keep each batch's loads ahead of
     // the previous batch's arithmetic; left alone, the scheduler moves them
-    // below it and only one batch is ever in flight.
+    // below it and only one batch is ever in flight.  A loop's last load
+    // fetches the next chunk's first batch, so the flush overlaps it.
     for (int c0 = b0; c0 < b1; c0 += CAP) {
         const int c1 = c0 + CAP < b1 ? c0 + CAP : b1;
-        // The chunk's first batch is in ba: loaded before the activation
-        // set-up for the first chunk, after the previous flush otherwise.
         for (int b = c0; b < c1; b += 2) {
-            load_batch<B, UNIT, LPR, XC, U, WIDE>(bb, mr, (b + 1) * ROWS, b + 1 < c1, wpr, gpr, slot, unit, gidx, nu, lane);
+            load_batch<B, UNIT, LPR, XC, U, WIDE>(bb, mr, (b + 1) * ROWS, b + 1 < b1, wpr, gpr, slot, unit, gidx, nu, lane);
             __builtin_amdgcn_sched_barrier(0);
             finish(ba, b);
-            if (b + 1 >= c1) break;
-            load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, (b + 2) * ROWS, b + 2 < c1, wpr, gpr, slot, unit, gidx, nu, lane);
+            load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, (b + 2) * ROWS, b + 2 < b1, wpr, gpr, slot, unit, gidx, nu, lane);
             __builtin_amdgcn_sched_barrier(0);
             finish(bb, b + 1);
         }
         flush(c1);
-        // Next chunk's first batch, unconditionally (nothing past the run).
-        load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, c1 * ROWS, c1 < b1, wpr, gpr, slot, unit, gidx, nu, lane);
     }
 }
 
