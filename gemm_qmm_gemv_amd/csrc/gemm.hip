@@ -26,8 +26,11 @@
 //   * X (fp16) is the shared operand: the work-group copies its TILE_M x 128
 //     block to LDS once per step (double-buffered, one barrier per step) and
 //     every wave reads 32x16 A fragments from there.
-//   * The next step's X and W loads are issued before the current step's
-//     dequantization and matrix work, so memory, VALU and MFMA overlap.
+//   * Software pipeline: a step's loads are issued PD steps ahead, and while
+//     the matrix core works on step s the same wave dequantizes W and stages
+//     X for step s + 1 (no dependence between the two, so VALU and MFMA
+//     instructions interleave within the wave instead of alternating between
+//     barrier-separated phases).
 //
 // When the tile grid alone would leave compute units idle, K is split across
 // work-groups; partial sums go to a caller-provided workspace and a second
@@ -111,8 +114,15 @@ __device__ __forceinline__ void dequant_pairs(const u32 (&w)[B], u32 s_bits, u32
     }
 }
 
-// Steps U..N-1 of one pass of the unrolled main loop, stopping at the end of
-// the range.
+// Steps U..N-1 of one pass of the unrolled main loop: all of them, or (for
+// the remainder after the loop) only those before st1.
+template <int U, int N, class F>
+__device__ __forceinline__ void all_steps(F& f, int st) {
+    if constexpr (U < N) {
+        f(std::integral_constant<int, U>{}, st + U);
+        all_steps<U + 1, N>(f, st);
+    }
+}
 template <int U, int N, class F>
 __device__ __forceinline__ void unrolled_steps(F& f, int st, int st1) {
     if constexpr (U < N) {
@@ -123,19 +133,21 @@ __device__ __forceinline__ void unrolled_steps(F& f, int st, int st1) {
     }
 }
 
-// Pipeline depths and the occupancy target (work-groups per CU the register
-// allocation must allow).
-#ifndef GEMM_WD
-#define GEMM_WD 1
-#endif
-#ifndef GEMM_XD
-#define GEMM_XD 1
+// Prefetch distance (steps between a step's loads and its matrix work) and
+// the occupancy target (work-groups per CU the register allocation must
+// allow).
+#ifndef GEMM_PD
+#define GEMM_PD 2
 #endif
 #ifndef GEMM_MINB
 #define GEMM_MINB 2
 #endif
-constexpr int WD = GEMM_WD;
-constexpr int XD = GEMM_XD;
+constexpr int PD = GEMM_PD;
+static_assert(PD >= 2 && PD <= 4, "prefetch distance");
+// The main loop is unrolled so that every ring index is a compile-time
+// constant: the raw rings have PD slots, the dequantized W and the LDS
+// buffers two.
+constexpr int UNROLL = PD % 2 ? 2 * PD : PD;
 
 // MS: 32-row fragments per wave along M (TILE_M = 32 * MS); WN: waves along
 // N (each with BN / WN columns, NS = BN / (32 WN) fragments); two waves
@@ -222,17 +234,13 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
         x_row[r] = (uint32_t)(m0 + row) * (uint32_t)K * 2;
     }
 
-    // Register rings: W (codes, scale, min) runs WD steps ahead of the
-    // matrix work; X is loaded XD steps ahead (XD = 2: one step in
-    // registers while the previous one sits in LDS).  The main loop is
-    // unrolled by the W ring length so every ring index is a compile-time
-    // constant.
-    constexpr int WR = WD + 1;
-    static_assert(XD == 1 || XD == 2, "X runs one or two steps ahead");
-    static_assert(WR % XD == 0, "the X ring must divide the W ring");
-    u32 xq[XD][XU][XW];
-    u32 wq[WR][CH][NS][B];
-    u32 sq[WR][CH][NS], mq[WR][CH][NS];
+    // Raw rings: slot r holds the codes, scales and mins of W and the X
+    // block of every step st with (st - st0) % PD == r.  Dequantized W pairs
+    // live in a ring of two (this step's and the next one's).
+    u32 xq[PD][XU][XW];
+    u32 wq[PD][CH][NS][B];
+    u32 sq[PD][CH][NS], mq[PD][CH][NS];
+    f16x2 wv[2][CH][NS][16];
 
     // Loads are unconditional: a step past this split's range, like a row
     // or column past the matrix, reads zeros through the buffer range check.
@@ -278,6 +286,13 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
             for (int h = 0; h < XW / 4; ++h) dst[h] = u32x4{o[4 * h], o[4 * h + 1], o[4 * h + 2], o[4 * h + 3]};
         }
     };
+    auto dequant = [&](const u32 (&w)[CH][NS][B], const u32 (&sv)[CH][NS], const u32 (&mv)[CH][NS],
+                       f16x2 (&out)[CH][NS][16]) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) dequant_pairs<B>(w[c][ns], sv[c][ns], mv[c][ns], out[c][ns]);
+    };
 
     f32x16 acc[MS][NS];
 #pragma unroll
@@ -287,34 +302,39 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][ns][v] = 0.f;
 
-    // Prologue: X for the first XD steps (the first one staged), W for the
-    // first WD steps.
+    // Prologue: raw data for the first PD steps; the first step's X staged
+    // and its W dequantized.
 #pragma unroll
-    for (int d = 0; d < XD; ++d) load_x(st0 + d, xq[d]);
-#pragma unroll
-    for (int d = 0; d < WD; ++d) load_w(st0 + d, wq[d], sq[d], mq[d]);
+    for (int d = 0; d < PD; ++d) {
+        load_x(st0 + d, xq[d]);
+        load_w(st0 + d, wq[d], sq[d], mq[d]);
+    }
     stage_x(xq[0], 0);
+    dequant(wq[0], sq[0], mq[0], wv[0]);
     __syncthreads();
 
-    // One step at ring position U (= (st - st0) mod WR); its X sits in LDS
-    // buffer U % 2 (WR is even).
-    static_assert(WR % 2 == 0, "LDS buffer parity must follow the ring position");
+    // One step at position U = (st - st0) mod UNROLL.  On entry X(st) sits
+    // in LDS buffer U % 2 and W(st) is dequantized in wv[U % 2]; raw slot
+    // U % PD is free (its data went into this step's operands during the
+    // previous step).  The step
+    //   * issues the loads of step st + PD into that slot,
+    //   * runs its matrix work, and -- independent of it, so the two overlap
+    //     within the wave -- dequantizes W(st + 1) and stages X(st + 1) into
+    //     the other LDS buffer,
+    //   * ends with the barrier that publishes X(st + 1) and frees buffer
+    //     U % 2 for step st + 2.
+    static_assert(UNROLL % 2 == 0 && UNROLL % PD == 0, "ring positions must be compile-time");
     auto step = [&](auto u_c, int st) {
         constexpr int U = decltype(u_c)::value;
         constexpr int BUF = U % 2;
-        load_w(st + WD, wq[(U + WD) % WR], sq[(U + WD) % WR], mq[(U + WD) % WR]);
-        // XD = 2: slot U % 2 held X(st), staged a step ago; X(st + 1) waits
-        // in the other slot.  XD = 1: the single slot was staged a step ago.
-        load_x(st + XD, xq[U % XD]);
+        constexpr int SLOT = U % PD, NEXT = (U + 1) % PD;
+        load_w(st + PD, wq[SLOT], sq[SLOT], mq[SLOT]);
+        load_x(st + PD, xq[SLOT]);
         // Keep the loads at the top of the step: left alone, the scheduler
-        // sinks them towards their first use and the step then waits for
-        // their full latency.
+        // sinks them towards their first use.
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            f16x2 wv[NS][16];
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns) dequant_pairs<B>(wq[U][c][ns], sq[U][c][ns], mq[U][c][ns], wv[ns]);
             const f16* xa = xs + BUF * XBUF + col * XROW + HK * wk + 64 * c + 32 * kh;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -323,8 +343,8 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
                 for (int i = 0; i < MS; ++i) a[i] = *reinterpret_cast<const f16x8*>(xa + 32 * i * XROW + 8 * j);
 #pragma unroll
                 for (int ns = 0; ns < NS; ++ns) {
-                    const u32x4 bw = {as_u32(wv[ns][4 * j]), as_u32(wv[ns][4 * j + 1]),
-                                      as_u32(wv[ns][4 * j + 2]), as_u32(wv[ns][4 * j + 3])};
+                    const u32x4 bw = {as_u32(wv[BUF][c][ns][4 * j]), as_u32(wv[BUF][c][ns][4 * j + 1]),
+                                      as_u32(wv[BUF][c][ns][4 * j + 2]), as_u32(wv[BUF][c][ns][4 * j + 3])};
                     const f16x8 b = __builtin_bit_cast(f16x8, bw);
 #pragma unroll
                     for (int i = 0; i < MS; ++i)
@@ -332,10 +352,17 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
                 }
             }
         }
-        stage_x(xq[(U + 1) % XD], BUF ^ 1);
+        dequant(wq[NEXT], sq[NEXT], mq[NEXT], wv[BUF ^ 1]);
+        stage_x(xq[NEXT], BUF ^ 1);
         __syncthreads();
     };
-    for (int st = st0; st < st1; st += WR) unrolled_steps<0, WR>(step, st, st1);
+    // Whole passes in the loop, the remainder after it: an exit from the
+    // middle of a pass would reach the loop's back edge with that step's
+    // loads in flight, and the compiler would then drain the memory queue
+    // at the top of every pass.
+    int st = st0;
+    for (; st + UNROLL <= st1; st += UNROLL) all_steps<0, UNROLL>(step, st);
+    unrolled_steps<0, UNROLL>(step, st, st1);
 
     // Add the two K-halves.  Fragment f = i * NS + ns; wave (wn, wk) keeps
     // the fragments with f % 2 == wk (all of them for wk == 0 when it has

@@ -261,18 +261,32 @@ RowsShape plan_rows(int64_t rows_bound, int64_t n, int64_t k, int bits, int grou
     return sh;
 }
 
+// Tile height and K split.  Measured on the Llama-3.2-1B projections at
+// m = 128 and 512: a work-group per CU (two for short splits) is the target;
+// 64-row tiles win wherever they need no more work-groups than there are CUs
+// (twice the waves per SIMD of the 128-row tile), except for long K with
+// several 128-row tiles, where the 128-row tile's halved W traffic wins; a
+// split shorter than four K steps costs more in partial sums than it gains.
 GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int cus, size_t ws_bytes, size_t* ws_need) {
     GemmShape sh{};
+    const int k_tiles = (int)((k + GEMM_BK - 1) / GEMM_BK);
+    const int64_t grid_n = (n + 127) / 128;
     sh.tile_m = m <= 32 ? 32 : m <= 64 ? 64 : 128;
+    if (sh.tile_m == 128) {
+        const int64_t tiles64 = (m + 63) / 64 * grid_n;
+        const bool long_k = k_tiles >= 64 && m > 128;
+        if (tiles64 <= cus && !long_k) sh.tile_m = 64;
+    }
+    const int et = env_int("QMM_GEMM_TILE_M", 0);
+    if (et == 32 || et == 64 || et == 128) sh.tile_m = et;
     sh.tile_n = 128;
     sh.grid_m = (int)((m + sh.tile_m - 1) / sh.tile_m);
-    sh.grid_n = (int)((n + sh.tile_n - 1) / sh.tile_n);
-    const int k_tiles = (int)((k + GEMM_BK - 1) / GEMM_BK);
+    sh.grid_n = (int)grid_n;
     const int64_t tiles = (int64_t)sh.grid_m * sh.grid_n;
     int split = 1;
     if (tiles < cus) {
         split = (int)((cus + tiles - 1) / tiles);
-        const int by_k = k_tiles / 2 > 1 ? k_tiles / 2 : 1;
+        const int by_k = k_tiles / 4 > 1 ? k_tiles / 4 : 1;
         if (split > by_k) split = by_k;
         if (split > 16) split = 16;
     }

@@ -153,21 +153,53 @@ def test_gemv_plan_small_vs_large(lib):
     assert large["grid"] <= 256 * 32 // 4   # persistent-sized grid
 
 
+def _expected_tile(m, n, k, cus=256):
+    # 64-row tiles unless they would need more work-groups than CUs, or K is
+    # long (64 steps of 128 or more) with more than one 128-row tile.
+    if m <= 32:
+        return 32
+    if m <= 64:
+        return 64
+    tiles64 = -(-m // 64) * -(-n // 128)
+    long_k = -(-k // 128) >= 64 and m > 128
+    return 64 if tiles64 <= cus and not long_k else 128
+
+
 @pytest.mark.parametrize("m", (3, 64, 128, 512, 1000))
 @pytest.mark.parametrize("n,k", [(512, 2048), (2048, 2048), (8192, 2048), (2048, 8192)])
 def test_gemm_plan(lib, m, n, k):
     unlimited = 1 << 40
     pl = qmm.qmm_get_plan(1, m, n, k, 4, 64, cu_count=256, workspace_bytes=unlimited)
     assert pl["variant"] == 2
-    assert pl["tile_m"] == (32 if m <= 32 else 64 if m <= 64 else 128) and pl["tile_n"] == 128
+    assert pl["tile_m"] == _expected_tile(m, n, k) and pl["tile_n"] == 128
     assert pl["block"] == (256 if pl["tile_m"] == 32 else 512)
     tiles = -(-m // pl["tile_m"]) * -(-n // 128)
     assert pl["grid"] >= tiles * pl["split_k"]
     assert 1 <= pl["split_k"] <= 16
+    # Every split keeps at least four K steps of 128.
+    assert pl["split_k"] == 1 or -(-k // 128) // pl["split_k"] >= 4
     if tiles >= 256:
         assert pl["split_k"] == 1
     none = qmm.qmm_get_plan(1, m, n, k, 4, 64, cu_count=256, workspace_bytes=0)
     assert none["split_k"] == 1
+
+
+def test_gemm_plan_on_the_prefill_shapes(lib):
+    # The measured choices: (m, n, k) -> (tile_m, split_k).
+    want = {(128, 2048, 2048): (64, 4), (128, 512, 2048): (64, 4), (128, 8192, 2048): (64, 2),
+            (128, 2048, 8192): (64, 8), (512, 2048, 2048): (64, 2), (512, 512, 2048): (64, 4),
+            (512, 8192, 2048): (128, 1), (512, 2048, 8192): (128, 4)}
+    for (m, n, k), (tile, split) in want.items():
+        pl = qmm.qmm_get_plan(1, m, n, k, 4, 64, cu_count=256, workspace_bytes=1 << 40)
+        assert (pl["tile_m"], pl["split_k"]) == (tile, split), (m, n, k)
+
+
+def test_gemm_tile_override(lib, monkeypatch):
+    monkeypatch.setenv("QMM_GEMM_TILE_M", "128")
+    assert qmm.qmm_get_plan(1, 100, 512, 1024, 4, 64, cu_count=256)["tile_m"] == 128
+    monkeypatch.setenv("QMM_GEMM_TILE_M", "32")
+    pl = qmm.qmm_get_plan(1, 100, 512, 1024, 4, 64, cu_count=256)
+    assert pl["tile_m"] == 32 and pl["block"] == 256
 
 
 def test_small_m_routes(lib):

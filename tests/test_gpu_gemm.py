@@ -38,6 +38,20 @@ def test_gemm_parity(bits, m, n, k, group):
     assert_within(y, y_ref, a_ref, "gemm b%d m%d %dx%d g%d" % (bits, m, n, k, group))
 
 
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("tile", (32, 64, 128))
+@pytest.mark.parametrize("m,n,k", [(100, 300, 1024), (130, 257, 320), (257, 384, 2048)])
+def test_gemm_parity_every_tile(monkeypatch, bits, tile, m, n, k):
+    # Each tile height on shapes the planner would give another one.
+    monkeypatch.setenv("QMM_GEMM_TILE_M", str(tile))
+    q = inputs.quantized_matrix(n, k, bits, 64, key=(62, m, n, k, bits))
+    x = inputs.activation_rows(m, k, key=(62, m, n, k, bits))
+    announce("gemm-tile", tile, bits, m, n, k)
+    y = _run_gemm(q, x)
+    y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, 64)
+    assert_within(y, y_ref, a_ref, "gemm tile%d b%d m%d %dx%d" % (tile, bits, m, n, k))
+
+
 @pytest.mark.parametrize("bits", (4, 8))
 def test_gemm_without_workspace_matches_split(bits):
     # Same product with and without a K split: both within tolerance, and the
