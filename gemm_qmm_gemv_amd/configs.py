@@ -35,7 +35,8 @@ LLAMA32_3B_PROJ = [
     ("down_proj", 3072, 8192),
     ("lm_head", 128256, 3072),
 ]
-SWEEP_BITS = (2, 3, 4, 6, 8)
+# Q5 is not among the pages' measured widths; it is swept beside them.
+SWEEP_BITS = (2, 3, 4, 5, 6, 8)
 
 # Llama-3.2-1B-shaped prefill GEMMs, Q4, M tokens.
 LLAMA32_1B_PROJ = [

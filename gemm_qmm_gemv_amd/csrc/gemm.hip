@@ -74,7 +74,7 @@ constexpr bool slot_blocks_ok() {
     return true;
 }
 static_assert(slot_blocks_ok<2>() && slot_blocks_ok<3>() && slot_blocks_ok<4>() &&
-                  slot_blocks_ok<6>() && slot_blocks_ok<8>(),
+                  slot_blocks_ok<5>() && slot_blocks_ok<6>() && slot_blocks_ok<8>(),
               "slot order must stay within aligned blocks of x_unit_halves codes");
 
 // XH halves of X in natural k order -> slot order, one byte permute per
@@ -466,6 +466,7 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmShape& sh, hipStream_t st) {
         case 2: return launch_gemm_b<2>(a, sh, st);
         case 3: return launch_gemm_b<3>(a, sh, st);
         case 4: return launch_gemm_b<4>(a, sh, st);
+        case 5: return launch_gemm_b<5>(a, sh, st);
         case 6: return launch_gemm_b<6>(a, sh, st);
         case 8: return launch_gemm_b<8>(a, sh, st);
         default: return hipErrorInvalidValue;

@@ -1,5 +1,5 @@
 // gemv_bits.hip -- instantiates the GEMV-family launchers for one bit width.
-// Built once per supported width with -DQMM_BITS=<b> (2, 3, 4, 6, 8) so the
+// Built once per supported width with -DQMM_BITS=<b> (2, 3, 4, 5, 6, 8) so the
 // template-heavy kernels compile in parallel.
 #include "gemv_kernels.h"
 

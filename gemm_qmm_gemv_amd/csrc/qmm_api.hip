@@ -27,6 +27,7 @@ namespace {
         case 2: return FN<2>(__VA_ARGS__);                \
         case 3: return FN<3>(__VA_ARGS__);                \
         case 4: return FN<4>(__VA_ARGS__);                \
+        case 5: return FN<5>(__VA_ARGS__);                \
         case 6: return FN<6>(__VA_ARGS__);                \
         case 8: return FN<8>(__VA_ARGS__);                \
         default: return hipErrorInvalidValue;             \
@@ -58,7 +59,7 @@ qmm_status ok() {
 }
 
 bool bits_supported(int bits) {
-    return bits == 2 || bits == 3 || bits == 4 || bits == 6 || bits == 8;
+    return bits == 2 || bits == 3 || bits == 4 || bits == 5 || bits == 6 || bits == 8;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -69,7 +70,7 @@ constexpr int64_t OFFSET_LIMIT = 0xffffffffLL;  // largest byte size a 32-bit of
 qmm_status check_format(int64_t n, int64_t k, int bits, int group) {
     if (bits < 2 || bits > 8) return fail(QMM_ERR_INVALID_ARGUMENT, "bits=%d outside 2..8", bits);
     if (!bits_supported(bits))
-        return fail(QMM_ERR_UNSUPPORTED, "bits=%d not built (supported: 2, 3, 4, 6, 8)", bits);
+        return fail(QMM_ERR_UNSUPPORTED, "bits=%d not built (supported: 2, 3, 4, 5, 6, 8)", bits);
     if (group <= 0 || group % 32)
         return fail(QMM_ERR_INVALID_ARGUMENT, "group_size=%d must be a positive multiple of 32", group);
     if (k < 32 || k % group)

@@ -196,6 +196,34 @@ template <> struct PairFmt<4> {
     }
 };
 
+// 20-bit field t (codes at bits 0..19) -> low 10 bits kept, bits 10..19
+// moved to 16..25; bits 10..15 and 26..31 of the result are don't-care.
+__device__ __forceinline__ u32 spread10(u32 t) {
+    return (t & 0x3FFu) | ((t << 6) & 0x03FF0000u);
+}
+
+// Q5: 5 words = 160 bits = eight 20-bit pieces of 4 codes.  Spread puts
+// codes 0,1 at bits 0,5 and codes 2,3 at 16,21: mask 0x001F001F gives
+// (c0,c2) x1 and mask 0x03E003E0 gives (c1,c3) x32 (32 * 31 < 1024, exact).
+template <> struct PairFmt<5> {
+    static constexpr int NACC = 2;
+    static constexpr int ka(int i) { return 4 * (i / 2) + (i % 2); }
+    static constexpr int kb(int i) { return ka(i) + 2; }
+    static constexpr int acc(int i) { return i % 2; }
+    static constexpr float inv_factor(int a) { return a == 0 ? 1.f : 0.03125f; }
+    __device__ static __forceinline__ void extract(const u32* w, u32* p) {
+        // Piece q starts at stream bit 20q.
+        const u32 t[8] = {w[0], funnel(w[1], w[0], 20), w[1] >> 8, funnel(w[2], w[1], 28),
+                          funnel(w[3], w[2], 16), w[3] >> 4, funnel(w[4], w[3], 24), w[4] >> 12};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const u32 u = spread10(t[q]);
+            p[2 * q + 0] = mask_or_magic(u, 0x001F001Fu);
+            p[2 * q + 1] = mask_or_magic(u, 0x03E003E0u);
+        }
+    }
+};
+
 // Q6: 6 words = 192 bits = eight 24-bit pieces of 4 codes.  Spread puts
 // codes 0,1 at bits 0,6 and codes 2,3 at 16,22: mask 0x003F003F gives (c0,c2),
 // the same mask after >> 6 gives (c1,c3).

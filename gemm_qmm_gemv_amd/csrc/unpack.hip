@@ -50,7 +50,7 @@ hipError_t launch_unpack(const uint32_t* w, uint8_t* codes, int64_t n, int64_t k
         hipLaunchKernelGGL(unpack_kernel<B>, dim3((unsigned)grid), dim3(256), 0, st, w, codes, \
                            chunks, cpr);                                                        \
         break;
-        CASE(2) CASE(3) CASE(4) CASE(6) CASE(8)
+        CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(8)
 #undef CASE
         default: return hipErrorInvalidValue;
     }

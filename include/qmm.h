@@ -17,7 +17,7 @@
  *
  * Format (the pages fix none of these details; this is the library's format):
  *   W is N x K (output rows x reduction).  Codes are unsigned b-bit integers,
- *   b in {2, 3, 4, 6, 8}.  Row n is a little-endian bitstream of K*b bits held
+ *   b in {2, 3, 4, 5, 6, 8}.  Row n is a little-endian bitstream of K*b bits held
  *   in K*b/32 uint32 words: code k occupies stream bits [k*b, k*b + b), and
  *   stream bit i is bit (i mod 32) of word floor(i / 32) of the row.  Rows are
  *   contiguous (row n starts at word n*K*b/32).
@@ -28,7 +28,8 @@
  *   row-major:  y[i][n] = sum_k w[n][k] * x[i][k].
  *
  * Requirements checked on the host before anything is launched:
- *   bits in {2, 3, 4, 6, 8}; group_size a positive multiple of 32;
+ *   bits in {2, 3, 4, 5, 6, 8} (7 is QMM_ERR_UNSUPPORTED); group_size a
+ *   positive multiple of 32;
  *   k >= 32 and k a multiple of group_size; n >= 0, m >= 0 (0 is a no-op);
  *   weight, activation and output pointers 16-byte aligned; scale and min
  *   pointers 2-byte aligned; non-NULL pointers wherever work is to be done.

@@ -165,7 +165,7 @@ def check_qmm_library_matmul():
 
 def check_constant_codes_closed_form():
     # q == c everywhere: y[n] = sum_g (c * s[n,g] + m[n,g]) * sum_{k in g} x[k].
-    for bits in (2, 3, 4, 6, 8):
+    for bits in (2, 3, 4, 5, 6, 8):
         n, k, group = 11, 320, 64
         rng = inputs.rng_for(9, bits)
         s, mn = inputs.scales_mins(rng, n, k, group)
@@ -181,7 +181,7 @@ def check_constant_codes_closed_form():
 
 def check_one_hot():
     # x = e_j: y[n] = s[n, j/g] * q[n, j] + m[n, j/g], exactly.
-    for bits in (2, 3, 4, 6, 8):
+    for bits in (2, 3, 4, 5, 6, 8):
         n, k, group = 13, 192, 64
         q, _ = _rand_problem(n, k, bits, group, 1, 3)
         codes = np_unpack(q["w"], n, k, bits)
@@ -197,7 +197,7 @@ def check_one_hot():
 
 def check_exact_integer():
     # scale 1, min 0, integer x in [-2, 2]: y is an exact integer sum.
-    for bits in (2, 3, 4, 6, 8):
+    for bits in (2, 3, 4, 5, 6, 8):
         n, k, m, group = 9, 512, 3, 64
         rng = inputs.rng_for(10, bits)
         w = inputs.packed_words(rng, n, k, bits)

@@ -62,7 +62,6 @@ def _gemv(lib, w=A16, s=A16, m=A16, x=A16, y=A16, n=64, k=128, bits=4, g=64):
 
 
 @pytest.mark.parametrize("kwargs,status", [
-    (dict(bits=5), qmm.QMM_ERR_UNSUPPORTED),
     (dict(bits=7), qmm.QMM_ERR_UNSUPPORTED),
     (dict(bits=1), qmm.QMM_ERR_INVALID_ARGUMENT),
     (dict(bits=9), qmm.QMM_ERR_INVALID_ARGUMENT),
@@ -113,7 +112,7 @@ def test_gemm_and_moe_argument_checks(lib):
     assert mo(p(A16), p(A16), p(A16), p(A16), None, 8, p(A16), p(A16), 0, 2, 64, 128, 4, 64, None) == \
         qmm.QMM_OK
     assert lib.qmm_unpack(p(A16), p(A16 + 8), 4, 64, 4, None) == qmm.QMM_ERR_MISALIGNED
-    assert lib.qmm_unpack(p(A16), p(A16), 4, 64, 5, None) == qmm.QMM_ERR_UNSUPPORTED
+    assert lib.qmm_unpack(p(A16), p(A16), 4, 64, 7, None) == qmm.QMM_ERR_UNSUPPORTED
 
 
 # ---- launch planning (host integer logic) -----------------------------------------
@@ -124,7 +123,7 @@ ALL_DECODE_SHAPES = sorted({(n, k) for _, n, k in configs.QWEN3_06B_PROJ + [conf
                            | {(n, k) for _, n, k in configs.MOE_PROJ})
 
 
-@pytest.mark.parametrize("bits", (2, 3, 4, 6, 8))
+@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6, 8))
 @pytest.mark.parametrize("n,k", ALL_DECODE_SHAPES + [(5, 16384), (7, 96), (1, 64)])
 @pytest.mark.parametrize("group", (64, 32, 128))
 def test_gemv_plan_covers_the_row(lib, bits, n, k, group):

@@ -26,7 +26,7 @@ def _run_batch(shapes, bits, group, seed):
     return qs, [it[2].cpu().numpy() for it in items]
 
 
-@pytest.mark.parametrize("bits", (2, 3, 4, 6, 8))
+@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6, 8))
 def test_batched_mixed_shapes(bits):
     shapes = [(2048, 1024), (0, 1024), (1, 64), (1000, 1024), (37, 1024), (513, 512), (3, 1024)]
     announce("batched-mixed", bits)
@@ -39,7 +39,7 @@ def test_batched_mixed_shapes(bits):
         assert_within(y[:n], y_ref, a_ref, "batched b%d %dx%d" % (bits, n, k))
 
 
-@pytest.mark.parametrize("bits", (2, 3, 4, 6, 8))
+@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6, 8))
 def test_batched_mixed_k_one_launch(bits):
     # Different K per descriptor in one launch: each gets its own lane layout
     # (16, 32 or 64 lanes per row; two units per lane for K = 8192).

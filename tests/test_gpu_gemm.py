@@ -8,7 +8,7 @@ from tests.gpu_util import announce, assert_within
 
 pytestmark = pytest.mark.gpu
 
-BITS = (2, 3, 4, 6, 8)
+BITS = (2, 3, 4, 5, 6, 8)
 
 
 def _run_gemm(q, x, workspace="auto"):
