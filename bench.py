@@ -17,8 +17,11 @@ Also measured (outside the timed region, reported in the same JSON line):
     then the LM head) replayed from a HIP graph: per-token projection time;
   * the LM head alone with four rotating copies (steady state);
   * the single 3072 x 1024 Q4 GEMV;
-  * the Llama-3.2-3B-shaped bit-width sweep (Q2/Q3/Q4/Q6/Q8);
-  * Llama-3.2-1B-shaped prefill GEMMs at M = 128 and 512: TFLOP/s, % MFMA;
+  * the Llama-3.2-3B-shaped bit-width sweep (Q2/Q3/Q4/Q5/Q6/Q8 and fp16
+    weights);
+  * Llama-3.2-1B-shaped prefill GEMMs at M = 128 and 512: TFLOP/s, % MFMA,
+    with Q4 weights and again with fp16 weights, the dense fp16 library
+    matmul of each shape beside them;
   * Qwen3-30B-A3B-shaped MoE expert projections at 1 and 16 tokens;
   * the CPU oracle on the host cores over the same projection set.
 
@@ -348,52 +351,11 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
         log("sweep q%d: lm_head %.0f GB/s" % (bits, row["lm_head"]["GBps"]))
     out["llama3.2_3b_bit_sweep"] = sweep
 
-    # Prefill GEMMs (Llama-3.2-1B shapes).
-    pre = {}
-    for m in configs.PREFILL_M:
-        tot_flops, tot_ms, dense_ms = 0.0, 0.0, 0.0
-        row = {}
-        for j, (pname, n, k) in enumerate(configs.LLAMA32_1B_PROJ):
-            q = inputs.quantized_matrix(n, k, 4, G, key=(configs.CFG_PREFILL, 0, j, 4))
-            dq = tensors.upload_matrix(q)
-            xm = tensors.device_tensor(inputs.activation_rows(m, k, key=(configs.CFG_PREFILL, 0, j, 4, m)))
-            ym = torch.empty((m, n), dtype=torch.float32, device="cuda")
-            need = qmm.qmm_gemm_workspace_bytes(m, n, k, 4, G)
-            ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
-            # Device-side copies of the same matrix, rotated so that the
-            # weights come from HBM (total above twice the 256 MB last-level
-            # cache, at most 64 copies).
-            wb = configs.weight_bytes(n, k, 4)
-            ncp = max(4, min(64, -(-512 * 2**20 // wb)))
-            cps = [dq] + [{**dq, "w": dq["w"].clone(), "scales": dq["scales"].clone(),
-                           "mins": dq["mins"].clone()} for _ in range(ncp - 1)]
-            ii = [0]
-
-            def call():
-                tensors.gemm(cps[ii[0] % ncp], xm, ym, workspace=ws)
-                ii[0] += 1
-            ms = timer(call, reps=ncp)
-            fl = 2.0 * m * n * k
-            tf = fl / ms / 1e9
-            pl = qmm.qmm_get_plan(1, m, n, k, 4, G, workspace_bytes=ws.numel())
-            # Context only: dense fp16 matmul of the same shape through the
-            # installed BLAS library (weights already dequantized, 4x the bytes).
-            wd = torch.randn((k, n), dtype=torch.float16, device="cuda")
-            ms_dense = timer(lambda: torch.matmul(xm, wd), reps=20)
-            row[pname] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
-                          "pct_mfma": round(100 * tf / MFMA_FP16_PEAK_TFLOPS, 2),
-                          "split_k": pl["split_k"], "tile_m": pl["tile_m"], "copies": ncp,
-                          "dense_fp16_matmul_us": round(ms_dense * 1e3, 2)}
-            del cps, wd
-            tot_flops += fl
-            tot_ms += ms
-            dense_ms += ms_dense
-        tf = tot_flops / tot_ms / 1e9
-        pre["m%d" % m] = {"layer_us": round(tot_ms * 1e3, 2), "TFLOPs": round(tf, 1),
-                          "pct_mfma": round(100 * tf / MFMA_FP16_PEAK_TFLOPS, 2),
-                          "dense_fp16_matmul_layer_us": round(dense_ms * 1e3, 2), "shapes": row}
-        log("prefill m=%d: %.1f TFLOP/s" % (m, tf))
-    out["prefill_llama3.2_1b_q4"] = pre
+    # Prefill GEMMs (Llama-3.2-1B shapes), Q4, then the same layer with fp16
+    # weights through the same kernel family.
+    for bits in (4, 16):
+        out["prefill_llama3.2_1b_" + ("q4" if bits == 4 else "fp16")] = prefill_layers(
+            torch, qmm, configs, inputs, tensors, timer, bits)
 
     # MoE expert projections (Qwen3-30B-A3B shapes).
     moe = {}
@@ -428,6 +390,59 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
         log("moe T=%d: %.1f us" % (tokens, tot_ms * 1e3))
     out["moe_qwen3_30b_a3b_q4"] = moe
     return out
+
+
+def prefill_layers(torch, qmm, configs, inputs, tensors, timer, bits):
+    """Per-shape and per-layer times of the prefill GEMMs at each M (weights
+    at `bits`: 4, or 16 for fp16), with the dense fp16 library matmul of the
+    same shape timed beside them for context."""
+    G = configs.GROUP
+    pre = {}
+    for m in configs.PREFILL_M:
+        tot_flops, tot_ms, dense_ms = 0.0, 0.0, 0.0
+        row = {}
+        for j, (pname, n, k) in enumerate(configs.LLAMA32_1B_PROJ):
+            q = inputs.quantized_matrix(n, k, bits, G, key=(configs.CFG_PREFILL, 0, j, bits))
+            dq = tensors.upload_matrix(q)
+            xm = tensors.device_tensor(inputs.activation_rows(m, k, key=(configs.CFG_PREFILL, 0, j, 4, m)))
+            ym = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            need = qmm.qmm_gemm_workspace_bytes(m, n, k, bits, G)
+            ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
+            # Device-side copies of the same matrix, rotated so that the
+            # weights come from HBM (total above twice the 256 MB last-level
+            # cache, at most 64 copies).
+            wb = configs.weight_bytes(n, k, bits)
+            ncp = max(4, min(64, -(-512 * 2**20 // wb)))
+            clone = lambda t: None if t is None else t.clone()
+            cps = [dq] + [{**dq, "w": dq["w"].clone(), "scales": clone(dq["scales"]),
+                           "mins": clone(dq["mins"])} for _ in range(ncp - 1)]
+            ii = [0]
+
+            def call():
+                tensors.gemm(cps[ii[0] % ncp], xm, ym, workspace=ws)
+                ii[0] += 1
+            ms = timer(call, reps=ncp)
+            fl = 2.0 * m * n * k
+            tf = fl / ms / 1e9
+            pl = qmm.qmm_get_plan(1, m, n, k, bits, G, workspace_bytes=ws.numel())
+            # Context only: dense fp16 matmul of the same shape through the
+            # installed BLAS library (fp16 weights, fp16 output).
+            wd = torch.randn((k, n), dtype=torch.float16, device="cuda")
+            ms_dense = timer(lambda: torch.matmul(xm, wd), reps=20)
+            row[pname] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
+                          "pct_mfma": round(100 * tf / MFMA_FP16_PEAK_TFLOPS, 2),
+                          "split_k": pl["split_k"], "tile_m": pl["tile_m"], "copies": ncp,
+                          "dense_fp16_matmul_us": round(ms_dense * 1e3, 2)}
+            del cps, wd
+            tot_flops += fl
+            tot_ms += ms
+            dense_ms += ms_dense
+        tf = tot_flops / tot_ms / 1e9
+        pre["m%d" % m] = {"layer_us": round(tot_ms * 1e3, 2), "TFLOPs": round(tf, 1),
+                          "pct_mfma": round(100 * tf / MFMA_FP16_PEAK_TFLOPS, 2),
+                          "dense_fp16_matmul_layer_us": round(dense_ms * 1e3, 2), "shapes": row}
+        log("prefill b%d m=%d: %.1f TFLOP/s" % (bits, m, tf))
+    return pre
 
 
 def cpu_baseline(np, configs, inputs, set_bytes):

@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libqmm.so")
 # (source, extra defines, object name); gemv_bits.hip is built once per width.
 SOURCES = [("qmm_api.hip", [], "qmm_api.o"), ("gemm.hip", [], "gemm.o"),
            ("unpack.hip", [], "unpack.o")] + [
-    ("gemv_bits.hip", ["-DQMM_BITS=%d" % b], "gemv_b%d.o" % b) for b in (2, 3, 4, 5, 6, 8)]
+    ("gemv_bits.hip", ["-DQMM_BITS=%d" % b], "gemv_b%d.o" % b) for b in (2, 3, 4, 5, 6, 8, 16)]
 ARCH = os.environ.get("QMM_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

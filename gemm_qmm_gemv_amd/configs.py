@@ -35,8 +35,9 @@ LLAMA32_3B_PROJ = [
     ("down_proj", 3072, 8192),
     ("lm_head", 128256, 3072),
 ]
-# Q5 is not among the pages' measured widths; it is swept beside them.
-SWEEP_BITS = (2, 3, 4, 5, 6, 8)
+# Q5 and fp16 weights (16) are not among the pages' measured widths; they
+# are swept beside them.
+SWEEP_BITS = (2, 3, 4, 5, 6, 8, 16)
 
 # Llama-3.2-1B-shaped prefill GEMMs, Q4, M tokens.
 LLAMA32_1B_PROJ = [
@@ -75,7 +76,10 @@ def decode_set():
 
 
 def weight_bytes(n: int, k: int, bits: int, group: int = GROUP) -> int:
-    """Compressed bytes of one N x K matrix: codes + fp16 scale + fp16 min."""
+    """Compressed bytes of one N x K matrix: codes + fp16 scale + fp16 min
+    (bits 16: the fp16 weights alone)."""
+    if bits == 16:
+        return 2 * n * k
     return n * k * bits // 8 + 4 * n * (k // group)
 
 

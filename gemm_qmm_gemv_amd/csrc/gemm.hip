@@ -74,7 +74,8 @@ constexpr bool slot_blocks_ok() {
     return true;
 }
 static_assert(slot_blocks_ok<2>() && slot_blocks_ok<3>() && slot_blocks_ok<4>() &&
-                  slot_blocks_ok<5>() && slot_blocks_ok<6>() && slot_blocks_ok<8>(),
+                  slot_blocks_ok<5>() && slot_blocks_ok<6>() && slot_blocks_ok<8>() &&
+                  slot_blocks_ok<16>(),
               "slot order must stay within aligned blocks of x_unit_halves codes");
 
 // XH halves of X in natural k order -> slot order, one byte permute per
@@ -97,6 +98,12 @@ template <int B>
 __device__ __forceinline__ void dequant_pairs(const u32 (&w)[B], u32 s_bits, u32 m_bits,
                                               f16x2 (&out)[16]) {
     using F = PairFmt<B>;
+    if constexpr (!has_affine<B>()) {
+        // fp16 weights: the words are the operand pairs already.
+#pragma unroll
+        for (int i = 0; i < 16; ++i) out[i] = as_h2(w[i]);
+        return;
+    }
     u32 p[16];
     F::extract(w, p);
     const f16 s = __builtin_bit_cast(f16, (uint16_t)s_bits);
@@ -205,7 +212,9 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
     const uint32_t gpr = group_of((uint32_t)K);
 
     const uint32_t w_bytes = (uint32_t)N * wpr * 4;
-    const uint32_t sm_bytes = (uint32_t)N * gpr * 2;
+    // Formats without scales and mins read none (empty resources, null
+    // pointers allowed).
+    const uint32_t sm_bytes = has_affine<B>() ? (uint32_t)N * gpr * 2 : 0u;
     const uint32_t x_bytes = (uint32_t)M * (uint32_t)K * 2;
     const rsrc_t wr = make_rsrc(W, w_bytes);
     const rsrc_t sr = make_rsrc(S, sm_bytes);
@@ -269,9 +278,14 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
                 const bool ok = n_ok[ns] && live;
                 const uint32_t wo = ok ? w_row[ns] + (uint32_t)(kc / 32) * B * 4 : w_bytes;
                 buffer_words<B, unit_align(B, 32)>(wr, wo, w[c][ns]);
-                const uint32_t so = ok ? s_row[ns] + group_of((uint32_t)kc) * 2 : sm_bytes;
-                sv[c][ns] = buffer_u16(sr, so);
-                mv[c][ns] = buffer_u16(mr, so);
+                if constexpr (has_affine<B>()) {
+                    const uint32_t so = ok ? s_row[ns] + group_of((uint32_t)kc) * 2 : sm_bytes;
+                    sv[c][ns] = buffer_u16(sr, so);
+                    mv[c][ns] = buffer_u16(mr, so);
+                } else {
+                    sv[c][ns] = 0u;
+                    mv[c][ns] = 0u;
+                }
             }
         }
     };
@@ -469,6 +483,7 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmShape& sh, hipStream_t st) {
         case 5: return launch_gemm_b<5>(a, sh, st);
         case 6: return launch_gemm_b<6>(a, sh, st);
         case 8: return launch_gemm_b<8>(a, sh, st);
+        case 16: return launch_gemm_b<16>(a, sh, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -59,9 +59,13 @@ struct MatRsrc {
     rsrc_t w, s, m;
     uint32_t wbytes, sbytes;
 };
+// Formats without scales and mins get empty resources for them: every such
+// load reads zero without touching memory, so those pointers may be null.
+template <int B>
 __device__ __forceinline__ MatRsrc mat_rsrc(const void* W, const void* S, const void* Mn, int n,
                                             int wpr, int gpr) {
-    const uint32_t wb = (uint32_t)n * (uint32_t)wpr * 4u, sb = (uint32_t)n * (uint32_t)gpr * 2u;
+    const uint32_t wb = (uint32_t)n * (uint32_t)wpr * 4u;
+    const uint32_t sb = has_affine<B>() ? (uint32_t)n * (uint32_t)gpr * 2u : 0u;
     return {make_rsrc(W, wb), make_rsrc(S, sb), make_rsrc(Mn, sb), wb, sb};
 }
 
@@ -80,7 +84,7 @@ __device__ __forceinline__ void load_batch(RowBatch<B, UNIT, XC, U>& bt, const M
     constexpr int SLOTS = 64 / LPR;
     constexpr int WPU = UNIT * B / 32;
     constexpr int ALIGN = unit_align(B, UNIT);
-    if constexpr (WIDE) {
+    if constexpr (WIDE && has_affine<B>()) {
         const int words = SLOTS * U * gpr / 2;
         const uint32_t off = (batch_live && lane < words)
                                  ? ((uint32_t)rb * (uint32_t)gpr + 2u * (uint32_t)lane) * 2u
@@ -96,7 +100,7 @@ __device__ __forceinline__ void load_batch(RowBatch<B, UNIT, XC, U>& bt, const M
             const bool live = batch_live && unit[c] < nu;  // rows past n fall past the end by themselves
             const uint32_t woff = live ? (row * (uint32_t)wpr + (uint32_t)(unit[c] * WPU)) * 4u : mr.wbytes;
             buffer_words<WPU, ALIGN>(mr.w, woff, bt.w[r][c]);
-            if constexpr (!WIDE) {
+            if constexpr (!WIDE && has_affine<B>()) {
                 const uint32_t so = live ? (row * (uint32_t)gpr + (uint32_t)gidx[c]) * 2u : mr.sbytes;
                 bt.s[r][c] = buffer_u16(mr.s, so);
                 bt.m[r][c] = buffer_u16(mr.m, so);
@@ -115,8 +119,9 @@ __device__ __forceinline__ void accumulate_batch(const RowBatch<B, UNIT, XC, U>&
     for (int r = 0; r < U; ++r)
 #pragma unroll
         for (int c = 0; c < XC; ++c) {
-            u32 sb, mb;
-            if constexpr (!WIDE) {
+            u32 sb = 0, mb = 0;
+            if constexpr (!has_affine<B>()) {
+            } else if constexpr (!WIDE) {
                 sb = bt.s[r][c];
                 mb = bt.m[r][c];
             } else {
@@ -130,8 +135,11 @@ __device__ __forceinline__ void accumulate_batch(const RowBatch<B, UNIT, XC, U>&
                 mb = (mw >> sh) & 0xFFFFu;
             }
             const float t = unit_qx<B, UNIT>(bt.w[r][c], xu[c]);
-            yacc[r] = __builtin_fmaf(half_bits_to_float((uint16_t)sb), t,
-                                     __builtin_fmaf(half_bits_to_float((uint16_t)mb), xu[c].xsum, yacc[r]));
+            if constexpr (has_affine<B>())
+                yacc[r] = __builtin_fmaf(scale_value<B>(sb), t,
+                                         __builtin_fmaf(half_bits_to_float((uint16_t)mb), xu[c].xsum, yacc[r]));
+            else
+                yacc[r] += t;
         }
 }
 
@@ -171,7 +179,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
     const int wpr = k / 32 * B;
     const int gpr = k / group;
     const int stride = nwaves * SLOTS * U;
-    const MatRsrc mr = mat_rsrc(W, S, Mn, n, wpr, gpr);
+    const MatRsrc mr = mat_rsrc<B>(W, S, Mn, n, wpr, gpr);
     const rsrc_t xr = make_rsrc(X, (uint32_t)k * 2u);
     const rsrc_t yr = make_rsrc(Y, (uint32_t)n * 4u);
 
@@ -267,6 +275,12 @@ __device__ __forceinline__ void accumulate_rows(const RowBatch<B, UNIT, XC, 1>& 
                                                 const int (&gidx)[XC]) {
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
+        if constexpr (!has_affine<B>()) {
+            // No scale or min (none was loaded): the dot product itself.
+#pragma unroll
+            for (int r = 0; r < MR; ++r) yacc[r] += unit_qx<B, UNIT>(bt.w[0][c], xu[r][c]);
+            continue;
+        }
         u32 sb, mb;
         if constexpr (!WIDE) {
             sb = bt.s[0][c];
@@ -280,7 +294,7 @@ __device__ __forceinline__ void accumulate_rows(const RowBatch<B, UNIT, XC, 1>& 
             sb = (sw >> sh) & 0xFFFFu;
             mb = (mw >> sh) & 0xFFFFu;
         }
-        const float sf = half_bits_to_float((uint16_t)sb), mf = half_bits_to_float((uint16_t)mb);
+        const float sf = scale_value<B>(sb), mf = half_bits_to_float((uint16_t)mb);
 #pragma unroll
         for (int r = 0; r < MR; ++r) {
             const float t = unit_qx<B, UNIT>(bt.w[0][c], xu[r][c]);
@@ -365,7 +379,7 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
         const u32* We = W + (size_t)e * n * wpr;
         const uint16_t* Se = S + (size_t)e * n * gpr;
         const uint16_t* Me = Mn + (size_t)e * n * gpr;
-        const MatRsrc mr = mat_rsrc(We, Se, Me, n, wpr, gpr);
+        const MatRsrc mr = mat_rsrc<B>(We, Se, Me, n, wpr, gpr);
         const uint32_t x_bytes = (uint32_t)x_count * (uint32_t)k * 2u;
         const rsrc_t xbuf = make_rsrc(X, x_bytes);
         const uint32_t y_bytes = (uint32_t)m_total * (uint32_t)n * 4u;
@@ -438,7 +452,7 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
 #pragma unroll
                             for (int c = 0; c < XC; ++c) {
                                 const float t = unit_qx<B, UNIT>(wv[c], xu[r][c]);
-                                yacc[r] = __builtin_fmaf(half_bits_to_float((uint16_t)sv[c]), t,
+                                yacc[r] = __builtin_fmaf(scale_value<B>(sv[c]), t,
                                                          __builtin_fmaf(half_bits_to_float((uint16_t)mv[c]),
                                                                         xu[r][c].xsum, yacc[r]));
                             }
@@ -530,7 +544,7 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
     const int nu = k / UNIT;
     const int wpr = k / 32 * B;
     const int gpr = k / group;
-    const MatRsrc mr = mat_rsrc(W, S, Mn, n, wpr, gpr);
+    const MatRsrc mr = mat_rsrc<B>(W, S, Mn, n, wpr, gpr);
     const rsrc_t xr = make_rsrc(X, (uint32_t)k * 2u);
     const rsrc_t yr = make_rsrc(Y, (uint32_t)n * 4u);
     int unit[XC], gidx[XC];

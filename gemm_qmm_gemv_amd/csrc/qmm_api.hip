@@ -30,6 +30,7 @@ namespace {
         case 5: return FN<5>(__VA_ARGS__);                \
         case 6: return FN<6>(__VA_ARGS__);                \
         case 8: return FN<8>(__VA_ARGS__);                \
+        case 16: return FN<16>(__VA_ARGS__);              \
         default: return hipErrorInvalidValue;             \
     }
 
@@ -59,7 +60,7 @@ qmm_status ok() {
 }
 
 bool bits_supported(int bits) {
-    return bits == 2 || bits == 3 || bits == 4 || bits == 5 || bits == 6 || bits == 8;
+    return bits == 2 || bits == 3 || bits == 4 || bits == 5 || bits == 6 || bits == 8 || bits == 16;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -68,9 +69,10 @@ constexpr int64_t INT_LIMIT = 0x7fffffff;
 constexpr int64_t OFFSET_LIMIT = 0xffffffffLL;  // largest byte size a 32-bit offset covers
 
 qmm_status check_format(int64_t n, int64_t k, int bits, int group) {
-    if (bits < 2 || bits > 8) return fail(QMM_ERR_INVALID_ARGUMENT, "bits=%d outside 2..8", bits);
+    if (bits != 16 && (bits < 2 || bits > 8))
+        return fail(QMM_ERR_INVALID_ARGUMENT, "bits=%d is neither 2..8 nor 16 (fp16)", bits);
     if (!bits_supported(bits))
-        return fail(QMM_ERR_UNSUPPORTED, "bits=%d not built (supported: 2, 3, 4, 5, 6, 8)", bits);
+        return fail(QMM_ERR_UNSUPPORTED, "bits=%d not built (supported: 2, 3, 4, 5, 6, 8, 16)", bits);
     if (group <= 0 || group % 32)
         return fail(QMM_ERR_INVALID_ARGUMENT, "group_size=%d must be a positive multiple of 32", group);
     if (k < 32 || k % group)
@@ -101,12 +103,17 @@ qmm_status check_activation_bytes(int64_t rows, int64_t k) {
     return QMM_OK;
 }
 
-qmm_status check_weight_ptrs(const void* w, const void* s, const void* m) {
-    if (!w || !s || !m) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL weight, scale or min pointer");
+// fp16 weights (bits 16) have no scales or mins: those pointers are not read
+// and may be NULL.
+qmm_status check_weight_ptrs(const void* w, const void* s, const void* m, int bits) {
+    if (!w) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL weight pointer");
     if (!aligned(w, 16)) return fail(QMM_ERR_MISALIGNED, "w_packed not 16-byte aligned");
+    if (bits == 16) return QMM_OK;
+    if (!s || !m) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL scale or min pointer");
     if (!aligned(s, 2) || !aligned(m, 2)) return fail(QMM_ERR_MISALIGNED, "scales/mins not 2-byte aligned");
     return QMM_OK;
 }
+
 
 // Compute units of the current device, cached per device id.
 std::atomic<int> g_cu_cache[64];
@@ -140,6 +147,12 @@ int env_int(const char* name, int dflt) {
     return atoi(v);
 }
 
+// Codes per activation unit: 64 when the group allows; fp16 weights use 32
+// (a 64-code unit would be 32 weight words per lane and row).
+int unit_codes(int bits, int group) {
+    return (bits != 16 && group % 64 == 0 && env_int("QMM_UNIT", 64) != 32) ? 64 : 32;
+}
+
 // ---- planning ------------------------------------------------------------------
 
 struct LaneSplit {
@@ -166,7 +179,7 @@ bool rows_split_ok(int lpr, int xc) { return rows_shape_supported(lpr, xc, 1); }
 
 GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     GemvShape sh{};
-    sh.unit = (group % 64 == 0 && env_int("QMM_UNIT", 64) != 32) ? 64 : 32;
+    sh.unit = unit_codes(bits, group);
     const int nu = (int)(k / sh.unit);
     LaneSplit ls = choose_split(nu, 3, gemv_split_ok);
     const int el = env_int("QMM_GEMV_LPR", 0), ex = env_int("QMM_GEMV_XC", 0);
@@ -202,9 +215,8 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
 // launch, chosen from the largest K (at most 128 units per row) and the total
 // row count; lanes per row are chosen per descriptor from its own K.
 bool plan_batched(int64_t total_rows, int64_t kmax, int bits, int group, GemvShape* out) {
-    (void)bits;
     GemvShape sh{};
-    sh.unit = (group % 64 == 0 && env_int("QMM_UNIT", 64) != 32) ? 64 : 32;
+    sh.unit = unit_codes(bits, group);
     const int nu = (int)(kmax / sh.unit);
     sh.xc = (nu + 63) / 64;
     if (sh.xc > 2) return false;
@@ -233,9 +245,8 @@ int64_t batched_items(const GemvShape& sh, int64_t n, int64_t k) {
 
 RowsShape plan_rows(int64_t rows_bound, int64_t n, int64_t k, int bits, int group, int cus,
                     int64_t n_seg_active) {
-    (void)bits;
     RowsShape sh{};
-    sh.unit = (group % 64 == 0) ? 64 : 32;
+    sh.unit = bits != 16 && group % 64 == 0 ? 64 : 32;
     const int nu = (int)(k / sh.unit);
     LaneSplit ls = choose_split(nu, 2, rows_split_ok);
     sh.lpr = ls.lpr;
@@ -338,7 +349,7 @@ qmm_status qmm_gemv(const void* w_packed, const void* scales, const void* mins, 
     qmm_status st = check_format(n, k, bits, group_size);
     if (st != QMM_OK) return st;
     if (n == 0) return ok();
-    if ((st = check_weight_ptrs(w_packed, scales, mins)) != QMM_OK) return st;
+    if ((st = check_weight_ptrs(w_packed, scales, mins, bits)) != QMM_OK) return st;
     if (!x || !y) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x or y");
     if (!aligned(x, 16) || !aligned(y, 16)) return fail(QMM_ERR_MISALIGNED, "x or y not 16-byte aligned");
     int cus = 0;
@@ -370,7 +381,7 @@ qmm_status qmm_gemm(const void* w_packed, const void* scales, const void* mins, 
     if (m == 0 || n == 0) return ok();
     if ((st = check_activation_bytes(m, k)) != QMM_OK) return st;
     if ((st = check_output_bytes(m, n)) != QMM_OK) return st;
-    if ((st = check_weight_ptrs(w_packed, scales, mins)) != QMM_OK) return st;
+    if ((st = check_weight_ptrs(w_packed, scales, mins, bits)) != QMM_OK) return st;
     if (!x || !y) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x or y");
     if (!aligned(x, 16) || !aligned(y, 16)) return fail(QMM_ERR_MISALIGNED, "x or y not 16-byte aligned");
     if (workspace_bytes && !workspace)
@@ -411,7 +422,7 @@ qmm_status qmm_moe_gemm(const void* w_packed, const void* scales, const void* mi
     if (p_rows == 0 || n == 0 || n_experts == 0) return ok();
     if ((st = check_activation_bytes(x_rows ? x_rows_count : p_rows, k)) != QMM_OK) return st;
     if ((st = check_output_bytes(p_rows, n)) != QMM_OK) return st;
-    if ((st = check_weight_ptrs(w_packed, scales, mins)) != QMM_OK) return st;
+    if ((st = check_weight_ptrs(w_packed, scales, mins, bits)) != QMM_OK) return st;
     if (!x || !y || !expert_offsets) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x, y or expert_offsets");
     if (!x_rows && x_rows_count < p_rows)
         return fail(QMM_ERR_INVALID_ARGUMENT, "x_rows is NULL and x has fewer than p_rows rows");
@@ -438,7 +449,7 @@ static qmm_status check_batch(const qmm_gemv_desc* d, int64_t count, int bits, i
     char why[sizeof g_err];
     for (int64_t i = 0; i < count; ++i) {
         qmm_status st = check_format(d[i].n, d[i].k, bits, group);
-        if (st == QMM_OK && d[i].n > 0) st = check_weight_ptrs(d[i].w_packed, d[i].scales, d[i].mins);
+        if (st == QMM_OK && d[i].n > 0) st = check_weight_ptrs(d[i].w_packed, d[i].scales, d[i].mins, bits);
         if (st != QMM_OK) {
             memcpy(why, g_err, sizeof why);
             return fail(st, "descriptor %lld: %s", (long long)i, why);
@@ -501,6 +512,7 @@ qmm_status qmm_unpack(const void* w_packed, uint8_t* codes, int64_t n, int64_t k
                       void* stream) {
     qmm_status st = check_format(n, k, bits, 32);
     if (st != QMM_OK) return st;
+    if (bits == 16) return fail(QMM_ERR_UNSUPPORTED, "bits=16 holds fp16 weights, not codes to unpack");
     if (n == 0) return ok();
     if (!w_packed || !codes) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL w_packed or codes");
     if (!aligned(w_packed, 16) || !aligned(codes, 16))

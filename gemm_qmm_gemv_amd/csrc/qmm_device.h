@@ -261,6 +261,31 @@ template <> struct PairFmt<8> {
     }
 };
 
+// Unquantized fp16 weights ("Q16"): the stream holds the fp16 values
+// themselves, two per word in k order, so a word already is the pair
+// (k, k+1).  No offset to remove and no scale or min: scale_value<16> is 1
+// and the min arrays are never read.
+template <> struct PairFmt<16> {
+    static constexpr int NACC = 1;
+    static constexpr int ka(int i) { return 2 * i; }
+    static constexpr int kb(int i) { return 2 * i + 1; }
+    static constexpr int acc(int) { return 0; }
+    static constexpr float inv_factor(int) { return 1.f; }
+    __device__ static __forceinline__ void extract(const u32* w, u32* p) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[i] = w[i];
+    }
+};
+// Formats with a scale and a min per group (all but fp16).
+template <int B>
+constexpr bool has_affine() { return B != 16; }
+// The group scale as a float; fp16 weights carry none.
+template <int B>
+__device__ __forceinline__ float scale_value(u32 bits) {
+    if constexpr (has_affine<B>()) return half_bits_to_float((uint16_t)bits);
+    return 1.f;
+}
+
 // Largest power-of-two alignment (<= 16 bytes) of a unit of `unit` codes at b
 // bits, given 16-byte aligned rows... rows start at multiples of the unit's
 // byte size, so the unit size alone decides.
@@ -322,8 +347,10 @@ __device__ __forceinline__ void prep_xunit(rsrc_t xr, uint32_t off, XUnit<B, UNI
             const u32 hi = (xw[b / 2] >> (16 * (b % 2))) & 0xFFFFu;
             const f16x2 pr = as_h2(lo | (hi << 16));
             xu.xp[16 * c + i] = pr;
-            const f16 cf = (f16)(1024.0f * F::inv_factor(F::acc(i)));
-            corr = __builtin_amdgcn_fdot2(pr, f16x2{cf, cf}, corr, false);
+            if constexpr (has_affine<B>()) {
+                const f16 cf = (f16)(1024.0f * F::inv_factor(F::acc(i)));
+                corr = __builtin_amdgcn_fdot2(pr, f16x2{cf, cf}, corr, false);
+            }
             xsum = __builtin_amdgcn_fdot2(pr, one2, xsum, false);
         }
     }

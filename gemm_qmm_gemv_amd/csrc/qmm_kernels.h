@@ -173,8 +173,10 @@ template <int B> hipError_t launch_rows_bits(const RowsArgs& a, const RowsShape&
 QMM_DECLARE_BITS(2)
 QMM_DECLARE_BITS(3)
 QMM_DECLARE_BITS(4)
+QMM_DECLARE_BITS(5)
 QMM_DECLARE_BITS(6)
 QMM_DECLARE_BITS(8)
+QMM_DECLARE_BITS(16)
 #undef QMM_DECLARE_BITS
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmShape& sh, hipStream_t st);

@@ -12,6 +12,8 @@ Recipe (the pages give no values; the workloads are synthetic):
   * scales  -- fp16(|z| * 0.02 + 1e-3), z ~ N(0, 1), rounded to nearest even;
   * mins    -- fp16(0.05 * z),           z ~ N(0, 1);
   * x       -- fp16(z),                  z ~ N(0, 1);
+  * fp16 weights (bits 16, no scales or mins) -- fp16(0.1 * z), z ~ N(0, 1),
+    stored two per uint32 word in k order (the low half holds the even k);
   * MoE routing -- logits ~ N(0, 1) per (token, expert); each token picks its
     top-k experts (equal logits: lower expert index first).  Softmax is
     monotone, so this is also the top-k of the softmax probabilities.
@@ -55,9 +57,21 @@ def activations(rng: np.random.Generator, m: int, k: int) -> np.ndarray:
     return rng.standard_normal((m, k)).astype(np.float16)
 
 
+def fp16_weight_words(rng: np.random.Generator, n: int, k: int) -> np.ndarray:
+    """fp16 [n][k] weights as uint32 words [n][k/2] (little-endian pairs)."""
+    if k % 2:
+        raise ValueError("k must be even")
+    h = (0.1 * rng.standard_normal((n, k))).astype(np.float16)
+    return np.ascontiguousarray(h).view(np.uint32)
+
+
 def quantized_matrix(n: int, k: int, bits: int, group: int, key=(0,)):
-    """dict(w, scales, mins) for one N x K weight matrix."""
+    """dict(w, scales, mins) for one N x K weight matrix (bits 16: fp16
+    weights, scales and mins None)."""
     rng = rng_for(*key, ROLE_WEIGHTS)
+    if bits == 16:
+        return {"w": fp16_weight_words(rng, n, k), "scales": None, "mins": None,
+                "n": n, "k": k, "bits": bits, "group": group}
     w = packed_words(rng, n, k, bits)
     s, m = scales_mins(rng, n, k, group)
     return {"w": w, "scales": s, "mins": m, "n": n, "k": k, "bits": bits, "group": group}
@@ -75,7 +89,8 @@ def stacked_experts(n_experts: int, n: int, k: int, bits: int, group: int, key=(
         ws.append(q["w"])
         ss.append(q["scales"])
         ms.append(q["mins"])
-    return {"w": np.stack(ws), "scales": np.stack(ss), "mins": np.stack(ms),
+    stack = (lambda v: None) if bits == 16 else np.stack
+    return {"w": np.stack(ws), "scales": stack(ss), "mins": stack(ms),
             "n_experts": n_experts, "n": n, "k": k, "bits": bits, "group": group}
 
 

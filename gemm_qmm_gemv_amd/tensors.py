@@ -26,7 +26,7 @@ def upload_matrix(q: dict, device="cuda") -> dict:
     """dict(w, scales, mins, n, k, bits, group) with device tensors."""
     out = dict(q)
     for key in ("w", "scales", "mins"):
-        out[key] = device_tensor(q[key], device)
+        out[key] = None if q[key] is None else device_tensor(q[key], device)
     return out
 
 
@@ -78,7 +78,8 @@ class GemvBatch:
         self.host = (GemvDesc * len(items))()
         for d, (dq, x, y) in zip(self.host, items):
             assert dq["bits"] == bits and dq["group"] == group
-            d.w_packed, d.scales, d.mins = dq["w"].data_ptr(), dq["scales"].data_ptr(), dq["mins"].data_ptr()
+            ptr = lambda t: 0 if t is None else t.data_ptr()
+            d.w_packed, d.scales, d.mins = ptr(dq["w"]), ptr(dq["scales"]), ptr(dq["mins"])
             d.x, d.y = x.data_ptr(), y.data_ptr()
             d.n, d.k = dq["n"], dq["k"]
         qmm_gemv_batch_prepare(self.host, bits, group)

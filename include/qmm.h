@@ -26,9 +26,15 @@
  *   The weight is w[n][k] = s[n][k/group_size] * q[n][k] + m[n][k/group_size].
  *   Activations x are fp16 [M][K] row-major; outputs y are fp32 [M][N]
  *   row-major:  y[i][n] = sum_k w[n][k] * x[i][k].
+ *   bits = 16 is the unquantized format ("FP16"/"Q16" in the per-format
+ *   kernel lists of the pages above): w_packed holds the fp16 weights
+ *   themselves, K/2 words per row, word j holding k = 2j in its low 16 bits
+ *   and k = 2j + 1 in its high 16 bits.  Scales and mins are not read and may
+ *   be NULL; group_size is still checked as above.  qmm_unpack rejects it
+ *   (QMM_ERR_UNSUPPORTED), and a batched launch covers K <= 4096 at 16 bits.
  *
  * Requirements checked on the host before anything is launched:
- *   bits in {2, 3, 4, 5, 6, 8} (7 is QMM_ERR_UNSUPPORTED); group_size a
+ *   bits in {2, 3, 4, 5, 6, 8, 16} (7 is QMM_ERR_UNSUPPORTED); group_size a
  *   positive multiple of 32;
  *   k >= 32 and k a multiple of group_size; n >= 0, m >= 0 (0 is a no-op);
  *   weight, activation and output pointers 16-byte aligned; scale and min

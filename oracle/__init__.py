@@ -25,6 +25,10 @@ Pinning (what each function is checked against, in ``tests/test_oracle_pins.py``
                          exact power-of-two scaling and sign symmetry.
   * qmm_sample        -- the same rows of full qmm.
   * moe               -- per-expert numpy matmuls over the expert's rows.
+  * fp16 weights (bits 16: the unquantized "Q16/FP16" format, no scales or
+    mins) -- decoded by the pinned fp16 decoder and multiplied in float64
+    with numpy; pinned against the Q8 path (integer codes with scale 1 and
+    min 0 are exact fp16 weights), one-hot activations and exact integers.
 """
 from __future__ import annotations
 
@@ -112,8 +116,8 @@ def _as_u16(a):
 
 
 def _check_format(k: int, bits: int, group: int):
-    if bits not in (2, 3, 4, 5, 6, 7, 8):
-        raise ValueError("bits must be in 2..8")
+    if bits not in (2, 3, 4, 5, 6, 7, 8, 16):
+        raise ValueError("bits must be in 2..8 or 16 (fp16 weights)")
     if (k * bits) % 32:
         raise ValueError("K*bits must be a multiple of 32")
     if group <= 0 or k % group:
@@ -169,15 +173,35 @@ def dequant(w_packed, scales, mins, n: int, k: int, bits: int, group: int) -> np
     return out
 
 
+def f16_weights(w_words, n: int, k: int) -> np.ndarray:
+    """fp16 weights [n][k] as float64 from their words: word j of a row holds
+    k = 2j in its low 16 bits and k = 2j + 1 in its high 16 bits."""
+    w = _c(w_words, np.uint32).reshape(n, k // 2)
+    h = np.empty((n, k), dtype=np.uint16)
+    h[:, 0::2] = (w & 0xFFFF).astype(np.uint16)
+    h[:, 1::2] = (w >> 16).astype(np.uint16)
+    return fp16_to_double(h)
+
+
+def _qmm_f16(w_words, x2, n: int, k: int):
+    wd = f16_weights(w_words, n, k)
+    xd = fp16_to_double(x2)
+    return xd @ wd.T, np.abs(xd) @ np.abs(wd).T
+
+
 def qmm(w_packed, scales, mins, x, n: int, k: int, bits: int, group: int):
     """(y, a) with y[M][N] = X W^T and a[M][N] = sum_k |w x|, both float64.
 
-    x is fp16 [M][K] (or [K] for the GEMV; y and a are then [N])."""
+    x is fp16 [M][K] (or [K] for the GEMV; y and a are then [N]).  bits 16:
+    w_packed holds fp16 weights (see f16_weights); scales and mins unused."""
     _check_format(k, bits, group)
     x = _as_u16(x)
     vec = x.ndim == 1
     x2 = x.reshape(-1, k)
     m = x2.shape[0]
+    if bits == 16:
+        y, a = _qmm_f16(w_packed, x2, n, k)
+        return (y[0], a[0]) if vec else (y, a)
     w = _c(w_packed, np.uint32)
     s, mn = _as_u16(scales), _as_u16(mins)
     assert w.size == n * k * bits // 32
@@ -197,10 +221,17 @@ def qmm_sample(w_packed, scales, mins, x, k: int, bits: int, group: int,
     _check_format(k, bits, group)
     x = _as_u16(x).reshape(-1, k)
     w = _c(w_packed, np.uint32)
-    s, mn = _as_u16(scales), _as_u16(mins)
     rm = _c(rows_m, np.int64)
     rn = _c(rows_n, np.int64)
     assert rm.shape == rn.shape
+    if bits == 16:
+        n = w.size // (k // 2)
+        if rm.size and (rm.min() < 0 or rm.max() >= x.shape[0] or rn.min() < 0 or rn.max() >= n):
+            raise IndexError("sample position out of range")
+        wd = f16_weights(w.reshape(n, k // 2)[rn], rn.size, k)
+        xd = fp16_to_double(x[rm])
+        return np.sum(wd * xd, axis=1), np.sum(np.abs(wd) * np.abs(xd), axis=1)
+    s, mn = _as_u16(scales), _as_u16(mins)
     n = s.size // (k // group)
     if rm.size and (rm.min() < 0 or rm.max() >= x.shape[0]
                     or rn.min() < 0 or rn.max() >= n):
@@ -220,9 +251,11 @@ def moe(w_packed, scales, mins, x, x_rows, offsets, n_experts: int, n: int, k: i
     x_rows int32 [P] or None, offsets int32 [E+1]."""
     _check_format(k, bits, group)
     w = _c(w_packed, np.uint32)
-    s, mn = _as_u16(scales), _as_u16(mins)
     x = _as_u16(x).reshape(-1, k)
     off = _c(offsets, np.int32)
+    if bits == 16:
+        return _moe_f16(w, x, x_rows, off, n_experts, n, k)
+    s, mn = _as_u16(scales), _as_u16(mins)
     assert off.size == n_experts + 1
     p = int(off[-1])
     if x_rows is not None:
@@ -240,6 +273,27 @@ def moe(w_packed, scales, mins, x, x_rows, offsets, n_experts: int, n: int, k: i
     a = np.zeros((p, n), dtype=np.float64)
     _load().qmo_moe(_ptr(w), _ptr(s), _ptr(mn), _ptr(x), xr_ptr, _ptr(off),
                     n_experts, n, k, bits, group, _ptr(y), _ptr(a))
+    return y, a
+
+
+def _moe_f16(w, x, x_rows, off, n_experts: int, n: int, k: int):
+    """Row p of expert e (off[e] <= p < off[e+1]) times activation row
+    x_rows[p] (or p), with expert e's fp16 weights."""
+    assert off.size == n_experts + 1 and w.size == n_experts * n * k // 2
+    p = int(off[-1])
+    xr = np.arange(p) if x_rows is None else _c(x_rows, np.int32)
+    assert xr.size == p
+    if p and (xr.min() < 0 or xr.max() >= x.shape[0]):
+        raise IndexError("x_rows out of range")
+    we = w.reshape(n_experts, n, k // 2)
+    y = np.zeros((p, n), dtype=np.float64)
+    a = np.zeros((p, n), dtype=np.float64)
+    for e in range(n_experts):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi <= lo:
+            continue
+        yy, aa = _qmm_f16(we[e], x[xr[lo:hi]], n, k)
+        y[lo:hi], a[lo:hi] = yy, aa
     return y, a
 
 

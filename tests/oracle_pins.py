@@ -255,6 +255,81 @@ def check_moe_per_expert():
     assert np.array_equal(y2, y)
 
 
+# ---- fp16 weights (bits 16) -------------------------------------------------------
+
+def _f16_words(h):
+    """uint16 [n][k] fp16 patterns -> the library's words: k = 2j in the low
+    half of word j, k = 2j + 1 in the high half (written out bit by bit)."""
+    h = np.asarray(h, dtype=np.uint32)
+    return (h[:, 0::2] | (h[:, 1::2] << 16)).astype(np.uint32)
+
+
+def check_f16_matches_q8_path():
+    # Q8 codes with scale 1 and min 0 are integers 0..255, exact in fp16: the
+    # fp16-weight product must equal the quantized path's product.
+    n, k, m = 9, 256, 3
+    rng = inputs.rng_for(11)
+    codes = rng.integers(0, 256, size=(n, k))
+    x = inputs.activations(rng, m, k)
+    w8 = np_pack(codes, 8)
+    s = np.ones((n, k // 64), dtype=np.float16)
+    mn = np.zeros((n, k // 64), dtype=np.float16)
+    y8, a8 = oracle.qmm(w8, s, mn, x, n, k, 8, 64)
+    h = codes.astype(np.float16).view(np.uint16)
+    y16, a16 = oracle.qmm(_f16_words(h), None, None, x, n, k, 16, 64)
+    assert np.allclose(y16, y8, rtol=0, atol=1e-12 * np.abs(a8).max())
+    assert np.allclose(a16, a8, rtol=1e-12, atol=0)
+
+
+def check_f16_one_hot_and_layout():
+    # x = e_j picks weight (n, j) exactly; a row with distinct values in every
+    # half-word shows which half holds which k.
+    n, k = 5, 64
+    rng = inputs.rng_for(12)
+    h = (0.1 * rng.standard_normal((n, k))).astype(np.float16)
+    words = _f16_words(h.view(np.uint16))
+    for j in (0, 1, 2, 31, 62, 63):
+        x = np.zeros(k, dtype=np.float16)
+        x[j] = 1.0
+        y, _ = oracle.qmm(words, None, None, x, n, k, 16, 64)
+        assert np.array_equal(y, h[:, j].astype(np.float64)), j
+    # Weight 1.0 (0x3C00) only in the high half of word 0: it is k = 1.
+    w = np.zeros((1, k // 2), dtype=np.uint32)
+    w[0, 0] = 0x3C000000
+    x = np.arange(k).astype(np.float16)
+    y, _ = oracle.qmm(w, None, None, x, 1, k, 16, 64)
+    assert y[0] == 1.0
+
+
+def check_f16_exact_integer():
+    # Integer weights in [-8, 8] and activations in [-2, 2]: exact sums.
+    n, k, m = 7, 512, 4
+    rng = inputs.rng_for(13)
+    wi = rng.integers(-8, 9, size=(n, k))
+    xi = rng.integers(-2, 3, size=(m, k))
+    words = _f16_words(wi.astype(np.float16).view(np.uint16))
+    y, a = oracle.qmm(words, None, None, xi.astype(np.float16), n, k, 16, 64)
+    assert np.array_equal(y, (xi @ wi.T).astype(np.float64))
+    assert np.array_equal(a, (np.abs(xi) @ np.abs(wi).T).astype(np.float64))
+    ys, _ = oracle.qmm_sample(words, None, None, xi.astype(np.float16), k, 16, 64,
+                              [0, 3, 2], [6, 0, 1])
+    assert np.array_equal(ys, y[[0, 3, 2], [6, 0, 1]])
+
+
+def check_f16_moe_per_expert():
+    e, n, k = 3, 6, 128
+    rng = inputs.rng_for(14)
+    wi = rng.integers(-8, 9, size=(e, n, k))
+    words = np.stack([_f16_words(wi[i].astype(np.float16).view(np.uint16)) for i in range(e)])
+    x = rng.integers(-2, 3, size=(5, k)).astype(np.float16)
+    x_rows = np.array([4, 0, 2, 2, 1, 3], dtype=np.int32)
+    off = np.array([0, 2, 2, 6], dtype=np.int32)
+    y, _ = oracle.moe(words, None, None, x, x_rows, off, e, n, k, 16, 64)
+    xd = x.astype(np.float64)
+    for p, ex in enumerate([0, 0, 2, 2, 2, 2]):
+        assert np.array_equal(y[p], wi[ex] @ xd[x_rows[p]]), p
+
+
 ALL_CHECKS = [
     check_fp16_exhaustive,
     check_hand_vectors,
@@ -268,4 +343,8 @@ ALL_CHECKS = [
     check_exact_invariants,
     check_sample_matches_full,
     check_moe_per_expert,
+    check_f16_matches_q8_path,
+    check_f16_one_hot_and_layout,
+    check_f16_exact_integer,
+    check_f16_moe_per_expert,
 ]

@@ -65,6 +65,7 @@ def _gemv(lib, w=A16, s=A16, m=A16, x=A16, y=A16, n=64, k=128, bits=4, g=64):
     (dict(bits=7), qmm.QMM_ERR_UNSUPPORTED),
     (dict(bits=1), qmm.QMM_ERR_INVALID_ARGUMENT),
     (dict(bits=9), qmm.QMM_ERR_INVALID_ARGUMENT),
+    (dict(bits=17), qmm.QMM_ERR_INVALID_ARGUMENT),
     (dict(g=48), qmm.QMM_ERR_INVALID_ARGUMENT),
     (dict(g=0), qmm.QMM_ERR_INVALID_ARGUMENT),
     (dict(k=96, g=64), qmm.QMM_ERR_INVALID_ARGUMENT),
@@ -113,6 +114,21 @@ def test_gemm_and_moe_argument_checks(lib):
         qmm.QMM_OK
     assert lib.qmm_unpack(p(A16), p(A16 + 8), 4, 64, 4, None) == qmm.QMM_ERR_MISALIGNED
     assert lib.qmm_unpack(p(A16), p(A16), 4, 64, 7, None) == qmm.QMM_ERR_UNSUPPORTED
+    # fp16 weights (bits 16) hold no codes to unpack.
+    assert lib.qmm_unpack(p(A16), p(A16), 4, 64, 16, None) == qmm.QMM_ERR_UNSUPPORTED
+
+
+def test_fp16_weights_need_no_scales(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    # NULL scales and mins pass the checks for bits 16 (and only for 16).
+    assert _gemv(lib, s=0, m=0, bits=16) == qmm.QMM_ERR_DEVICE
+    assert _gemv(lib, s=0, m=0, bits=8) == qmm.QMM_ERR_INVALID_ARGUMENT
+    assert _gemv(lib, s=A16 + 1, bits=16) == qmm.QMM_ERR_DEVICE  # not read, not checked
+    assert _gemv(lib, bits=12) == qmm.QMM_ERR_INVALID_ARGUMENT
+    pl = qmm.qmm_get_plan(0, 1, 4096, 4096, 16, 64, cu_count=256)
+    assert pl["unit_codes"] == 32
 
 
 # ---- launch planning (host integer logic) -----------------------------------------
@@ -123,7 +139,7 @@ ALL_DECODE_SHAPES = sorted({(n, k) for _, n, k in configs.QWEN3_06B_PROJ + [conf
                            | {(n, k) for _, n, k in configs.MOE_PROJ})
 
 
-@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6, 8))
+@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6, 8, 16))
 @pytest.mark.parametrize("n,k", ALL_DECODE_SHAPES + [(5, 16384), (7, 96), (1, 64)])
 @pytest.mark.parametrize("group", (64, 32, 128))
 def test_gemv_plan_covers_the_row(lib, bits, n, k, group):
@@ -131,7 +147,7 @@ def test_gemv_plan_covers_the_row(lib, bits, n, k, group):
         pytest.skip("k not a multiple of the group")
     pl = qmm.qmm_get_plan(0, 1, n, k, bits, group, cu_count=256)
     unit = pl["unit_codes"]
-    assert unit == (64 if group % 64 == 0 else 32)
+    assert unit == (64 if group % 64 == 0 and bits != 16 else 32)
     assert pl["block"] == 256
     cover = pl["lanes_per_row"] * pl["units_per_lane"] * unit
     assert pl["multipass"] == (cover < k)

@@ -26,7 +26,7 @@ def _run_batch(shapes, bits, group, seed):
     return qs, [it[2].cpu().numpy() for it in items]
 
 
-@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6, 8))
+@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6, 8, 16))
 def test_batched_mixed_shapes(bits):
     shapes = [(2048, 1024), (0, 1024), (1, 64), (1000, 1024), (37, 1024), (513, 512), (3, 1024)]
     announce("batched-mixed", bits)
@@ -39,12 +39,18 @@ def test_batched_mixed_shapes(bits):
         assert_within(y[:n], y_ref, a_ref, "batched b%d %dx%d" % (bits, n, k))
 
 
-@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6, 8))
+@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6, 8, 16))
 def test_batched_mixed_k_one_launch(bits):
     # Different K per descriptor in one launch: each gets its own lane layout
     # (16, 32 or 64 lanes per row; two units per lane for K = 8192).
     shapes = [(300, 1024), (129, 2048), (77, 3072), (1000, 1024), (5, 768), (40, 8192), (64, 4096),
               (1, 64), (33, 2048)]
+    if bits == 16:
+        # fp16 rows use 32-code units: a batched launch covers K <= 4096.
+        from gemm_qmm_gemv_amd import QmmError
+        with pytest.raises(QmmError, match="too large for a batched launch"):
+            _run_batch(shapes, bits, 64, 4)
+        shapes = [s for s in shapes if s[1] <= 4096]
     announce("batched-mixed-k", bits)
     qs, ys = _run_batch(shapes, bits, 64, 4)
     for (q, x), y, (n, k) in zip(qs, ys, shapes):

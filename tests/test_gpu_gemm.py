@@ -9,6 +9,7 @@ from tests.gpu_util import announce, assert_within
 pytestmark = pytest.mark.gpu
 
 BITS = (2, 3, 4, 5, 6, 8)
+PARITY_BITS = BITS + (16,)  # 16: fp16 weights
 
 
 def _run_gemm(q, x, workspace="auto"):
@@ -24,7 +25,7 @@ def _run_gemm(q, x, workspace="auto"):
     return y.cpu().numpy()
 
 
-@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("bits", PARITY_BITS)
 @pytest.mark.parametrize("m,n,k,group", [
     (2, 130, 256, 64), (3, 64, 128, 64), (5, 200, 1024, 64), (64, 128, 512, 64),
     (100, 300, 1024, 64), (128, 512, 2048, 64), (130, 257, 320, 64), (256, 640, 768, 32),
@@ -38,7 +39,7 @@ def test_gemm_parity(bits, m, n, k, group):
     assert_within(y, y_ref, a_ref, "gemm b%d m%d %dx%d g%d" % (bits, m, n, k, group))
 
 
-@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("bits", PARITY_BITS)
 @pytest.mark.parametrize("tile", (32, 64, 128))
 @pytest.mark.parametrize("m,n,k", [(100, 300, 1024), (130, 257, 320), (257, 384, 2048)])
 def test_gemm_parity_every_tile(monkeypatch, bits, tile, m, n, k):

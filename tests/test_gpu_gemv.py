@@ -9,6 +9,7 @@ from tests.gpu_util import announce, assert_within
 pytestmark = pytest.mark.gpu
 
 BITS = (2, 3, 4, 5, 6, 8)
+PARITY_BITS = BITS + (16,)  # 16: fp16 weights
 
 
 def _torch():
@@ -40,7 +41,7 @@ def test_unpack_bit_exact(bits, n, k):
     assert np.array_equal(codes.cpu().numpy(), oracle.unpack(q["w"], n, k, bits))
 
 
-@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("bits", PARITY_BITS)
 @pytest.mark.parametrize("n,k,group", [
     (1, 64, 64), (7, 64, 32), (17, 192, 64), (3072, 1024, 64), (1000, 3072, 64),
     (300, 2048, 128), (129, 768, 64), (96, 8192, 64), (40, 16384, 64), (50, 96, 32),

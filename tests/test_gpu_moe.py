@@ -46,7 +46,7 @@ def test_moe_config(tokens, proj):
     assert_within(y, y_ref, a_ref, "moe T%d %s" % (tokens, name))
 
 
-@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6, 8))
+@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6, 8, 16))
 def test_moe_uneven_segments(bits):
     # Experts with 0, 1, 2, 5 and 9 rows, ragged N, an out-of-range index.
     e, n, k = 7, 70, 320
