@@ -68,3 +68,58 @@ def test_planted_mistake_is_caught(mutant, tmp_path):
     finally:
         oracle.use_library(None)
     assert failed, "planted mistake %r passed every pin" % name
+
+
+# Planted mistakes in the fp16-weight path (Python): each replaces one oracle
+# function for the duration of the test and must fail at least one pin.
+def _f16_halves_swapped(w_words, n, k):
+    import numpy as np
+    w = oracle._c(w_words, np.uint32).reshape(n, k // 2)
+    h = np.empty((n, k), dtype=np.uint16)
+    h[:, 0::2] = (w >> 16).astype(np.uint16)
+    h[:, 1::2] = (w & 0xFFFF).astype(np.uint16)
+    return oracle.fp16_to_double(h)
+
+
+def _f16_as_integers(w_words, n, k):
+    # Reads the 16-bit patterns as integers instead of decoding them.
+    import numpy as np
+    w = oracle._c(w_words, np.uint32).reshape(n, k // 2)
+    h = np.empty((n, k), dtype=np.float64)
+    h[:, 0::2] = w & 0xFFFF
+    h[:, 1::2] = w >> 16
+    return h
+
+
+_real_qmm_f16 = oracle._qmm_f16
+
+
+def _qmm_f16_abs_signed(w_words, x2, n, k):
+    y, _ = _real_qmm_f16(w_words, x2, n, k)
+    return y, y
+
+
+def _qmm_f16_x_shifted(w_words, x2, n, k):
+    import numpy as np
+    return _real_qmm_f16(w_words, np.roll(x2, 1, axis=1), n, k)
+
+
+PY_MUTANTS = [
+    ("f16_halves_swapped", "f16_weights", _f16_halves_swapped),
+    ("f16_not_decoded", "f16_weights", _f16_as_integers),
+    ("f16_abs_sum_signed", "_qmm_f16", _qmm_f16_abs_signed),
+    ("f16_x_off_by_one", "_qmm_f16", _qmm_f16_x_shifted),
+]
+
+
+@pytest.mark.parametrize("mutant", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_planted_python_mistake_is_caught(mutant, monkeypatch):
+    name, attr, fn = mutant
+    monkeypatch.setattr(oracle, attr, fn)
+    failed = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check()
+        except AssertionError:
+            failed.append(check.__name__)
+    assert failed, "planted mistake %r passed every pin" % name
