@@ -22,6 +22,8 @@ Also measured (outside the timed region, reported in the same JSON line):
   * Llama-3.2-1B-shaped prefill GEMMs at M = 128 and 512: TFLOP/s, % MFMA,
     with Q4 weights and again with fp16 weights, the dense fp16 library
     matmul of each shape beside them;
+  * the fused gate/up projection (silu(Wg x) * (Wu x), one launch) against
+    two GEMV launches, Q4, on Qwen3-0.6B and Llama-3.2-3B shapes;
   * Qwen3-30B-A3B-shaped MoE expert projections at 1 and 16 tokens;
   * the CPU oracle on the host cores over the same projection set.
 
@@ -356,6 +358,38 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
     for bits in (4, 16):
         out["prefill_llama3.2_1b_" + ("q4" if bits == 4 else "fp16")] = prefill_layers(
             torch, qmm, configs, inputs, tensors, timer, bits)
+
+    # Fused gate/up projection with the SiLU-gated product vs two GEMV
+    # launches (Q4, 8 rotating copies of the pair so the weights stream
+    # from HBM).
+    glu = {}
+    for label, n, k in (("qwen3_0.6b_gate_up", 3072, 1024), ("llama3.2_3b_gate_up", 8192, 3072)):
+        pairs = [(tensors.upload_matrix(inputs.quantized_matrix(n, k, 4, G, key=(configs.CFG_SWEEP, 90, r, 0))),
+                  tensors.upload_matrix(inputs.quantized_matrix(n, k, 4, G, key=(configs.CFG_SWEEP, 90, r, 1))))
+                 for r in range(8)]
+        xg = tensors.device_tensor(inputs.activation_rows(1, k, key=(configs.CFG_SWEEP, 90, k))[0])
+        hg = torch.empty(n, dtype=torch.float32, device="cuda")
+        yg2 = torch.empty(n, dtype=torch.float32, device="cuda")
+        ii = [0]
+
+        def fused():
+            dg, du = pairs[ii[0] % 8]
+            tensors.gemv_swiglu(dg, du, xg, hg)
+            ii[0] += 1
+
+        def separate():
+            dg, du = pairs[ii[0] % 8]
+            tensors.gemv(dg, xg, hg)
+            tensors.gemv(du, xg, yg2)
+            ii[0] += 1
+        ms_f = timer(fused, reps=40)
+        ms_s = timer(separate, reps=40)
+        b = 2 * configs.weight_bytes(n, k, 4) + 2 * k + 4 * n
+        glu[label] = {"fused_us": round(ms_f * 1e3, 2), "two_gemvs_us": round(ms_s * 1e3, 2),
+                      "fused_GBps": round(b / ms_f / 1e6, 1)}
+        del pairs
+        log("swiglu %s: fused %.1f us, two gemvs %.1f us" % (label, ms_f * 1e3, ms_s * 1e3))
+    out["swiglu_fusion_q4"] = glu
 
     # MoE expert projections (Qwen3-30B-A3B shapes).
     moe = {}

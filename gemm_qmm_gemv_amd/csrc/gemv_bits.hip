@@ -33,4 +33,11 @@ hipError_t launch_rows_bits<QMM_BITS>(const RowsArgs& a, const RowsShape& sh, hi
     return sh.unit == 32 ? launch_rows_unit<QMM_BITS, 32>(a, sh, st) : hipErrorInvalidValue;
 }
 
+template <>
+hipError_t launch_glu_bits<QMM_BITS>(const GluArgs& a, const GemvShape& sh, hipStream_t st) {
+    if constexpr (UNIT64)
+        if (sh.unit == 64) return launch_glu_unit<QMM_BITS, 64>(a, sh, st);
+    return sh.unit == 32 ? launch_glu_unit<QMM_BITS, 32>(a, sh, st) : hipErrorInvalidValue;
+}
+
 }  // namespace qmm

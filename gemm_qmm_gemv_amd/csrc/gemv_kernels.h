@@ -256,6 +256,92 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
         body(std::false_type{});
 }
 
+// Fused gate/up projection of a feed-forward block: h[n] = silu(g[n]) * u[n]
+// with g = Wg x, u = Wu x and silu(v) = v / (1 + e^-v), both matrices N x K in
+// one format.  Kernel fusion removes a launch and a global-memory round trip
+// ("BaseRT claims fastest Apple Silicon inference", section "What BaseRT does
+// differently"; gist.science summary, section "Metodologia", item "Fusão e
+// Especialização de Kernel": operator sequences of feed-forward blocks run as
+// one kernel).  Each row batch is loaded from both matrices (same row index),
+// so g and u meet in registers and only h is written.  The loop is the
+// single-pass pipelined loop of the decode GEMV (k <= LPR * XC * UNIT).
+template <int LPR>
+__device__ __forceinline__ void store_glu(float g, float u, rsrc_t hr, int rb, int n, int slot, int j) {
+    const float gs = group_sum<LPR>(g), us = group_sum<LPR>(u);
+    const float h = gs / (1.0f + expf(-gs)) * us;
+    const int row = rb + slot;
+    buffer_store_f32(h, hr, (j == 0 && row < n) ? (uint32_t)row * 4u : (uint32_t)n * 4u);
+}
+
+template <int B, int UNIT, int LPR, int XC>
+__global__ __launch_bounds__(256) void gemv_glu_kernel(
+    const u32* __restrict__ Wg, const uint16_t* __restrict__ Sg, const uint16_t* __restrict__ Mg,
+    const u32* __restrict__ Wu, const uint16_t* __restrict__ Su, const uint16_t* __restrict__ Mu,
+    const uint16_t* __restrict__ X, float* __restrict__ H, int n, int k, int group) {
+    constexpr int SLOTS = 64 / LPR;
+    const int lane = threadIdx.x & 63;
+    const int slot = lane / LPR, j = lane % LPR;
+    const int waves_per_block = blockDim.x >> 6;
+    const int wave = blockIdx.x * waves_per_block + (threadIdx.x >> 6);
+    const int nwaves = gridDim.x * waves_per_block;
+    const int nu = k / UNIT;
+    const int wpr = k / 32 * B;
+    const int gpr = k / group;
+    const int stride = nwaves * SLOTS;
+    const MatRsrc mg = mat_rsrc<B>(Wg, Sg, Mg, n, wpr, gpr);
+    const MatRsrc mu = mat_rsrc<B>(Wu, Su, Mu, n, wpr, gpr);
+    const rsrc_t xr = make_rsrc(X, (uint32_t)k * 2u);
+    const rsrc_t hr = make_rsrc(H, (uint32_t)n * 4u);
+    int unit[XC], gidx[XC];
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+        unit[c] = c * LPR + j;
+        gidx[c] = unit[c] < nu ? (unit[c] * UNIT) / group : 0;
+    }
+    XUnit<B, UNIT> xu[XC];
+
+    auto body = [&](auto wide_c) {
+        constexpr bool WIDE = decltype(wide_c)::value;
+        using RB = RowBatch<B, UNIT, XC, 1>;
+        int rb = wave * SLOTS;
+        if (rb >= n) return;
+        RB ga, ua, gb, ub;
+        load_batch<B, UNIT, LPR, XC, 1, WIDE>(ga, mg, rb, true, wpr, gpr, slot, unit, gidx, nu, lane);
+        load_batch<B, UNIT, LPR, XC, 1, WIDE>(ua, mu, rb, true, wpr, gpr, slot, unit, gidx, nu, lane);
+        // The first batch's weight loads go out before the activation set-up.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < XC; ++c)
+            prep_xunit<B, UNIT>(xr, unit[c] < nu ? (uint32_t)(unit[c] * UNIT * 2) : (uint32_t)k * 2u, xu[c]);
+        auto finish = [&](const RB& g_b, const RB& u_b, int at) {
+            float g[1] = {0.f}, u[1] = {0.f};
+            accumulate_batch<B, UNIT, LPR, XC, 1, WIDE>(g_b, xu, g, slot, gpr, gidx);
+            accumulate_batch<B, UNIT, LPR, XC, 1, WIDE>(u_b, xu, u, slot, gpr, gidx);
+            store_glu<LPR>(g[0], u[0], hr, at, n, slot, j);
+        };
+        while (true) {
+            int nxt = rb + stride;
+            load_batch<B, UNIT, LPR, XC, 1, WIDE>(gb, mg, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
+            load_batch<B, UNIT, LPR, XC, 1, WIDE>(ub, mu, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(ga, ua, rb);
+            rb = nxt;
+            if (rb >= n) break;
+            nxt = rb + stride;
+            load_batch<B, UNIT, LPR, XC, 1, WIDE>(ga, mg, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
+            load_batch<B, UNIT, LPR, XC, 1, WIDE>(ua, mu, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(gb, ub, rb);
+            rb = nxt;
+            if (rb >= n) break;
+        }
+    };
+    if (wide_scales_ok<LPR, 1>(Sg, Mg, gpr) && wide_scales_ok<LPR, 1>(Su, Mu, gpr))
+        body(std::true_type{});
+    else
+        body(std::false_type{});
+}
+
 // Multi-row product over row segments.  Segment e covers activation rows
 // [offsets[e], offsets[e+1]) (clamped to [0, m_total]; [0, m_total) when
 // offsets is NULL) and multiplies them by weight matrix e of a stack
@@ -729,6 +815,24 @@ hipError_t launch_rows_t(const RowsArgs& a, const RowsShape& sh, hipStream_t st)
                            a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group, sh.pairs);
     }
     return hipGetLastError();
+}
+
+template <int B, int UNIT, int LPR, int XC>
+hipError_t launch_glu_t(const GluArgs& a, const GemvShape& sh, hipStream_t st) {
+    constexpr auto kern = gemv_glu_kernel<B, UNIT, LPR, XC>;
+    const int grid = persistent_grid(sh.work, sh.cus, blocks_per_cu<kern>(), sh.waves_per_cu);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, a.wg, a.sg, a.mg, a.wu, a.su, a.mu, a.x, a.h,
+                       a.n, a.k, a.group);
+    return hipGetLastError();
+}
+
+template <int B, int UNIT>
+hipError_t launch_glu_unit(const GluArgs& a, const GemvShape& sh, hipStream_t st) {
+#define X(L, C) \
+    if (sh.lpr == L && sh.xc == C) return launch_glu_t<B, UNIT, L, C>(a, sh, st);
+    QMM_GLU_SHAPES(X)
+#undef X
+    return hipErrorInvalidValue;
 }
 
 template <int B, int UNIT>

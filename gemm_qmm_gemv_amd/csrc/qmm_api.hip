@@ -43,6 +43,9 @@ hipError_t launch_batched(const BatchArgs& a, const GemvShape& sh, hipStream_t s
 hipError_t launch_rows(const RowsArgs& a, const RowsShape& sh, hipStream_t st) {
     QMM_BITS_SWITCH(a.bits, launch_rows_bits, a, sh, st)
 }
+hipError_t launch_glu(const GluArgs& a, const GemvShape& sh, hipStream_t st) {
+    QMM_BITS_SWITCH(a.bits, launch_glu_bits, a, sh, st)
+}
 
 thread_local char g_err[512] = "";
 
@@ -359,6 +362,31 @@ qmm_status qmm_gemv(const void* w_packed, const void* scales, const void* mins, 
                static_cast<const uint16_t*>(mins), static_cast<const uint16_t*>(x), y, (int)n, (int)k,
                group_size, bits};
     return launched(launch_gemv(a, sh, as_stream(stream)), "qmm_gemv");
+}
+
+qmm_status qmm_gemv_swiglu(const void* gate_w, const void* gate_scales, const void* gate_mins,
+                           const void* up_w, const void* up_scales, const void* up_mins, const void* x,
+                           float* h, int64_t n, int64_t k, int bits, int group_size, void* stream) {
+    qmm_status st = check_format(n, k, bits, group_size);
+    if (st != QMM_OK) return st;
+    if (n == 0) return ok();
+    if ((st = check_weight_ptrs(gate_w, gate_scales, gate_mins, bits)) != QMM_OK) return st;
+    if ((st = check_weight_ptrs(up_w, up_scales, up_mins, bits)) != QMM_OK) return st;
+    if (!x || !h) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x or h");
+    if (!aligned(x, 16) || !aligned(h, 16)) return fail(QMM_ERR_MISALIGNED, "x or h not 16-byte aligned");
+    int cus = 0;
+    if ((st = device_cus(&cus)) != QMM_OK) return st;
+    GemvShape sh = plan_gemv(n, k, bits, group_size, cus);
+    if (sh.multipass || !glu_shape_supported(sh.lpr, sh.xc))
+        return fail(QMM_ERR_UNSUPPORTED, "k=%lld needs more than one pass of the fused gate/up kernel",
+                    (long long)k);
+    sh.u = 1;
+    sh.work = (n + 64 / sh.lpr - 1) / (64 / sh.lpr);
+    GluArgs a{static_cast<const uint32_t*>(gate_w), static_cast<const uint16_t*>(gate_scales),
+              static_cast<const uint16_t*>(gate_mins), static_cast<const uint32_t*>(up_w),
+              static_cast<const uint16_t*>(up_scales), static_cast<const uint16_t*>(up_mins),
+              static_cast<const uint16_t*>(x), h, (int)n, (int)k, group_size, bits};
+    return launched(launch_glu(a, sh, as_stream(stream)), "qmm_gemv_swiglu");
 }
 
 size_t qmm_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits, int group_size) {

@@ -56,6 +56,19 @@ inline int blocks_per_cu() {
     return cached;
 }
 
+// Fused gate/up projection: h = silu(Wg x) * (Wu x).
+struct GluArgs {
+    const uint32_t* wg;
+    const uint16_t* sg;
+    const uint16_t* mg;
+    const uint32_t* wu;
+    const uint16_t* su;
+    const uint16_t* mu;
+    const uint16_t* x;
+    float* h;
+    int n, k, group, bits;
+};
+
 struct RowsArgs {
     const uint32_t* w;
     const uint16_t* s;
@@ -125,6 +138,15 @@ struct BatchArgs {
 
 // Batched launches choose the lanes per row per descriptor at run time;
 // compiled shapes are (units per lane, rows per slot).
+// (lanes per row, units per lane) of the fused gate/up kernel: single pass,
+// one row per slot and iteration (two with both matrices).
+#define QMM_GLU_SHAPES(X) X(16, 1) X(32, 1) X(64, 1) X(64, 2)
+constexpr bool glu_shape_supported(int lpr, int xc) {
+#define X(L, C) if (lpr == L && xc == C) return true;
+    QMM_GLU_SHAPES(X)
+#undef X
+    return false;
+}
 #define QMM_BATCHED_SHAPES(X) X(1, 1) X(1, 2) X(2, 1)
 
 // Multi-row kernel: at most two activation units per lane in flight (MR*XC
@@ -166,10 +188,12 @@ constexpr bool rows_shape_supported(int lpr, int xc, int mr) {
 template <int B> hipError_t launch_gemv_bits(const GemvArgs& a, const GemvShape& sh, hipStream_t st);
 template <int B> hipError_t launch_batched_bits(const BatchArgs& a, const GemvShape& sh, hipStream_t st);
 template <int B> hipError_t launch_rows_bits(const RowsArgs& a, const RowsShape& sh, hipStream_t st);
+template <int B> hipError_t launch_glu_bits(const GluArgs& a, const GemvShape& sh, hipStream_t st);
 #define QMM_DECLARE_BITS(B)                                                                      \
     template <> hipError_t launch_gemv_bits<B>(const GemvArgs&, const GemvShape&, hipStream_t);  \
     template <> hipError_t launch_batched_bits<B>(const BatchArgs&, const GemvShape&, hipStream_t); \
-    template <> hipError_t launch_rows_bits<B>(const RowsArgs&, const RowsShape&, hipStream_t);
+    template <> hipError_t launch_rows_bits<B>(const RowsArgs&, const RowsShape&, hipStream_t);   \
+    template <> hipError_t launch_glu_bits<B>(const GluArgs&, const GemvShape&, hipStream_t);
 QMM_DECLARE_BITS(2)
 QMM_DECLARE_BITS(3)
 QMM_DECLARE_BITS(4)

@@ -8,6 +8,7 @@ import numpy as np
 import torch
 
 from . import (GemvDesc, qmm_gemm, qmm_gemm_workspace_bytes, qmm_gemv, qmm_gemv_batch_prepare,
+               qmm_gemv_swiglu,
                qmm_gemv_batched, qmm_moe_gemm, qmm_unpack)
 
 
@@ -36,6 +37,18 @@ def gemv(dq: dict, x: torch.Tensor, y: torch.Tensor | None = None, stream=None) 
     qmm_gemv(dq["w"], dq["scales"], dq["mins"], x, y, dq["n"], dq["k"], dq["bits"], dq["group"],
              stream=stream)
     return y
+
+
+def gemv_swiglu(dg: dict, du: dict, x: torch.Tensor, h: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """h = silu(Wg x) * (Wu x) in one launch (both matrices in one format)."""
+    assert dg["n"] == du["n"] and dg["k"] == du["k"]
+    assert dg["bits"] == du["bits"] and dg["group"] == du["group"]
+    if h is None:
+        h = torch.empty(dg["n"], dtype=torch.float32, device=x.device)
+    qmm_gemv_swiglu(dg["w"], dg["scales"], dg["mins"], du["w"], du["scales"], du["mins"], x, h,
+                    dg["n"], dg["k"], dg["bits"], dg["group"], stream=stream)
+    return h
 
 
 def gemm(dq: dict, x: torch.Tensor, y: torch.Tensor | None = None, workspace=None,

@@ -92,6 +92,25 @@ QMM_API qmm_status qmm_gemv(const void *w_packed, const void *scales, const void
                     const void *x, float *y, int64_t n, int64_t k,
                     int bits, int group_size, void *stream);
 
+/* Fused gate/up projection of a feed-forward block (decode, M = 1):
+ *   h[n] = silu(g[n]) * u[n],  g = Wg x,  u = Wu x,  silu(v) = v / (1 + e^-v).
+ * Pages: "BaseRT claims fastest Apple Silicon inference", section "What
+ * BaseRT does differently" (kernel fusion removes a launch and a global
+ * memory round trip per fusion); "BaseRT: Best-in-Class LLM Inference on
+ * Apple Silicon via Native Metal", section "Metodologia" (operator sequences
+ * of feed-forward blocks fused into one kernel).
+ * Both matrices are n x k in the same format (bits, group_size) with their
+ * own scale and min arrays; g and u stay in registers, only h is written.
+ *   x fp16 [k]      h fp32 [n] (written)
+ * k must fit one pass of the decode kernel (k <= 8192 codes for 64-multiple
+ * groups, 4096 for 32-code groups and for fp16 weights), else
+ * QMM_ERR_UNSUPPORTED.                                                      */
+QMM_API qmm_status qmm_gemv_swiglu(const void *gate_w, const void *gate_scales,
+                                   const void *gate_mins, const void *up_w,
+                                   const void *up_scales, const void *up_mins,
+                                   const void *x, float *h, int64_t n, int64_t k,
+                                   int bits, int group_size, void *stream);
+
 /* Prefill GEMM (M >= 1): y[i][n] = sum_k (s*q + m)[n][k] * x[i][k].
  * Pages: "BaseRT claims fastest Apple Silicon inference", section "What
  * BaseRT does differently" (GEMM kernels for prefill where M > 1); "BaseRT:

@@ -25,6 +25,8 @@ Pinning (what each function is checked against, in ``tests/test_oracle_pins.py``
                          exact power-of-two scaling and sign symmetry.
   * qmm_sample        -- the same rows of full qmm.
   * moe               -- per-expert numpy matmuls over the expert's rows.
+  * silu               -- printed values of the logistic function at +-1,
+                         the odd-part identity silu(v) - silu(-v) = v, limits.
   * fp16 weights (bits 16: the unquantized "Q16/FP16" format, no scales or
     mins) -- decoded by the pinned fp16 decoder and multiplied in float64
     with numpy; pinned against the Q8 path (integer codes with scale 1 and
@@ -295,6 +297,14 @@ def _moe_f16(w, x, x_rows, off, n_experts: int, n: int, k: int):
         yy, aa = _qmm_f16(we[e], x[xr[lo:hi]], n, k)
         y[lo:hi], a[lo:hi] = yy, aa
     return y, a
+
+
+def silu(v) -> np.ndarray:
+    """silu(v) = v / (1 + e^-v) = v * sigmoid(v), float64 (the gate of a
+    SwiGLU feed-forward block: h = silu(Wg x) * (Wu x))."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):  # e^-v -> inf gives the limit -0
+        return v / (1.0 + np.exp(-v))
 
 
 def within_tolerance(y, y_ref, a_ref, rel: float = 2e-3, abs_: float = 1e-5):

@@ -30,3 +30,17 @@ def assert_within(y_gpu, y_ref, a_ref, what: str) -> float:
     ratio = float(np.max(err / np.maximum(a_ref, 1e-30))) if err.size else 0.0
     print("[parity] %s: max |err|/a_ref = %.3e over %d outputs" % (what, ratio, err.size), flush=True)
     return ratio
+
+
+def glu_bound(g_ref, a_g, u_ref, a_u):
+    """Acceptance bound for h = silu(g) * u from the bounds of g and u.
+
+    With |dg| <= eg = REL_TOL * a_g + ABS_TOL (same for u) and |silu'| <= 1.1
+    everywhere, |silu(g + dg)(u + du) - silu(g) u| <= 1.1 eg (|u| + eu) +
+    |silu(g)| eu; fp32 evaluation of the exponential, division and product
+    adds a few ulp of |h| (bounded here by 1e-5 |h| + 1e-7)."""
+    import oracle
+    eg = REL_TOL * a_g + ABS_TOL
+    eu = REL_TOL * a_u + ABS_TOL
+    sg = oracle.silu(g_ref)
+    return 1.1 * eg * (np.abs(u_ref) + eu) + np.abs(sg) * eu + 1e-5 * np.abs(sg * u_ref) + 1e-7

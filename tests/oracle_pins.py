@@ -330,6 +330,18 @@ def check_f16_moe_per_expert():
         assert np.array_equal(y[p], wi[ex] @ xd[x_rows[p]]), p
 
 
+def check_silu():
+    # sigmoid(1) = 1 / (1 + 1/e) = 0.7310585786300049 (and 1 - that at -1).
+    v = oracle.silu(np.array([1.0, -1.0, 0.0, 40.0, -40.0, 2.5]))
+    assert abs(v[0] - 0.7310585786300049) < 1e-15
+    assert abs(v[1] + 0.2689414213699951) < 1e-15
+    assert v[2] == 0.0
+    assert abs(v[3] - 40.0) < 1e-12 and abs(v[4]) < 1e-15
+    # v * sigmoid(v) - (-v) * sigmoid(-v) = v (sigmoid(v) + sigmoid(-v) = 1).
+    z = np.linspace(-12, 12, 97)
+    assert np.allclose(oracle.silu(z) - oracle.silu(-z), z, rtol=0, atol=1e-13)
+
+
 ALL_CHECKS = [
     check_fp16_exhaustive,
     check_hand_vectors,
@@ -347,4 +359,5 @@ ALL_CHECKS = [
     check_f16_one_hot_and_layout,
     check_f16_exact_integer,
     check_f16_moe_per_expert,
+    check_silu,
 ]

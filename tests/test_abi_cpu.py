@@ -118,6 +118,19 @@ def test_gemm_and_moe_argument_checks(lib):
     assert lib.qmm_unpack(p(A16), p(A16), 4, 64, 16, None) == qmm.QMM_ERR_UNSUPPORTED
 
 
+def test_swiglu_argument_checks(lib):
+    p = ctypes.c_void_p
+    f = lib.qmm_gemv_swiglu
+    args = [p(A16)] * 6 + [p(A16), p(A16)]
+    assert f(*args, 64, 128, 4, 64, None) in (qmm.QMM_ERR_DEVICE, qmm.QMM_OK)
+    assert f(*args, 0, 128, 4, 64, None) == qmm.QMM_OK
+    assert f(*([p(A16)] * 6), p(A16), None, 64, 128, 4, 64, None) == qmm.QMM_ERR_INVALID_ARGUMENT
+    assert f(*([p(A16)] * 6), p(A16), p(A16 + 4), 64, 128, 4, 64, None) == qmm.QMM_ERR_MISALIGNED
+    bad_up = [p(A16)] * 3 + [None] + [p(A16)] * 2 + [p(A16), p(A16)]
+    assert f(*bad_up, 64, 128, 4, 64, None) == qmm.QMM_ERR_INVALID_ARGUMENT
+    assert f(*args, 64, 128, 7, 64, None) == qmm.QMM_ERR_UNSUPPORTED
+
+
 def test_fp16_weights_need_no_scales(lib):
     import torch
     if torch.cuda.is_available():
