@@ -20,8 +20,8 @@ Also measured (outside the timed region, reported in the same JSON line):
   * the Llama-3.2-3B-shaped bit-width sweep (Q2/Q3/Q4/Q5/Q6/Q8 and fp16
     weights);
   * Llama-3.2-1B-shaped prefill GEMMs at M = 128 and 512: TFLOP/s, % MFMA,
-    with Q4 weights and again with fp16 weights, the dense fp16 library
-    matmul of each shape beside them;
+    with Q4 weights and again with fp16 weights, and at M = 2048 with fp32
+    and fp16 output, the dense fp16 library matmul of each shape beside them;
   * the fused gate/up projection (silu(Wg x) * (Wu x), one launch) against
     two GEMV launches, Q4, on Qwen3-0.6B and Llama-3.2-3B shapes;
   * Qwen3-30B-A3B-shaped MoE expert projections at 1 and 16 tokens;
@@ -357,7 +357,12 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
     # weights through the same kernel family.
     for bits in (4, 16):
         out["prefill_llama3.2_1b_" + ("q4" if bits == 4 else "fp16")] = prefill_layers(
-            torch, qmm, configs, inputs, tensors, timer, bits)
+            torch, qmm, configs, inputs, tensors, timer, bits, configs.PREFILL_M)
+    # 2048-token prefill, Q4, with fp32 and with fp16 output.
+    out["prefill_llama3.2_1b_q4_pp2048"] = prefill_layers(
+        torch, qmm, configs, inputs, tensors, timer, 4, (configs.PREFILL_M_LONG,))
+    out["prefill_llama3.2_1b_q4_pp2048_fp16_out"] = prefill_layers(
+        torch, qmm, configs, inputs, tensors, timer, 4, (configs.PREFILL_M_LONG,), out_fp16=True)
 
     # Fused gate/up projection with the SiLU-gated product vs two GEMV
     # launches (Q4, 8 rotating copies of the pair so the weights stream
@@ -426,20 +431,21 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
     return out
 
 
-def prefill_layers(torch, qmm, configs, inputs, tensors, timer, bits):
+def prefill_layers(torch, qmm, configs, inputs, tensors, timer, bits, ms_list, out_fp16=False):
     """Per-shape and per-layer times of the prefill GEMMs at each M (weights
-    at `bits`: 4, or 16 for fp16), with the dense fp16 library matmul of the
-    same shape timed beside them for context."""
+    at `bits`: 4, or 16 for fp16; fp32 output, or fp16 with out_fp16), with
+    the dense fp16 library matmul of the same shape timed beside them for
+    context."""
     G = configs.GROUP
     pre = {}
-    for m in configs.PREFILL_M:
+    for m in ms_list:
         tot_flops, tot_ms, dense_ms = 0.0, 0.0, 0.0
         row = {}
         for j, (pname, n, k) in enumerate(configs.LLAMA32_1B_PROJ):
             q = inputs.quantized_matrix(n, k, bits, G, key=(configs.CFG_PREFILL, 0, j, bits))
             dq = tensors.upload_matrix(q)
             xm = tensors.device_tensor(inputs.activation_rows(m, k, key=(configs.CFG_PREFILL, 0, j, 4, m)))
-            ym = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            ym = torch.empty((m, n), dtype=torch.float16 if out_fp16 else torch.float32, device="cuda")
             need = qmm.qmm_gemm_workspace_bytes(m, n, k, bits, G)
             ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
             # Device-side copies of the same matrix, rotated so that the
@@ -453,7 +459,7 @@ def prefill_layers(torch, qmm, configs, inputs, tensors, timer, bits):
             ii = [0]
 
             def call():
-                tensors.gemm(cps[ii[0] % ncp], xm, ym, workspace=ws)
+                tensors.gemm(cps[ii[0] % ncp], xm, ym, workspace=ws, out_fp16=out_fp16)
                 ii[0] += 1
             ms = timer(call, reps=ncp)
             fl = 2.0 * m * n * k
@@ -475,7 +481,8 @@ def prefill_layers(torch, qmm, configs, inputs, tensors, timer, bits):
         pre["m%d" % m] = {"layer_us": round(tot_ms * 1e3, 2), "TFLOPs": round(tf, 1),
                           "pct_mfma": round(100 * tf / MFMA_FP16_PEAK_TFLOPS, 2),
                           "dense_fp16_matmul_layer_us": round(dense_ms * 1e3, 2), "shapes": row}
-        log("prefill b%d m=%d: %.1f TFLOP/s" % (bits, m, tf))
+        log("prefill b%d m=%d%s: %.1f TFLOP/s (layer %.1f us, dense fp16 %.1f us)"
+            % (bits, m, " fp16-out" if out_fp16 else "", tf, tot_ms * 1e3, dense_ms * 1e3))
     return pre
 
 

@@ -18,7 +18,7 @@ import os
 __all__ = [
     "QmmError", "library_path", "load",
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
-    "qmm_gemv_batch_prepare", "qmm_gemv_batched", "GemvDesc", "qmm_gemv_swiglu",
+    "qmm_gemv_batch_prepare", "qmm_gemv_batched", "GemvDesc", "qmm_gemv_swiglu", "qmm_gemm_f16out",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
     "QMM_OK", "QMM_ERR_INVALID_ARGUMENT", "QMM_ERR_UNSUPPORTED", "QMM_ERR_MISALIGNED",
     "QMM_ERR_DEVICE", "EXPORTED_SYMBOLS",
@@ -32,7 +32,7 @@ QMM_ERR_DEVICE = 4
 
 EXPORTED_SYMBOLS = (
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
-    "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu",
+    "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
 )
 
@@ -104,6 +104,7 @@ def load():
     lib.qmm_gemv.argtypes = [p, p, p, p, p, i64, i64, ci, ci, p]
     lib.qmm_gemm.argtypes = [p, p, p, p, p, i64, i64, i64, ci, ci, p, sz, p]
     lib.qmm_gemv_swiglu.argtypes = [p, p, p, p, p, p, p, p, i64, i64, ci, ci, p]
+    lib.qmm_gemm_f16out.argtypes = [p, p, p, p, p, i64, i64, i64, ci, ci, p, sz, p]
     lib.qmm_gemm_workspace_bytes.argtypes = [i64, i64, i64, ci, ci]
     lib.qmm_gemm_workspace_bytes.restype = sz
     lib.qmm_moe_gemm.argtypes = [p, p, p, p, p, i64, p, p, i64, i64, i64, i64, ci, ci, p]
@@ -112,7 +113,7 @@ def load():
     lib.qmm_gemv_batched.argtypes = [p, p, i64, ci, ci, p]
     lib.qmm_get_plan.argtypes = [ci, i64, i64, i64, ci, ci, ci, sz, ctypes.POINTER(_Plan)]
     for f in ("qmm_gemv", "qmm_gemm", "qmm_moe_gemm", "qmm_unpack", "qmm_get_plan",
-              "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu"):
+              "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out"):
         getattr(lib, f).restype = ci
     lib.qmm_status_string.argtypes = [ci]
     lib.qmm_status_string.restype = ctypes.c_char_p
@@ -171,6 +172,15 @@ def qmm_gemv_swiglu(gate_w, gate_scales, gate_mins, up_w, up_scales, up_mins, x,
                                   _addr(up_scales), _addr(up_mins), _addr(x), _addr(h), int(n),
                                   int(k), int(bits), int(group_size), _stream(stream)),
            "qmm_gemv_swiglu")
+
+
+def qmm_gemm_f16out(w_packed, scales, mins, x, y, m, n, k, bits, group_size, workspace=None,
+                    workspace_bytes=0, stream=None) -> None:
+    """As qmm_gemm with y fp16 [m][n] (each sum rounded once); asynchronous."""
+    _check(load().qmm_gemm_f16out(_addr(w_packed), _addr(scales), _addr(mins), _addr(x), _addr(y),
+                                  int(m), int(n), int(k), int(bits), int(group_size), _addr(workspace),
+                                  int(workspace_bytes), _stream(stream)),
+           "qmm_gemm_f16out")
 
 
 def qmm_gemm(w_packed, scales, mins, x, y, m, n, k, bits, group_size, workspace=None,

@@ -50,6 +50,9 @@ LLAMA32_1B_PROJ = [
     ("down_proj", 2048, 8192),
 ]
 PREFILL_M = (128, 512)
+# Longer prefill (2048 tokens, the length vendor prefill figures use), timed
+# with fp32 and with fp16 output.
+PREFILL_M_LONG = 2048
 
 # Qwen3-30B-A3B-shaped experts, Q4.
 MOE = {"n_experts": 128, "top_k": 8, "hidden": 2048, "inter": 768,

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
                                                    float* __restrict__ Y, float* __restrict__ P,
                                                    int M, int N, int K, uint64_t gmul, int gsh,
                                                    int grid_m, int grid_n, int split,
-                                                   int steps_per_split) {
+                                                   int steps_per_split, int out16) {
     constexpr int TILE_M = 32 * MS;
     constexpr int THREADS = 128 * WN;
     constexpr int NS = BN / (32 * WN);                   // 32-column fragments per wave
@@ -401,9 +401,13 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
         // element outside the matrix gets an offset past its end and is
         // dropped, so the epilogue has no branches (a branch per element
         // would wait for each LDS read in turn).
+        // fp16 output (out16, unsplit only: split partials stay fp32 and the
+        // reduction rounds): each sum rounded to nearest even, 2-byte stores.
         const float* src = red + ((wn * 2 + (1 - wk)) * GIVE) * 16 * 64 + lane;
         float* out = (split == 1) ? Y : P + (size_t)sk * M * N;
-        const uint32_t out_bytes = (uint32_t)M * (uint32_t)N * 4u;
+        const bool half_out = out16 && split == 1;
+        const uint32_t esz = half_out ? 2u : 4u;
+        const uint32_t out_bytes = (uint32_t)M * (uint32_t)N * esz;
         const rsrc_t orr = make_rsrc(out, out_bytes);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
@@ -417,22 +421,30 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * kh + (v & 3);
-                const uint32_t off = (row < M && c < N) ? ((uint32_t)row * (uint32_t)N + (uint32_t)c) * 4u : out_bytes;
-                buffer_store_f32(acc[i][ns][v] + part[v], orr, off);
+                const uint32_t off = (row < M && c < N) ? ((uint32_t)row * (uint32_t)N + (uint32_t)c) * esz : out_bytes;
+                const float sum = acc[i][ns][v] + part[v];
+                if (half_out)
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (f16)sum), orr, off, 0, 0);
+                else
+                    buffer_store_f32(sum, orr, off);
             }
         }
     }
 }
 
-// y = sum over splits of the partial sums, in split order.
+// y = sum over splits of the partial sums, in split order (fp32, or rounded
+// to fp16 when out16).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P,
                                                             float* __restrict__ Y, int64_t count,
-                                                            int split) {
+                                                            int split, int out16) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= count) return;
     float v = P[i];
     for (int s = 1; s < split; ++s) v += P[(size_t)s * count + i];
-    Y[i] = v;
+    if (out16)
+        reinterpret_cast<f16*>(Y)[i] = (f16)v;
+    else
+        Y[i] = v;
 }
 
 // floor(n / d) = (n * mul) >> shift for every n < 2^31: shift = 31 + ceil(log2 d),
@@ -456,12 +468,12 @@ static hipError_t launch_gemm_t(const GemmArgs& a, const GemmShape& sh, hipStrea
     const int grid = 8 * ((tiles + 7) / 8);
     hipLaunchKernelGGL((gemm_kernel<B, MS, WN>), dim3(grid), dim3(128 * WN), 0, st, a.w, a.s, a.m, a.x, a.y,
                        a.partial, a.m_rows, a.n, a.k, gm.mul, gm.shift, sh.grid_m, sh.grid_n,
-                       sh.split, sh.k_tiles_per_split);
+                       sh.split, sh.k_tiles_per_split, a.out16);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || sh.split == 1) return err;
     const int64_t count = (int64_t)a.m_rows * a.n;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st,
-                       a.partial, a.y, count, sh.split);
+                       a.partial, a.y, count, sh.split, a.out16);
     return hipGetLastError();
 }
 

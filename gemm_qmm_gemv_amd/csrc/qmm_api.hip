@@ -398,9 +398,16 @@ size_t qmm_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits, int g
     return need;
 }
 
-qmm_status qmm_gemm(const void* w_packed, const void* scales, const void* mins, const void* x,
-                    float* y, int64_t m, int64_t n, int64_t k, int bits, int group_size,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// qmm_gemm and qmm_gemm_f16out.  fp16 output always takes the MFMA kernel
+// (its epilogue does the rounding); fp32 output routes m <= 2 to the GEMV
+// kernels.
+qmm_status gemm_common(const void* w_packed, const void* scales, const void* mins, const void* x,
+                       void* y, int64_t m, int64_t n, int64_t k, int bits, int group_size,
+                       void* workspace, size_t workspace_bytes, void* stream, bool out16) {
     qmm_status st = check_format(n, k, bits, group_size);
     if (st != QMM_OK) return st;
     if (m < 0) return fail(QMM_ERR_INVALID_ARGUMENT, "m=%lld is negative", (long long)m);
@@ -421,20 +428,39 @@ qmm_status qmm_gemm(const void* w_packed, const void* scales, const void* mins, 
     const uint16_t* s = static_cast<const uint16_t*>(scales);
     const uint16_t* mn = static_cast<const uint16_t*>(mins);
     const uint16_t* xx = static_cast<const uint16_t*>(x);
-    if (m == 1) {
+    float* yf = static_cast<float*>(y);
+    if (!out16 && m == 1) {
         const GemvShape sh = plan_gemv(n, k, bits, group_size, cus);
-        GemvArgs a{w, s, mn, xx, y, (int)n, (int)k, group_size, bits};
+        GemvArgs a{w, s, mn, xx, yf, (int)n, (int)k, group_size, bits};
         return launched(launch_gemv(a, sh, as_stream(stream)), "qmm_gemm (gemv)");
     }
-    if (m <= ROWS_KERNEL_MAX_M) {
+    if (!out16 && m <= ROWS_KERNEL_MAX_M) {
         const RowsShape sh = plan_rows(m, n, k, bits, group_size, cus, 1);
-        RowsArgs a{w, s, mn, xx, nullptr, (int)m, nullptr, 1, (int)m, y, (int)n, (int)k, group_size, bits};
+        RowsArgs a{w, s, mn, xx, nullptr, (int)m, nullptr, 1, (int)m, yf, (int)n, (int)k, group_size, bits};
         return launched(launch_rows(a, sh, as_stream(stream)), "qmm_gemm (rows)");
     }
     const GemmShape sh = plan_gemm(m, n, k, cus, workspace ? workspace_bytes : 0, nullptr);
-    GemmArgs a{w, s, mn, xx, y, sh.split > 1 ? static_cast<float*>(workspace) : nullptr, (int)m, (int)n,
-               (int)k, group_size, bits};
-    return launched(launch_gemm(a, sh, as_stream(stream)), "qmm_gemm");
+    GemmArgs a{w, s, mn, xx, yf, sh.split > 1 ? static_cast<float*>(workspace) : nullptr, (int)m, (int)n,
+               (int)k, group_size, bits, out16 ? 1 : 0};
+    return launched(launch_gemm(a, sh, as_stream(stream)), out16 ? "qmm_gemm_f16out" : "qmm_gemm");
+}
+
+}  // namespace
+
+extern "C" {
+
+qmm_status qmm_gemm(const void* w_packed, const void* scales, const void* mins, const void* x,
+                    float* y, int64_t m, int64_t n, int64_t k, int bits, int group_size,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    return gemm_common(w_packed, scales, mins, x, y, m, n, k, bits, group_size, workspace,
+                       workspace_bytes, stream, false);
+}
+
+qmm_status qmm_gemm_f16out(const void* w_packed, const void* scales, const void* mins, const void* x,
+                           void* y, int64_t m, int64_t n, int64_t k, int bits, int group_size,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    return gemm_common(w_packed, scales, mins, x, y, m, n, k, bits, group_size, workspace,
+                       workspace_bytes, stream, true);
 }
 
 qmm_status qmm_moe_gemm(const void* w_packed, const void* scales, const void* mins, const void* x,

@@ -99,6 +99,7 @@ struct GemmArgs {
     float* y;
     float* partial;  // split-K partial sums [split][m][n], or null when split == 1
     int m_rows, n, k, group, bits;
+    int out16;       // y holds fp16 [m][n] (else fp32)
 };
 
 struct GemmShape {

@@ -7,7 +7,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (GemvDesc, qmm_gemm, qmm_gemm_workspace_bytes, qmm_gemv, qmm_gemv_batch_prepare,
+from . import (GemvDesc, qmm_gemm, qmm_gemm_f16out, qmm_gemm_workspace_bytes, qmm_gemv, qmm_gemv_batch_prepare,
                qmm_gemv_swiglu,
                qmm_gemv_batched, qmm_moe_gemm, qmm_unpack)
 
@@ -52,16 +52,19 @@ def gemv_swiglu(dg: dict, du: dict, x: torch.Tensor, h: torch.Tensor | None = No
 
 
 def gemm(dq: dict, x: torch.Tensor, y: torch.Tensor | None = None, workspace=None,
-         stream=None) -> torch.Tensor:
+         stream=None, out_fp16: bool = False) -> torch.Tensor:
+    """Y = X W^T: fp32 output, or fp16 (qmm_gemm_f16out) with out_fp16."""
     m = x.shape[0]
     if y is None:
-        y = torch.empty((m, dq["n"]), dtype=torch.float32, device=x.device)
+        y = torch.empty((m, dq["n"]), dtype=torch.float16 if out_fp16 else torch.float32,
+                        device=x.device)
     if workspace is None:
         need = qmm_gemm_workspace_bytes(m, dq["n"], dq["k"], dq["bits"], dq["group"])
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device) if need else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    qmm_gemm(dq["w"], dq["scales"], dq["mins"], x, y, m, dq["n"], dq["k"], dq["bits"],
-             dq["group"], workspace=workspace, workspace_bytes=ws_bytes, stream=stream)
+    fn = qmm_gemm_f16out if out_fp16 else qmm_gemm
+    fn(dq["w"], dq["scales"], dq["mins"], x, y, m, dq["n"], dq["k"], dq["bits"],
+       dq["group"], workspace=workspace, workspace_bytes=ws_bytes, stream=stream)
     return y
 
 

@@ -129,6 +129,19 @@ QMM_API qmm_status qmm_gemm(const void *w_packed, const void *scales, const void
                     int bits, int group_size, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/* Prefill GEMM with fp16 output: y[i][n] as qmm_gemm, rounded once from the
+ * fp32 sums to fp16 (nearest even; beyond the fp16 range +-inf).  Halves the
+ * output bytes for long prefills ("BaseRT: Best-in-Class LLM Inference on
+ * Apple Silicon via Native Metal", section "Resultados": prefill measured at
+ * 2048 tokens).  Every m runs on the matrix-core kernel; workspace as for
+ * qmm_gemm (split partial sums stay fp32; qmm_gemm_workspace_bytes gives the
+ * preferred size for m > 2, none is needed below that).
+ *   y  fp16 [m][n] (written), 16-byte aligned.                             */
+QMM_API qmm_status qmm_gemm_f16out(const void *w_packed, const void *scales,
+                                   const void *mins, const void *x, void *y, int64_t m,
+                                   int64_t n, int64_t k, int bits, int group_size,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* Many independent decode GEMVs in one launch.
  * Pages: "BaseRT claims fastest Apple Silicon inference", section "What
  * BaseRT does differently" (operations other runtimes dispatch separately

@@ -136,3 +136,69 @@ def test_gemm_prefill_config_sampled(m, proj):
     y_ref, a_ref = oracle.qmm_sample(q["w"], q["scales"], q["mins"], x, k, 4, configs.GROUP, rm, rn)
     assert_within(y[rm, rn], y_ref, a_ref, "prefill m%d %s" % (m, name))
     assert np.all(np.isfinite(y))
+
+
+def _run_gemm_f16(q, x, workspace="auto"):
+    import torch
+    from gemm_qmm_gemv_amd import tensors
+    dq = tensors.upload_matrix(q)
+    xd = tensors.device_tensor(x)
+    ws = None if workspace == "auto" else workspace
+    if workspace is None:
+        ws = torch.empty(0, dtype=torch.uint8, device="cuda")
+    y = tensors.gemm(dq, xd, workspace=ws, out_fp16=True)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("bits", (2, 4, 8, 16))
+@pytest.mark.parametrize("tile", (32, 64, 128))
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (2, 129, 512), (100, 300, 1024), (257, 384, 2048),
+                                   (130, 640, 4096)])
+def test_gemm_f16out_parity(monkeypatch, bits, tile, m, n, k):
+    monkeypatch.setenv("QMM_GEMM_TILE_M", str(tile))
+    q = inputs.quantized_matrix(n, k, bits, 64, key=(63, m, n, k, bits))
+    x = inputs.activation_rows(m, k, key=(63, m, n, k, bits))
+    announce("gemm-f16out", tile, bits, m, n, k)
+    y = _run_gemm_f16(q, x)
+    assert y.dtype == np.float16
+    y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, 64)
+    assert_within(y, y_ref, a_ref, "gemm f16out tile%d b%d m%d %dx%d" % (tile, bits, m, n, k),
+                  fp16_out=True)
+
+
+@pytest.mark.parametrize("bits", (4, 16))
+@pytest.mark.parametrize("split", (1, 3))
+def test_gemm_f16out_is_the_rounded_fp32_result(monkeypatch, bits, split):
+    # Same plan, same sums: the fp16 output is the fp32 output rounded to
+    # nearest even, bit for bit (with and without a K split).
+    monkeypatch.setenv("QMM_GEMM_SPLIT", str(split))
+    m, n, k = 200, 520, 3072
+    q = inputs.quantized_matrix(n, k, bits, 64, key=(64, bits))
+    x = inputs.activation_rows(m, k, key=(64, bits))
+    announce("gemm-f16out-vs-fp32", bits, split)
+    y32 = _run_gemm(q, x)
+    y16 = _run_gemm_f16(q, x)
+    assert np.array_equal(y16.view(np.uint16), y32.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("out_fp16", (False, True), ids=("fp32_out", "fp16_out"))
+@pytest.mark.parametrize("proj", configs.LLAMA32_1B_PROJ, ids=[p[0] for p in configs.LLAMA32_1B_PROJ])
+def test_gemm_long_prefill_sampled(proj, out_fp16):
+    """2048-token prefill on the Llama-3.2-1B projections, full size, in the
+    benchmark's launch configuration; sampled outputs against the oracle."""
+    m = configs.PREFILL_M_LONG
+    name, n, k = proj
+    j = [p[0] for p in configs.LLAMA32_1B_PROJ].index(name)
+    q = inputs.quantized_matrix(n, k, 4, configs.GROUP, key=(configs.CFG_PREFILL, 0, j, 4))
+    x = inputs.activation_rows(m, k, key=(configs.CFG_PREFILL, 0, j, 4, m))
+    announce("gemm-prefill-long", m, name, out_fp16)
+    y = _run_gemm_f16(q, x) if out_fp16 else _run_gemm(q, x)
+    rng = np.random.default_rng(8)
+    rm = rng.integers(0, m, 256)
+    rn = rng.integers(0, n, 256)
+    rm[:4] = [0, m - 1, 0, m - 1]
+    rn[:4] = [0, 0, n - 1, n - 1]
+    y_ref, a_ref = oracle.qmm_sample(q["w"], q["scales"], q["mins"], x, k, 4, configs.GROUP, rm, rn)
+    assert_within(y[rm, rn], y_ref, a_ref, "prefill m%d %s" % (m, name), fp16_out=out_fp16)
+    assert np.all(np.isfinite(y))
