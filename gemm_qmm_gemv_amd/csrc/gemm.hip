@@ -405,30 +405,37 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
         // reduction rounds): each sum rounded to nearest even, 2-byte stores.
         const float* src = red + ((wn * 2 + (1 - wk)) * GIVE) * 16 * 64 + lane;
         float* out = (split == 1) ? Y : P + (size_t)sk * M * N;
-        const bool half_out = out16 && split == 1;
-        const uint32_t esz = half_out ? 2u : 4u;
-        const uint32_t out_bytes = (uint32_t)M * (uint32_t)N * esz;
-        const rsrc_t orr = make_rsrc(out, out_bytes);
+        auto store_all = [&](auto half_c) {
+            constexpr bool HALF = decltype(half_c)::value;
+            constexpr uint32_t ESZ = HALF ? 2u : 4u;
+            const uint32_t out_bytes = (uint32_t)M * (uint32_t)N * ESZ;
+            const rsrc_t orr = make_rsrc(out, out_bytes);
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            if (!keeps(f)) continue;
-            const int slot = NF > 1 ? f / 2 : 0;
-            const int i = f / NS, ns = f % NS;
-            const int c = n0 + 32 * NS * wn + 32 * ns + col;
-            float part[16];
+            for (int f = 0; f < NF; ++f) {
+                if (!keeps(f)) continue;
+                const int slot = NF > 1 ? f / 2 : 0;
+                const int i = f / NS, ns = f % NS;
+                const int c = n0 + 32 * NS * wn + 32 * ns + col;
+                float part[16];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) part[v] = src[(slot * 16 + v) * 64];
+                for (int v = 0; v < 16; ++v) part[v] = src[(slot * 16 + v) * 64];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * kh + (v & 3);
-                const uint32_t off = (row < M && c < N) ? ((uint32_t)row * (uint32_t)N + (uint32_t)c) * esz : out_bytes;
-                const float sum = acc[i][ns][v] + part[v];
-                if (half_out)
-                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (f16)sum), orr, off, 0, 0);
-                else
-                    buffer_store_f32(sum, orr, off);
+                for (int v = 0; v < 16; ++v) {
+                    const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * kh + (v & 3);
+                    const uint32_t off =
+                        (row < M && c < N) ? ((uint32_t)row * (uint32_t)N + (uint32_t)c) * ESZ : out_bytes;
+                    const float sum = acc[i][ns][v] + part[v];
+                    if constexpr (HALF)
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (f16)sum), orr, off, 0, 0);
+                    else
+                        buffer_store_f32(sum, orr, off);
+                }
             }
-        }
+        };
+        if (out16 && split == 1)
+            store_all(std::true_type{});
+        else
+            store_all(std::false_type{});
     }
 }
 
