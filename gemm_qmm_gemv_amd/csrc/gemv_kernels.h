@@ -729,13 +729,21 @@ __global__ __launch_bounds__(256) void gemv_batched_kernel(const BatchDesc* __re
     const int64_t i1 = total * (wave + 1) / nwaves;
     if (i0 >= i1) return;
 
-    // Last descriptor whose first item is <= i0 (binary search, wave-uniform).
-    int lo = 0, hi = count - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (D[mid].first <= i0) lo = mid; else hi = mid - 1;
-    }
-    int d = uniform(lo);
+    // Last descriptor whose first item is <= i0, in two rounds of 64 lanes:
+    // every S-th descriptor first (S = ceil(count / 64)), then the S after the
+    // chosen one.  Two dependent loads instead of a binary search's
+    // log2(count), which had delayed every wave's first weight load.  first
+    // is non-decreasing and D[0].first = 0 <= i0, so both ballots are
+    // non-empty.
+    const int S = (count + 63) / 64;
+    const bool in1 = lane * S < count;
+    const int64_t f1 = D[in1 ? lane * S : 0].first;
+    const uint64_t m1 = __ballot(in1 && f1 <= i0);
+    const int base = (63 - __clzll((long long)m1)) * S;
+    const bool in2 = lane < S && base + lane < count;
+    const int64_t f2 = D[in2 ? base + lane : base].first;
+    const uint64_t m2 = __ballot(in2 && f2 <= i0);
+    int d = uniform(base + (63 - __clzll((long long)m2)));
     int64_t i = i0;
     while (i < i1 && d < count) {
         // Descriptor fields, made explicitly wave-uniform: the table is read
