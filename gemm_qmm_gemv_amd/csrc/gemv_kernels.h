@@ -731,47 +731,66 @@ __global__ __launch_bounds__(256) void gemv_batched_kernel(const BatchDesc* __re
 
     // Last descriptor whose first item is <= i0, in two rounds of 64 lanes:
     // every S-th descriptor first (S = ceil(count / 64)), then the S after the
-    // chosen one.  Two dependent loads instead of a binary search's
-    // log2(count), which had delayed every wave's first weight load.  first
-    // is non-decreasing and D[0].first = 0 <= i0, so both ballots are
-    // non-empty.
+    // chosen one, each lane holding a whole candidate descriptor so that the
+    // chosen one needs no further load.  Two dependent loads instead of a
+    // binary search's log2(count) and a reload, which had delayed every
+    // wave's first weight load.  first is non-decreasing and D[0].first = 0
+    // <= i0, so both ballots are non-empty.
     const int S = (count + 63) / 64;
     const bool in1 = lane * S < count;
     const int64_t f1 = D[in1 ? lane * S : 0].first;
     const uint64_t m1 = __ballot(in1 && f1 <= i0);
     const int base = (63 - __clzll((long long)m1)) * S;
     const bool in2 = lane < S && base + lane < count;
-    const int64_t f2 = D[in2 ? base + lane : base].first;
-    const uint64_t m2 = __ballot(in2 && f2 <= i0);
-    int d = uniform(base + (63 - __clzll((long long)m2)));
+    const BatchDesc cand = D[in2 ? base + lane : base];
+    const uint64_t m2 = __ballot(in2 && cand.first <= i0);
+    const int win = uniform(63 - __clzll((long long)m2));
+    int d = base + win;
+    // Descriptor fields are made explicitly wave-uniform: the table is read
+    // through the vector path (the kernel writes memory), and the values feed
+    // buffer resources that must live in scalar registers.
+    auto lane_u64 = [&](uint64_t v) -> uint64_t {
+        const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, win);
+        const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), win);
+        return ((uint64_t)hi << 32) | lo;
+    };
+    BatchDesc bd;
+    bd.w = reinterpret_cast<const u32*>(lane_u64(reinterpret_cast<uint64_t>(cand.w)));
+    bd.s = reinterpret_cast<const uint16_t*>(lane_u64(reinterpret_cast<uint64_t>(cand.s)));
+    bd.m = reinterpret_cast<const uint16_t*>(lane_u64(reinterpret_cast<uint64_t>(cand.m)));
+    bd.x = reinterpret_cast<const uint16_t*>(lane_u64(reinterpret_cast<uint64_t>(cand.x)));
+    bd.y = reinterpret_cast<float*>(lane_u64(reinterpret_cast<uint64_t>(cand.y)));
+    bd.n = (int64_t)lane_u64((uint64_t)cand.n);
+    bd.k = (int64_t)lane_u64((uint64_t)cand.k);
+    bd.first = (int64_t)lane_u64((uint64_t)cand.first);
     int64_t i = i0;
-    while (i < i1 && d < count) {
-        // Descriptor fields, made explicitly wave-uniform: the table is read
-        // through the vector path (the kernel writes memory), and the values
-        // feed buffer resources that must live in scalar registers.
-        const BatchDesc& bd = D[d];
-        const int n = uniform((int)bd.n), k = uniform((int)bd.k);
-        const int64_t first = uniform(bd.first);
+    while (true) {
+        const int n = (int)bd.n, k = (int)bd.k;
+        const int64_t first = bd.first;
         const int lpr = batched_lanes_per_row<XC>(k / UNIT);
         const int rows = (64 / lpr) * U;
         const int64_t end = first + (n + rows - 1) / rows;
         if (i < end) {
             const int b0 = (int)(i - first);
             const int b1 = (int)((i1 < end ? i1 : end) - first);
-            const u32* w = uniform(bd.w);
-            const uint16_t* sp = uniform(bd.s);
-            const uint16_t* mp = uniform(bd.m);
-            const uint16_t* xp = uniform(bd.x);
-            float* yp = uniform(bd.y);
             if (lpr == 16)
-                gemv_run<B, UNIT, 16, XC, U>(w, sp, mp, xp, yp, n, k, group, b0, b1, lane, ystage);
+                gemv_run<B, UNIT, 16, XC, U>(bd.w, bd.s, bd.m, bd.x, bd.y, n, k, group, b0, b1, lane, ystage);
             else if (lpr == 32)
-                gemv_run<B, UNIT, 32, XC, U>(w, sp, mp, xp, yp, n, k, group, b0, b1, lane, ystage);
+                gemv_run<B, UNIT, 32, XC, U>(bd.w, bd.s, bd.m, bd.x, bd.y, n, k, group, b0, b1, lane, ystage);
             else
-                gemv_run<B, UNIT, 64, XC, U>(w, sp, mp, xp, yp, n, k, group, b0, b1, lane, ystage);
+                gemv_run<B, UNIT, 64, XC, U>(bd.w, bd.s, bd.m, bd.x, bd.y, n, k, group, b0, b1, lane, ystage);
             i = first + b1;
         }
-        ++d;
+        if (++d >= count || i >= i1) break;
+        const BatchDesc& nx = D[d];
+        bd.w = uniform(nx.w);
+        bd.s = uniform(nx.s);
+        bd.m = uniform(nx.m);
+        bd.x = uniform(nx.x);
+        bd.y = uniform(nx.y);
+        bd.n = uniform((int)nx.n);
+        bd.k = uniform((int)nx.k);
+        bd.first = uniform(nx.first);
     }
 }
 
