@@ -24,7 +24,8 @@ Also measured (outside the timed region, reported in the same JSON line):
     and fp16 output, the dense fp16 library matmul of each shape beside them;
   * the fused gate/up projection (silu(Wg x) * (Wu x), one launch) against
     two GEMV launches, Q4, on Qwen3-0.6B and Llama-3.2-3B shapes;
-  * Qwen3-30B-A3B-shaped MoE expert projections at 1 and 16 tokens;
+  * Qwen3-30B-A3B-shaped MoE expert projections at 1 and 16 tokens, also with
+    gate and up fused with the SiLU-gated product;
   * the CPU oracle on the host cores over the same projection set.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
@@ -424,9 +425,16 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
             row[pname] = {"us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1)}
             tot_b += b
             tot_ms += ms
+        # Gate and up fused with the SiLU-gated product (one launch), then down.
+        ho = torch.empty((p, 768), dtype=torch.float32, device="cuda")
+        ms_glu = timer(lambda: tensors.moe_swiglu(stacks["gate_proj"], stacks["up_proj"], x_tok, rows,
+                                                  off, p, h=ho), reps=30)
+        ms_fused = ms_glu + row["down_proj"]["us"] * 1e-3
         moe["t%d" % tokens] = {"distinct_experts": distinct, "us": round(tot_ms * 1e3, 2),
-                               "GBps": round(tot_b / tot_ms / 1e6, 1), "proj": row}
-        log("moe T=%d: %.1f us" % (tokens, tot_ms * 1e3))
+                               "GBps": round(tot_b / tot_ms / 1e6, 1), "proj": row,
+                               "fused_gate_up_us": round(ms_glu * 1e3, 2),
+                               "us_with_fused_gate_up": round(ms_fused * 1e3, 2)}
+        log("moe T=%d: %.1f us (gate|up fused: %.1f us)" % (tokens, tot_ms * 1e3, ms_fused * 1e3))
     out["moe_qwen3_30b_a3b_q4"] = moe
     return out
 

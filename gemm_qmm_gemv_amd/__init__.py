@@ -19,6 +19,7 @@ __all__ = [
     "QmmError", "library_path", "load",
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
     "qmm_gemv_batch_prepare", "qmm_gemv_batched", "GemvDesc", "qmm_gemv_swiglu", "qmm_gemm_f16out",
+    "qmm_moe_swiglu",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
     "QMM_OK", "QMM_ERR_INVALID_ARGUMENT", "QMM_ERR_UNSUPPORTED", "QMM_ERR_MISALIGNED",
     "QMM_ERR_DEVICE", "EXPORTED_SYMBOLS",
@@ -33,6 +34,7 @@ QMM_ERR_DEVICE = 4
 EXPORTED_SYMBOLS = (
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
     "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out",
+    "qmm_moe_swiglu",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
 )
 
@@ -108,12 +110,13 @@ def load():
     lib.qmm_gemm_workspace_bytes.argtypes = [i64, i64, i64, ci, ci]
     lib.qmm_gemm_workspace_bytes.restype = sz
     lib.qmm_moe_gemm.argtypes = [p, p, p, p, p, i64, p, p, i64, i64, i64, i64, ci, ci, p]
+    lib.qmm_moe_swiglu.argtypes = [p, p, p, p, p, p, p, p, i64, p, p, i64, i64, i64, i64, ci, ci, p]
     lib.qmm_unpack.argtypes = [p, p, i64, i64, ci, p]
     lib.qmm_gemv_batch_prepare.argtypes = [p, i64, ci, ci]
     lib.qmm_gemv_batched.argtypes = [p, p, i64, ci, ci, p]
     lib.qmm_get_plan.argtypes = [ci, i64, i64, i64, ci, ci, ci, sz, ctypes.POINTER(_Plan)]
     for f in ("qmm_gemv", "qmm_gemm", "qmm_moe_gemm", "qmm_unpack", "qmm_get_plan",
-              "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out"):
+              "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out", "qmm_moe_swiglu"):
         getattr(lib, f).restype = ci
     lib.qmm_status_string.argtypes = [ci]
     lib.qmm_status_string.restype = ctypes.c_char_p
@@ -204,6 +207,18 @@ def qmm_moe_gemm(w_packed, scales, mins, x, x_rows, x_rows_count, expert_offsets
                                int(p_rows), int(n_experts), int(n), int(k), int(bits),
                                int(group_size), _stream(stream)),
            "qmm_moe_gemm")
+
+
+def qmm_moe_swiglu(gate_w, gate_scales, gate_mins, up_w, up_scales, up_mins, x, x_rows,
+                   x_rows_count, expert_offsets, h, p_rows, n_experts, n, k, bits, group_size,
+                   stream=None) -> None:
+    """h[p] = silu(Wg_{e(p)} x[row(p)]) * (Wu_{e(p)} x[row(p)]); asynchronous."""
+    _check(load().qmm_moe_swiglu(_addr(gate_w), _addr(gate_scales), _addr(gate_mins), _addr(up_w),
+                                 _addr(up_scales), _addr(up_mins), _addr(x), _addr(x_rows),
+                                 int(x_rows_count), _addr(expert_offsets), _addr(h), int(p_rows),
+                                 int(n_experts), int(n), int(k), int(bits), int(group_size),
+                                 _stream(stream)),
+           "qmm_moe_swiglu")
 
 
 def qmm_unpack(w_packed, codes, n, k, bits, stream=None) -> None:

@@ -389,9 +389,15 @@ __device__ __forceinline__ void accumulate_rows(const RowBatch<B, UNIT, XC, 1>& 
     }
 }
 
-template <int B, int UNIT, int LPR, int XC, int MR, bool MP>
+//
+// GLU: a second stack (W2, S2, M2, same shapes) is multiplied alongside and
+// each output is silu(first) * second -- the gate and up projections of the
+// selected experts and their SiLU-gated product in one launch (the fusion of
+// qmm_gemv_swiglu applied to expert rows).  Single pass only.
+template <int B, int UNIT, int LPR, int XC, int MR, bool MP, bool GLU = false>
 __global__ __launch_bounds__(256) void gemv_rows_kernel(
     const u32* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ Mn,
+    const u32* __restrict__ W2, const uint16_t* __restrict__ S2, const uint16_t* __restrict__ M2,
     const uint16_t* __restrict__ X, const int32_t* __restrict__ x_rows, int x_count,
     const int32_t* __restrict__ offsets, int n_seg, int m_total, float* __restrict__ Y, int n,
     int k, int group, int pair_bound) {
@@ -466,6 +472,11 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
         const uint16_t* Se = S + (size_t)e * n * gpr;
         const uint16_t* Me = Mn + (size_t)e * n * gpr;
         const MatRsrc mr = mat_rsrc<B>(We, Se, Me, n, wpr, gpr);
+        // The second stack (GLU only; otherwise an unused copy of the first).
+        const u32* We2 = GLU ? W2 + (size_t)e * n * wpr : We;
+        const uint16_t* Se2 = GLU ? S2 + (size_t)e * n * gpr : Se;
+        const uint16_t* Me2 = GLU ? M2 + (size_t)e * n * gpr : Me;
+        const MatRsrc mr2 = mat_rsrc<B>(We2, Se2, Me2, n, wpr, gpr);
         const uint32_t x_bytes = (uint32_t)x_count * (uint32_t)k * 2u;
         const rsrc_t xbuf = make_rsrc(X, x_bytes);
         const uint32_t y_bytes = (uint32_t)m_total * (uint32_t)n * 4u;
@@ -507,6 +518,18 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
                                  ok ? ((uint32_t)p * (uint32_t)n + (uint32_t)row) * 4u : y_bytes);
             }
         };
+        auto store_rows_glu = [&](float (&gacc)[MR], float (&uacc)[MR], int pb, int row) {
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                const float g = group_sum<LPR>(gacc[r]), u = group_sum<LPR>(uacc[r]);
+                const float v = g / (1.0f + expf(-g)) * u;
+                const int p = pb + r;
+                const bool ok = j == 0 && row < n && p < p1;
+                buffer_store_f32(bad[r] ? __builtin_nanf("") : v, yr,
+                                 ok ? ((uint32_t)p * (uint32_t)n + (uint32_t)row) * 4u : y_bytes);
+            }
+        };
+        static_assert(!(MP && GLU), "the fused gate/up rows are single-pass only");
 
         if constexpr (MP) {
             for (int pb = p0; pb < p1; pb += MR) {
@@ -556,36 +579,50 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
             const int stride = nwaves * SLOTS;
             auto body = [&](auto wide_c) {
                 constexpr bool WIDE = decltype(wide_c)::value;
+                using RB = RowBatch<B, UNIT, XC, 1>;
+                auto load = [&](RB& bt, RB& bt2, int at, bool live) {
+                    load_batch<B, UNIT, LPR, XC, 1, WIDE>(bt, mr, at, live, wpr, gpr, slot, unit, gidx, nu, lane);
+                    if constexpr (GLU)
+                        load_batch<B, UNIT, LPR, XC, 1, WIDE>(bt2, mr2, at, live, wpr, gpr, slot, unit, gidx, nu, lane);
+                };
+                auto finish = [&](const RB& bt, const RB& bt2, int pb, int row) {
+                    float yacc[MR];
+#pragma unroll
+                    for (int r = 0; r < MR; ++r) yacc[r] = 0.f;
+                    accumulate_rows<B, UNIT, LPR, XC, MR, WIDE>(bt, xu, yacc, slot, gpr, gidx);
+                    if constexpr (GLU) {
+                        float uacc[MR];
+#pragma unroll
+                        for (int r = 0; r < MR; ++r) uacc[r] = 0.f;
+                        accumulate_rows<B, UNIT, LPR, XC, MR, WIDE>(bt2, xu, uacc, slot, gpr, gidx);
+                        store_rows_glu(yacc, uacc, pb, row);
+                    } else {
+                        store_rows(yacc, pb, row);
+                    }
+                };
                 for (int pb = p0; pb < p1; pb += MR) {
                     int rb = wave * SLOTS;
                     if (rb >= n) return;
-                    RowBatch<B, UNIT, XC, 1> ba, bb;
-                    load_batch<B, UNIT, LPR, XC, 1, WIDE>(ba, mr, rb, true, wpr, gpr, slot, unit, gidx, nu, lane);
+                    RB ba, bb, ba2, bb2;
+                    load(ba, ba2, rb, true);
                     __builtin_amdgcn_sched_barrier(0);
                     rows_of(pb);
                     prep(0);
                     while (true) {
-                        float yacc[MR];
                         int nxt = rb + stride;
-                        load_batch<B, UNIT, LPR, XC, 1, WIDE>(bb, mr, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
-#pragma unroll
-                        for (int r = 0; r < MR; ++r) yacc[r] = 0.f;
-                        accumulate_rows<B, UNIT, LPR, XC, MR, WIDE>(ba, xu, yacc, slot, gpr, gidx);
-                        store_rows(yacc, pb, rb + slot);
+                        load(bb, bb2, nxt, nxt < n);
+                        finish(ba, ba2, pb, rb + slot);
                         rb = nxt;
                         if (rb >= n) break;
                         nxt = rb + stride;
-                        load_batch<B, UNIT, LPR, XC, 1, WIDE>(ba, mr, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
-#pragma unroll
-                        for (int r = 0; r < MR; ++r) yacc[r] = 0.f;
-                        accumulate_rows<B, UNIT, LPR, XC, MR, WIDE>(bb, xu, yacc, slot, gpr, gidx);
-                        store_rows(yacc, pb, rb + slot);
+                        load(ba, ba2, nxt, nxt < n);
+                        finish(bb, bb2, pb, rb + slot);
                         rb = nxt;
                         if (rb >= n) break;
                     }
                 }
             };
-            if (wide_scales_ok<LPR, 1>(Se, Me, gpr))
+            if (wide_scales_ok<LPR, 1>(Se, Me, gpr) && (!GLU || wide_scales_ok<LPR, 1>(Se2, Me2, gpr)))
                 body(std::true_type{});
             else
                 body(std::false_type{});
@@ -832,14 +869,19 @@ inline dim3 rows_grid(const RowsShape& sh) {
 
 template <int B, int UNIT, int LPR, int XC, int MR>
 hipError_t launch_rows_t(const RowsArgs& a, const RowsShape& sh, hipStream_t st) {
-    if (sh.multipass) {
+    if (a.w2) {
+        if (sh.multipass) return hipErrorInvalidValue;  // the host rejects this before
+        constexpr auto kern = gemv_rows_kernel<B, UNIT, LPR, XC, MR, false, true>;
+        hipLaunchKernelGGL(kern, rows_grid<kern>(sh), dim3(256), 0, st, a.w, a.s, a.m, a.w2, a.s2, a.m2, a.x,
+                           a.x_rows, a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group, sh.pairs);
+    } else if (sh.multipass) {
         constexpr auto kern = gemv_rows_kernel<B, UNIT, LPR, XC, MR, true>;
-        hipLaunchKernelGGL(kern, rows_grid<kern>(sh), dim3(256), 0, st, a.w, a.s, a.m, a.x, a.x_rows,
-                           a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group, sh.pairs);
+        hipLaunchKernelGGL(kern, rows_grid<kern>(sh), dim3(256), 0, st, a.w, a.s, a.m, a.w, a.s, a.m, a.x,
+                           a.x_rows, a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group, sh.pairs);
     } else {
         constexpr auto kern = gemv_rows_kernel<B, UNIT, LPR, XC, MR, false>;
-        hipLaunchKernelGGL(kern, rows_grid<kern>(sh), dim3(256), 0, st, a.w, a.s, a.m, a.x, a.x_rows,
-                           a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group, sh.pairs);
+        hipLaunchKernelGGL(kern, rows_grid<kern>(sh), dim3(256), 0, st, a.w, a.s, a.m, a.w, a.s, a.m, a.x,
+                           a.x_rows, a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group, sh.pairs);
     }
     return hipGetLastError();
 }

@@ -463,10 +463,16 @@ qmm_status qmm_gemm_f16out(const void* w_packed, const void* scales, const void*
                        workspace_bytes, stream, true);
 }
 
-qmm_status qmm_moe_gemm(const void* w_packed, const void* scales, const void* mins, const void* x,
-                        const int32_t* x_rows, int64_t x_rows_count, const int32_t* expert_offsets,
-                        float* y, int64_t p_rows, int64_t n_experts, int64_t n, int64_t k, int bits,
-                        int group_size, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// qmm_moe_gemm, and qmm_moe_swiglu when up_w is given (y = silu(W x) * (Wup x)).
+qmm_status moe_common(const void* w_packed, const void* scales, const void* mins, const void* up_w,
+                      const void* up_s, const void* up_m, const void* x, const int32_t* x_rows,
+                      int64_t x_rows_count, const int32_t* expert_offsets, float* y, int64_t p_rows,
+                      int64_t n_experts, int64_t n, int64_t k, int bits, int group_size, void* stream,
+                      bool glu) {
     qmm_status st = check_format(n, k, bits, group_size);
     if (st != QMM_OK) return st;
     if (p_rows < 0 || n_experts < 0 || x_rows_count < 0)
@@ -477,6 +483,7 @@ qmm_status qmm_moe_gemm(const void* w_packed, const void* scales, const void* mi
     if ((st = check_activation_bytes(x_rows ? x_rows_count : p_rows, k)) != QMM_OK) return st;
     if ((st = check_output_bytes(p_rows, n)) != QMM_OK) return st;
     if ((st = check_weight_ptrs(w_packed, scales, mins, bits)) != QMM_OK) return st;
+    if (glu && (st = check_weight_ptrs(up_w, up_s, up_m, bits)) != QMM_OK) return st;
     if (!x || !y || !expert_offsets) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x, y or expert_offsets");
     if (!x_rows && x_rows_count < p_rows)
         return fail(QMM_ERR_INVALID_ARGUMENT, "x_rows is NULL and x has fewer than p_rows rows");
@@ -487,11 +494,40 @@ qmm_status qmm_moe_gemm(const void* w_packed, const void* scales, const void* mi
     if ((st = device_cus(&cus)) != QMM_OK) return st;
     const int64_t active = n_experts < p_rows ? n_experts : p_rows;
     const RowsShape sh = plan_rows(p_rows, n, k, bits, group_size, cus, active);
+    if (glu && sh.multipass)
+        return fail(QMM_ERR_UNSUPPORTED, "k=%lld needs more than one pass of the fused gate/up kernel",
+                    (long long)k);
     RowsArgs a{static_cast<const uint32_t*>(w_packed), static_cast<const uint16_t*>(scales),
                static_cast<const uint16_t*>(mins), static_cast<const uint16_t*>(x), x_rows,
                (int)x_rows_count, expert_offsets, (int)n_experts, (int)p_rows, y, (int)n, (int)k,
                group_size, bits};
-    return launched(launch_rows(a, sh, as_stream(stream)), "qmm_moe_gemm");
+    if (glu) {
+        a.w2 = static_cast<const uint32_t*>(up_w);
+        a.s2 = static_cast<const uint16_t*>(up_s);
+        a.m2 = static_cast<const uint16_t*>(up_m);
+    }
+    return launched(launch_rows(a, sh, as_stream(stream)), glu ? "qmm_moe_swiglu" : "qmm_moe_gemm");
+}
+
+}  // namespace
+
+extern "C" {
+
+qmm_status qmm_moe_gemm(const void* w_packed, const void* scales, const void* mins, const void* x,
+                        const int32_t* x_rows, int64_t x_rows_count, const int32_t* expert_offsets,
+                        float* y, int64_t p_rows, int64_t n_experts, int64_t n, int64_t k, int bits,
+                        int group_size, void* stream) {
+    return moe_common(w_packed, scales, mins, nullptr, nullptr, nullptr, x, x_rows, x_rows_count,
+                      expert_offsets, y, p_rows, n_experts, n, k, bits, group_size, stream, false);
+}
+
+qmm_status qmm_moe_swiglu(const void* gate_w, const void* gate_scales, const void* gate_mins,
+                          const void* up_w, const void* up_scales, const void* up_mins, const void* x,
+                          const int32_t* x_rows, int64_t x_rows_count, const int32_t* expert_offsets,
+                          float* h, int64_t p_rows, int64_t n_experts, int64_t n, int64_t k, int bits,
+                          int group_size, void* stream) {
+    return moe_common(gate_w, gate_scales, gate_mins, up_w, up_scales, up_mins, x, x_rows, x_rows_count,
+                      expert_offsets, h, p_rows, n_experts, n, k, bits, group_size, stream, true);
 }
 
 static qmm_status check_batch(const qmm_gemv_desc* d, int64_t count, int bits, int group,

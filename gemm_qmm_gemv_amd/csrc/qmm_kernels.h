@@ -81,6 +81,11 @@ struct RowsArgs {
     int m_total;            // output rows
     float* y;
     int n, k, group, bits;
+    // Second stack for the fused gate/up rows (y = silu(W x) * (W2 x)); null
+    // for a plain product.
+    const uint32_t* w2 = nullptr;
+    const uint16_t* s2 = nullptr;
+    const uint16_t* m2 = nullptr;
 };
 
 struct RowsShape {

@@ -8,7 +8,7 @@ import numpy as np
 import torch
 
 from . import (GemvDesc, qmm_gemm, qmm_gemm_f16out, qmm_gemm_workspace_bytes, qmm_gemv, qmm_gemv_batch_prepare,
-               qmm_gemv_swiglu,
+               qmm_gemv_swiglu, qmm_moe_swiglu,
                qmm_gemv_batched, qmm_moe_gemm, qmm_unpack)
 
 
@@ -75,6 +75,18 @@ def moe(dst: dict, x: torch.Tensor, x_rows: torch.Tensor | None, offsets: torch.
     qmm_moe_gemm(dst["w"], dst["scales"], dst["mins"], x, x_rows, x.shape[0], offsets, y, p_rows,
                  dst["n_experts"], dst["n"], dst["k"], dst["bits"], dst["group"], stream=stream)
     return y
+
+
+def moe_swiglu(dg: dict, du: dict, x: torch.Tensor, x_rows: torch.Tensor | None,
+               offsets: torch.Tensor, p_rows: int, h: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """Fused gate/up rows of the selected experts: h = silu(g) * u."""
+    if h is None:
+        h = torch.empty((p_rows, dg["n"]), dtype=torch.float32, device=x.device)
+    qmm_moe_swiglu(dg["w"], dg["scales"], dg["mins"], du["w"], du["scales"], du["mins"], x, x_rows,
+                   x.shape[0], offsets, h, p_rows, dg["n_experts"], dg["n"], dg["k"], dg["bits"],
+                   dg["group"], stream=stream)
+    return h
 
 
 def unpack(dq: dict, stream=None) -> torch.Tensor:

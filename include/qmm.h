@@ -200,6 +200,22 @@ QMM_API qmm_status qmm_moe_gemm(const void *w_packed, const void *scales, const 
                         int64_t n_experts, int64_t n, int64_t k, int bits,
                         int group_size, void *stream);
 
+/* Fused gate/up projection of the selected experts:
+ *   h[p][j] = silu(g[p][j]) * u[p][j], g and u as qmm_moe_gemm over the
+ *   gate stack and the up stack, silu(v) = v / (1 + e^-v).
+ * Pages: as qmm_gemv_swiglu (fusion of feed-forward operator sequences) and
+ * as qmm_moe_gemm (expert rows).  Both stacks [n_experts][n][...] in one
+ * format; the remaining arguments and the NaN rule are those of
+ * qmm_moe_gemm.  k must fit one pass (as qmm_gemv_swiglu), else
+ * QMM_ERR_UNSUPPORTED.                                                      */
+QMM_API qmm_status qmm_moe_swiglu(const void *gate_w, const void *gate_scales,
+                                  const void *gate_mins, const void *up_w,
+                                  const void *up_scales, const void *up_mins, const void *x,
+                                  const int32_t *x_rows, int64_t x_rows_count,
+                                  const int32_t *expert_offsets, float *h, int64_t p_rows,
+                                  int64_t n_experts, int64_t n, int64_t k, int bits,
+                                  int group_size, void *stream);
+
 /* Codes as bytes: codes[n][k] = q[n][k] (uint8).  Bit-exact view of the
  * packed format, used to check the GPU's bit extraction.                   */
 QMM_API qmm_status qmm_unpack(const void *w_packed, uint8_t *codes, int64_t n, int64_t k,
