@@ -53,14 +53,19 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+# The sources the batched GEMV kernel is compiled and launched from (its
+# device code, shared device helpers, the launch plumbing and the host plan).
+TRAFFIC_SOURCES = ("gemv_bits.hip", "gemv_kernels.h", "qmm_api.hip", "qmm_device.h", "qmm_kernels.h")
+
+
 def kernel_source_digest() -> str:
-    """sha256 over the HIP sources; ties stored counter readings to a build."""
+    """sha256 over the batched GEMV's sources; ties stored counter readings to
+    a build of that kernel."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gemm_qmm_gemv_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
