@@ -155,11 +155,24 @@ static_assert(PD >= 2 && PD <= 4, "prefetch distance");
 // constant: the raw rings have PD slots, the dequantized W and the LDS
 // buffers two.
 constexpr int UNROLL = PD % 2 ? 2 * PD : PD;
+// Wide scale loads (SW): with groups of 64 codes and steps of 128, a lane's
+// scales for four consecutive steps are eight consecutive fp16 values of its
+// own row (its K-half takes every other group), fetched as one 16-byte load
+// for the scales and one for the mins instead of eight 2-byte loads.
+constexpr int SW_STEPS = 4;
+// With wide scales the loop is unrolled by a multiple of four as well, so a
+// block's word index is a compile-time constant.
+constexpr int UNROLL_SW = UNROLL % SW_STEPS ? UNROLL * SW_STEPS / (UNROLL % SW_STEPS == 2 ? 2 : 1) : UNROLL;
+static_assert(UNROLL_SW % SW_STEPS == 0 && UNROLL_SW % UNROLL == 0, "wide-scale unroll");
 
 // MS: 32-row fragments per wave along M (TILE_M = 32 * MS); WN: waves along
 // N (each with BN / WN columns, NS = BN / (32 WN) fragments); two waves
 // along K.  The work-group has 128 * WN threads.
-template <int B, int MS, int WN>
+//
+// SW: wide scale loads (see SW_STEPS); the host enables it only for groups of
+// 64, rows of scales 16-byte aligned (K a multiple of 512) and splits that
+// start at multiples of four steps.
+template <int B, int MS, int WN, bool SW = false>
 __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(const u32* __restrict__ W,
                                                    const uint16_t* __restrict__ S,
                                                    const uint16_t* __restrict__ Mn,
@@ -250,6 +263,29 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
     u32 wq[PD][CH][NS][B];
     u32 sq[PD][CH][NS], mq[PD][CH][NS];
     f16x2 wv[2][CH][NS][16];
+    // SW: scale and min blocks of the current and the next four steps.
+    static_assert(!SW || (BK == 128 && CH == 1 && has_affine<B>()), "wide scales: 64-code groups, 128-deep steps");
+    u32x4 s_cur[NS], m_cur[NS], s_nxt[NS], m_nxt[NS];
+    auto load_sm_block = [&](int st, u32x4 (&sb)[NS], u32x4 (&mb)[NS]) {
+        // Groups 2*st .. 2*st + 7 of each of this lane's columns.
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+            const uint32_t so = n_ok[ns] ? s_row[ns] + (uint32_t)st * 4u : sm_bytes;
+            sb[ns] = __builtin_amdgcn_raw_buffer_load_b128(sr, so, 0, 0);
+            mb[ns] = __builtin_amdgcn_raw_buffer_load_b128(mr, so, 0, 0);
+        }
+    };
+    // Step st's scale and min from the current block: word st % 4, the half
+    // of this wave's K-half (group 2*st + wk).
+    auto sm_of_block = [&](auto w_c, u32 (&sv)[CH][NS], u32 (&mv)[CH][NS]) {
+        constexpr int WI = decltype(w_c)::value;
+        const uint32_t sh = 16u * (uint32_t)wk;
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+            sv[0][ns] = (s_cur[ns][WI] >> sh) & 0xFFFFu;
+            mv[0][ns] = (m_cur[ns][WI] >> sh) & 0xFFFFu;
+        }
+    };
 
     // Loads are unconditional: a step past this split's range, like a row
     // or column past the matrix, reads zeros through the buffer range check.
@@ -278,7 +314,9 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
                 const bool ok = n_ok[ns] && live;
                 const uint32_t wo = ok ? w_row[ns] + (uint32_t)(kc / 32) * B * 4 : w_bytes;
                 buffer_words<B, unit_align(B, 32)>(wr, wo, w[c][ns]);
-                if constexpr (has_affine<B>()) {
+                if constexpr (SW) {
+                    // Scales come from the block registers.
+                } else if constexpr (has_affine<B>()) {
                     const uint32_t so = ok ? s_row[ns] + group_of((uint32_t)kc) * 2 : sm_bytes;
                     sv[c][ns] = buffer_u16(sr, so);
                     mv[c][ns] = buffer_u16(mr, so);
@@ -323,11 +361,15 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
         load_x(st0 + d, xq[d]);
         load_w(st0 + d, wq[d], sq[d], mq[d]);
     }
+    if constexpr (SW) {
+        load_sm_block(st0, s_cur, m_cur);
+        sm_of_block(std::integral_constant<int, 0>{}, sq[0], mq[0]);
+    }
     stage_x(xq[0], 0);
     dequant(wq[0], sq[0], mq[0], wv[0]);
     __syncthreads();
 
-    // One step at position U = (st - st0) mod UNROLL.  On entry X(st) sits
+    // One step at position U = (st - st0) mod UNR.  On entry X(st) sits
     // in LDS buffer U % 2 and W(st) is dequantized in wv[U % 2]; raw slot
     // U % PD is free (its data went into this step's operands during the
     // previous step).  The step
@@ -337,13 +379,18 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
     //     the other LDS buffer,
     //   * ends with the barrier that publishes X(st + 1) and frees buffer
     //     U % 2 for step st + 2.
-    static_assert(UNROLL % 2 == 0 && UNROLL % PD == 0, "ring positions must be compile-time");
+    constexpr int UNR = SW ? UNROLL_SW : UNROLL;
+    static_assert(UNR % 2 == 0 && UNR % PD == 0, "ring positions must be compile-time");
     auto step = [&](auto u_c, int st) {
         constexpr int U = decltype(u_c)::value;
         constexpr int BUF = U % 2;
         constexpr int SLOT = U % PD, NEXT = (U + 1) % PD;
         load_w(st + PD, wq[SLOT], sq[SLOT], mq[SLOT]);
         load_x(st + PD, xq[SLOT]);
+        // SW: the next block (steps st + 2 .. st + 5) goes out two steps
+        // before its first use, the dequantization of step st + 2 in step
+        // st + 1.  (st0 is a multiple of four, so U == st % 4.)
+        if constexpr (SW && U % SW_STEPS == 2) load_sm_block(st + 2, s_nxt, m_nxt);
         // Keep the loads at the top of the step: left alone, the scheduler
         // sinks them towards their first use.
         __builtin_amdgcn_sched_barrier(0);
@@ -366,6 +413,17 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
                 }
             }
         }
+        if constexpr (SW) {
+            // Step st + 1 opens a new block at U % 4 == 3.
+            if constexpr (U % SW_STEPS == SW_STEPS - 1) {
+#pragma unroll
+                for (int ns = 0; ns < NS; ++ns) {
+                    s_cur[ns] = s_nxt[ns];
+                    m_cur[ns] = m_nxt[ns];
+                }
+            }
+            sm_of_block(std::integral_constant<int, (U + 1) % SW_STEPS>{}, sq[NEXT], mq[NEXT]);
+        }
         dequant(wq[NEXT], sq[NEXT], mq[NEXT], wv[BUF ^ 1]);
         stage_x(xq[NEXT], BUF ^ 1);
         __syncthreads();
@@ -375,8 +433,8 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
     // loads in flight, and the compiler would then drain the memory queue
     // at the top of every pass.
     int st = st0;
-    for (; st + UNROLL <= st1; st += UNROLL) all_steps<0, UNROLL>(step, st);
-    unrolled_steps<0, UNROLL>(step, st, st1);
+    for (; st + UNR <= st1; st += UNR) all_steps<0, UNR>(step, st);
+    unrolled_steps<0, UNR>(step, st, st1);
 
     // Add the two K-halves.  Fragment f = i * NS + ns; wave (wn, wk) keeps
     // the fragments with f % 2 == wk (all of them for wk == 0 when it has
@@ -473,9 +531,15 @@ static hipError_t launch_gemm_t(const GemmArgs& a, const GemmShape& sh, hipStrea
     const DivMagic gm = div_magic(a.group);
     const int tiles = sh.grid_m * sh.grid_n * sh.split;
     const int grid = 8 * ((tiles + 7) / 8);
-    hipLaunchKernelGGL((gemm_kernel<B, MS, WN>), dim3(grid), dim3(128 * WN), 0, st, a.w, a.s, a.m, a.x, a.y,
-                       a.partial, a.m_rows, a.n, a.k, gm.mul, gm.shift, sh.grid_m, sh.grid_n,
-                       sh.split, sh.k_tiles_per_split, a.out16);
+    constexpr bool SW_OK = has_affine<B>() && BK == 128;
+    if (SW_OK && sh.wide_scales)
+        hipLaunchKernelGGL((gemm_kernel<B, MS, WN, SW_OK>), dim3(grid), dim3(128 * WN), 0, st, a.w, a.s, a.m, a.x,
+                           a.y, a.partial, a.m_rows, a.n, a.k, gm.mul, gm.shift, sh.grid_m, sh.grid_n,
+                           sh.split, sh.k_tiles_per_split, a.out16);
+    else
+        hipLaunchKernelGGL((gemm_kernel<B, MS, WN>), dim3(grid), dim3(128 * WN), 0, st, a.w, a.s, a.m, a.x, a.y,
+                           a.partial, a.m_rows, a.n, a.k, gm.mul, gm.shift, sh.grid_m, sh.grid_n,
+                           sh.split, sh.k_tiles_per_split, a.out16);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || sh.split == 1) return err;
     const int64_t count = (int64_t)a.m_rows * a.n;

@@ -282,7 +282,7 @@ RowsShape plan_rows(int64_t rows_bound, int64_t n, int64_t k, int bits, int grou
 // (twice the waves per SIMD of the 128-row tile), except for long K with
 // several 128-row tiles, where the 128-row tile's halved W traffic wins; a
 // split shorter than four K steps costs more in partial sums than it gains.
-GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int cus, size_t ws_bytes, size_t* ws_need) {
+GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int group, int cus, size_t ws_bytes, size_t* ws_need) {
     GemmShape sh{};
     const int k_tiles = (int)((k + GEMM_BK - 1) / GEMM_BK);
     const int64_t grid_n = (n + 127) / 128;
@@ -314,7 +314,11 @@ GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int cus, size_t ws_bytes, s
         if (split < 2) split = 1;
     }
     sh.k_tiles_per_split = (k_tiles + split - 1) / split;
+    // Wide scale loads need splits that start at multiples of four steps.
+    const bool wide = group == 64 && GEMM_BK == 128 && k % 512 == 0 && env_int("QMM_GEMM_WIDE_SCALES", 1) != 0;
+    if (wide && split > 1) sh.k_tiles_per_split = (sh.k_tiles_per_split + 3) / 4 * 4;
     sh.split = (k_tiles + sh.k_tiles_per_split - 1) / sh.k_tiles_per_split;
+    sh.wide_scales = wide;
     return sh;
 }
 
@@ -394,7 +398,7 @@ size_t qmm_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits, int g
     int cus = 0;
     if (device_cus(&cus) != QMM_OK) cus = 256;
     size_t need = 0;
-    (void)plan_gemm(m, n, k, cus, (size_t)-1, &need);
+    (void)plan_gemm(m, n, k, group_size, cus, (size_t)-1, &need);
     return need;
 }
 
@@ -439,7 +443,7 @@ qmm_status gemm_common(const void* w_packed, const void* scales, const void* min
         RowsArgs a{w, s, mn, xx, nullptr, (int)m, nullptr, 1, (int)m, yf, (int)n, (int)k, group_size, bits};
         return launched(launch_rows(a, sh, as_stream(stream)), "qmm_gemm (rows)");
     }
-    const GemmShape sh = plan_gemm(m, n, k, cus, workspace ? workspace_bytes : 0, nullptr);
+    const GemmShape sh = plan_gemm(m, n, k, group_size, cus, workspace ? workspace_bytes : 0, nullptr);
     GemmArgs a{w, s, mn, xx, yf, sh.split > 1 ? static_cast<float*>(workspace) : nullptr, (int)m, (int)n,
                (int)k, group_size, bits, out16 ? 1 : 0};
     return launched(launch_gemm(a, sh, as_stream(stream)), out16 ? "qmm_gemm_f16out" : "qmm_gemm");
@@ -660,7 +664,7 @@ qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits, int g
         return ok();
     }
     if (op == 1) {
-        const GemmShape sh = plan_gemm(m, n, k, cus, workspace_bytes, nullptr);
+        const GemmShape sh = plan_gemm(m, n, k, group_size, cus, workspace_bytes, nullptr);
         plan->variant = 2;
         plan->block = gemm_threads(sh.tile_m);
         plan->split_k = sh.split;
