@@ -45,10 +45,8 @@
 namespace qmm {
 
 constexpr int BK = GEMM_BK;     // K per step
-constexpr int HK = BK / 2;      // K per wave and step (one half of the step)
-constexpr int CH = HK / 64;     // 64-code chunks per wave and step (a lane holds half of each)
-static_assert(HK % 64 == 0, "each wave takes whole 64-code chunks");
-constexpr int BN = 128;         // columns per work-group
+static_assert(BK % 128 == 0, "each of two waves along K takes whole 64-code chunks");
+constexpr int BN = 128;         // columns per work-group (default tile width)
 constexpr int XPAD = 8;         // halves of padding per LDS row (conflict-free 16-byte reads)
 constexpr int XROW = BK + XPAD; // halves per LDS row
 
@@ -166,14 +164,18 @@ constexpr int UNROLL_SW = UNROLL % SW_STEPS ? UNROLL * SW_STEPS / (UNROLL % SW_S
 static_assert(UNROLL_SW % SW_STEPS == 0 && UNROLL_SW % UNROLL == 0, "wide-scale unroll");
 
 // MS: 32-row fragments per wave along M (TILE_M = 32 * MS); WN: waves along
-// N (each with BN / WN columns, NS = BN / (32 WN) fragments); two waves
-// along K.  The work-group has 128 * WN threads.
+// N (each with TN / WN columns, NS = TN / (32 WN) fragments); KW: waves
+// along K (two: each takes one half of every step and the halves are added
+// at the end; one: a wave takes whole steps).  The work-group has
+// 64 * WN * KW threads and covers TILE_M x TN of Y.
 //
 // SW: wide scale loads (see SW_STEPS); the host enables it only for groups of
 // 64, rows of scales 16-byte aligned (K a multiple of 512) and splits that
 // start at multiples of four steps.
-template <int B, int MS, int WN, bool SW = false>
-__global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(const u32* __restrict__ W,
+constexpr int gemm_min_blocks(int wn) { return GEMM_MINB * 2 / wn > 0 ? GEMM_MINB * 2 / wn : 1; }
+
+template <int B, int MS, int WN, int KW = 2, int TN = BN, bool SW = false>
+__global__ __launch_bounds__(64 * WN * KW, gemm_min_blocks(WN)) void gemm_kernel(const u32* __restrict__ W,
                                                    const uint16_t* __restrict__ S,
                                                    const uint16_t* __restrict__ Mn,
                                                    const uint16_t* __restrict__ X,
@@ -182,8 +184,12 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
                                                    int grid_m, int grid_n, int split,
                                                    int steps_per_split, int out16) {
     constexpr int TILE_M = 32 * MS;
-    constexpr int THREADS = 128 * WN;
-    constexpr int NS = BN / (32 * WN);                   // 32-column fragments per wave
+    constexpr int THREADS = 64 * WN * KW;
+    constexpr int NS = TN / (32 * WN);                   // 32-column fragments per wave
+    constexpr int HK = BK / KW;                          // K per wave and step
+    constexpr int CH = HK / 64;                          // 64-code chunks per wave and step
+    static_assert(KW == 1 || KW == 2, "one or two waves along K");
+    static_assert(NS * 32 * WN == TN && CH * 64 == HK, "tile shape");
     constexpr int NF = MS * NS;                          // fragments per wave
     constexpr int XH = x_unit_halves<B>();               // halves per X unit
     constexpr int XW = XH / 2;                           // dwords per X unit
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
     // K-half exchange: every wave hands over half of its fragments (all of
     // them when it has only one).
     constexpr int GIVE = NF > 1 ? NF / 2 : 1;
-    constexpr int R_BYTES = 2 * WN * GIVE * 16 * 64 * 4;
+    constexpr int R_BYTES = KW == 2 ? 2 * WN * GIVE * 16 * 64 * 4 : 0;
     constexpr int LDS_BYTES = X_BYTES > R_BYTES ? X_BYTES : R_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
     f16* xs = reinterpret_cast<f16*>(smem);
@@ -209,7 +215,7 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
     const int rest = t / grid_m;
     const int sk = rest % split;
     const int nt = rest / split;
-    const int m0 = mt * TILE_M, n0 = nt * BN;
+    const int m0 = mt * TILE_M, n0 = nt * TN;
     const int steps = (K + BK - 1) / BK;
     const int st0 = sk * steps_per_split;
     const int st1 = min(steps, st0 + steps_per_split);
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
     u32 sq[PD][CH][NS], mq[PD][CH][NS];
     f16x2 wv[2][CH][NS][16];
     // SW: scale and min blocks of the current and the next four steps.
-    static_assert(!SW || (BK == 128 && CH == 1 && has_affine<B>()), "wide scales: 64-code groups, 128-deep steps");
+    static_assert(!SW || (BK == 128 && has_affine<B>()), "wide scales: 64-code groups, 128-deep steps");
     u32x4 s_cur[NS], m_cur[NS], s_nxt[NS], m_nxt[NS];
     auto load_sm_block = [&](int st, u32x4 (&sb)[NS], u32x4 (&mb)[NS]) {
         // Groups 2*st .. 2*st + 7 of each of this lane's columns.
@@ -275,15 +281,18 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
             mb[ns] = __builtin_amdgcn_raw_buffer_load_b128(mr, so, 0, 0);
         }
     };
-    // Step st's scale and min from the current block: word st % 4, the half
-    // of this wave's K-half (group 2*st + wk).
+    // Step st's scales and mins from the current block: word st % 4, half
+    // (HK / 64) * wk + c (group 2 * st + that).
     auto sm_of_block = [&](auto w_c, u32 (&sv)[CH][NS], u32 (&mv)[CH][NS]) {
         constexpr int WI = decltype(w_c)::value;
-        const uint32_t sh = 16u * (uint32_t)wk;
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-            sv[0][ns] = (s_cur[ns][WI] >> sh) & 0xFFFFu;
-            mv[0][ns] = (m_cur[ns][WI] >> sh) & 0xFFFFu;
+        for (int c = 0; c < CH; ++c) {
+            const uint32_t sh = 16u * (uint32_t)((HK / 64) * wk + c);
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) {
+                sv[c][ns] = (s_cur[ns][WI] >> sh) & 0xFFFFu;
+                mv[c][ns] = (m_cur[ns][WI] >> sh) & 0xFFFFu;
+            }
         }
     };
 
@@ -436,13 +445,14 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
     for (; st + UNR <= st1; st += UNR) all_steps<0, UNR>(step, st);
     unrolled_steps<0, UNR>(step, st, st1);
 
-    // Add the two K-halves.  Fragment f = i * NS + ns; wave (wn, wk) keeps
-    // the fragments with f % 2 == wk (all of them for wk == 0 when it has
-    // only one) and hands the others to its partner through LDS (the X
-    // buffers are free after the loop's last barrier).
+    // Add the two K-halves (KW = 2).  Fragment f = i * NS + ns; wave (wn, wk)
+    // keeps the fragments with f % 2 == wk (all of them for wk == 0 when it
+    // has only one) and hands the others to its partner through LDS (the X
+    // buffers are free after the loop's last barrier).  With one wave along
+    // K every wave stores all of its fragments.
     float* red = reinterpret_cast<float*>(smem);
-    auto keeps = [&](int f) { return NF > 1 ? (f % 2) == wk : wk == 0; };
-    {
+    auto keeps = [&](int f) { return KW == 1 ? true : NF > 1 ? (f % 2) == wk : wk == 0; };
+    if constexpr (KW == 2) {
         float* dst = red + ((wn * 2 + wk) * GIVE) * 16 * 64 + lane;
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
@@ -451,8 +461,8 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
 #pragma unroll
             for (int v = 0; v < 16; ++v) dst[(slot * 16 + v) * 64] = acc[f / NS][f % NS][v];
         }
+        __syncthreads();
     }
-    __syncthreads();
     {
         // Store: lane holds column (lane % 32) of each 32x32 fragment, rows
         // 8*(v/4) + 4*(lane/32) + v%4.  Buffer stores, unconditional: an
@@ -476,7 +486,7 @@ __global__ __launch_bounds__(128 * WN, GEMM_MINB * 2 / WN) void gemm_kernel(cons
                 const int c = n0 + 32 * NS * wn + 32 * ns + col;
                 float part[16];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) part[v] = src[(slot * 16 + v) * 64];
+                for (int v = 0; v < 16; ++v) part[v] = KW == 2 ? src[(slot * 16 + v) * 64] : 0.f;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * kh + (v & 3);
@@ -526,19 +536,20 @@ static DivMagic div_magic(int d) {
     return {((1ULL << shift) + (uint64_t)d - 1) / (uint64_t)d, shift};
 }
 
-template <int B, int MS, int WN>
+template <int B, int MS, int WN, int KW = 2, int TN = BN>
 static hipError_t launch_gemm_t(const GemmArgs& a, const GemmShape& sh, hipStream_t st) {
     const DivMagic gm = div_magic(a.group);
     const int tiles = sh.grid_m * sh.grid_n * sh.split;
     const int grid = 8 * ((tiles + 7) / 8);
     constexpr bool SW_OK = has_affine<B>() && BK == 128;
+    constexpr int THREADS = 64 * WN * KW;
     if (SW_OK && sh.wide_scales)
-        hipLaunchKernelGGL((gemm_kernel<B, MS, WN, SW_OK>), dim3(grid), dim3(128 * WN), 0, st, a.w, a.s, a.m, a.x,
-                           a.y, a.partial, a.m_rows, a.n, a.k, gm.mul, gm.shift, sh.grid_m, sh.grid_n,
-                           sh.split, sh.k_tiles_per_split, a.out16);
+        hipLaunchKernelGGL((gemm_kernel<B, MS, WN, KW, TN, SW_OK>), dim3(grid), dim3(THREADS), 0, st, a.w, a.s,
+                           a.m, a.x, a.y, a.partial, a.m_rows, a.n, a.k, gm.mul, gm.shift, sh.grid_m,
+                           sh.grid_n, sh.split, sh.k_tiles_per_split, a.out16);
     else
-        hipLaunchKernelGGL((gemm_kernel<B, MS, WN>), dim3(grid), dim3(128 * WN), 0, st, a.w, a.s, a.m, a.x, a.y,
-                           a.partial, a.m_rows, a.n, a.k, gm.mul, gm.shift, sh.grid_m, sh.grid_n,
+        hipLaunchKernelGGL((gemm_kernel<B, MS, WN, KW, TN>), dim3(grid), dim3(THREADS), 0, st, a.w, a.s, a.m,
+                           a.x, a.y, a.partial, a.m_rows, a.n, a.k, gm.mul, gm.shift, sh.grid_m, sh.grid_n,
                            sh.split, sh.k_tiles_per_split, a.out16);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || sh.split == 1) return err;
@@ -550,6 +561,14 @@ static hipError_t launch_gemm_t(const GemmArgs& a, const GemmShape& sh, hipStrea
 
 template <int B>
 static hipError_t launch_gemm_b(const GemmArgs& a, const GemmShape& sh, hipStream_t st) {
+    if (sh.tile_n == 256) {
+        // Eight waves along N, each taking whole steps.
+        switch (sh.tile_m) {
+            case 64: return launch_gemm_t<B, 2, 8, 1, 256>(a, sh, st);
+            case 128: return launch_gemm_t<B, 4, 8, 1, 256>(a, sh, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (sh.tile_m) {
         case 32: return launch_gemm_t<B, 1, gemm_threads(32) / 128>(a, sh, st);
         case 64: return launch_gemm_t<B, 2, gemm_threads(64) / 128>(a, sh, st);

@@ -199,9 +199,12 @@ def test_gemm_plan(lib, m, n, k):
     unlimited = 1 << 40
     pl = qmm.qmm_get_plan(1, m, n, k, 4, 64, cu_count=256, workspace_bytes=unlimited)
     assert pl["variant"] == 2
-    assert pl["tile_m"] == _expected_tile(m, n, k) and pl["tile_n"] == 128
+    assert pl["tile_m"] == _expected_tile(m, n, k)
+    # 256-column tiles exactly where a 128-row grid of them fills the CUs.
+    wide = pl["tile_m"] == 128 and -(-m // 128) * -(-n // 256) >= 256
+    assert pl["tile_n"] == (256 if wide else 128)
     assert pl["block"] == (256 if pl["tile_m"] == 32 else 512)
-    tiles = -(-m // pl["tile_m"]) * -(-n // 128)
+    tiles = -(-m // pl["tile_m"]) * -(-n // pl["tile_n"])
     assert pl["grid"] >= tiles * pl["split_k"]
     assert 1 <= pl["split_k"] <= 16
     # Every split keeps at least four K steps of 128.

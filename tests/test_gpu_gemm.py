@@ -202,3 +202,19 @@ def test_gemm_long_prefill_sampled(proj, out_fp16):
     y_ref, a_ref = oracle.qmm_sample(q["w"], q["scales"], q["mins"], x, k, 4, configs.GROUP, rm, rn)
     assert_within(y[rm, rn], y_ref, a_ref, "prefill m%d %s" % (m, name), fp16_out=out_fp16)
     assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("bits", (2, 4, 5, 8, 16))
+@pytest.mark.parametrize("tile", (64, 128))
+@pytest.mark.parametrize("m,n,k", [(100, 300, 1024), (257, 600, 2048), (130, 520, 3072)])
+def test_gemm_parity_wide_tile(monkeypatch, bits, tile, m, n, k):
+    # 256-column tiles (eight waves along N taking whole steps), with and
+    # without the wide scale loads (K a multiple of 512 or not).
+    monkeypatch.setenv("QMM_GEMM_TILE_M", str(tile))
+    monkeypatch.setenv("QMM_GEMM_TILE_N", "256")
+    q = inputs.quantized_matrix(n, k, bits, 64, key=(65, m, n, k, bits))
+    x = inputs.activation_rows(m, k, key=(65, m, n, k, bits))
+    announce("gemm-wide-tile", tile, bits, m, n, k)
+    y = _run_gemm(q, x)
+    y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, 64)
+    assert_within(y, y_ref, a_ref, "gemm tile%dx256 b%d m%d %dx%d" % (tile, bits, m, n, k))
