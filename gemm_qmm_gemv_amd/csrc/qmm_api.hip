@@ -237,7 +237,7 @@ bool plan_batched(int64_t total_rows, int64_t kmax, int bits, int group, GemvSha
     return true;
 }
 
-constexpr int BATCHED_WAVES_PER_CU = 8;
+constexpr int BATCHED_WAVES_PER_CU = 12;
 
 // Row batches of one descriptor in a batched launch planned as sh.
 int64_t batched_items(const GemvShape& sh, int64_t n, int64_t k) {
@@ -601,8 +601,10 @@ qmm_status qmm_gemv_batched(const qmm_gemv_desc* descs_device, const qmm_gemv_de
     if ((st = device_cus(&cus)) != QMM_OK) return st;
     sh.work = first;
     sh.cus = cus;
-    // Two 4-wave work-groups per CU: measured on the decode projection set,
-    // fewer concurrent streams than full occupancy read HBM faster.
+    // Three 4-wave work-groups per CU, what this kernel's register count
+    // lets a CU hold at once: measured on the decode projection set, 2 %
+    // faster than two, and a grid sized for four (more work-groups than fit,
+    // so the last ones queue) is 6 % slower.
     sh.waves_per_cu = env_int("QMM_GEMV_WAVES_PER_CU", BATCHED_WAVES_PER_CU);
     BatchArgs a{reinterpret_cast<const BatchDesc*>(descs_device), (int)count, first, group_size, bits};
     return launched(launch_batched(a, sh, as_stream(stream)), "qmm_gemv_batched");
