@@ -860,7 +860,7 @@ hipError_t launch_batched_t(const BatchArgs& a, const GemvShape& sh, hipStream_t
 // once and loops over its rows instead of queueing behind other work-groups.
 template <auto Kernel>
 inline dim3 rows_grid(const RowsShape& sh) {
-    const int64_t resident = (int64_t)sh.cus * blocks_per_cu<Kernel>();
+    const int64_t resident = (int64_t)sh.cus * (sh.waves_per_cu > 0 ? sh.waves_per_cu / 4 : blocks_per_cu<Kernel>());
     int64_t gx = resident / (sh.grid_y > 0 ? sh.grid_y : 1);
     if (gx > sh.grid_x) gx = sh.grid_x;
     if (gx < 1) gx = 1;

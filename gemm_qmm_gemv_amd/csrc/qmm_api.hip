@@ -279,6 +279,13 @@ RowsShape plan_rows(int64_t rows_bound, int64_t n, int64_t k, int bits, int grou
     sh.pairs = (int)(pairs > 0 ? (pairs < INT_LIMIT ? pairs : INT_LIMIT) : 1);
     sh.grid_y = sh.pairs < 65535 ? sh.pairs : 65535;
     sh.cus = cus;
+    // Little work (one token's experts: a handful of segments of one row) runs
+    // faster on one 4-wave work-group per CU than at full occupancy
+    // (measured ~20 % on the Qwen3-30B-A3B experts at one token: longer-lived
+    // waves keep their pipelined loops busy); more work keeps the
+    // occupancy-sized grid.
+    const int64_t row_batches = (int64_t)sh.pairs * ((n + slots - 1) / slots);
+    sh.waves_per_cu = env_int("QMM_ROWS_WAVES_PER_CU", row_batches <= (int64_t)16 * cus ? 4 : 0);
     return sh;
 }
 

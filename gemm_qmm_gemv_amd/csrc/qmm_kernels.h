@@ -94,6 +94,7 @@ struct RowsShape {
     int grid_x, grid_y;  // grid_x: row chunks wanted per segment (capped at launch)
     int pairs;           // upper bound on (segment, row batch) pairs; grid_y = min(pairs, 65535)
     int cus;
+    int waves_per_cu;    // > 0: resident waves per CU the grid assumes; 0: the kernel's occupancy
 };
 
 struct GemmArgs {
