@@ -402,6 +402,32 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
         log("swiglu %s: fused %.1f us, two gemvs %.1f us" % (label, ms_f * 1e3, ms_s * 1e3))
     out["swiglu_fusion_q4"] = glu
 
+    # Output projections with the residual add fused (y = r + W x, in place)
+    # against the plain GEMV followed by a separate add launch.
+    resid = {}
+    for label, n, k in (("qwen3_0.6b_o_proj", 1024, 2048), ("llama3.2_3b_down", 3072, 8192)):
+        mats = [tensors.upload_matrix(inputs.quantized_matrix(n, k, 4, G, key=(configs.CFG_SWEEP, 91, r)))
+                for r in range(8)]
+        xr = tensors.device_tensor(inputs.activation_rows(1, k, key=(configs.CFG_SWEEP, 91, k))[0])
+        hr = torch.zeros(n, dtype=torch.float32, device="cuda")
+        yr = torch.empty(n, dtype=torch.float32, device="cuda")
+        ii = [0]
+
+        def fused_res():
+            tensors.gemv_residual(mats[ii[0] % 8], xr, hr, hr)
+            ii[0] += 1
+
+        def gemv_then_add():
+            tensors.gemv(mats[ii[0] % 8], xr, yr)
+            hr.add_(yr)
+            ii[0] += 1
+        ms_f = timer(fused_res, reps=40)
+        ms_s = timer(gemv_then_add, reps=40)
+        resid[label] = {"fused_us": round(ms_f * 1e3, 2), "gemv_plus_add_us": round(ms_s * 1e3, 2)}
+        del mats
+        log("residual %s: fused %.1f us, gemv + add %.1f us" % (label, ms_f * 1e3, ms_s * 1e3))
+    out["residual_fusion_q4"] = resid
+
     # MoE expert projections (Qwen3-30B-A3B shapes).
     moe = {}
     e, top = configs.MOE["n_experts"], configs.MOE["top_k"]

@@ -19,7 +19,7 @@ __all__ = [
     "QmmError", "library_path", "load",
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
     "qmm_gemv_batch_prepare", "qmm_gemv_batched", "GemvDesc", "qmm_gemv_swiglu", "qmm_gemm_f16out",
-    "qmm_moe_swiglu",
+    "qmm_moe_swiglu", "qmm_gemv_residual",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
     "QMM_OK", "QMM_ERR_INVALID_ARGUMENT", "QMM_ERR_UNSUPPORTED", "QMM_ERR_MISALIGNED",
     "QMM_ERR_DEVICE", "EXPORTED_SYMBOLS",
@@ -34,7 +34,7 @@ QMM_ERR_DEVICE = 4
 EXPORTED_SYMBOLS = (
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
     "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out",
-    "qmm_moe_swiglu",
+    "qmm_moe_swiglu", "qmm_gemv_residual",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
 )
 
@@ -106,6 +106,7 @@ def load():
     lib.qmm_gemv.argtypes = [p, p, p, p, p, i64, i64, ci, ci, p]
     lib.qmm_gemm.argtypes = [p, p, p, p, p, i64, i64, i64, ci, ci, p, sz, p]
     lib.qmm_gemv_swiglu.argtypes = [p, p, p, p, p, p, p, p, i64, i64, ci, ci, p]
+    lib.qmm_gemv_residual.argtypes = [p, p, p, p, p, p, i64, i64, ci, ci, p]
     lib.qmm_gemm_f16out.argtypes = [p, p, p, p, p, i64, i64, i64, ci, ci, p, sz, p]
     lib.qmm_gemm_workspace_bytes.argtypes = [i64, i64, i64, ci, ci]
     lib.qmm_gemm_workspace_bytes.restype = sz
@@ -116,7 +117,8 @@ def load():
     lib.qmm_gemv_batched.argtypes = [p, p, i64, ci, ci, p]
     lib.qmm_get_plan.argtypes = [ci, i64, i64, i64, ci, ci, ci, sz, ctypes.POINTER(_Plan)]
     for f in ("qmm_gemv", "qmm_gemm", "qmm_moe_gemm", "qmm_unpack", "qmm_get_plan",
-              "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out", "qmm_moe_swiglu"):
+              "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out", "qmm_moe_swiglu",
+              "qmm_gemv_residual"):
         getattr(lib, f).restype = ci
     lib.qmm_status_string.argtypes = [ci]
     lib.qmm_status_string.restype = ctypes.c_char_p
@@ -166,6 +168,15 @@ def qmm_gemv(w_packed, scales, mins, x, y, n, k, bits, group_size, stream=None) 
     _check(load().qmm_gemv(_addr(w_packed), _addr(scales), _addr(mins), _addr(x), _addr(y),
                            int(n), int(k), int(bits), int(group_size), _stream(stream)),
            "qmm_gemv")
+
+
+def qmm_gemv_residual(w_packed, scales, mins, x, residual, y, n, k, bits, group_size,
+                      stream=None) -> None:
+    """y[n] = residual[n] + sum_k (s*q + m)[n][k] x[k] (residual may be y); asynchronous."""
+    _check(load().qmm_gemv_residual(_addr(w_packed), _addr(scales), _addr(mins), _addr(x),
+                                    _addr(residual), _addr(y), int(n), int(k), int(bits),
+                                    int(group_size), _stream(stream)),
+           "qmm_gemv_residual")
 
 
 def qmm_gemv_swiglu(gate_w, gate_scales, gate_mins, up_w, up_scales, up_mins, x, h, n, k, bits,

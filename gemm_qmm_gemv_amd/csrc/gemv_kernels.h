@@ -147,11 +147,11 @@ __device__ __forceinline__ void accumulate_batch(const RowBatch<B, UNIT, XC, U>&
 // store is unconditional: lanes with nothing to write aim past the end of y.
 template <int LPR, int U>
 __device__ __forceinline__ void store_batch(float (&yacc)[U], rsrc_t yr, int rb, int n, int slot,
-                                            int j) {
+                                            int j, const float (&res)[U]) {
     constexpr int SLOTS = 64 / LPR;
 #pragma unroll
     for (int r = 0; r < U; ++r) {
-        const float v = group_sum<LPR>(yacc[r]);
+        const float v = group_sum<LPR>(yacc[r]) + res[r];
         const int row = rb + r * SLOTS + slot;
         buffer_store_f32(v, yr, (j == 0 && row < n) ? (uint32_t)row * 4u : (uint32_t)n * 4u);
     }
@@ -163,12 +163,21 @@ __device__ __forceinline__ void store_batch(float (&yacc)[U], rsrc_t yr, int rb,
 // the first batch's loads before the activation set-up, so memory latency
 // overlaps both.  Multi-pass (MP, larger k): each row batch walks k in passes
 // and rebuilds the activation units per pass (no pipelining).
-template <int B, int UNIT, int LPR, int XC, int U, bool MP>
+//
+// The output pointer is restrict-qualified unless the residual may alias it.
+template <bool RES>
+using out_ptr = std::conditional_t<RES, float*, float* __restrict__>;
+
+// RES: R holds an fp32 residual [n] added to every output (y = r + W x).  It
+// may be y itself: each row's residual is read, by the lanes of that row's
+// slot, before the row is written.  Without RES, R is ignored and the
+// kernel issues no residual loads.
+template <int B, int UNIT, int LPR, int XC, int U, bool MP, bool RES = false>
 __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
                                                    const uint16_t* __restrict__ S,
                                                    const uint16_t* __restrict__ Mn,
                                                    const uint16_t* __restrict__ X,
-                                                   float* __restrict__ Y, int n, int k, int group) {
+                                                   out_ptr<RES> Y, int n, int k, int group, const float* R) {
     constexpr int SLOTS = 64 / LPR;
     const int lane = threadIdx.x & 63;
     const int slot = lane / LPR, j = lane % LPR;
@@ -182,6 +191,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
     const MatRsrc mr = mat_rsrc<B>(W, S, Mn, n, wpr, gpr);
     const rsrc_t xr = make_rsrc(X, (uint32_t)k * 2u);
     const rsrc_t yr = make_rsrc(Y, (uint32_t)n * 4u);
+    const rsrc_t rr = make_rsrc(R, RES ? (uint32_t)n * 4u : 0u);
+    // The residuals of a batch's rows (zero past n, or without RES).
+    auto load_res = [&](int rb, bool live, float (&res)[U]) {
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            if constexpr (!RES) {
+                res[r] = -0.f;  // x + (-0) is x for every x: the add folds away
+                continue;
+            }
+            const int row = rb + r * SLOTS + slot;
+            res[r] = __builtin_bit_cast(float, buffer_u32(rr, (live && row < n) ? (uint32_t)row * 4u : (uint32_t)n * 4u));
+        }
+    };
 
     XUnit<B, UNIT> xu[XC];
     int unit[XC], gidx[XC];
@@ -210,6 +232,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
                 float yacc[U];
 #pragma unroll
                 for (int r = 0; r < U; ++r) yacc[r] = 0.f;
+                float res[U];
+                load_res(rb, true, res);
                 for (int pass = 0; pass < passes; ++pass) {
                     units_of_pass(pass);
                     RowBatch<B, UNIT, XC, U> bt;
@@ -217,14 +241,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
                     prep();
                     accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(bt, xu, yacc, slot, gpr, gidx);
                 }
-                store_batch<LPR, U>(yacc, yr, rb, n, slot, j);
+                store_batch<LPR, U>(yacc, yr, rb, n, slot, j, res);
             }
         } else {
             units_of_pass(0);
             int rb = wave * SLOTS * U;
             if (rb >= n) return;
             RowBatch<B, UNIT, XC, U> ba, bb;
+            float ra[U], rb_res[U];
             load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, rb, true, wpr, gpr, slot, unit, gidx, nu, lane);
+            load_res(rb, true, ra);
             // The first batch's weight loads go out before the activation
             // loads and their set-up arithmetic.
             __builtin_amdgcn_sched_barrier(0);
@@ -233,18 +259,20 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
                 float yacc[U];
                 int nxt = rb + stride;
                 load_batch<B, UNIT, LPR, XC, U, WIDE>(bb, mr, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
+                load_res(nxt, nxt < n, rb_res);
 #pragma unroll
                 for (int r = 0; r < U; ++r) yacc[r] = 0.f;
                 accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(ba, xu, yacc, slot, gpr, gidx);
-                store_batch<LPR, U>(yacc, yr, rb, n, slot, j);
+                store_batch<LPR, U>(yacc, yr, rb, n, slot, j, ra);
                 rb = nxt;
                 if (rb >= n) break;
                 nxt = rb + stride;
                 load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, nxt, nxt < n, wpr, gpr, slot, unit, gidx, nu, lane);
+                load_res(nxt, nxt < n, ra);
 #pragma unroll
                 for (int r = 0; r < U; ++r) yacc[r] = 0.f;
                 accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(bb, xu, yacc, slot, gpr, gidx);
-                store_batch<LPR, U>(yacc, yr, rb, n, slot, j);
+                store_batch<LPR, U>(yacc, yr, rb, n, slot, j, rb_res);
                 rb = nxt;
                 if (rb >= n) break;
             }
@@ -833,18 +861,21 @@ __global__ __launch_bounds__(256) void gemv_batched_kernel(const BatchDesc* __re
 
 // ---- launch templates (instantiated per bit width in gemv_bits.hip) -----------
 
+template <auto Kernel>
+hipError_t launch_gemv_k(const GemvArgs& a, const GemvShape& sh, hipStream_t st) {
+    const int grid = persistent_grid(sh.work, sh.cus, blocks_per_cu<Kernel>(), sh.waves_per_cu);
+    hipLaunchKernelGGL(Kernel, dim3(grid), dim3(256), 0, st, a.w, a.s, a.m, a.x, a.y, a.n, a.k, a.group, a.r);
+    return hipGetLastError();
+}
+
 template <int B, int UNIT, int LPR, int XC, int U>
 hipError_t launch_gemv_t(const GemvArgs& a, const GemvShape& sh, hipStream_t st) {
     if (sh.multipass) {
-        constexpr auto kern = gemv_kernel<B, UNIT, LPR, XC, U, true>;
-        const int grid = persistent_grid(sh.work, sh.cus, blocks_per_cu<kern>(), sh.waves_per_cu);
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, a.w, a.s, a.m, a.x, a.y, a.n, a.k, a.group);
-    } else {
-        constexpr auto kern = gemv_kernel<B, UNIT, LPR, XC, U, false>;
-        const int grid = persistent_grid(sh.work, sh.cus, blocks_per_cu<kern>(), sh.waves_per_cu);
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, a.w, a.s, a.m, a.x, a.y, a.n, a.k, a.group);
+        if (a.r) return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, true, true>>(a, sh, st);
+        return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, true, false>>(a, sh, st);
     }
-    return hipGetLastError();
+    if (a.r) return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, false, true>>(a, sh, st);
+    return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, false, false>>(a, sh, st);
 }
 
 template <int B, int UNIT, int XC, int U>

@@ -387,6 +387,25 @@ qmm_status qmm_gemv(const void* w_packed, const void* scales, const void* mins, 
     return launched(launch_gemv(a, sh, as_stream(stream)), "qmm_gemv");
 }
 
+qmm_status qmm_gemv_residual(const void* w_packed, const void* scales, const void* mins, const void* x,
+                             const float* residual, float* y, int64_t n, int64_t k, int bits,
+                             int group_size, void* stream) {
+    qmm_status st = check_format(n, k, bits, group_size);
+    if (st != QMM_OK) return st;
+    if (n == 0) return ok();
+    if ((st = check_weight_ptrs(w_packed, scales, mins, bits)) != QMM_OK) return st;
+    if (!x || !y || !residual) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x, residual or y");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(QMM_ERR_MISALIGNED, "x or y not 16-byte aligned");
+    if (!aligned(residual, 4)) return fail(QMM_ERR_MISALIGNED, "residual not 4-byte aligned");
+    int cus = 0;
+    if ((st = device_cus(&cus)) != QMM_OK) return st;
+    const GemvShape sh = plan_gemv(n, k, bits, group_size, cus);
+    GemvArgs a{static_cast<const uint32_t*>(w_packed), static_cast<const uint16_t*>(scales),
+               static_cast<const uint16_t*>(mins), static_cast<const uint16_t*>(x), y, (int)n, (int)k,
+               group_size, bits, residual};
+    return launched(launch_gemv(a, sh, as_stream(stream)), "qmm_gemv_residual");
+}
+
 qmm_status qmm_gemv_swiglu(const void* gate_w, const void* gate_scales, const void* gate_mins,
                            const void* up_w, const void* up_scales, const void* up_mins, const void* x,
                            float* h, int64_t n, int64_t k, int bits, int group_size, void* stream) {

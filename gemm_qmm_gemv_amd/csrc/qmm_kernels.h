@@ -14,6 +14,7 @@ struct GemvArgs {
     const uint16_t* x;
     float* y;
     int n, k, group, bits;
+    const float* r = nullptr;  // residual added to y (may be y), or null
 };
 
 struct GemvShape {

@@ -8,7 +8,7 @@ import numpy as np
 import torch
 
 from . import (GemvDesc, qmm_gemm, qmm_gemm_f16out, qmm_gemm_workspace_bytes, qmm_gemv, qmm_gemv_batch_prepare,
-               qmm_gemv_swiglu, qmm_moe_swiglu,
+               qmm_gemv_swiglu, qmm_moe_swiglu, qmm_gemv_residual,
                qmm_gemv_batched, qmm_moe_gemm, qmm_unpack)
 
 
@@ -36,6 +36,16 @@ def gemv(dq: dict, x: torch.Tensor, y: torch.Tensor | None = None, stream=None) 
         y = torch.empty(dq["n"], dtype=torch.float32, device=x.device)
     qmm_gemv(dq["w"], dq["scales"], dq["mins"], x, y, dq["n"], dq["k"], dq["bits"], dq["group"],
              stream=stream)
+    return y
+
+
+def gemv_residual(dq: dict, x: torch.Tensor, residual: torch.Tensor, y: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """y = residual + W x in one launch (residual may be y)."""
+    if y is None:
+        y = torch.empty(dq["n"], dtype=torch.float32, device=x.device)
+    qmm_gemv_residual(dq["w"], dq["scales"], dq["mins"], x, residual, y, dq["n"], dq["k"], dq["bits"],
+                      dq["group"], stream=stream)
     return y
 
 

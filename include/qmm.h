@@ -92,6 +92,19 @@ QMM_API qmm_status qmm_gemv(const void *w_packed, const void *scales, const void
                     const void *x, float *y, int64_t n, int64_t k,
                     int bits, int group_size, void *stream);
 
+/* Decode GEMV with the residual add fused into its epilogue:
+ *   y[n] = residual[n] + sum_k (s*q + m)[n][k] * x[k].
+ * Pages: "BaseRT claims fastest Apple Silicon inference", section "What
+ * BaseRT does differently" (fusion removes a launch and a global-memory round
+ * trip per fusion; residual buffers are part of the decode loop's state).
+ *   residual fp32 [n], 4-byte aligned, non-NULL; it may be y itself (y +=
+ *   W x: each row's residual is read before that row is written).  Other
+ *   arguments as qmm_gemv.                                                  */
+QMM_API qmm_status qmm_gemv_residual(const void *w_packed, const void *scales,
+                                     const void *mins, const void *x, const float *residual,
+                                     float *y, int64_t n, int64_t k, int bits, int group_size,
+                                     void *stream);
+
 /* Fused gate/up projection of a feed-forward block (decode, M = 1):
  *   h[n] = silu(g[n]) * u[n],  g = Wg x,  u = Wu x,  silu(v) = v / (1 + e^-v).
  * Pages: "BaseRT claims fastest Apple Silicon inference", section "What

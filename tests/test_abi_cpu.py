@@ -131,6 +131,19 @@ def test_swiglu_argument_checks(lib):
     assert f(*args, 64, 128, 7, 64, None) == qmm.QMM_ERR_UNSUPPORTED
 
 
+def test_residual_argument_checks(lib):
+    p = ctypes.c_void_p
+    f = lib.qmm_gemv_residual
+    w4 = [p(A16)] * 4
+    assert f(*w4, p(A16), p(A16), 64, 128, 4, 64, None) in (qmm.QMM_ERR_DEVICE, qmm.QMM_OK)
+    assert f(*w4, p(A16), p(A16), 0, 128, 4, 64, None) == qmm.QMM_OK
+    assert f(*w4, None, p(A16), 64, 128, 4, 64, None) == qmm.QMM_ERR_INVALID_ARGUMENT
+    assert f(*w4, p(A16 + 2), p(A16), 64, 128, 4, 64, None) == qmm.QMM_ERR_MISALIGNED
+    assert f(*w4, p(A16), p(A16 + 4), 64, 128, 4, 64, None) == qmm.QMM_ERR_MISALIGNED
+    assert f(*w4, p(A16), p(A16), 64, 128, 7, 64, None) == qmm.QMM_ERR_UNSUPPORTED
+    assert f(*w4, p(A16), p(A16), 64, 100, 4, 64, None) == qmm.QMM_ERR_INVALID_ARGUMENT
+
+
 def test_fp16_weights_need_no_scales(lib):
     import torch
     if torch.cuda.is_available():
