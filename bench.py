@@ -461,11 +461,30 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
         ms_glu = timer(lambda: tensors.moe_swiglu(stacks["gate_proj"], stacks["up_proj"], x_tok, rows,
                                                   off, p, h=ho), reps=30)
         ms_fused = ms_glu + row["down_proj"]["us"] * 1e-3
+        # Down projection with the routing-weighted combine into the token
+        # rows (one launch), against the plain down projection followed by a
+        # weighted scatter-add in torch.
+        pt = tensors.device_tensor(r["pair_token"])
+        pt64 = pt.long()
+        pw = tensors.device_tensor(r["pair_weight"])
+        yc = torch.zeros((tokens, 2048), dtype=torch.float32, device="cuda")
+        ms_cmb = timer(lambda: tensors.moe_combine(stacks["down_proj"], x_pair, None, off, pt, pw, p, yc),
+                       reps=30)
+
+        def down_then_scatter():
+            tensors.moe(stacks["down_proj"], x_pair, None, off, p, y=yo_down)
+            yc.index_add_(0, pt64, yo_down * pw[:, None])
+        yo_down = torch.empty((p, 2048), dtype=torch.float32, device="cuda")
+        ms_scatter = timer(down_then_scatter, reps=30)
         moe["t%d" % tokens] = {"distinct_experts": distinct, "us": round(tot_ms * 1e3, 2),
                                "GBps": round(tot_b / tot_ms / 1e6, 1), "proj": row,
                                "fused_gate_up_us": round(ms_glu * 1e3, 2),
-                               "us_with_fused_gate_up": round(ms_fused * 1e3, 2)}
-        log("moe T=%d: %.1f us (gate|up fused: %.1f us)" % (tokens, tot_ms * 1e3, ms_fused * 1e3))
+                               "us_with_fused_gate_up": round(ms_fused * 1e3, 2),
+                               "down_combine_fused_us": round(ms_cmb * 1e3, 2),
+                               "down_then_scatter_add_us": round(ms_scatter * 1e3, 2),
+                               "us_fully_fused": round((ms_glu + ms_cmb) * 1e3, 2)}
+        log("moe T=%d: %.1f us (gate|up fused: %.1f us; + fused combine: %.1f us)"
+            % (tokens, tot_ms * 1e3, ms_fused * 1e3, (ms_glu + ms_cmb) * 1e3))
     out["moe_qwen3_30b_a3b_q4"] = moe
     return out
 

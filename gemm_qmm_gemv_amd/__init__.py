@@ -19,7 +19,7 @@ __all__ = [
     "QmmError", "library_path", "load",
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
     "qmm_gemv_batch_prepare", "qmm_gemv_batched", "GemvDesc", "qmm_gemv_swiglu", "qmm_gemm_f16out",
-    "qmm_moe_swiglu", "qmm_gemv_residual",
+    "qmm_moe_swiglu", "qmm_gemv_residual", "qmm_moe_combine",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
     "QMM_OK", "QMM_ERR_INVALID_ARGUMENT", "QMM_ERR_UNSUPPORTED", "QMM_ERR_MISALIGNED",
     "QMM_ERR_DEVICE", "EXPORTED_SYMBOLS",
@@ -34,7 +34,7 @@ QMM_ERR_DEVICE = 4
 EXPORTED_SYMBOLS = (
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
     "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out",
-    "qmm_moe_swiglu", "qmm_gemv_residual",
+    "qmm_moe_swiglu", "qmm_gemv_residual", "qmm_moe_combine",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
 )
 
@@ -112,13 +112,14 @@ def load():
     lib.qmm_gemm_workspace_bytes.restype = sz
     lib.qmm_moe_gemm.argtypes = [p, p, p, p, p, i64, p, p, i64, i64, i64, i64, ci, ci, p]
     lib.qmm_moe_swiglu.argtypes = [p, p, p, p, p, p, p, p, i64, p, p, i64, i64, i64, i64, ci, ci, p]
+    lib.qmm_moe_combine.argtypes = [p, p, p, p, p, i64, p, p, p, p, i64, i64, i64, i64, i64, ci, ci, p]
     lib.qmm_unpack.argtypes = [p, p, i64, i64, ci, p]
     lib.qmm_gemv_batch_prepare.argtypes = [p, i64, ci, ci]
     lib.qmm_gemv_batched.argtypes = [p, p, i64, ci, ci, p]
     lib.qmm_get_plan.argtypes = [ci, i64, i64, i64, ci, ci, ci, sz, ctypes.POINTER(_Plan)]
     for f in ("qmm_gemv", "qmm_gemm", "qmm_moe_gemm", "qmm_unpack", "qmm_get_plan",
               "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out", "qmm_moe_swiglu",
-              "qmm_gemv_residual"):
+              "qmm_gemv_residual", "qmm_moe_combine"):
         getattr(lib, f).restype = ci
     lib.qmm_status_string.argtypes = [ci]
     lib.qmm_status_string.restype = ctypes.c_char_p
@@ -218,6 +219,18 @@ def qmm_moe_gemm(w_packed, scales, mins, x, x_rows, x_rows_count, expert_offsets
                                int(p_rows), int(n_experts), int(n), int(k), int(bits),
                                int(group_size), _stream(stream)),
            "qmm_moe_gemm")
+
+
+def qmm_moe_combine(w_packed, scales, mins, x, x_rows, x_rows_count, expert_offsets, pair_token,
+                    pair_weight, y, n_tokens, p_rows, n_experts, n, k, bits, group_size,
+                    stream=None) -> None:
+    """y[token[p]] += weight[p] * W_{e(p)} x[row(p)] (accumulates into y); asynchronous."""
+    _check(load().qmm_moe_combine(_addr(w_packed), _addr(scales), _addr(mins), _addr(x),
+                                  _addr(x_rows), int(x_rows_count), _addr(expert_offsets),
+                                  _addr(pair_token), _addr(pair_weight), _addr(y), int(n_tokens),
+                                  int(p_rows), int(n_experts), int(n), int(k), int(bits),
+                                  int(group_size), _stream(stream)),
+           "qmm_moe_combine")
 
 
 def qmm_moe_swiglu(gate_w, gate_scales, gate_mins, up_w, up_scales, up_mins, x, x_rows,

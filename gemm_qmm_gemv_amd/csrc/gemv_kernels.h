@@ -422,13 +422,21 @@ __device__ __forceinline__ void accumulate_rows(const RowBatch<B, UNIT, XC, 1>& 
 // each output is silu(first) * second -- the gate and up projections of the
 // selected experts and their SiLU-gated product in one launch (the fusion of
 // qmm_gemv_swiglu applied to expert rows).  Single pass only.
-template <int B, int UNIT, int LPR, int XC, int MR, bool MP, bool GLU = false>
+//
+// CMB: weighted combine.  Output row p is not stored; instead
+// pair_weight[p] * (row p) is added to row pair_token[p] of Y [n_tokens][n]
+// with a float atomic add, so the top-k expert outputs of a token land in
+// one row (on top of whatever Y held, e.g. the residual stream).  The order
+// of the adds into one element is not fixed.  Pairs whose token is outside
+// [0, n_tokens) add nothing.
+template <int B, int UNIT, int LPR, int XC, int MR, bool MP, bool GLU = false, bool CMB = false>
 __global__ __launch_bounds__(256) void gemv_rows_kernel(
     const u32* __restrict__ W, const uint16_t* __restrict__ S, const uint16_t* __restrict__ Mn,
     const u32* __restrict__ W2, const uint16_t* __restrict__ S2, const uint16_t* __restrict__ M2,
     const uint16_t* __restrict__ X, const int32_t* __restrict__ x_rows, int x_count,
     const int32_t* __restrict__ offsets, int n_seg, int m_total, float* __restrict__ Y, int n,
-    int k, int group, int pair_bound) {
+    int k, int group, int pair_bound, const int32_t* __restrict__ pair_token,
+    const float* __restrict__ pair_weight, int n_tokens) {
     constexpr int SLOTS = 64 / LPR;
     constexpr int WPU = UNIT * B / 32;
     constexpr int ALIGN = unit_align(B, UNIT);
@@ -507,12 +515,14 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
         const MatRsrc mr2 = mat_rsrc<B>(We2, Se2, Me2, n, wpr, gpr);
         const uint32_t x_bytes = (uint32_t)x_count * (uint32_t)k * 2u;
         const rsrc_t xbuf = make_rsrc(X, x_bytes);
-        const uint32_t y_bytes = (uint32_t)m_total * (uint32_t)n * 4u;
+        const uint32_t y_bytes = (uint32_t)(CMB ? n_tokens : m_total) * (uint32_t)n * 4u;
         const rsrc_t yr = make_rsrc(Y, y_bytes);
 
-        // Activation row indices of one MR-batch; out-of-range indices give NaN.
-        int xr[MR];
+        // Activation row indices of one MR-batch; out-of-range indices give
+        // NaN.  With CMB also each row's token (-1: adds nothing) and weight.
+        int xr[MR], tok[MR];
         bool bad[MR];
+        float wgt[MR];
         auto rows_of = [&](int pb) {
 #pragma unroll
             for (int r = 0; r < MR; ++r) {
@@ -520,6 +530,11 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
                 const int idx = (p < p1) ? (x_rows ? x_rows[p] : p) : -1;
                 bad[r] = (p < p1) && (idx < 0 || idx >= x_count);
                 xr[r] = (p < p1 && !bad[r]) ? idx : -1;
+                if constexpr (CMB) {
+                    const int t = (p < p1) ? pair_token[p] : -1;
+                    tok[r] = (t >= 0 && t < n_tokens) ? t : -1;
+                    wgt[r] = (p < p1) ? pair_weight[p] : 0.f;
+                }
             }
         };
         XUnit<B, UNIT> xu[MR][XC];
@@ -539,11 +554,17 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
         auto store_rows = [&](float (&yacc)[MR], int pb, int row) {
 #pragma unroll
             for (int r = 0; r < MR; ++r) {
-                const float v = group_sum<LPR>(yacc[r]);
+                const float sum = group_sum<LPR>(yacc[r]);
+                const float v = bad[r] ? __builtin_nanf("") : sum;
                 const int p = pb + r;
-                const bool ok = j == 0 && row < n && p < p1;
-                buffer_store_f32(bad[r] ? __builtin_nanf("") : v, yr,
-                                 ok ? ((uint32_t)p * (uint32_t)n + (uint32_t)row) * 4u : y_bytes);
+                if constexpr (CMB) {
+                    const bool ok = j == 0 && row < n && tok[r] >= 0;
+                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                        wgt[r] * v, yr, ok ? ((uint32_t)tok[r] * (uint32_t)n + (uint32_t)row) * 4u : y_bytes, 0, 0);
+                } else {
+                    const bool ok = j == 0 && row < n && p < p1;
+                    buffer_store_f32(v, yr, ok ? ((uint32_t)p * (uint32_t)n + (uint32_t)row) * 4u : y_bytes);
+                }
             }
         };
         auto store_rows_glu = [&](float (&gacc)[MR], float (&uacc)[MR], int pb, int row) {
@@ -558,6 +579,7 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
             }
         };
         static_assert(!(MP && GLU), "the fused gate/up rows are single-pass only");
+        static_assert(!(GLU && CMB), "the combine follows the down projection, not gate/up");
 
         if constexpr (MP) {
             for (int pb = p0; pb < p1; pb += MR) {
@@ -898,23 +920,27 @@ inline dim3 rows_grid(const RowsShape& sh) {
     return dim3((unsigned)gx, (unsigned)sh.grid_y);
 }
 
+template <auto Kernel>
+hipError_t launch_rows_k(const RowsArgs& a, const RowsShape& sh, hipStream_t st, bool second_stack) {
+    hipLaunchKernelGGL(Kernel, rows_grid<Kernel>(sh), dim3(256), 0, st, a.w, a.s, a.m,
+                       second_stack ? a.w2 : a.w, second_stack ? a.s2 : a.s, second_stack ? a.m2 : a.m, a.x,
+                       a.x_rows, a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group, sh.pairs,
+                       a.pair_token, a.pair_weight, a.n_tokens);
+    return hipGetLastError();
+}
+
 template <int B, int UNIT, int LPR, int XC, int MR>
 hipError_t launch_rows_t(const RowsArgs& a, const RowsShape& sh, hipStream_t st) {
     if (a.w2) {
         if (sh.multipass) return hipErrorInvalidValue;  // the host rejects this before
-        constexpr auto kern = gemv_rows_kernel<B, UNIT, LPR, XC, MR, false, true>;
-        hipLaunchKernelGGL(kern, rows_grid<kern>(sh), dim3(256), 0, st, a.w, a.s, a.m, a.w2, a.s2, a.m2, a.x,
-                           a.x_rows, a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group, sh.pairs);
-    } else if (sh.multipass) {
-        constexpr auto kern = gemv_rows_kernel<B, UNIT, LPR, XC, MR, true>;
-        hipLaunchKernelGGL(kern, rows_grid<kern>(sh), dim3(256), 0, st, a.w, a.s, a.m, a.w, a.s, a.m, a.x,
-                           a.x_rows, a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group, sh.pairs);
-    } else {
-        constexpr auto kern = gemv_rows_kernel<B, UNIT, LPR, XC, MR, false>;
-        hipLaunchKernelGGL(kern, rows_grid<kern>(sh), dim3(256), 0, st, a.w, a.s, a.m, a.w, a.s, a.m, a.x,
-                           a.x_rows, a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group, sh.pairs);
+        return launch_rows_k<gemv_rows_kernel<B, UNIT, LPR, XC, MR, false, true>>(a, sh, st, true);
     }
-    return hipGetLastError();
+    if (a.pair_token) {
+        if (sh.multipass) return launch_rows_k<gemv_rows_kernel<B, UNIT, LPR, XC, MR, true, false, true>>(a, sh, st, false);
+        return launch_rows_k<gemv_rows_kernel<B, UNIT, LPR, XC, MR, false, false, true>>(a, sh, st, false);
+    }
+    if (sh.multipass) return launch_rows_k<gemv_rows_kernel<B, UNIT, LPR, XC, MR, true>>(a, sh, st, false);
+    return launch_rows_k<gemv_rows_kernel<B, UNIT, LPR, XC, MR, false>>(a, sh, st, false);
 }
 
 template <int B, int UNIT, int LPR, int XC>

@@ -514,16 +514,24 @@ qmm_status moe_common(const void* w_packed, const void* scales, const void* mins
                       const void* up_s, const void* up_m, const void* x, const int32_t* x_rows,
                       int64_t x_rows_count, const int32_t* expert_offsets, float* y, int64_t p_rows,
                       int64_t n_experts, int64_t n, int64_t k, int bits, int group_size, void* stream,
-                      bool glu) {
+                      bool glu, const int32_t* pair_token = nullptr, const float* pair_weight = nullptr,
+                      int64_t n_tokens = 0) {
+    const bool combine = pair_token != nullptr || pair_weight != nullptr;
     qmm_status st = check_format(n, k, bits, group_size);
     if (st != QMM_OK) return st;
     if (p_rows < 0 || n_experts < 0 || x_rows_count < 0)
         return fail(QMM_ERR_INVALID_ARGUMENT, "negative p_rows, n_experts or x_rows_count");
     if (p_rows > INT_LIMIT || n_experts > INT_LIMIT || x_rows_count > INT_LIMIT)
         return fail(QMM_ERR_INVALID_ARGUMENT, "p_rows, n_experts or x_rows_count above 2^31-1");
-    if (p_rows == 0 || n == 0 || n_experts == 0) return ok();
+    if (combine && (n_tokens < 0 || n_tokens > INT_LIMIT))
+        return fail(QMM_ERR_INVALID_ARGUMENT, "n_tokens=%lld out of range", (long long)n_tokens);
+    if (p_rows == 0 || n == 0 || n_experts == 0 || (combine && n_tokens == 0)) return ok();
     if ((st = check_activation_bytes(x_rows ? x_rows_count : p_rows, k)) != QMM_OK) return st;
-    if ((st = check_output_bytes(p_rows, n)) != QMM_OK) return st;
+    if ((st = check_output_bytes(combine ? n_tokens : p_rows, n)) != QMM_OK) return st;
+    if (combine && (!pair_token || !pair_weight))
+        return fail(QMM_ERR_INVALID_ARGUMENT, "NULL pair_token or pair_weight");
+    if (combine && (!aligned(pair_token, 4) || !aligned(pair_weight, 4)))
+        return fail(QMM_ERR_MISALIGNED, "pair_token or pair_weight not 4-byte aligned");
     if ((st = check_weight_ptrs(w_packed, scales, mins, bits)) != QMM_OK) return st;
     if (glu && (st = check_weight_ptrs(up_w, up_s, up_m, bits)) != QMM_OK) return st;
     if (!x || !y || !expert_offsets) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x, y or expert_offsets");
@@ -543,12 +551,18 @@ qmm_status moe_common(const void* w_packed, const void* scales, const void* mins
                static_cast<const uint16_t*>(mins), static_cast<const uint16_t*>(x), x_rows,
                (int)x_rows_count, expert_offsets, (int)n_experts, (int)p_rows, y, (int)n, (int)k,
                group_size, bits};
+    if (combine) {
+        a.pair_token = pair_token;
+        a.pair_weight = pair_weight;
+        a.n_tokens = (int)n_tokens;
+    }
     if (glu) {
         a.w2 = static_cast<const uint32_t*>(up_w);
         a.s2 = static_cast<const uint16_t*>(up_s);
         a.m2 = static_cast<const uint16_t*>(up_m);
     }
-    return launched(launch_rows(a, sh, as_stream(stream)), glu ? "qmm_moe_swiglu" : "qmm_moe_gemm");
+    return launched(launch_rows(a, sh, as_stream(stream)),
+                    glu ? "qmm_moe_swiglu" : combine ? "qmm_moe_combine" : "qmm_moe_gemm");
 }
 
 }  // namespace
@@ -561,6 +575,17 @@ qmm_status qmm_moe_gemm(const void* w_packed, const void* scales, const void* mi
                         int group_size, void* stream) {
     return moe_common(w_packed, scales, mins, nullptr, nullptr, nullptr, x, x_rows, x_rows_count,
                       expert_offsets, y, p_rows, n_experts, n, k, bits, group_size, stream, false);
+}
+
+qmm_status qmm_moe_combine(const void* w_packed, const void* scales, const void* mins, const void* x,
+                           const int32_t* x_rows, int64_t x_rows_count, const int32_t* expert_offsets,
+                           const int32_t* pair_token, const float* pair_weight, float* y, int64_t n_tokens,
+                           int64_t p_rows, int64_t n_experts, int64_t n, int64_t k, int bits,
+                           int group_size, void* stream) {
+    if (!pair_token || !pair_weight) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL pair_token or pair_weight");
+    return moe_common(w_packed, scales, mins, nullptr, nullptr, nullptr, x, x_rows, x_rows_count,
+                      expert_offsets, y, p_rows, n_experts, n, k, bits, group_size, stream, false, pair_token,
+                      pair_weight, n_tokens);
 }
 
 qmm_status qmm_moe_swiglu(const void* gate_w, const void* gate_scales, const void* gate_mins,

@@ -87,6 +87,11 @@ struct RowsArgs {
     const uint32_t* w2 = nullptr;
     const uint16_t* s2 = nullptr;
     const uint16_t* m2 = nullptr;
+    // Weighted combine into y [n_tokens][n] (y[token[p]] += weight[p] * row
+    // p); null pair_token for a plain product.
+    const int32_t* pair_token = nullptr;
+    const float* pair_weight = nullptr;
+    int n_tokens = 0;
 };
 
 struct RowsShape {

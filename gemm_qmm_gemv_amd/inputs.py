@@ -103,6 +103,7 @@ def routing(tokens: int, n_experts: int, top_k: int, key=(0,)):
       weights float64 [T][top_k] softmax probabilities of the chosen experts
       pair_token  int32 [P]      token of each (token, slot) pair, P = T*top_k,
       pair_expert int32 [P]      sorted by expert, ties by token
+      pair_weight float32 [P]    routing weight of each pair (same order)
       offsets int32 [E+1]        pairs of expert e are [offsets[e], offsets[e+1])
     """
     rng = rng_for(*key, ROLE_ROUTING)
@@ -120,5 +121,7 @@ def routing(tokens: int, n_experts: int, top_k: int, key=(0,)):
     counts = np.bincount(pair_expert, minlength=n_experts)
     offsets = np.zeros(n_experts + 1, dtype=np.int32)
     offsets[1:] = np.cumsum(counts)
+    pair_weight = weights.reshape(-1)[perm].astype(np.float32)
     return {"logits": logits, "experts": order, "weights": weights,
-            "pair_token": pair_token, "pair_expert": pair_expert, "offsets": offsets}
+            "pair_token": pair_token, "pair_expert": pair_expert, "pair_weight": pair_weight,
+            "offsets": offsets}

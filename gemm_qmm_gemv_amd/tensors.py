@@ -8,7 +8,7 @@ import numpy as np
 import torch
 
 from . import (GemvDesc, qmm_gemm, qmm_gemm_f16out, qmm_gemm_workspace_bytes, qmm_gemv, qmm_gemv_batch_prepare,
-               qmm_gemv_swiglu, qmm_moe_swiglu, qmm_gemv_residual,
+               qmm_gemv_swiglu, qmm_moe_swiglu, qmm_gemv_residual, qmm_moe_combine,
                qmm_gemv_batched, qmm_moe_gemm, qmm_unpack)
 
 
@@ -84,6 +84,17 @@ def moe(dst: dict, x: torch.Tensor, x_rows: torch.Tensor | None, offsets: torch.
         y = torch.empty((p_rows, dst["n"]), dtype=torch.float32, device=x.device)
     qmm_moe_gemm(dst["w"], dst["scales"], dst["mins"], x, x_rows, x.shape[0], offsets, y, p_rows,
                  dst["n_experts"], dst["n"], dst["k"], dst["bits"], dst["group"], stream=stream)
+    return y
+
+
+def moe_combine(dst: dict, x: torch.Tensor, x_rows: torch.Tensor | None, offsets: torch.Tensor,
+                pair_token: torch.Tensor, pair_weight: torch.Tensor, p_rows: int, y: torch.Tensor,
+                stream=None) -> torch.Tensor:
+    """Expert rows with the routing-weighted combine: y[token[p]] += weight[p] * row p
+    (y [tokens][n] fp32, accumulated in place)."""
+    qmm_moe_combine(dst["w"], dst["scales"], dst["mins"], x, x_rows, x.shape[0], offsets, pair_token,
+                    pair_weight, y, y.shape[0], p_rows, dst["n_experts"], dst["n"], dst["k"], dst["bits"],
+                    dst["group"], stream=stream)
     return y
 
 

@@ -229,6 +229,28 @@ QMM_API qmm_status qmm_moe_swiglu(const void *gate_w, const void *gate_scales,
                                   int64_t n_experts, int64_t n, int64_t k, int bits,
                                   int group_size, void *stream);
 
+/* Expert projection with the routing-weighted combine fused into its store:
+ *   y[pair_token[p]][j] += pair_weight[p] * sum_k w_e[j][k] * x[row(p)][k]
+ * for every row p of expert e, so each token's row of y receives the
+ * weighted sum of its selected experts' outputs (the MoE down projection and
+ * combine in one launch; y may hold the residual stream beforehand).
+ * Pages: as qmm_moe_gemm (expert rows) and as qmm_gemv_swiglu (fusion of
+ * operator sequences saves a launch and a round trip through memory).
+ *   pair_token int32 [p_rows], pair_weight fp32 [p_rows] (device, 4-byte
+ *     aligned): token and routing weight of row p.
+ *   y fp32 [n_tokens][n], 16-byte aligned, read and written (accumulated).
+ * Other arguments as qmm_moe_gemm.  The adds into one element of y happen in
+ * no fixed order (float atomics), so results may differ in the last bits
+ * from run to run.  Rows with an activation index out of range add NaN to
+ * their token's row; rows whose token is outside [0, n_tokens) add nothing.
+ * n_tokens == 0 or p_rows == 0 is a no-op.                                  */
+QMM_API qmm_status qmm_moe_combine(const void *w_packed, const void *scales, const void *mins,
+                                   const void *x, const int32_t *x_rows, int64_t x_rows_count,
+                                   const int32_t *expert_offsets, const int32_t *pair_token,
+                                   const float *pair_weight, float *y, int64_t n_tokens,
+                                   int64_t p_rows, int64_t n_experts, int64_t n, int64_t k,
+                                   int bits, int group_size, void *stream);
+
 /* Codes as bytes: codes[n][k] = q[n][k] (uint8).  Bit-exact view of the
  * packed format, used to check the GPU's bit extraction.                   */
 QMM_API qmm_status qmm_unpack(const void *w_packed, uint8_t *codes, int64_t n, int64_t k,

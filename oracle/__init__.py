@@ -299,6 +299,28 @@ def _moe_f16(w, x, x_rows, off, n_experts: int, n: int, k: int):
     return y, a
 
 
+def moe_combine(y_pair, a_pair, pair_token, pair_weight, n_tokens: int, y0=None):
+    """(y, a) [T][N] float64: the routing-weighted sum of each token's expert
+    outputs (the combine step of a mixture-of-experts layer, BaseRT pages,
+    MoE sections): y[t] = y0[t] + sum of pair_weight[p] * y_pair[p] over the
+    pairs p routed from token t; a[t] = sum of |pair_weight[p]| * a_pair[p]
+    (the error scale of the weighted sum).  y0 defaults to zeros.  Weights are
+    taken as given (float32 inputs widened exactly to float64)."""
+    y_pair = np.asarray(y_pair, dtype=np.float64)
+    a_pair = np.asarray(a_pair, dtype=np.float64)
+    tok = np.asarray(pair_token, dtype=np.int64)
+    wgt = np.asarray(pair_weight, dtype=np.float64)
+    n = y_pair.shape[1]
+    y = np.zeros((n_tokens, n)) if y0 is None else np.array(y0, dtype=np.float64).reshape(n_tokens, n)
+    a = np.zeros((n_tokens, n))
+    for p in range(tok.size):
+        t = int(tok[p])
+        if 0 <= t < n_tokens:
+            y[t] += wgt[p] * y_pair[p]
+            a[t] += abs(wgt[p]) * a_pair[p]
+    return y, a
+
+
 def silu(v) -> np.ndarray:
     """silu(v) = v / (1 + e^-v) = v * sigmoid(v), float64 (the gate of a
     SwiGLU feed-forward block: h = silu(Wg x) * (Wu x))."""

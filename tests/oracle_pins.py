@@ -255,6 +255,43 @@ def check_moe_per_expert():
     assert np.array_equal(y2, y)
 
 
+def check_moe_combine():
+    # Token-major brute force: token t's output is the sum over its chosen
+    # experts (slot order) of weight * (dequantized expert matrix @ x[t]),
+    # built from the per-token routing table, not from the expert-sorted
+    # pairs the oracle walks.
+    e, n, k, bits, group, t, top = 7, 20, 128, 3, 64, 6, 3
+    st = inputs.stacked_experts(e, n, k, bits, group, key=(99,))
+    r = inputs.routing(t, e, top, key=(99,))
+    x = inputs.activation_rows(t, k, key=(99,))
+    y0 = inputs.activation_rows(t, n, key=(99, 1)).astype(np.float64)
+    yp, ap = oracle.moe(st["w"], st["scales"], st["mins"], x, r["pair_token"], r["offsets"], e, n, k,
+                        bits, group)
+    y, a = oracle.moe_combine(yp, ap, r["pair_token"], r["pair_weight"], t, y0)
+    for ti in range(t):
+        want, scale = y0[ti].copy(), np.zeros(n)
+        for j in range(top):
+            ex = int(r["experts"][ti, j])
+            wgt = float(np.float32(r["weights"][ti, j]))
+            wd = np_dequant(np_unpack(st["w"][ex], n, k, bits), st["scales"][ex], st["mins"][ex], group)
+            xv = x[ti].astype(np.float64)
+            want += wgt * (wd @ xv)
+            scale += abs(wgt) * (np.abs(wd) @ np.abs(xv))
+        assert np.allclose(y[ti], want, rtol=1e-12, atol=1e-12), ti
+        assert np.allclose(a[ti], scale, rtol=1e-12, atol=0), ti
+    # Top-1 routing with unit weights and no y0 only permutes the rows.
+    r1 = inputs.routing(t, e, 1, key=(99, 2))
+    yp1, ap1 = oracle.moe(st["w"], st["scales"], st["mins"], x, r1["pair_token"], r1["offsets"], e, n,
+                          k, bits, group)
+    y1, _ = oracle.moe_combine(yp1, ap1, r1["pair_token"], np.ones(t, np.float32), t)
+    assert np.array_equal(y1[r1["pair_token"]], yp1)
+    # A pair whose token is out of range adds nothing.
+    tok = r1["pair_token"].copy()
+    tok[0] = t
+    y2, _ = oracle.moe_combine(yp1, ap1, tok, np.ones(t, np.float32), t)
+    assert not np.any(y2[r1["pair_token"][0]]) and np.array_equal(y2[tok[1:]], yp1[1:])
+
+
 # ---- fp16 weights (bits 16) -------------------------------------------------------
 
 def _f16_words(h):
@@ -360,4 +397,5 @@ ALL_CHECKS = [
     check_f16_exact_integer,
     check_f16_moe_per_expert,
     check_silu,
+    check_moe_combine,
 ]

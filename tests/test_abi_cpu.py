@@ -131,6 +131,27 @@ def test_swiglu_argument_checks(lib):
     assert f(*args, 64, 128, 7, 64, None) == qmm.QMM_ERR_UNSUPPORTED
 
 
+def test_combine_argument_checks(lib):
+    p = ctypes.c_void_p
+    f = lib.qmm_moe_combine
+    w3 = [p(A16)] * 3
+
+    def call(tok=A16, wgt=A16, y=A16, n_tokens=4, p_rows=8, bits=4, k=128):
+        return f(*w3, p(A16), None, 8, p(A16), p(tok) if tok else None, p(wgt) if wgt else None,
+                 p(y), n_tokens, p_rows, 2, 64, k, bits, 64, None)
+    assert call() in (qmm.QMM_ERR_DEVICE, qmm.QMM_OK)
+    assert call(n_tokens=0) == qmm.QMM_OK
+    assert call(p_rows=0) == qmm.QMM_OK
+    assert call(tok=0) == qmm.QMM_ERR_INVALID_ARGUMENT
+    assert call(wgt=0) == qmm.QMM_ERR_INVALID_ARGUMENT
+    assert call(tok=A16 + 2) == qmm.QMM_ERR_MISALIGNED
+    assert call(wgt=A16 + 1) == qmm.QMM_ERR_MISALIGNED
+    assert call(y=A16 + 4) == qmm.QMM_ERR_MISALIGNED
+    assert call(n_tokens=-1) == qmm.QMM_ERR_INVALID_ARGUMENT
+    assert call(bits=7) == qmm.QMM_ERR_UNSUPPORTED
+    assert call(k=100) == qmm.QMM_ERR_INVALID_ARGUMENT
+
+
 def test_residual_argument_checks(lib):
     p = ctypes.c_void_p
     f = lib.qmm_gemv_residual

@@ -104,7 +104,34 @@ def _qmm_f16_x_shifted(w_words, x2, n, k):
     return _real_qmm_f16(w_words, np.roll(x2, 1, axis=1), n, k)
 
 
+_real_moe_combine = oracle.moe_combine
+
+
+def _combine_by_pair_index(y_pair, a_pair, pair_token, pair_weight, n_tokens, y0=None):
+    # Sends pair p to row p % n_tokens instead of its token's row.
+    import numpy as np
+    tok = np.arange(len(pair_token), dtype=np.int32) % n_tokens
+    return _real_moe_combine(y_pair, a_pair, tok, pair_weight, n_tokens, y0)
+
+
+def _combine_unweighted(y_pair, a_pair, pair_token, pair_weight, n_tokens, y0=None):
+    import numpy as np
+    return _real_moe_combine(y_pair, a_pair, pair_token, np.ones(len(pair_token)), n_tokens, y0)
+
+
+def _combine_drops_y0(y_pair, a_pair, pair_token, pair_weight, n_tokens, y0=None):
+    return _real_moe_combine(y_pair, a_pair, pair_token, pair_weight, n_tokens, None)
+
+
+def _combine_weight_order_reversed(y_pair, a_pair, pair_token, pair_weight, n_tokens, y0=None):
+    return _real_moe_combine(y_pair, a_pair, pair_token, pair_weight[::-1], n_tokens, y0)
+
+
 PY_MUTANTS = [
+    ("combine_by_pair_index", "moe_combine", _combine_by_pair_index),
+    ("combine_unweighted", "moe_combine", _combine_unweighted),
+    ("combine_drops_y0", "moe_combine", _combine_drops_y0),
+    ("combine_weights_reversed", "moe_combine", _combine_weight_order_reversed),
     ("f16_halves_swapped", "f16_weights", _f16_halves_swapped),
     ("f16_not_decoded", "f16_weights", _f16_as_integers),
     ("f16_abs_sum_signed", "_qmm_f16", _qmm_f16_abs_signed),
