@@ -172,14 +172,102 @@ static_assert(UNROLL_SW % SW_STEPS == 0 && UNROLL_SW % UNROLL == 0, "wide-scale 
 // SW: wide scale loads (see SW_STEPS); the host enables it only for groups of
 // 64, rows of scales 16-byte aligned (K a multiple of 512) and splits that
 // start at multiples of four steps.
+// One tile of y = the sum over splits of the partial sums P [split][M][N],
+// in split order (fp32, or rounded once to fp16 when out16).  Each thread
+// takes up to four 4-column groups at a time and issues the loads of four
+// splits for all of them before adding, so the latencies overlap; loads past
+// the last split or outside the matrix read zeros, and stores outside it are
+// dropped (buffer range checks).  N % 4 != 0 takes single columns.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Cache policy of the split-K partial sums: sc0 | sc1 (system coherence), so
+// stores write through to memory and loads fetch from it, past every cache.
+constexpr int CPOL_COHERENT = 1 | 16;
+// s_waitcnt with vmcnt = 0 (expcnt and lgkmcnt at their maxima, not waited on).
+constexpr int WAITCNT_VM0 = 0x0F70;
+template <int TILE_M, int TN, int THREADS>
+__device__ __forceinline__ void reduce_tile(const float* P, float* Y, int M, int N, int split, int m0, int n0,
+                                            int tid, int out16) {
+    const uint32_t mn = (uint32_t)M * (uint32_t)N;  // floats per split
+    const uint32_t p_bytes = mn * 4u * (uint32_t)split;  // < 2^32: checked on the host
+    const uint32_t y_bytes = mn * (out16 ? 2u : 4u);
+    const rsrc_t pr = make_rsrc(P, p_bytes);
+    const rsrc_t yr = make_rsrc(Y, y_bytes);
+    auto sum_groups = [&](auto vec_c) {
+        constexpr int V = decltype(vec_c)::value;      // columns per group: 4 or 1
+        constexpr int GROUPS = TILE_M * TN / V;          // groups in the tile
+        static_assert(GROUPS % THREADS == 0, "tile reduction layout");
+        constexpr int PER = GROUPS / THREADS;
+        constexpr int E = PER < 4 ? PER : 4;
+        using vec = std::conditional_t<V == 4, f32x4, float>;
+#pragma unroll 1
+        for (int e0 = 0; e0 < PER; e0 += E) {
+            uint32_t off[E];
+            bool ok[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int q = (e0 + e) * THREADS + tid;
+                const int r = m0 + q / (TN / V), c = n0 + V * (q % (TN / V));
+                ok[e] = r < M && c < N;
+                off[e] = (uint32_t)r * (uint32_t)N + (uint32_t)c;  // element index
+            }
+            vec acc[E];
+#pragma unroll 1
+            for (int s0 = 0; s0 < split; s0 += 4) {
+                vec v[4][E];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const uint32_t o = (ok[e] && s0 + j < split) ? ((uint32_t)(s0 + j) * mn + off[e]) * 4u : p_bytes;
+                        if constexpr (V == 4)
+                            v[j][e] = __builtin_bit_cast(
+                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, o, 0, CPOL_COHERENT));
+                        else
+                            v[j][e] = __builtin_bit_cast(
+                                float, __builtin_amdgcn_raw_buffer_load_b32(pr, o, 0, CPOL_COHERENT));
+                    }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[e] = (s0 == 0 && j == 0) ? v[j][e] : acc[e] + v[j][e];
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                if (out16) {
+                    const uint32_t o = ok[e] ? off[e] * 2u : y_bytes;
+                    if constexpr (V == 4) {
+                        const f16 h[4] = {(f16)acc[e][0], (f16)acc[e][1], (f16)acc[e][2], (f16)acc[e][3]};
+                        u32x2 w;
+                        __builtin_memcpy(&w, h, 8);
+                        __builtin_amdgcn_raw_buffer_store_b64(w, yr, o, 0, 0);
+                    } else {
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (f16)acc[e]), yr, o, 0, 0);
+                    }
+                } else {
+                    const uint32_t o = ok[e] ? off[e] * 4u : y_bytes;
+                    if constexpr (V == 4)
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[e]), yr, o, 0, 0);
+                    else
+                        buffer_store_f32(acc[e], yr, o);
+                }
+            }
+        }
+    };
+    if (N % 4 == 0)
+        sum_groups(std::integral_constant<int, 4>{});
+    else
+        sum_groups(std::integral_constant<int, 1>{});
+}
+
 constexpr int gemm_min_blocks(int wn) { return GEMM_MINB * 2 / wn > 0 ? GEMM_MINB * 2 / wn : 1; }
 
-template <int B, int MS, int WN, int KW = 2, int TN = BN, bool SW = false>
+template <int B, int MS, int WN, int KW = 2, int TN = BN, bool SW = false, bool RED = false>
 __global__ __launch_bounds__(64 * WN * KW, gemm_min_blocks(WN)) void gemm_kernel(const u32* __restrict__ W,
                                                    const uint16_t* __restrict__ S,
                                                    const uint16_t* __restrict__ Mn,
                                                    const uint16_t* __restrict__ X,
                                                    float* __restrict__ Y, float* __restrict__ P,
+                                                   int* __restrict__ counters,
                                                    int M, int N, int K, uint64_t gmul, int gsh,
                                                    int grid_m, int grid_n, int split,
                                                    int steps_per_split, int out16) {
@@ -495,6 +583,9 @@ __global__ __launch_bounds__(64 * WN * KW, gemm_min_blocks(WN)) void gemm_kernel
                     const float sum = acc[i][ns][v] + part[v];
                     if constexpr (HALF)
                         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (f16)sum), orr, off, 0, 0);
+                    else if constexpr (RED)
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, sum), orr, off, 0,
+                                                              CPOL_COHERENT);
                     else
                         buffer_store_f32(sum, orr, off);
                 }
@@ -505,10 +596,37 @@ __global__ __launch_bounds__(64 * WN * KW, gemm_min_blocks(WN)) void gemm_kernel
         else
             store_all(std::false_type{});
     }
+    if constexpr (!RED) return;  // no split, or a separate reduction kernel
+
+    // RED (split K, in-kernel reduction; launched only with split > 1): the
+    // work-group that finishes a tile last adds the partial sums of all
+    // splits and writes y.  The partial sums are written through to
+    // memory (coherent stores, above) and every wave waits until its stores
+    // are acknowledged before the work-group counts itself in, so whoever
+    // counts in last finds all of them in memory and reads them with
+    // cache-bypassing loads.  (A device-scope fence would do the same by
+    // writing back and invalidating whole L2 caches, once per wave.)  The
+    // last arrival also resets the tile's counter to zero for the next call.
+    // Nothing waits on another work-group.
+    int* flag = reinterpret_cast<int*>(smem);  // the exchange area is no longer read
+    __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
+    __syncthreads();
+    if (tid == 0) {
+        int* cnt = counters + (nt * grid_m + mt);
+        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = prev == split - 1;
+        if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last;
+    }
+    __syncthreads();
+    if (!*flag) return;
+    reduce_tile<TILE_M, TN, THREADS>(P, Y, M, N, split, m0, n0, tid, out16);
 }
 
-// y = sum over splits of the partial sums, in split order (fp32, or rounded
-// to fp16 when out16).
+// Split K, separate reduction: y = sum over splits of the partial sums, in
+// split order (fp32, or rounded to fp16 when out16), spread over the whole
+// GPU.  Used for more than two splits, where one work-group per tile would
+// have to read too many partial sums by itself.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P,
                                                             float* __restrict__ Y, int64_t count,
                                                             int split, int out16) {
@@ -543,16 +661,28 @@ static hipError_t launch_gemm_t(const GemmArgs& a, const GemmShape& sh, hipStrea
     const int grid = 8 * ((tiles + 7) / 8);
     constexpr bool SW_OK = has_affine<B>() && BK == 128;
     constexpr int THREADS = 64 * WN * KW;
-    if (SW_OK && sh.wide_scales)
-        hipLaunchKernelGGL((gemm_kernel<B, MS, WN, KW, TN, SW_OK>), dim3(grid), dim3(THREADS), 0, st, a.w, a.s,
-                           a.m, a.x, a.y, a.partial, a.m_rows, a.n, a.k, gm.mul, gm.shift, sh.grid_m,
-                           sh.grid_n, sh.split, sh.k_tiles_per_split, a.out16);
-    else
-        hipLaunchKernelGGL((gemm_kernel<B, MS, WN, KW, TN>), dim3(grid), dim3(THREADS), 0, st, a.w, a.s, a.m,
-                           a.x, a.y, a.partial, a.m_rows, a.n, a.k, gm.mul, gm.shift, sh.grid_m, sh.grid_n,
-                           sh.split, sh.k_tiles_per_split, a.out16);
+    // The in-kernel split reduction exists for the tiles that split (32 and
+    // 64 rows, 128 columns); the host passes counters only for those.
+    constexpr bool RED_OK = MS <= 2 && TN == BN && KW == 2;
+    const bool red = RED_OK && sh.split > 1 && a.counters;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), 0, st, a.w, a.s, a.m, a.x, a.y, a.partial, a.counters,
+                           a.m_rows, a.n, a.k, gm.mul, gm.shift, sh.grid_m, sh.grid_n, sh.split,
+                           sh.k_tiles_per_split, a.out16);
+    };
+    if (SW_OK && sh.wide_scales) {
+        if (red)
+            go(gemm_kernel<B, MS, WN, KW, TN, SW_OK, RED_OK>);
+        else
+            go(gemm_kernel<B, MS, WN, KW, TN, SW_OK>);
+    } else {
+        if (red)
+            go(gemm_kernel<B, MS, WN, KW, TN, false, RED_OK>);
+        else
+            go(gemm_kernel<B, MS, WN, KW, TN>);
+    }
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || sh.split == 1) return err;
+    if (err != hipSuccess || sh.split == 1 || red) return err;
     const int64_t count = (int64_t)a.m_rows * a.n;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st,
                        a.partial, a.y, count, sh.split, a.out16);

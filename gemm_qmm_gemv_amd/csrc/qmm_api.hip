@@ -295,6 +295,19 @@ RowsShape plan_rows(int64_t rows_bound, int64_t n, int64_t k, int bits, int grou
 // (twice the waves per SIMD of the 128-row tile), except for long K with
 // several 128-row tiles, where the 128-row tile's halved W traffic wins; a
 // split shorter than four K steps costs more in partial sums than it gains.
+// Splits up to this are added up inside the GEMM kernel by the last
+// work-group of each tile (measured: 15.4 vs 18.7 us on 128 x 8192 x 2048);
+// more splits go to a separate reduction kernel spread over the GPU (one
+// work-group reading four or eight tiles' worth of partial sums measured
+// 1-1.3 us slower than that kernel).
+constexpr int GEMM_INKERNEL_REDUCE_MAX_SPLIT = 2;
+
+// Split-K arrival counters: a fixed area at the start of the workspace, one
+// int per output tile, the same for every shape so that the partial sums of
+// one call (which follow it) never land on another call's counters.
+constexpr size_t GEMM_COUNTER_BYTES = 4096;
+constexpr int64_t GEMM_COUNTER_TILES = GEMM_COUNTER_BYTES / sizeof(int);
+
 GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int group, int cus, size_t ws_bytes, size_t* ws_need) {
     GemmShape sh{};
     const int k_tiles = (int)((k + GEMM_BK - 1) / GEMM_BK);
@@ -326,10 +339,15 @@ GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int group, int cus, size_t 
     }
     const int es = env_int("QMM_GEMM_SPLIT", 0);
     if (es > 0) split = es < k_tiles ? es : k_tiles;
+    if (split > 16) split = 16;  // the reduction handles at most 16 splits
+    // Workspace: the tiles' arrival counters, then the partial sums (their
+    // byte offsets must stay below 2^32).
     const size_t per_split = (size_t)m * n * sizeof(float);
-    if (ws_need) *ws_need = split > 1 ? per_split * split : 0;
-    if (split > 1 && ws_bytes < per_split * split) {
-        split = per_split ? (int)(ws_bytes / per_split) : 1;
+    const size_t cnt_bytes = GEMM_COUNTER_BYTES;
+    if (per_split && split > 1 && per_split * split > 0xFFFFFFFFull) split = (int)(0xFFFFFFFFull / per_split);
+    if (ws_need) *ws_need = split > 1 ? cnt_bytes + per_split * split : 0;
+    if (split > 1 && ws_bytes < cnt_bytes + per_split * split) {
+        split = (per_split && ws_bytes > cnt_bytes) ? (int)((ws_bytes - cnt_bytes) / per_split) : 1;
         if (split < 2) split = 1;
     }
     sh.k_tiles_per_split = (k_tiles + split - 1) / split;
@@ -482,8 +500,15 @@ qmm_status gemm_common(const void* w_packed, const void* scales, const void* min
         return launched(launch_rows(a, sh, as_stream(stream)), "qmm_gemm (rows)");
     }
     const GemmShape sh = plan_gemm(m, n, k, group_size, cus, workspace ? workspace_bytes : 0, nullptr);
-    GemmArgs a{w, s, mn, xx, yf, sh.split > 1 ? static_cast<float*>(workspace) : nullptr, (int)m, (int)n,
-               (int)k, group_size, bits, out16 ? 1 : 0};
+    float* partial = nullptr;
+    int* counters = nullptr;
+    if (sh.split > 1) {
+        partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + GEMM_COUNTER_BYTES);
+        if (sh.split <= GEMM_INKERNEL_REDUCE_MAX_SPLIT && sh.tile_m <= 64 && sh.tile_n == 128 &&
+            (int64_t)sh.grid_m * sh.grid_n <= GEMM_COUNTER_TILES)
+            counters = static_cast<int*>(workspace);
+    }
+    GemmArgs a{w, s, mn, xx, yf, partial, counters, (int)m, (int)n, (int)k, group_size, bits, out16 ? 1 : 0};
     return launched(launch_gemm(a, sh, as_stream(stream)), out16 ? "qmm_gemm_f16out" : "qmm_gemm");
 }
 

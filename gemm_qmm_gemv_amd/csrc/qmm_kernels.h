@@ -110,6 +110,7 @@ struct GemmArgs {
     const uint16_t* x;
     float* y;
     float* partial;  // split-K partial sums [split][m][n], or null when split == 1
+    int* counters;   // split-K arrival counter per tile (zero between calls), or null
     int m_rows, n, k, group, bits;
     int out16;       // y holds fp16 [m][n] (else fp32)
 };

@@ -70,7 +70,9 @@ def gemm(dq: dict, x: torch.Tensor, y: torch.Tensor | None = None, workspace=Non
                         device=x.device)
     if workspace is None:
         need = qmm_gemm_workspace_bytes(m, dq["n"], dq["k"], dq["bits"], dq["group"])
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device) if need else None
+        # Zeroed: the split-K arrival counters at its start must read zero
+        # before the first call (every call leaves them zero).
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=x.device) if need else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     fn = qmm_gemm_f16out if out_fp16 else qmm_gemm
     fn(dq["w"], dq["scales"], dq["mins"], x, y, m, dq["n"], dq["k"], dq["bits"],

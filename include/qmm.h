@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define QMM_ABI_VERSION 1
+#define QMM_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define QMM_API __attribute__((visibility("default")))
@@ -133,10 +133,15 @@ QMM_API qmm_status qmm_gemv_swiglu(const void *gate_w, const void *gate_scales,
  * cores with fp32 accumulation.  Small m is routed to the bandwidth-bound
  * multi-row GEMV kernel.
  *   x  fp16 [m][k]      y  fp32 [m][n] (written)
- *   workspace: optional device scratch (may be NULL / 0 bytes).  When the
- *   shape leaves the GPU under-filled, up to qmm_gemm_workspace_bytes() of it
- *   is used to split the K loop; with less, the split shrinks to what fits
- *   (no split with none).  Contents on return are unspecified.             */
+ *   workspace: optional device scratch (may be NULL / 0 bytes), 16-byte
+ *   aligned.  When the shape leaves the GPU under-filled, up to
+ *   qmm_gemm_workspace_bytes() of it is used to split the K loop; with less,
+ *   the split shrinks to what fits (no split with none).  Its first 4096
+ *   bytes hold per-tile arrival counters: the workspace must be all zero before
+ *   its first use (allocate it zeroed once), and every call leaves those
+ *   counters zero again, so one workspace serves any sequence of calls on
+ *   one stream.  Calls that overlap (other streams) need their own
+ *   workspace.  The rest of its contents on return are unspecified.        */
 QMM_API qmm_status qmm_gemm(const void *w_packed, const void *scales, const void *mins,
                     const void *x, float *y, int64_t m, int64_t n, int64_t k,
                     int bits, int group_size, void *workspace,

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert len(names) >= 9
     for name in names:
         assert hasattr(lib, name), name
-    assert qmm.qmm_abi_version() == 1
+    assert qmm.qmm_abi_version() == 2
 
 
 def test_exports_are_only_the_abi(lib):

@@ -70,6 +70,40 @@ def test_gemm_without_workspace_matches_split(bits):
     assert_within(y_none, y_ref, a_ref, "gemm no-split b%d" % bits)
 
 
+def test_gemm_split_workspace_reuse():
+    # One zeroed workspace across a sequence of split GEMMs of different
+    # shapes (and splits, with fp16 output too): each result within the bound,
+    # each repeat bit-identical (the partial sums are added in split order),
+    # and the arrival counters at the workspace's start back at zero after
+    # every call.
+    import torch
+    import gemm_qmm_gemv_amd as qmm
+    from gemm_qmm_gemv_amd import tensors
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    # Splits of 2 are added up inside the GEMM kernel, larger ones by a
+    # separate reduction kernel: both kinds, and odd N, in one sequence.
+    cases = [(128, 8192, 2048, 4), (128, 2048, 2048, 4), (512, 2048, 2048, 3), (64, 512, 8192, 4),
+             (128, 2048, 8192, 8), (96, 300, 1024, 4), (128, 8196, 2048, 5), (128, 2052, 2048, 4),
+             (200, 1000, 4096, 2)]
+    for m, n, k, bits in cases:
+        pl = qmm.qmm_get_plan(1, m, n, k, bits, 64, workspace_bytes=ws.numel())
+        assert pl["split_k"] > 1, (m, n, k)
+        q = inputs.quantized_matrix(n, k, bits, 64, key=(66, m, n, k, bits))
+        x = inputs.activation_rows(m, k, key=(66, m, n, k))
+        dq = tensors.upload_matrix(q)
+        xd = tensors.device_tensor(x)
+        announce("gemm-split-reuse", m, n, k, bits, pl["split_k"])
+        y1 = tensors.gemm(dq, xd, workspace=ws)
+        y2 = tensors.gemm(dq, xd, workspace=ws)
+        h = tensors.gemm(dq, xd, workspace=ws, out_fp16=True)
+        torch.cuda.synchronize()
+        assert not torch.any(ws[:4096]), "arrival counters not reset"  # the partial sums follow
+        assert torch.equal(y1, y2)
+        y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, 64)
+        assert_within(y1.cpu().numpy(), y_ref, a_ref, "split reuse %dx%dx%d" % (m, n, k))
+        assert np.array_equal(h.cpu().numpy(), y1.cpu().numpy().astype(np.float16))
+
+
 def test_gemm_exact_integer():
     # scale 1, min 0, integer x: fp16 weights are exact small integers, MFMA
     # products and fp32 sums stay below 2^24 -> exact.
