@@ -100,7 +100,7 @@ class Timer:
     def __init__(self, torch):
         self.torch = torch
 
-    def __call__(self, fn, reps=20, warmup=3, replays=5):
+    def __call__(self, fn, reps=20, warmup=3, replays=5, settle_ms=20.0):
         t = self.torch
         for _ in range(warmup):
             fn()
@@ -109,9 +109,18 @@ class Timer:
         with t.cuda.graph(g):
             for _ in range(reps):
                 fn()
-        g.replay()
-        t.cuda.synchronize()
+        # Untimed replays for at least settle_ms, so that the timed ones run
+        # at steady-state clocks (inputs are generated on the host between
+        # measurements, and the GPU idles meanwhile).
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        t.cuda.synchronize()
+        once = max(a.elapsed_time(b), 1e-3)
+        for _ in range(min(200, int(settle_ms / once) + 1)):
+            g.replay()
+        t.cuda.synchronize()
         a.record()
         for _ in range(replays):
             g.replay()
@@ -119,10 +128,18 @@ class Timer:
         t.cuda.synchronize()
         return a.elapsed_time(b) / (replays * reps)
 
-    def replay(self, g, replays=20):
-        """Average milliseconds per replay of an already captured graph."""
+    def replay(self, g, replays=20, settle_ms=20.0):
+        """Average milliseconds per replay of an already captured graph
+        (after untimed replays for at least settle_ms, as in __call__)."""
         t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
         g.replay()
+        b.record()
+        t.cuda.synchronize()
+        once = max(a.elapsed_time(b), 1e-3)
+        for _ in range(min(200, int(settle_ms / once) + 1)):
+            g.replay()
         t.cuda.synchronize()
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         a.record()
@@ -136,8 +153,10 @@ class Timer:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # Defaults: about 0.1 s of warm-up launches (identical to the timed ones)
+    # so the GPU runs at its steady-state clocks, then 1000 timed launches.
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--quick", action="store_true", help="headline only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
