@@ -26,7 +26,9 @@ Also measured (outside the timed region, reported in the same JSON line):
     two GEMV launches, Q4, on Qwen3-0.6B and Llama-3.2-3B shapes;
   * Qwen3-30B-A3B-shaped MoE expert projections at 1 and 16 tokens, also with
     gate and up fused with the SiLU-gated product;
-  * the CPU oracle on the host cores over the same projection set.
+  * the CPU oracle on the host cores over the same projection set;
+  * measured ceilings (a plain streaming read and an fp16 MFMA loop built
+    here), reported beside the spec peaks as second denominators.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 """
@@ -277,11 +279,72 @@ def main():
     }
 
     if not args.quick:
+        ceil = measured_ceilings(torch, set_bytes)
+        result["measured_ceilings"] = ceil
+        result["roofline"]["measured_peak"] = ceil["hbm_read_GBps"]
+        result["roofline"]["frac_of_measured"] = round(dom_gbs / ceil["hbm_read_GBps"], 4)
         result["extras"] = extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys,
                                   set_bytes)
+        for key, per_m in result["extras"].items():
+            if key.startswith("prefill_"):
+                for row in per_m.values():
+                    row["pct_of_measured_mfma"] = round(100 * row["TFLOPs"] / ceil["mfma_f16_TFLOPs"], 2)
     if not args.no_cpu_baseline and not args.quick:
         result["cpu_baseline"] = cpu_baseline(np, configs, inputs, set_bytes)
     print(json.dumps(result), flush=True)
+
+
+def measured_ceilings(torch, set_bytes):
+    """Second denominators, measured here: a plain streaming read of a buffer
+    of the decode set's size (larger than the last-level cache) and of 2 GiB,
+    and a loop of independent fp16 32x32x16 MFMAs on every SIMD.  Each is the
+    best of a few launch shapes (work-groups per CU), after warm-up."""
+    import ctypes
+    from gemm_qmm_gemv_amd import build as qbuild
+    if not os.path.exists(qbuild.CEILING_LIB):
+        raise RuntimeError("%s is missing: run gemm_qmm_gemv_amd.build first" % qbuild.CEILING_LIB)
+    lib = ctypes.CDLL(qbuild.CEILING_LIB)
+    p, u64, ci = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int
+    lib.qmm_ceiling_read.argtypes = [p, u64, ci, p, p]
+    lib.qmm_ceiling_mfma.argtypes = [ci, ci, p, p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+
+    def best_ms(calls, reps):
+        best = float("inf")
+        for fn in calls:
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b) / reps)
+        return best
+
+    out = {}
+    for label, nbytes in (("hbm_read_GBps", set_bytes // 16 * 16), ("hbm_read_2GiB_GBps", 2 << 30)):
+        buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")  # XOR-folds to 0: sink untouched
+        calls = [lambda blocks=cus * mult: lib.qmm_ceiling_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), st)
+                 for mult in (1, 2, 4, 8, 32)]
+        ms = best_ms(calls, 20)
+        out[label] = round(nbytes / ms / 1e6, 1)
+        del buf, calls
+    iters = 4000
+    tf = 0.0
+    for mult in (2, 8):
+        blocks = cus * mult  # four waves each, 4 * iters MFMAs of 32768 flops per wave
+        ms = best_ms([lambda: lib.qmm_ceiling_mfma(blocks, iters, sink.data_ptr(), st)], 5)
+        tf = max(tf, blocks * 4 * iters * 4 * 32768.0 / ms / 1e9)
+    out["mfma_f16_TFLOPs"] = round(tf, 1)
+    out["read_buffer_bytes"] = set_bytes // 16 * 16
+    log("measured ceilings: read %.0f GB/s (set-sized), %.0f GB/s (2 GiB); fp16 MFMA %.0f TFLOP/s"
+        % (out["hbm_read_GBps"], out["hbm_read_2GiB_GBps"], out["mfma_f16_TFLOPs"]))
+    return out
 
 
 def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_bytes):

@@ -287,3 +287,20 @@ def test_sizes_beyond_32bit_offsets_are_rejected(lib):
     import torch
     if not torch.cuda.is_available():
         assert _gemv(lib, n=(1 << 20) - 64, k=1 << 13) == qmm.QMM_ERR_DEVICE
+
+
+def test_ceiling_library_exports():
+    # The measurement kernels bench.py times beside the spec peaks (not part
+    # of the qmm.h interface): the library loads and argument checks run on
+    # the host.
+    import os
+    from gemm_qmm_gemv_amd import build as qbuild
+    if not os.path.exists(qbuild.CEILING_LIB):
+        pytest.skip("libqmm_ceiling.so not built")
+    cl = ctypes.CDLL(qbuild.CEILING_LIB)
+    p, u64, ci = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int
+    cl.qmm_ceiling_read.argtypes = [p, u64, ci, p, p]
+    cl.qmm_ceiling_mfma.argtypes = [ci, ci, p, p]
+    assert cl.qmm_ceiling_read(None, 16, 1, p(A16), None) == 1
+    assert cl.qmm_ceiling_read(p(A16), 15, 1, p(A16), None) == 1
+    assert cl.qmm_ceiling_mfma(0, 10, p(A16), None) == 1
