@@ -415,7 +415,30 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
     y = torch.empty(c["n"], dtype=torch.float32, device="cuda")
     ms = timer(lambda: tensors.gemv(dq, x, y), reps=100)
     b = configs.gemv_bytes(c["n"], c["k"], 4)
-    out["single_3072x1024_q4"] = {"us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1)}
+    out["single_3072x1024_q4"] = {"us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1),
+                                  "pct_peak": round(100 * b / ms / 1e6 / HBM_PEAK_GBS, 2)}
+
+    # Per-shape single launches of the Qwen3-0.6B projections: the 28 layers'
+    # own matrices of each shape in turn (one launch each, graph-replayed).
+    # The 28 matrices of one shape total 29-50 MB, which the 256 MB last-level
+    # cache can hold between replays, so these rates are upper bounds of what
+    # a decode step sees; at 0.6-1.8 MB a launch is too short to reach a
+    # steady stream (it is dominated by its fixed start-up cost).
+    per_shape = {}
+    for pname, n, k in configs.QWEN3_06B_PROJ:
+        sel = [(d, x, y) for (layer, name, d), x, y in zip(mats, xs, ys) if name == pname]
+        jj = [0]
+
+        def shape_call():
+            d, x, y = sel[jj[0] % len(sel)]
+            tensors.gemv(d, x, y)
+            jj[0] += 1
+        ms = timer(shape_call, reps=len(sel))
+        b = configs.gemv_bytes(n, k, 4)
+        per_shape[pname] = {"n": n, "k": k, "us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1),
+                            "pct_peak": round(100 * b / ms / 1e6 / HBM_PEAK_GBS, 2)}
+    out["qwen3_0.6b_per_shape_q4"] = per_shape
+    log("qwen3 per shape: " + ", ".join("%s %.2f us" % (k2, v["us"]) for k2, v in per_shape.items()))
 
     # Bit-width sweep on Llama-3.2-3B shapes (rotating 2 copies of each).
     sweep = {}
@@ -437,8 +460,16 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
             b = configs.gemv_bytes(n, k, bits)
             row[pname] = {"us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1)}
             del cps
+        # Per-token projection time: 28 layers of q, k, v, o, gate, up, down
+        # (k as v, o as q, up as gate: same shapes) plus the LM head, from the
+        # per-launch times above.
+        layer_us = 2 * row["q_proj"]["us"] + 2 * row["v_proj"]["us"] + 2 * row["gate_proj"]["us"] \
+            + row["down_proj"]["us"]
+        tok_us = configs.LLAMA32_3B_LAYERS * layer_us + row["lm_head"]["us"]
+        row["per_token_projection_us"] = round(tok_us, 1)
+        row["projection_tok_per_s"] = round(1e6 / tok_us, 1)
         sweep["q%d" % bits] = row
-        log("sweep q%d: lm_head %.0f GB/s" % (bits, row["lm_head"]["GBps"]))
+        log("sweep q%d: lm_head %.0f GB/s, %.0f us per token" % (bits, row["lm_head"]["GBps"], tok_us))
     out["llama3.2_3b_bit_sweep"] = sweep
 
     # Prefill GEMMs (Llama-3.2-1B shapes), Q4, then the same layer with fp16
@@ -653,10 +684,40 @@ def cpu_baseline(np, configs, inputs, set_bytes):
         if el >= 10.0:  # about ten seconds of CPU work
             break
     gbs = reps * b / el / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": "layer 0's 7 Q4 projections + LM head rows 0..8191 (%d bytes), %d passes in %.1f s"
-                      % (b, reps, el),
-            "seconds_per_decode_set": round(set_bytes / (gbs * 1e9), 2)}
+    cores = oracle.threads()
+    result = {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+              "sample": "layer 0's 7 Q4 projections + LM head rows 0..8191 (%d bytes), %d passes in %.1f s"
+                        % (b, reps, el),
+              "seconds_per_decode_set": round(set_bytes / (gbs * 1e9), 2)}
+    # The same oracle on one thread, and on a prefill GEMM (all threads):
+    # about five seconds each.
+    try:
+        oracle.set_threads(1)
+        reps1, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 5.0:
+            for q, x in work:
+                oracle.qmm(q["w"], q["scales"], q["mins"], x, q["n"], q["k"], 4, G)
+            reps1 += 1
+        el1 = time.perf_counter() - t0
+        result["single_thread"] = {"value": round(reps1 * b / el1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                   "sample": "the same sample, %d passes in %.1f s" % (reps1, el1)}
+    finally:
+        oracle.set_threads(cores)
+    m = 128
+    j = [p[0] for p in configs.LLAMA32_1B_PROJ].index("k_proj")
+    _, n, k = configs.LLAMA32_1B_PROJ[j]
+    q = inputs.quantized_matrix(n, k, 4, G, key=(configs.CFG_PREFILL, 0, j, 4))
+    xm = inputs.activation_rows(m, k, key=(configs.CFG_PREFILL, 0, j, 4, m))
+    reps2, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < 5.0:
+        oracle.qmm(q["w"], q["scales"], q["mins"], xm, n, k, 4, G)
+        reps2 += 1
+    el2 = time.perf_counter() - t0
+    result["prefill"] = {"value": round(reps2 * 2.0 * m * n * k / el2 / 1e9, 3), "unit": "GFLOP/s",
+                         "cores": cores,
+                         "sample": "Llama-3.2-1B k_proj %dx%d, M = %d, Q4, %d calls in %.1f s"
+                                   % (n, k, m, reps2, el2)}
+    return result
 
 
 if __name__ == "__main__":

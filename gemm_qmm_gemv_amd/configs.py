@@ -35,6 +35,9 @@ LLAMA32_3B_PROJ = [
     ("down_proj", 3072, 8192),
     ("lm_head", 128256, 3072),
 ]
+# Decoder layers of that model's public configuration (used only to add the
+# per-launch times up to a per-token projection time).
+LLAMA32_3B_LAYERS = 28
 # Q5 and fp16 weights (16) are not among the pages' measured widths; they
 # are swept beside them.
 SWEEP_BITS = (2, 3, 4, 5, 6, 8, 16)
