@@ -77,7 +77,7 @@ extern "C" {
 typedef enum qmm_status {
     QMM_OK = 0,
     QMM_ERR_INVALID_ARGUMENT = 1, /* shape, size or NULL pointer problem      */
-    QMM_ERR_UNSUPPORTED = 2,      /* valid request this build does not cover  */
+    QMM_ERR_UNSUPPORTED = 2,      /* valid request the library does not cover */
     QMM_ERR_MISALIGNED = 3,       /* pointer alignment below the requirement  */
     QMM_ERR_DEVICE = 4            /* HIP runtime error at launch / no device  */
 } qmm_status;
