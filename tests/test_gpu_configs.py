@@ -67,3 +67,33 @@ def test_llama3b_sweep(bits, proj):
     announce("sweep", bits, proj, n, k)
     y = _gemv_device(q, x)
     _check(q, x, y, "llama3b b%d %s %dx%d" % (bits, proj, n, k), full_limit=1_000_000)
+
+
+def test_qwen3_decode_set_one_batched_launch():
+    """The headline step exactly as the benchmark issues it: all 197 GEMVs of
+    the Qwen3-0.6B-shaped decode set (28 layers x 7 projections + the LM
+    head, each with its own seeded matrix and activation) in one batched
+    launch; sampled rows of every matrix checked against the oracle."""
+    import torch
+    from gemm_qmm_gemv_amd import tensors
+    G = configs.GROUP
+    host, items = [], []
+    for layer, j, name, n, k in configs.decode_set():
+        key = (configs.CFG_DECODE_SET, layer, j, 4)
+        q = inputs.quantized_matrix(n, k, 4, G, key=key)
+        x = inputs.activation_rows(1, k, key=key)[0]
+        items.append((tensors.upload_matrix(q), tensors.device_tensor(x),
+                      torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")))
+        host.append((layer, name, q, x))
+    assert len(items) == 197
+    batch = tensors.GemvBatch(items, 4, G)
+    announce("decode-set-batched", len(items))
+    batch()
+    torch.cuda.synchronize()
+    for (layer, name, q, x), (_, _, y) in zip(host, items):
+        yh = y.cpu().numpy()
+        assert np.all(np.isfinite(yh)), (layer, name)  # every row written
+        rn = _sample_rows(q["n"], 48 if name != "lm_head" else 512, 1000 * layer + len(name))
+        y_ref, a_ref = oracle.qmm_sample(q["w"], q["scales"], q["mins"], x, q["k"], 4, G,
+                                         np.zeros_like(rn), rn)
+        assert_within(yh[rn], y_ref, a_ref, "decode set layer %d %s (sampled)" % (layer, name))
