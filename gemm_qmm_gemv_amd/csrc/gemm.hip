@@ -471,9 +471,9 @@ __global__ __launch_bounds__(64 * WN * KW, gemm_min_blocks(WN)) void gemm_kernel
     // U % PD is free (its data went into this step's operands during the
     // previous step).  The step
     //   * issues the loads of step st + PD into that slot,
-    //   * runs its matrix work, and -- independent of it, so the two overlap
-    //     within the wave -- dequantizes W(st + 1) and stages X(st + 1) into
-    //     the other LDS buffer,
+    //   * stages X(st + 1) into the other LDS buffer (the previous step's
+    //     barrier freed it), then runs its matrix work and -- independent of
+    //     it, so the two overlap within the wave -- dequantizes W(st + 1),
     //   * ends with the barrier that publishes X(st + 1) and frees buffer
     //     U % 2 for step st + 2.
     constexpr int UNR = SW ? UNROLL_SW : UNROLL;
@@ -491,6 +491,10 @@ __global__ __launch_bounds__(64 * WN * KW, gemm_min_blocks(WN)) void gemm_kernel
         // Keep the loads at the top of the step: left alone, the scheduler
         // sinks them towards their first use.
         __builtin_amdgcn_sched_barrier(0);
+        // X(st + 1) (loaded a step ago) goes into the other buffer before the
+        // matrix work, so the LDS writes overlap it instead of queueing just
+        // before the barrier (measured -4 % on 2048 x 8192 x 2048).
+        stage_x(xq[NEXT], BUF ^ 1);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const f16* xa = xs + BUF * XBUF + col * XROW + HK * wk + 64 * c + 32 * kh;
@@ -522,7 +526,6 @@ __global__ __launch_bounds__(64 * WN * KW, gemm_min_blocks(WN)) void gemm_kernel
             sm_of_block(std::integral_constant<int, (U + 1) % SW_STEPS>{}, sq[NEXT], mq[NEXT]);
         }
         dequant(wq[NEXT], sq[NEXT], mq[NEXT], wv[BUF ^ 1]);
-        stage_x(xq[NEXT], BUF ^ 1);
         __syncthreads();
     };
     // Whole passes in the loop, the remainder after it: an exit from the
