@@ -21,7 +21,8 @@ Also measured (outside the timed region, reported in the same JSON line):
     weights);
   * Llama-3.2-1B-shaped prefill GEMMs at M = 128 and 512: TFLOP/s, % MFMA,
     with Q4 weights and again with fp16 weights, and at M = 2048 with fp32
-    and fp16 output, the dense fp16 library matmul of each shape beside them;
+    and fp16 output, the dense fp16 library matmul of each shape beside them,
+    and the layer with q|k|v and gate|up as grouped GEMMs;
   * the fused gate/up projection (silu(Wg x) * (Wu x), one launch) against
     two GEMV launches, Q4, on Qwen3-0.6B and Llama-3.2-3B shapes;
   * Qwen3-30B-A3B-shaped MoE expert projections at 1 and 16 tokens, also with
@@ -289,6 +290,9 @@ def main():
             if key.startswith("prefill_"):
                 for row in per_m.values():
                     row["pct_of_measured_mfma"] = round(100 * row["TFLOPs"] / ceil["mfma_f16_TFLOPs"], 2)
+                    if "grouped" in row:
+                        row["grouped"]["pct_of_measured_mfma"] = round(
+                            100 * row["grouped"]["TFLOPs"] / ceil["mfma_f16_TFLOPs"], 2)
     if not args.no_cpu_baseline and not args.quick:
         result["cpu_baseline"] = cpu_baseline(np, configs, inputs, set_bytes)
     print(json.dumps(result), flush=True)
@@ -652,8 +656,45 @@ def prefill_layers(torch, qmm, configs, inputs, tensors, timer, bits, ms_list, o
         pre["m%d" % m] = {"layer_us": round(tot_ms * 1e3, 2), "TFLOPs": round(tf, 1),
                           "pct_mfma": round(100 * tf / MFMA_FP16_PEAK_TFLOPS, 2),
                           "dense_fp16_matmul_layer_us": round(dense_ms * 1e3, 2), "shapes": row}
-        log("prefill b%d m=%d%s: %.1f TFLOP/s (layer %.1f us, dense fp16 %.1f us)"
-            % (bits, m, " fp16-out" if out_fp16 else "", tf, tot_ms * 1e3, dense_ms * 1e3))
+        msg = ""
+        if not out_fp16:
+            # The same layer with the projections that share their input
+            # (q|k|v, gate|up) issued as grouped GEMMs: four dependent
+            # launches per layer instead of seven.
+            grouped = {}
+            for gname, names in (("qkv", ("q_proj", "k_proj", "v_proj")), ("gate_up", ("gate_proj", "up_proj"))):
+                sel = [(j, n, k) for j, (pname, n, k) in enumerate(configs.LLAMA32_1B_PROJ) if pname in names]
+                k = sel[0][2]
+                bases = [tensors.upload_matrix(inputs.quantized_matrix(n, k, bits, G, key=(configs.CFG_PREFILL, 0, j, bits)))
+                         for j, n, _ in sel]
+                wb = sum(configs.weight_bytes(n, k, bits) for _, n, _ in sel)
+                ncp = max(4, min(64, -(-512 * 2**20 // wb)))
+                clone = lambda t: None if t is None else t.clone()
+                sets = [bases] + [[{**d, "w": d["w"].clone(), "scales": clone(d["scales"]), "mins": clone(d["mins"])}
+                                   for d in bases] for _ in range(ncp - 1)]
+                xg = tensors.device_tensor(inputs.activation_rows(m, k, key=(configs.CFG_PREFILL, 0, sel[0][0], 4, m)))
+                ysg = [torch.empty((m, n), dtype=torch.float32, device="cuda") for _, n, _ in sel]
+                members = [(d["w"], d["scales"], d["mins"], y, d["n"]) for d, y in zip(bases, ysg)]
+                need = qmm.qmm_gemm_grouped_workspace_bytes(members, m, k, bits, G)
+                wsg = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
+                gi = [0]
+
+                def gcall():
+                    tensors.gemm_grouped(sets[gi[0] % ncp], xg, ys=ysg, workspace=wsg)
+                    gi[0] += 1
+                ms_g = timer(gcall, reps=ncp)
+                grouped[gname] = {"us": round(ms_g * 1e3, 2),
+                                  "separate_us": round(sum(row[nm]["us"] for nm in names), 2)}
+                del sets
+            layer_g = (grouped["qkv"]["us"] + row["o_proj"]["us"] + grouped["gate_up"]["us"]
+                       + row["down_proj"]["us"])
+            tf_g = tot_flops / layer_g / 1e6
+            pre["m%d" % m]["grouped"] = {"layer_us": round(layer_g, 2), "TFLOPs": round(tf_g, 1),
+                                         "pct_mfma": round(100 * tf_g / MFMA_FP16_PEAK_TFLOPS, 2),
+                                         "launch_groups": grouped}
+            msg = "; grouped q|k|v, gate|up: layer %.1f us, %.1f TFLOP/s" % (layer_g, tf_g)
+        log("prefill b%d m=%d%s: %.1f TFLOP/s (layer %.1f us, dense fp16 %.1f us)%s"
+            % (bits, m, " fp16-out" if out_fp16 else "", tf, tot_ms * 1e3, dense_ms * 1e3, msg))
     return pre
 
 

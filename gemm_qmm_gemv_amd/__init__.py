@@ -18,8 +18,10 @@ import os
 __all__ = [
     "QmmError", "library_path", "load",
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
-    "qmm_gemv_batch_prepare", "qmm_gemv_batched", "GemvDesc", "qmm_gemv_swiglu", "qmm_gemm_f16out",
-    "qmm_moe_swiglu", "qmm_gemv_residual", "qmm_moe_combine",
+    "qmm_gemv_batch_prepare", "qmm_gemv_batched", "GemvDesc", "GemmMember", "qmm_gemv_swiglu",
+    "qmm_gemm_f16out",
+    "qmm_moe_swiglu", "qmm_gemv_residual", "qmm_moe_combine", "qmm_gemm_grouped",
+    "qmm_gemm_grouped_workspace_bytes",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
     "QMM_OK", "QMM_ERR_INVALID_ARGUMENT", "QMM_ERR_UNSUPPORTED", "QMM_ERR_MISALIGNED",
     "QMM_ERR_DEVICE", "EXPORTED_SYMBOLS",
@@ -34,7 +36,8 @@ QMM_ERR_DEVICE = 4
 EXPORTED_SYMBOLS = (
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
     "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out",
-    "qmm_moe_swiglu", "qmm_gemv_residual", "qmm_moe_combine",
+    "qmm_moe_swiglu", "qmm_gemv_residual", "qmm_moe_combine", "qmm_gemm_grouped",
+    "qmm_gemm_grouped_workspace_bytes",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
 )
 
@@ -82,6 +85,20 @@ class GemvDesc(ctypes.Structure):
 assert ctypes.sizeof(GemvDesc) == 64
 
 
+class GemmMember(ctypes.Structure):
+    """qmm_gemm_member: one weight matrix of a grouped GEMM and its output."""
+    _fields_ = [
+        ("w_packed", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("mins", ctypes.c_void_p),
+        ("y", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
+    ]
+
+
+assert ctypes.sizeof(GemmMember) == 40
+
+
 def library_path() -> str:
     """In-tree libqmm.so, or the file named by $QMM_LIBRARY (tuning builds)."""
     return os.environ.get("QMM_LIBRARY") or os.path.join(_HERE, _LIB_NAME)
@@ -113,13 +130,16 @@ def load():
     lib.qmm_moe_gemm.argtypes = [p, p, p, p, p, i64, p, p, i64, i64, i64, i64, ci, ci, p]
     lib.qmm_moe_swiglu.argtypes = [p, p, p, p, p, p, p, p, i64, p, p, i64, i64, i64, i64, ci, ci, p]
     lib.qmm_moe_combine.argtypes = [p, p, p, p, p, i64, p, p, p, p, i64, i64, i64, i64, i64, ci, ci, p]
+    lib.qmm_gemm_grouped.argtypes = [p, ci, p, i64, i64, ci, ci, p, ctypes.c_size_t, p]
+    lib.qmm_gemm_grouped_workspace_bytes.argtypes = [p, ci, i64, i64, ci, ci]
+    lib.qmm_gemm_grouped_workspace_bytes.restype = ctypes.c_size_t
     lib.qmm_unpack.argtypes = [p, p, i64, i64, ci, p]
     lib.qmm_gemv_batch_prepare.argtypes = [p, i64, ci, ci]
     lib.qmm_gemv_batched.argtypes = [p, p, i64, ci, ci, p]
     lib.qmm_get_plan.argtypes = [ci, i64, i64, i64, ci, ci, ci, sz, ctypes.POINTER(_Plan)]
     for f in ("qmm_gemv", "qmm_gemm", "qmm_moe_gemm", "qmm_unpack", "qmm_get_plan",
               "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out", "qmm_moe_swiglu",
-              "qmm_gemv_residual", "qmm_moe_combine"):
+              "qmm_gemv_residual", "qmm_moe_combine", "qmm_gemm_grouped"):
         getattr(lib, f).restype = ci
     lib.qmm_status_string.argtypes = [ci]
     lib.qmm_status_string.restype = ctypes.c_char_p
@@ -205,6 +225,29 @@ def qmm_gemm(w_packed, scales, mins, x, y, m, n, k, bits, group_size, workspace=
                            int(m), int(n), int(k), int(bits), int(group_size), _addr(workspace),
                            int(workspace_bytes), _stream(stream)),
            "qmm_gemm")
+
+
+def _members(members):
+    arr = (GemmMember * len(members))()
+    for d, (w, s, mn, y, n) in zip(arr, members):
+        d.w_packed, d.scales, d.mins, d.y, d.n = _addr(w), _addr(s), _addr(mn), _addr(y), int(n)
+    return arr
+
+
+def qmm_gemm_grouped(members, x, m, k, bits, group_size, workspace=None, workspace_bytes=0,
+                     stream=None) -> None:
+    """members: [(w_packed, scales, mins, y, n)]; y_i = X W_i^T for all in one launch."""
+    arr = _members(members)
+    _check(load().qmm_gemm_grouped(ctypes.addressof(arr), len(members), _addr(x), int(m), int(k),
+                                   int(bits), int(group_size), _addr(workspace), int(workspace_bytes),
+                                   _stream(stream)),
+           "qmm_gemm_grouped")
+
+
+def qmm_gemm_grouped_workspace_bytes(members, m, k, bits, group_size) -> int:
+    arr = _members(members)
+    return int(load().qmm_gemm_grouped_workspace_bytes(ctypes.addressof(arr), len(members), int(m), int(k),
+                                                       int(bits), int(group_size)))
 
 
 def qmm_gemm_workspace_bytes(m, n, k, bits, group_size) -> int:

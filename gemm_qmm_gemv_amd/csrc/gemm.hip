@@ -261,16 +261,20 @@ __device__ __forceinline__ void reduce_tile(const float* P, float* Y, int M, int
 
 constexpr int gemm_min_blocks(int wn) { return GEMM_MINB * 2 / wn > 0 ? GEMM_MINB * 2 / wn : 1; }
 
-template <int B, int MS, int WN, int KW = 2, int TN = BN, bool SW = false, bool RED = false>
-__global__ __launch_bounds__(64 * WN * KW, gemm_min_blocks(WN)) void gemm_kernel(const u32* __restrict__ W,
-                                                   const uint16_t* __restrict__ S,
-                                                   const uint16_t* __restrict__ Mn,
+//
+// GRP (grouped launch): W, S, Mn, Y, N and the partial-sum area come from
+// the member of `grp` that owns the work-group's N-tile; the plain
+// arguments are unused.  Grouped launches reduce K splits in the kernel.
+template <int B, int MS, int WN, int KW = 2, int TN = BN, bool SW = false, bool RED = false, bool GRP = false>
+__global__ __launch_bounds__(64 * WN * KW, gemm_min_blocks(WN)) void gemm_kernel(const u32* __restrict__ W_arg,
+                                                   const uint16_t* __restrict__ S_arg,
+                                                   const uint16_t* __restrict__ Mn_arg,
                                                    const uint16_t* __restrict__ X,
-                                                   float* __restrict__ Y, float* __restrict__ P,
+                                                   float* __restrict__ Y_arg, float* __restrict__ P_arg,
                                                    int* __restrict__ counters,
-                                                   int M, int N, int K, uint64_t gmul, int gsh,
+                                                   int M, int N_arg, int K, uint64_t gmul, int gsh,
                                                    int grid_m, int grid_n, int split,
-                                                   int steps_per_split, int out16) {
+                                                   int steps_per_split, int out16, GemmGroupArgs grp) {
     constexpr int TILE_M = 32 * MS;
     constexpr int THREADS = 64 * WN * KW;
     constexpr int NS = TN / (32 * WN);                   // 32-column fragments per wave
@@ -302,7 +306,20 @@ __global__ __launch_bounds__(64 * WN * KW, gemm_min_blocks(WN)) void gemm_kernel
     const int mt = t % grid_m;
     const int rest = t / grid_m;
     const int sk = rest % split;
-    const int nt = rest / split;
+    const int ntg = rest / split;  // N-tile over the whole launch
+    // The member owning N-tile ntg (wave-uniform; at most three compares).
+    int d = 0;
+    if constexpr (GRP) {
+#pragma unroll
+        for (int i = 1; i < GEMM_GROUP_MAX; ++i) d += (i < grp.count && ntg >= grp.tile0[i]) ? 1 : 0;
+    }
+    const u32* __restrict__ W = GRP ? grp.w[d] : W_arg;
+    const uint16_t* __restrict__ S = GRP ? grp.s[d] : S_arg;
+    const uint16_t* __restrict__ Mn = GRP ? grp.m[d] : Mn_arg;
+    float* __restrict__ Y = GRP ? grp.y[d] : Y_arg;
+    const int N = GRP ? grp.n[d] : N_arg;
+    float* __restrict__ P = GRP ? P_arg + (size_t)split * M * grp.col0[d] : P_arg;
+    const int nt = GRP ? ntg - grp.tile0[d] : ntg;
     const int m0 = mt * TILE_M, n0 = nt * TN;
     const int steps = (K + BK - 1) / BK;
     const int st0 = sk * steps_per_split;
@@ -615,7 +632,7 @@ __global__ __launch_bounds__(64 * WN * KW, gemm_min_blocks(WN)) void gemm_kernel
     __builtin_amdgcn_s_waitcnt(WAITCNT_VM0);
     __syncthreads();
     if (tid == 0) {
-        int* cnt = counters + (nt * grid_m + mt);
+        int* cnt = counters + (ntg * grid_m + mt);
         const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int last = prev == split - 1;
         if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -668,11 +685,33 @@ static hipError_t launch_gemm_t(const GemmArgs& a, const GemmShape& sh, hipStrea
     // 64 rows, 128 columns); the host passes counters only for those.
     constexpr bool RED_OK = MS <= 2 && TN == BN && KW == 2;
     const bool red = RED_OK && sh.split > 1 && a.counters;
+    const GemmGroupArgs g = a.grp ? *a.grp : GemmGroupArgs{};
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3(grid), dim3(THREADS), 0, st, a.w, a.s, a.m, a.x, a.y, a.partial, a.counters,
                            a.m_rows, a.n, a.k, gm.mul, gm.shift, sh.grid_m, sh.grid_n, sh.split,
-                           sh.k_tiles_per_split, a.out16);
+                           sh.k_tiles_per_split, a.out16, g);
     };
+    if (a.grp) {
+        // Grouped launches: 128-column tiles, K splits reduced in the kernel
+        // (the host plans no split for the tiles without that reduction).
+        if constexpr (TN == BN) {
+            if (sh.split > 1 && !red) return hipErrorInvalidValue;
+            if (SW_OK && sh.wide_scales) {
+                if (red)
+                    go(gemm_kernel<B, MS, WN, KW, TN, SW_OK, RED_OK, true>);
+                else
+                    go(gemm_kernel<B, MS, WN, KW, TN, SW_OK, false, true>);
+            } else {
+                if (red)
+                    go(gemm_kernel<B, MS, WN, KW, TN, false, RED_OK, true>);
+                else
+                    go(gemm_kernel<B, MS, WN, KW, TN, false, false, true>);
+            }
+            return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
     if (SW_OK && sh.wide_scales) {
         if (red)
             go(gemm_kernel<B, MS, WN, KW, TN, SW_OK, RED_OK>);

@@ -308,10 +308,15 @@ constexpr int GEMM_INKERNEL_REDUCE_MAX_SPLIT = 2;
 constexpr size_t GEMM_COUNTER_BYTES = 4096;
 constexpr int64_t GEMM_COUNTER_TILES = GEMM_COUNTER_BYTES / sizeof(int);
 
-GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int group, int cus, size_t ws_bytes, size_t* ws_need) {
+// n: output columns (the sum over the members of a grouped launch);
+// tiles128: 128-column tiles (per member, summed); grouped launches keep
+// 128-column tiles and split K only where the kernel reduces the split
+// itself (32/64-row tiles, counters for every tile).
+GemmShape plan_gemm_impl(int64_t m, int64_t n, int64_t tiles128, bool grouped, int64_t k, int group, int cus,
+                         size_t ws_bytes, size_t* ws_need) {
     GemmShape sh{};
     const int k_tiles = (int)((k + GEMM_BK - 1) / GEMM_BK);
-    const int64_t grid_n = (n + 127) / 128;
+    const int64_t grid_n = tiles128;
     sh.tile_m = m <= 32 ? 32 : m <= 64 ? 64 : 128;
     if (sh.tile_m == 128) {
         const int64_t tiles64 = (m + 63) / 64 * grid_n;
@@ -324,11 +329,11 @@ GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int group, int cus, size_t 
     // bytes per flop; they pay off where their grid alone fills the CUs
     // (measured: 12 % on 8192 x 2048 at m = 2048, a loss wherever they would
     // need a K split).
-    sh.tile_n = (sh.tile_m == 128 && (m + 127) / 128 * ((n + 255) / 256) >= cus) ? 256 : 128;
+    sh.tile_n = (!grouped && sh.tile_m == 128 && (m + 127) / 128 * ((n + 255) / 256) >= cus) ? 256 : 128;
     const int etn = env_int("QMM_GEMM_TILE_N", 0);
-    if ((etn == 128 || etn == 256) && sh.tile_m >= 64) sh.tile_n = etn;
+    if (!grouped && (etn == 128 || etn == 256) && sh.tile_m >= 64) sh.tile_n = etn;
     sh.grid_m = (int)((m + sh.tile_m - 1) / sh.tile_m);
-    sh.grid_n = (int)((n + sh.tile_n - 1) / sh.tile_n);
+    sh.grid_n = grouped ? (int)tiles128 : (int)((n + sh.tile_n - 1) / sh.tile_n);
     const int64_t tiles = (int64_t)sh.grid_m * sh.grid_n;
     int split = 1;
     if (tiles < cus) {
@@ -340,6 +345,7 @@ GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int group, int cus, size_t 
     const int es = env_int("QMM_GEMM_SPLIT", 0);
     if (es > 0) split = es < k_tiles ? es : k_tiles;
     if (split > 16) split = 16;  // the reduction handles at most 16 splits
+    if (grouped && (sh.tile_m > 64 || tiles > GEMM_COUNTER_TILES)) split = 1;
     // Workspace: the tiles' arrival counters, then the partial sums (their
     // byte offsets must stay below 2^32).
     const size_t per_split = (size_t)m * n * sizeof(float);
@@ -357,6 +363,10 @@ GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int group, int cus, size_t 
     sh.split = (k_tiles + sh.k_tiles_per_split - 1) / sh.k_tiles_per_split;
     sh.wide_scales = wide;
     return sh;
+}
+
+GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int group, int cus, size_t ws_bytes, size_t* ws_need) {
+    return plan_gemm_impl(m, n, (n + 127) / 128, false, k, group, cus, ws_bytes, ws_need);
 }
 
 // m rows at or below this go to the multi-row GEMV kernel instead of MFMA.
@@ -515,6 +525,135 @@ qmm_status gemm_common(const void* w_packed, const void* scales, const void* min
 }  // namespace
 
 extern "C" {
+
+// Members of a grouped GEMM, checked, with zero-column members dropped.
+static qmm_status check_group(const qmm_gemm_member* members, int count, int64_t m, int64_t k, int bits,
+                              int group_size, int64_t* ns, int* kept, int64_t* n_sum, int64_t* tiles128,
+                              bool pointers = true) {
+    if (count < 1 || count > GEMM_GROUP_MAX)
+        return fail(QMM_ERR_INVALID_ARGUMENT, "count=%d outside 1..%d", count, GEMM_GROUP_MAX);
+    if (!members) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL members");
+    *kept = 0;
+    *n_sum = 0;
+    *tiles128 = 0;
+    char why[sizeof g_err];
+    for (int i = 0; i < count; ++i) {
+        const qmm_gemm_member& g = members[i];
+        qmm_status st = check_format(g.n, k, bits, group_size);
+        const bool live = g.n > 0 && m > 0;
+        if (st == QMM_OK && live) st = check_output_bytes(m, g.n);
+        if (st == QMM_OK && live && pointers) st = check_weight_ptrs(g.w_packed, g.scales, g.mins, bits);
+        if (st == QMM_OK && live && pointers && !g.y) st = fail(QMM_ERR_INVALID_ARGUMENT, "NULL y");
+        if (st == QMM_OK && live && pointers && !aligned(g.y, 16))
+            st = fail(QMM_ERR_MISALIGNED, "y not 16-byte aligned");
+        if (st != QMM_OK) {
+            memcpy(why, g_err, sizeof why);
+            return fail(st, "member %d: %s", i, why);
+        }
+        if (g.n == 0) continue;
+        ns[(*kept)++] = i;
+        *n_sum += g.n;
+        *tiles128 += (g.n + 127) / 128;
+    }
+    if (*n_sum > INT_LIMIT) return fail(QMM_ERR_INVALID_ARGUMENT, "total n above 2^31-1");
+    return QMM_OK;
+}
+
+// A grouped launch pays where the members underfill the GPU on their own
+// (q|k|v, and gate|up at 128 tokens: 11.5 vs 27.8 us and 17.9 vs 28.0 us);
+// where every member's own tile grid already fills it, separate launches
+// keep the best tile shape per member (gate|up at 2048 tokens: 159 us
+// separate against 205 grouped).
+static bool members_fill_alone(const qmm_gemm_member* members, const int64_t* idx, int kept, int64_t m,
+                               int64_t k, int group_size, int cus) {
+    if (env_int("QMM_GEMM_GROUPED", 0) == 1) return false;  // always one launch (for measurements)
+    for (int j = 0; j < kept; ++j) {
+        const GemmShape sh = plan_gemm(m, members[idx[j]].n, k, group_size, cus, 0, nullptr);
+        if ((int64_t)sh.grid_m * sh.grid_n < cus) return false;
+    }
+    return true;
+}
+
+size_t qmm_gemm_grouped_workspace_bytes(const qmm_gemm_member* members, int count, int64_t m, int64_t k,
+                                        int bits, int group_size) {
+    int64_t idx[GEMM_GROUP_MAX];
+    int kept = 0;
+    int64_t n_sum = 0, tiles128 = 0;
+    if (m <= 0 ||
+        check_group(members, count, m, k, bits, group_size, idx, &kept, &n_sum, &tiles128, false) != QMM_OK ||
+        kept == 0)
+        return 0;
+    int cus = 0;
+    if (device_cus(&cus) != QMM_OK) cus = 256;
+    size_t need = 0;
+    if (members_fill_alone(members, idx, kept, m, k, group_size, cus)) {
+        for (int j = 0; j < kept; ++j) {
+            size_t one = 0;
+            (void)plan_gemm(m, members[idx[j]].n, k, group_size, cus, (size_t)-1, &one);
+            if (one > need) need = one;
+        }
+        return need;
+    }
+    (void)plan_gemm_impl(m, n_sum, tiles128, true, k, group_size, cus, (size_t)-1, &need);
+    return need;
+}
+
+qmm_status qmm_gemm_grouped(const qmm_gemm_member* members, int count, const void* x, int64_t m, int64_t k,
+                            int bits, int group_size, void* workspace, size_t workspace_bytes, void* stream) {
+    if (m < 0) return fail(QMM_ERR_INVALID_ARGUMENT, "m=%lld is negative", (long long)m);
+    if (m > INT_LIMIT) return fail(QMM_ERR_INVALID_ARGUMENT, "m too large");
+    int64_t idx[GEMM_GROUP_MAX];
+    int kept = 0;
+    int64_t n_sum = 0, tiles128 = 0;
+    qmm_status st = check_group(members, count, m, k, bits, group_size, idx, &kept, &n_sum, &tiles128);
+    if (st != QMM_OK) return st;
+    if (m == 0 || kept == 0) return ok();
+    if ((st = check_activation_bytes(m, k)) != QMM_OK) return st;
+    if (!x) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL x");
+    if (!aligned(x, 16)) return fail(QMM_ERR_MISALIGNED, "x not 16-byte aligned");
+    if (workspace_bytes && !workspace)
+        return fail(QMM_ERR_INVALID_ARGUMENT, "workspace_bytes > 0 with a NULL workspace");
+    if (workspace && !aligned(workspace, 16)) return fail(QMM_ERR_MISALIGNED, "workspace not 16-byte aligned");
+    int cus = 0;
+    if ((st = device_cus(&cus)) != QMM_OK) return st;
+    if (members_fill_alone(members, idx, kept, m, k, group_size, cus)) {
+        for (int j = 0; j < kept; ++j) {
+            const qmm_gemm_member& mb = members[idx[j]];
+            if ((st = gemm_common(mb.w_packed, mb.scales, mb.mins, x, mb.y, m, mb.n, k, bits, group_size,
+                                  workspace, workspace_bytes, stream, false)) != QMM_OK)
+                return st;
+        }
+        return ok();
+    }
+    const GemmShape sh =
+        plan_gemm_impl(m, n_sum, tiles128, true, k, group_size, cus, workspace ? workspace_bytes : 0, nullptr);
+    GemmGroupArgs g{};
+    g.count = kept;
+    int tile = 0, col = 0;
+    for (int j = 0; j < kept; ++j) {
+        const qmm_gemm_member& mb = members[idx[j]];
+        g.w[j] = static_cast<const uint32_t*>(mb.w_packed);
+        g.s[j] = static_cast<const uint16_t*>(mb.scales);
+        g.m[j] = static_cast<const uint16_t*>(mb.mins);
+        g.y[j] = mb.y;
+        g.n[j] = (int)mb.n;
+        g.col0[j] = col;
+        g.tile0[j] = tile;
+        col += (int)mb.n;
+        tile += (int)((mb.n + 127) / 128);
+    }
+    for (int j = kept; j <= GEMM_GROUP_MAX; ++j) g.tile0[j] = tile;
+    float* partial = nullptr;
+    int* counters = nullptr;
+    if (sh.split > 1) {
+        counters = static_cast<int*>(workspace);
+        partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + GEMM_COUNTER_BYTES);
+    }
+    GemmArgs a{g.w[0], g.s[0], g.m[0], static_cast<const uint16_t*>(x), g.y[0], partial, counters, (int)m,
+               (int)n_sum, (int)k, group_size, bits, 0};
+    a.grp = &g;
+    return launched(launch_gemm(a, sh, as_stream(stream)), "qmm_gemm_grouped");
+}
 
 qmm_status qmm_gemm(const void* w_packed, const void* scales, const void* mins, const void* x,
                     float* y, int64_t m, int64_t n, int64_t k, int bits, int group_size,

@@ -103,6 +103,22 @@ struct RowsShape {
     int waves_per_cu;    // > 0: resident waves per CU the grid assumes; 0: the kernel's occupancy
 };
 
+// A grouped GEMM: up to GEMM_GROUP_MAX weight matrices sharing X, M and K
+// in one launch.  Their N-tiles are concatenated: member d owns global tiles
+// [tile0[d], tile0[d + 1]) and, with a K split, the partial sums from
+// column col0[d] of a [split][M][sum of N] area.
+constexpr int GEMM_GROUP_MAX = 4;
+struct GemmGroupArgs {
+    const uint32_t* w[GEMM_GROUP_MAX];
+    const uint16_t* s[GEMM_GROUP_MAX];
+    const uint16_t* m[GEMM_GROUP_MAX];
+    float* y[GEMM_GROUP_MAX];
+    int n[GEMM_GROUP_MAX];
+    int col0[GEMM_GROUP_MAX];
+    int tile0[GEMM_GROUP_MAX + 1];
+    int count;
+};
+
 struct GemmArgs {
     const uint32_t* w;
     const uint16_t* s;
@@ -113,6 +129,7 @@ struct GemmArgs {
     int* counters;   // split-K arrival counter per tile (zero between calls), or null
     int m_rows, n, k, group, bits;
     int out16;       // y holds fp16 [m][n] (else fp32)
+    const GemmGroupArgs* grp = nullptr;  // grouped launch (members replace w, s, m, y, n)
 };
 
 struct GemmShape {

@@ -8,7 +8,8 @@ import numpy as np
 import torch
 
 from . import (GemvDesc, qmm_gemm, qmm_gemm_f16out, qmm_gemm_workspace_bytes, qmm_gemv, qmm_gemv_batch_prepare,
-               qmm_gemv_swiglu, qmm_moe_swiglu, qmm_gemv_residual, qmm_moe_combine,
+               qmm_gemv_swiglu, qmm_moe_swiglu, qmm_gemv_residual, qmm_moe_combine, qmm_gemm_grouped,
+               qmm_gemm_grouped_workspace_bytes,
                qmm_gemv_batched, qmm_moe_gemm, qmm_unpack)
 
 
@@ -78,6 +79,24 @@ def gemm(dq: dict, x: torch.Tensor, y: torch.Tensor | None = None, workspace=Non
     fn(dq["w"], dq["scales"], dq["mins"], x, y, m, dq["n"], dq["k"], dq["bits"],
        dq["group"], workspace=workspace, workspace_bytes=ws_bytes, stream=stream)
     return y
+
+
+def gemm_grouped(dqs: list, x: torch.Tensor, ys: list | None = None, workspace=None,
+                 stream=None) -> list:
+    """Y_i = X W_i^T for every matrix in dqs (same bits, group and K) in one launch."""
+    m = x.shape[0]
+    if ys is None:
+        ys = [torch.empty((m, dq["n"]), dtype=torch.float32, device=x.device) for dq in dqs]
+    members = [(dq["w"], dq["scales"], dq["mins"], y, dq["n"]) for dq, y in zip(dqs, ys)]
+    bits, group, k = dqs[0]["bits"], dqs[0]["group"], dqs[0]["k"]
+    if workspace is None:
+        need = qmm_gemm_grouped_workspace_bytes(members, m, k, bits, group)
+        # Zeroed: the arrival counters at its start must read zero at first use.
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=x.device) if need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    qmm_gemm_grouped(members, x, m, k, bits, group, workspace=workspace, workspace_bytes=ws_bytes,
+                     stream=stream)
+    return ys
 
 
 def moe(dst: dict, x: torch.Tensor, x_rows: torch.Tensor | None, offsets: torch.Tensor,

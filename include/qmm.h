@@ -160,6 +160,37 @@ QMM_API qmm_status qmm_gemm_f16out(const void *w_packed, const void *scales,
                                    int64_t n, int64_t k, int bits, int group_size,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* Grouped prefill GEMM: up to 4 weight matrices that share the activations
+ * x [m][k] (the q, k and v projections of a layer, or gate and up), one
+ * launch: y_i[r][j] = sum_k (s*q + m)_i[j][k] * x[r][k] for every member i.
+ * Pages: "BaseRT claims fastest Apple Silicon inference", section "What
+ * BaseRT does differently" (operations other runtimes dispatch separately
+ * run as one fused dispatch; GEMM kernels for prefill).
+ *   members (host array of count, 1..4): each member's packed weights,
+ *     scales and mins in the qmm_gemm layout with its own n (n == 0: the
+ *     member is skipped), and its output y fp32 [m][n], 16-byte aligned.
+ *   x fp16 [m][k], 16-byte aligned; bits and group_size shared.
+ *   workspace: as qmm_gemm (zero before its first use, counters left zero);
+ *     qmm_gemm_grouped_workspace_bytes gives the preferred size (it reads
+ *     the members' n only).
+ * The members go into one launch where they underfill the GPU on their own;
+ * where each member's own tile grid fills it, they are launched one after
+ * another as qmm_gemm would (same stream, same workspace).  Either way each
+ * y_i is member i's product to qmm_gemm's accuracy.                       */
+typedef struct {
+    const void *w_packed;
+    const void *scales;
+    const void *mins;
+    float *y;
+    int64_t n;
+} qmm_gemm_member;
+
+QMM_API qmm_status qmm_gemm_grouped(const qmm_gemm_member *members, int count, const void *x,
+                                    int64_t m, int64_t k, int bits, int group_size,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+QMM_API size_t qmm_gemm_grouped_workspace_bytes(const qmm_gemm_member *members, int count,
+                                                int64_t m, int64_t k, int bits, int group_size);
+
 /* Many independent decode GEMVs in one launch.
  * Pages: "BaseRT claims fastest Apple Silicon inference", section "What
  * BaseRT does differently" (operations other runtimes dispatch separately

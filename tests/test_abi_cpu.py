@@ -304,3 +304,29 @@ def test_ceiling_library_exports():
     assert cl.qmm_ceiling_read(None, 16, 1, p(A16), None) == 1
     assert cl.qmm_ceiling_read(p(A16), 15, 1, p(A16), None) == 1
     assert cl.qmm_ceiling_mfma(0, 10, p(A16), None) == 1
+
+
+def test_grouped_argument_checks(lib):
+    p = ctypes.c_void_p
+    import gemm_qmm_gemv_amd as q
+    f = lib.qmm_gemm_grouped
+
+    def call(members, count=None, x=A16, m=64, k=128, bits=4, ws=None, wsb=0):
+        arr = (q.GemmMember * max(len(members), 1))()
+        for d, (w, y, n) in zip(arr, members):
+            d.w_packed, d.scales, d.mins, d.y, d.n = w, A16, A16, y, n
+        return f(ctypes.addressof(arr), len(members) if count is None else count, p(x) if x else None,
+                 m, k, bits, 64, p(ws) if ws else None, wsb, None)
+    good = [(A16, A16, 128), (A16, A16, 64)]
+    assert call(good) in (qmm.QMM_ERR_DEVICE, qmm.QMM_OK)
+    assert call(good, count=0) == qmm.QMM_ERR_INVALID_ARGUMENT
+    assert call(good * 3, count=5) == qmm.QMM_ERR_INVALID_ARGUMENT
+    assert call(good, m=0) == qmm.QMM_OK
+    assert call([(A16, A16, 0)]) == qmm.QMM_OK  # nothing to compute
+    assert call([(A16, A16 + 4, 128)]) == qmm.QMM_ERR_MISALIGNED
+    assert call([(A16, 0, 128)]) == qmm.QMM_ERR_INVALID_ARGUMENT
+    assert call(good, x=A16 + 2) == qmm.QMM_ERR_MISALIGNED
+    assert call(good, bits=7) == qmm.QMM_ERR_UNSUPPORTED
+    assert call(good, k=100) == qmm.QMM_ERR_INVALID_ARGUMENT
+    assert call(good, ws=A16 + 8, wsb=1024) == qmm.QMM_ERR_MISALIGNED
+    assert f(None, 2, p(A16), 64, 128, 4, 64, None, 0, None) == qmm.QMM_ERR_INVALID_ARGUMENT
