@@ -362,6 +362,11 @@ GemmShape plan_gemm_impl(int64_t m, int64_t n, int64_t tiles128, bool grouped, i
     if (wide && split > 1) sh.k_tiles_per_split = (sh.k_tiles_per_split + 3) / 4 * 4;
     sh.split = (k_tiles + sh.k_tiles_per_split - 1) / sh.k_tiles_per_split;
     sh.wide_scales = wide;
+    // Tile order (see gemm_kernel): column tiles fastest from 16 row tiles
+    // on, unless there are more column tiles than row tiles (8192 x 2048 at
+    // 2048 tokens: +1 % that way).
+    const int eo = env_int("QMM_GEMM_ORDER", 0);
+    sh.n_fast = eo == 1 ? true : eo == 2 ? false : (sh.grid_m >= 16 && sh.grid_n <= sh.grid_m);
     return sh;
 }
 

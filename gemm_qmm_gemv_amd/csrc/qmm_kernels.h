@@ -138,6 +138,7 @@ struct GemmShape {
     int k_tiles_per_split;
     int grid_m, grid_n;
     bool wide_scales;  // 16-byte scale/min loads per four steps (group 64, K % 512 == 0)
+    bool n_fast;       // tile order: column tile fastest within an XCD's range
 };
 
 // One GEMV of a batched launch.  Same layout as qmm_gemv_desc in qmm.h.
