@@ -8,9 +8,11 @@
 //
 // Y[M][N] = X[M][K] * W^T with W = s*q + m, on v_mfma_f32_32x32x16_f16.
 //
-// Work-group: 4 waves, tile TILE_M (= 32*MS) x 128 of Y, K in steps of 128.
-// Wave (wn, wk) owns 64 columns (two 32-column fragments) and one 64-wide
-// half of every K step; the two K-halves are added through LDS at the end.
+// Work-group: tile TILE_M (= 32*MS) x TN of Y, K in steps of 128.  With
+// 128-column tiles, eight waves: four along N (32 columns each) times two
+// along K (each takes one 64-wide half of every step; the halves are added
+// through LDS at the end).  With 256-column tiles, eight waves along N, each
+// taking whole steps.
 //
 //   * W never goes through LDS.  The matrix core's B operand for lane l is
 //     eight K values of column l%32, and lanes l and l+32 cover the two
@@ -26,17 +28,18 @@
 //   * X (fp16) is the shared operand: the work-group copies its TILE_M x 128
 //     block to LDS once per step (double-buffered, one barrier per step) and
 //     every wave reads 32x16 A fragments from there.
-//   * Software pipeline: a step's loads are issued PD steps ahead, and while
-//     the matrix core works on step s the same wave dequantizes W and stages
-//     X for step s + 1 (no dependence between the two, so VALU and MFMA
-//     instructions interleave within the wave instead of alternating between
-//     barrier-separated phases).
+//   * Software pipeline: a step's loads are issued PD steps ahead; each step
+//     first stages X for step s + 1, then the matrix core works on step s
+//     while the same wave dequantizes W for step s + 1 (no dependence
+//     between the two, so VALU and MFMA instructions interleave within the
+//     wave instead of alternating between barrier-separated phases).
 //
 // When the tile grid alone would leave compute units idle, K is split across
-// work-groups; partial sums go to a caller-provided workspace and a second
-// kernel adds them in split order (deterministic, no atomics).  Work-group ids
-// are remapped so that tiles sharing a W column block land on the same XCD
-// (and its L2).
+// work-groups; partial sums go to a caller-provided workspace and are added
+// in split order (deterministic) -- two splits by the last work-group of each
+// tile inside this kernel, more by a second kernel.  Work-group ids are
+// remapped so that each XCD (and its L2) takes a contiguous range of tiles.
+// A grouped launch runs several weight matrices that share X as one grid.
 #include "qmm_device.h"
 #include "qmm_kernels.h"
 
