@@ -16,7 +16,13 @@
 //   (U*XC units in flight per lane).  The activation side of each owned unit
 //   (pairs, offset constant, plain sum) is built once per wave and reused for
 //   every row the wave visits.  Partial sums are reduced across the LPR lanes
-//   with cross-lane shuffles; no atomics, so results are deterministic.
+//   with cross-lane shuffles; results are deterministic (the one exception is
+//   the expert rows' weighted combine, which adds into token rows with float
+//   atomics in no fixed order).
+//
+// Fused variants share these loops: the SiLU-gated product of two matrices
+// and the residual add (decode), the gate/up product and the weighted
+// combine (expert rows).
 #pragma once
 
 #include "qmm_device.h"
