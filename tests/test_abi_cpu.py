@@ -330,3 +330,23 @@ def test_grouped_argument_checks(lib):
     assert call(good, k=100) == qmm.QMM_ERR_INVALID_ARGUMENT
     assert call(good, ws=A16 + 8, wsb=1024) == qmm.QMM_ERR_MISALIGNED
     assert f(None, 2, p(A16), 64, 128, 4, 64, None, 0, None) == qmm.QMM_ERR_INVALID_ARGUMENT
+
+
+def test_grouped_workspace_follows_the_launch_decision(lib):
+    # Without a device the planner assumes 256 compute units.  q|k|v of a
+    # Llama-3.2-1B layer at 128 tokens underfill the GPU alone: one grouped
+    # launch of 2 x 24 tiles, K split in four (counters, then the partial
+    # sums of all three members).  gate|up at 2048 tokens fill it alone:
+    # separate launches without a split need no workspace.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+
+    def members(ns):
+        return [(A16, A16, A16, A16, n) for n in ns]
+    need = qmm.qmm_gemm_grouped_workspace_bytes(members([2048, 512, 512]), 128, 2048, 4, 64)
+    assert need == 4096 + 4 * 128 * 3072 * 4
+    assert qmm.qmm_gemm_grouped_workspace_bytes(members([8192, 8192]), 2048, 2048, 4, 64) == 0
+    # A member with n = 0 is skipped; an empty group needs nothing.
+    assert qmm.qmm_gemm_grouped_workspace_bytes(members([2048, 0, 512, 512]), 128, 2048, 4, 64) == need
+    assert qmm.qmm_gemm_grouped_workspace_bytes(members([0]), 128, 2048, 4, 64) == 0
