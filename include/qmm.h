@@ -172,7 +172,8 @@ QMM_API qmm_status qmm_gemm_f16out(const void *w_packed, const void *scales,
  *   x fp16 [m][k], 16-byte aligned; bits and group_size shared.
  *   workspace: as qmm_gemm (zero before its first use, counters left zero);
  *     qmm_gemm_grouped_workspace_bytes gives the preferred size (it reads
- *     the members' n only).
+ *     the members' n only; sized for the current device, or for 256
+ *     compute units where no device can be queried).
  * The members go into one launch where they underfill the GPU on their own;
  * where each member's own tile grid fills it, they are launched one after
  * another as qmm_gemm would (same stream, same workspace).  Either way each
@@ -222,7 +223,8 @@ QMM_API qmm_status qmm_gemv_batched(const qmm_gemv_desc *descs_device,
                                     int bits, int group_size, void *stream);
 
 /* Bytes of workspace that let qmm_gemm use its preferred K split for this
- * shape on the current device (0 when it would not split).  Host only.     */
+ * shape on the current device (0 when it would not split; sized for 256
+ * compute units where no device can be queried).  Host only.              */
 QMM_API size_t qmm_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits,
                                 int group_size);
 
