@@ -21,7 +21,7 @@ __all__ = [
     "qmm_gemv_batch_prepare", "qmm_gemv_batched", "GemvDesc", "GemmMember", "qmm_gemv_swiglu",
     "qmm_gemm_f16out",
     "qmm_moe_swiglu", "qmm_gemv_residual", "qmm_moe_combine", "qmm_gemm_grouped",
-    "qmm_gemm_grouped_workspace_bytes",
+    "qmm_gemm_grouped_workspace_bytes", "qmm_set_override", "overrides",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
     "QMM_OK", "QMM_ERR_INVALID_ARGUMENT", "QMM_ERR_UNSUPPORTED", "QMM_ERR_MISALIGNED",
     "QMM_ERR_DEVICE", "EXPORTED_SYMBOLS",
@@ -37,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
     "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out",
     "qmm_moe_swiglu", "qmm_gemv_residual", "qmm_moe_combine", "qmm_gemm_grouped",
-    "qmm_gemm_grouped_workspace_bytes",
+    "qmm_gemm_grouped_workspace_bytes", "qmm_set_override",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
 )
 
@@ -125,6 +125,7 @@ def load():
     lib.qmm_gemv_swiglu.argtypes = [p, p, p, p, p, p, p, p, i64, i64, ci, ci, p]
     lib.qmm_gemv_residual.argtypes = [p, p, p, p, p, p, i64, i64, ci, ci, p]
     lib.qmm_gemm_f16out.argtypes = [p, p, p, p, p, i64, i64, i64, ci, ci, p, sz, p]
+    lib.qmm_set_override.argtypes = [ctypes.c_char_p, ci]
     lib.qmm_gemm_workspace_bytes.argtypes = [i64, i64, i64, ci, ci]
     lib.qmm_gemm_workspace_bytes.restype = sz
     lib.qmm_moe_gemm.argtypes = [p, p, p, p, p, i64, p, p, i64, i64, i64, i64, ci, ci, p]
@@ -139,7 +140,8 @@ def load():
     lib.qmm_get_plan.argtypes = [ci, i64, i64, i64, ci, ci, ci, sz, ctypes.POINTER(_Plan)]
     for f in ("qmm_gemv", "qmm_gemm", "qmm_moe_gemm", "qmm_unpack", "qmm_get_plan",
               "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out", "qmm_moe_swiglu",
-              "qmm_gemv_residual", "qmm_moe_combine", "qmm_gemm_grouped"):
+              "qmm_gemv_residual", "qmm_moe_combine", "qmm_gemm_grouped",
+              "qmm_set_override"):
         getattr(lib, f).restype = ci
     lib.qmm_status_string.argtypes = [ci]
     lib.qmm_status_string.restype = ctypes.c_char_p
@@ -225,6 +227,29 @@ def qmm_gemm(w_packed, scales, mins, x, y, m, n, k, bits, group_size, workspace=
                            int(m), int(n), int(k), int(bits), int(group_size), _addr(workspace),
                            int(workspace_bytes), _stream(stream)),
            "qmm_gemm")
+
+
+def qmm_set_override(name: str, value: int) -> None:
+    """Process-wide launch-plan override (value < 0 removes it)."""
+    _check(load().qmm_set_override(name.encode(), int(value)), "qmm_set_override")
+
+
+class overrides:
+    """Context manager: ``with overrides(QMM_GEMM_TILE_M=64): ...`` sets the
+    named launch-plan overrides and removes them on exit."""
+
+    def __init__(self, **values):
+        self.values = values
+
+    def __enter__(self):
+        for name, value in self.values.items():
+            qmm_set_override(name, value)
+        return self
+
+    def __exit__(self, *exc):
+        for name in self.values:
+            qmm_set_override(name, -1)
+        return False
 
 
 def _members(members):

@@ -43,8 +43,22 @@ def _run(cmd, verbose):
         print("\n".join(msgs))
 
 
-def build(verbose: bool = False, out: str | None = None, extra_flags=(), objdir: str | None = None) -> str:
-    """Compile every source (in parallel) and link libqmm.so.  Always rebuilds.
+def _stale(obj: str, src: str) -> bool:
+    """An object is stale when it is missing or older than its source or any
+    header it may include (csrc/*.h, include/*.h)."""
+    if not os.path.exists(obj):
+        return True
+    deps = [src] + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + [
+        os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))]
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(verbose: bool = False, out: str | None = None, extra_flags=(), objdir: str | None = None,
+          incremental: bool = False) -> str:
+    """Compile every source (in parallel) and link libqmm.so.  Rebuilds every
+    object unless ``incremental`` (then only objects older than their
+    sources or headers; the library is always relinked).
     ``out``/``extra_flags``/``objdir`` produce variant builds (e.g. with a
     -D switch) next to the default one."""
     from concurrent.futures import ThreadPoolExecutor
@@ -57,12 +71,14 @@ def build(verbose: bool = False, out: str | None = None, extra_flags=(), objdir:
     jobs = []
     for src, defs, oname in SOURCES:
         obj = os.path.join(objdir, oname)
-        jobs.append(([hipcc] + compile_flags + defs + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
-    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "8"))))
+        jobs.append(([hipcc] + compile_flags + defs + ["-c", os.path.join(CSRC, src), "-o", obj], obj,
+                     os.path.join(CSRC, src)))
+    todo = [j for j in jobs if not incremental or _stale(j[1], j[2])]
+    workers = max(1, min(len(todo), int(os.environ.get("MAX_JOBS", "8"))))
     with ThreadPoolExecutor(max_workers=workers) as ex:
-        list(ex.map(lambda j: _run(j[0], verbose), jobs))
+        list(ex.map(lambda j: _run(j[0], verbose), todo))
     tmp = out + ".tmp%d" % os.getpid()
-    _run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH] + [o for _, o in jobs] + ["-o", tmp],
+    _run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH] + [j[1] for j in jobs] + ["-o", tmp],
          verbose)
     os.replace(tmp, out)
     if out == LIB:
@@ -84,4 +100,4 @@ def build_ceiling(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, incremental="--incremental" in sys.argv[1:]))

@@ -144,16 +144,39 @@ qmm_status device_cus(int* cus) {
     return QMM_OK;
 }
 
-int env_int(const char* name, int dflt) {
-    const char* v = getenv(name);
-    if (!v || !*v) return dflt;
-    return atoi(v);
+// Launch-plan overrides (measurement sweeps, tests that force a variant).
+// They are read from the environment once, when the library is loaded, and
+// changed in-process only through qmm_set_override: a call never reads the
+// environment.  A negative value means "no override".
+enum OverrideId {
+    OV_UNIT, OV_GEMV_LPR, OV_GEMV_XC, OV_GEMV_U, OV_GEMV_WAVES_PER_CU, OV_BATCH_U, OV_ROWS_MR,
+    OV_ROWS_WAVES_PER_CU, OV_GEMM_TILE_M, OV_GEMM_TILE_N, OV_GEMM_SPLIT, OV_GEMM_WIDE_SCALES,
+    OV_GEMM_ORDER, OV_GEMM_GROUPED, OV_COUNT
+};
+const char* const OVERRIDE_NAMES[OV_COUNT] = {
+    "QMM_UNIT", "QMM_GEMV_LPR", "QMM_GEMV_XC", "QMM_GEMV_U", "QMM_GEMV_WAVES_PER_CU", "QMM_BATCH_U",
+    "QMM_ROWS_MR", "QMM_ROWS_WAVES_PER_CU", "QMM_GEMM_TILE_M", "QMM_GEMM_TILE_N", "QMM_GEMM_SPLIT",
+    "QMM_GEMM_WIDE_SCALES", "QMM_GEMM_ORDER", "QMM_GEMM_GROUPED"};
+std::atomic<int> g_override[OV_COUNT];
+
+struct OverridesFromEnvironment {
+    OverridesFromEnvironment() {
+        for (int i = 0; i < OV_COUNT; ++i) {
+            const char* v = getenv(OVERRIDE_NAMES[i]);
+            g_override[i].store(v && *v ? atoi(v) : -1, std::memory_order_relaxed);
+        }
+    }
+} g_overrides_at_load;
+
+int override_or(OverrideId id, int dflt) {
+    const int v = g_override[id].load(std::memory_order_relaxed);
+    return v >= 0 ? v : dflt;
 }
 
 // Codes per activation unit: 64 when the group allows; fp16 weights use 32
 // (a 64-code unit would be 32 weight words per lane and row).
 int unit_codes(int bits, int group) {
-    return (bits != 16 && group % 64 == 0 && env_int("QMM_UNIT", 64) != 32) ? 64 : 32;
+    return (bits != 16 && group % 64 == 0 && override_or(OV_UNIT, 64) != 32) ? 64 : 32;
 }
 
 // ---- planning ------------------------------------------------------------------
@@ -185,7 +208,7 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     sh.unit = unit_codes(bits, group);
     const int nu = (int)(k / sh.unit);
     LaneSplit ls = choose_split(nu, 3, gemv_split_ok);
-    const int el = env_int("QMM_GEMV_LPR", 0), ex = env_int("QMM_GEMV_XC", 0);
+    const int el = override_or(OV_GEMV_LPR, 0), ex = override_or(OV_GEMV_XC, 0);
     if (el > 0 && ex > 0 && gemv_split_ok(el, ex)) ls = {el, ex, el * ex < nu};
     sh.lpr = ls.lpr;
     sh.xc = ls.xc;
@@ -201,7 +224,7 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     const int64_t waves_u1 = (n + slots - 1) / slots;
     int u = (waves_u1 > (int64_t)cus * 16 && sh.xc == 1) ? 2 : 1;
     while (u > 1 && !gemv_shape_supported(sh.lpr, sh.xc, u)) u /= 2;
-    const int ev = env_int("QMM_GEMV_U", 0);
+    const int ev = override_or(OV_GEMV_U, 0);
     if (ev > 0 && gemv_shape_supported(sh.lpr, sh.xc, ev)) u = ev;
     sh.u = u;
     const int64_t batches = (n + (int64_t)slots * u - 1) / ((int64_t)slots * u);
@@ -213,7 +236,7 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     // more batches through its pipelined loop); larger ones, the LM heads,
     // keep the occupancy-sized grid.
     const int wpc_default = batches <= (int64_t)16 * cus ? 8 : 0;
-    sh.waves_per_cu = env_int("QMM_GEMV_WAVES_PER_CU", wpc_default);
+    sh.waves_per_cu = override_or(OV_GEMV_WAVES_PER_CU, wpc_default);
     // Reported grid: the cap assumes 16 resident waves per CU; the launch
     // uses the kernel's real occupancy.
     sh.grid = persistent_grid(sh.work, cus, sh.waves_per_cu > 0 ? sh.waves_per_cu / 4 : 4, 0);
@@ -235,7 +258,7 @@ bool plan_batched(int64_t total_rows, int64_t kmax, int bits, int group, GemvSha
     // valid on any GPU: big batches stream two rows per slot per iteration.
     // Two units per lane already double the registers; those keep one row.
     int u = (total_rows > (int64_t)16 * 4096 && sh.xc == 1) ? 2 : 1;
-    const int ev = env_int("QMM_BATCH_U", 0);
+    const int ev = override_or(OV_BATCH_U, 0);
     if (ev > 0) u = ev;
     if (!batched_shape_supported(sh.xc, u)) u = 1;
     sh.u = u;
@@ -267,7 +290,7 @@ RowsShape plan_rows(int64_t rows_bound, int64_t n, int64_t k, int bits, int grou
     const int64_t segs = n_seg_active > 0 ? n_seg_active : 1;
     const int64_t per_seg = (rows_bound + segs - 1) / segs;
     sh.mr = (per_seg <= 1 || sh.xc > 1) ? 1 : 2;
-    const int em = env_int("QMM_ROWS_MR", 0);
+    const int em = override_or(OV_ROWS_MR, 0);
     if (em > 0 && rows_shape_supported(sh.lpr, sh.xc, em)) sh.mr = em;
     const int slots = 64 / sh.lpr;
     const int64_t rows_per_block = 4 * slots;
@@ -285,7 +308,7 @@ RowsShape plan_rows(int64_t rows_bound, int64_t n, int64_t k, int bits, int grou
     // waves keep their pipelined loops busy); more work keeps the
     // occupancy-sized grid.
     const int64_t row_batches = (int64_t)sh.pairs * ((n + slots - 1) / slots);
-    sh.waves_per_cu = env_int("QMM_ROWS_WAVES_PER_CU", row_batches <= (int64_t)16 * cus ? 4 : 0);
+    sh.waves_per_cu = override_or(OV_ROWS_WAVES_PER_CU, row_batches <= (int64_t)16 * cus ? 4 : 0);
     return sh;
 }
 
@@ -323,14 +346,14 @@ GemmShape plan_gemm_impl(int64_t m, int64_t n, int64_t tiles128, bool grouped, i
         const bool long_k = k_tiles >= 64 && m > 128;
         if (tiles64 <= cus && !long_k) sh.tile_m = 64;
     }
-    const int et = env_int("QMM_GEMM_TILE_M", 0);
+    const int et = override_or(OV_GEMM_TILE_M, 0);
     if (et == 32 || et == 64 || et == 128) sh.tile_m = et;
     // 128 x 256 tiles (eight waves along N, whole steps each) halve the X
     // bytes per flop; they pay off where their grid alone fills the CUs
     // (measured: 12 % on 8192 x 2048 at m = 2048, a loss wherever they would
     // need a K split).
     sh.tile_n = (!grouped && sh.tile_m == 128 && (m + 127) / 128 * ((n + 255) / 256) >= cus) ? 256 : 128;
-    const int etn = env_int("QMM_GEMM_TILE_N", 0);
+    const int etn = override_or(OV_GEMM_TILE_N, 0);
     if (!grouped && (etn == 128 || etn == 256) && sh.tile_m >= 64) sh.tile_n = etn;
     sh.grid_m = (int)((m + sh.tile_m - 1) / sh.tile_m);
     sh.grid_n = grouped ? (int)tiles128 : (int)((n + sh.tile_n - 1) / sh.tile_n);
@@ -342,7 +365,7 @@ GemmShape plan_gemm_impl(int64_t m, int64_t n, int64_t tiles128, bool grouped, i
         if (split > by_k) split = by_k;
         if (split > 16) split = 16;
     }
-    const int es = env_int("QMM_GEMM_SPLIT", 0);
+    const int es = override_or(OV_GEMM_SPLIT, 0);
     if (es > 0) split = es < k_tiles ? es : k_tiles;
     if (split > 16) split = 16;  // the reduction handles at most 16 splits
     if (grouped && (sh.tile_m > 64 || tiles > GEMM_COUNTER_TILES)) split = 1;
@@ -358,14 +381,14 @@ GemmShape plan_gemm_impl(int64_t m, int64_t n, int64_t tiles128, bool grouped, i
     }
     sh.k_tiles_per_split = (k_tiles + split - 1) / split;
     // Wide scale loads need splits that start at multiples of four steps.
-    const bool wide = group == 64 && GEMM_BK == 128 && k % 512 == 0 && env_int("QMM_GEMM_WIDE_SCALES", 1) != 0;
+    const bool wide = group == 64 && GEMM_BK == 128 && k % 512 == 0 && override_or(OV_GEMM_WIDE_SCALES, 1) != 0;
     if (wide && split > 1) sh.k_tiles_per_split = (sh.k_tiles_per_split + 3) / 4 * 4;
     sh.split = (k_tiles + sh.k_tiles_per_split - 1) / sh.k_tiles_per_split;
     sh.wide_scales = wide;
     // Tile order (see gemm_kernel): column tiles fastest from 16 row tiles
     // on, unless there are more column tiles than row tiles (8192 x 2048 at
     // 2048 tokens: +1 % that way).
-    const int eo = env_int("QMM_GEMM_ORDER", 0);
+    const int eo = override_or(OV_GEMM_ORDER, 0);
     sh.n_fast = eo == 1 ? true : eo == 2 ? false : (sh.grid_m >= 16 && sh.grid_n <= sh.grid_m);
     return sh;
 }
@@ -571,7 +594,7 @@ static qmm_status check_group(const qmm_gemm_member* members, int count, int64_t
 // separate against 205 grouped).
 static bool members_fill_alone(const qmm_gemm_member* members, const int64_t* idx, int kept, int64_t m,
                                int64_t k, int group_size, int cus) {
-    if (env_int("QMM_GEMM_GROUPED", 0) == 1) return false;  // always one launch (for measurements)
+    if (override_or(OV_GEMM_GROUPED, 0) == 1) return false;  // always one launch (for measurements)
     for (int j = 0; j < kept; ++j) {
         const GemmShape sh = plan_gemm(m, members[idx[j]].n, k, group_size, cus, 0, nullptr);
         if ((int64_t)sh.grid_m * sh.grid_n < cus) return false;
@@ -674,6 +697,16 @@ qmm_status qmm_gemm_f16out(const void* w_packed, const void* scales, const void*
                        workspace_bytes, stream, true);
 }
 
+qmm_status qmm_set_override(const char* name, int value) {
+    if (!name) return fail(QMM_ERR_INVALID_ARGUMENT, "NULL override name");
+    for (int i = 0; i < OV_COUNT; ++i)
+        if (strcmp(name, OVERRIDE_NAMES[i]) == 0) {
+            g_override[i].store(value < 0 ? -1 : value, std::memory_order_relaxed);
+            return ok();
+        }
+    return fail(QMM_ERR_INVALID_ARGUMENT, "unknown override %s", name);
+}
+
 }  // extern "C"
 
 namespace {
@@ -718,7 +751,7 @@ qmm_status moe_common(const void* w_packed, const void* scales, const void* mins
                     (long long)k);
     RowsArgs a{static_cast<const uint32_t*>(w_packed), static_cast<const uint16_t*>(scales),
                static_cast<const uint16_t*>(mins), static_cast<const uint16_t*>(x), x_rows,
-               (int)x_rows_count, expert_offsets, (int)n_experts, (int)p_rows, y, (int)n, (int)k,
+               (int)(x_rows ? x_rows_count : p_rows), expert_offsets, (int)n_experts, (int)p_rows, y, (int)n, (int)k,
                group_size, bits};
     if (combine) {
         a.pair_token = pair_token;
@@ -831,7 +864,7 @@ qmm_status qmm_gemv_batched(const qmm_gemv_desc* descs_device, const qmm_gemv_de
     // lets a CU hold at once: measured on the decode projection set, 2 %
     // faster than two, and a grid sized for four (more work-groups than fit,
     // so the last ones queue) is 6 % slower.
-    sh.waves_per_cu = env_int("QMM_GEMV_WAVES_PER_CU", BATCHED_WAVES_PER_CU);
+    sh.waves_per_cu = override_or(OV_GEMV_WAVES_PER_CU, BATCHED_WAVES_PER_CU);
     BatchArgs a{reinterpret_cast<const BatchDesc*>(descs_device), (int)count, first, group_size, bits};
     return launched(launch_batched(a, sh, as_stream(stream)), "qmm_gemv_batched");
 }

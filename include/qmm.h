@@ -51,8 +51,14 @@
  *   and keeps no per-call state.  Calls are asynchronous on `stream`
  *   (a hipStream_t passed as void*; NULL means the null stream); a kernel
  *   fault shows up at the caller's next synchronization.  Results are
- *   deterministic: no floating-point atomics; every output element is summed
- *   in a fixed order that depends only on the shape.
+ *   deterministic -- every output element is summed in a fixed order that
+ *   depends only on the shape and the launch plan -- except for
+ *   qmm_moe_combine, whose float atomic adds into a token's row happen in
+ *   no fixed order.
+ *   The launch plan (kernel variant, tiles, splits, grids) depends on the
+ *   shape, the bit width and the device's compute-unit count, and on the
+ *   overrides of qmm_set_override, which the library reads from the
+ *   environment once, when it is loaded; no call reads the environment.
  *   QMM_ERR_DEVICE is returned when the HIP runtime reports an error at
  *   launch time, or when no GPU is present.
  */
@@ -66,7 +72,7 @@
 extern "C" {
 #endif
 
-#define QMM_ABI_VERSION 2
+#define QMM_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define QMM_API __attribute__((visibility("default")))
@@ -141,7 +147,17 @@ QMM_API qmm_status qmm_gemv_swiglu(const void *gate_w, const void *gate_scales,
  *   its first use (allocate it zeroed once), and every call leaves those
  *   counters zero again, so one workspace serves any sequence of calls on
  *   one stream.  Calls that overlap (other streams) need their own
- *   workspace.  The rest of its contents on return are unspecified.        */
+ *   workspace.  The rest of its contents on return are unspecified.
+ *   Two-way splits are summed inside the GEMM kernel: each work-group
+ *   writes its partial sums with stores that go through every cache to
+ *   memory (the system-coherent cache policy of gfx950 buffer stores),
+ *   waits until they are acknowledged, then bumps its tile's counter with a
+ *   relaxed device-scope atomic add; the work-group that arrives last reads
+ *   the partial sums with loads that bypass the caches, writes y and resets
+ *   the counter.  Correctness rests on those cache-policy bits and the
+ *   store acknowledgement, not on release/acquire fences (a device-scope
+ *   fence would write back and invalidate a whole L2 per wave).  Larger
+ *   splits are summed by a second kernel on the same stream.               */
 QMM_API qmm_status qmm_gemm(const void *w_packed, const void *scales, const void *mins,
                     const void *x, float *y, int64_t m, int64_t n, int64_t k,
                     int bits, int group_size, void *workspace,
@@ -315,6 +331,17 @@ typedef struct qmm_plan {
 QMM_API qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits,
                         int group_size, int cu_count, size_t workspace_bytes,
                         qmm_plan *plan /* host */);
+
+/* Launch-plan override for measurement sweeps and for tests that force a
+ * kernel variant (host only, process-wide, not meant for production: a
+ * forced variant may be slower, and a value the chosen kernel cannot take
+ * is ignored).  name is one of QMM_UNIT, QMM_GEMV_LPR, QMM_GEMV_XC,
+ * QMM_GEMV_U, QMM_GEMV_WAVES_PER_CU, QMM_BATCH_U, QMM_ROWS_MR,
+ * QMM_ROWS_WAVES_PER_CU, QMM_GEMM_TILE_M, QMM_GEMM_TILE_N, QMM_GEMM_SPLIT,
+ * QMM_GEMM_WIDE_SCALES, QMM_GEMM_ORDER, QMM_GEMM_GROUPED; value < 0 removes
+ * the override.  The same names are read from the environment once, when
+ * the library is loaded.  Unknown name: QMM_ERR_INVALID_ARGUMENT.          */
+QMM_API qmm_status qmm_set_override(const char *name, int value);
 
 QMM_API const char *qmm_status_string(qmm_status s);
 QMM_API const char *qmm_last_error(void);   /* thread-local; "" when none */

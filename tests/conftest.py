@@ -28,3 +28,19 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture
+def qmm_override():
+    """Set launch-plan overrides in the loaded library for one test (they are
+    removed afterwards): ``qmm_override("QMM_GEMM_TILE_M", 64)``."""
+    import gemm_qmm_gemv_amd as qmm
+    names = []
+
+    def set_override(name, value):
+        qmm.qmm_set_override(name, int(value))
+        names.append(name)
+
+    yield set_override
+    for name in names:
+        qmm.qmm_set_override(name, -1)

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert len(names) >= 9
     for name in names:
         assert hasattr(lib, name), name
-    assert qmm.qmm_abi_version() == 2
+    assert qmm.qmm_abi_version() == 3
 
 
 def test_exports_are_only_the_abi(lib):
@@ -259,12 +259,47 @@ def test_gemm_plan_on_the_prefill_shapes(lib):
         assert (pl["tile_m"], pl["split_k"]) == (tile, split), (m, n, k)
 
 
-def test_gemm_tile_override(lib, monkeypatch):
-    monkeypatch.setenv("QMM_GEMM_TILE_M", "128")
+def test_gemm_tile_override(lib, qmm_override):
+    qmm_override("QMM_GEMM_TILE_M", 128)
     assert qmm.qmm_get_plan(1, 100, 512, 1024, 4, 64, cu_count=256)["tile_m"] == 128
-    monkeypatch.setenv("QMM_GEMM_TILE_M", "32")
+    qmm_override("QMM_GEMM_TILE_M", 32)
     pl = qmm.qmm_get_plan(1, 100, 512, 1024, 4, 64, cu_count=256)
     assert pl["tile_m"] == 32 and pl["block"] == 256
+
+
+def test_unknown_override_is_rejected(lib):
+    with pytest.raises(qmm.QmmError) as e:
+        qmm.qmm_set_override("QMM_NO_SUCH_KNOB", 1)
+    assert e.value.status == qmm.QMM_ERR_INVALID_ARGUMENT
+
+
+def _plans():
+    return [qmm.qmm_get_plan(1, 100, 512, 1024, 4, 64, cu_count=256),
+            qmm.qmm_get_plan(0, 1, 3072, 1024, 4, 64, cu_count=256),
+            qmm.qmm_get_plan(2, 16, 768, 2048, 4, 64, cu_count=256),
+            qmm.qmm_get_plan(3, 1, 200000, 3072, 4, 64, cu_count=256)]
+
+
+def test_environment_after_load_changes_no_plan(lib, monkeypatch):
+    # The library reads its overrides once, at load: setting them in the
+    # environment afterwards changes nothing.
+    before = _plans()
+    for name, value in (("QMM_GEMM_TILE_M", "32"), ("QMM_GEMM_SPLIT", "3"), ("QMM_GEMV_LPR", "16"),
+                        ("QMM_GEMV_XC", "1"), ("QMM_GEMV_U", "2"), ("QMM_ROWS_MR", "1"),
+                        ("QMM_UNIT", "32"), ("QMM_BATCH_U", "2"), ("QMM_GEMV_WAVES_PER_CU", "4")):
+        monkeypatch.setenv(name, value)
+    assert _plans() == before
+
+
+def test_environment_at_load_is_read(lib):
+    # A fresh process with the override in its environment at load time.
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import gemm_qmm_gemv_amd as q; q.load(); "
+            "print(q.qmm_get_plan(1, 100, 512, 1024, 4, 64, cu_count=256)['tile_m'])" % ROOT)
+    env = dict(os.environ, QMM_GEMM_TILE_M="32")
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True)
+    assert out.stdout.strip().splitlines()[-1] == "32"
 
 
 def test_small_m_routes(lib):

@@ -22,11 +22,11 @@ def _matrix(w_f16):
             "n": n, "k": k, "bits": 16, "group": 64}
 
 
-def _run(q, x, m=None, tile=None, monkeypatch=None):
+def _run(q, x, m=None, tile=None, qmm_override=None):
     import torch
     from gemm_qmm_gemv_amd import tensors
     if tile is not None:
-        monkeypatch.setenv("QMM_GEMM_TILE_M", str(tile))
+        qmm_override("QMM_GEMM_TILE_M", tile)
     dq = tensors.upload_matrix(q)
     xd = tensors.device_tensor(x)
     y = tensors.gemv(dq, xd) if m is None else tensors.gemm(dq, xd)
@@ -35,7 +35,7 @@ def _run(q, x, m=None, tile=None, monkeypatch=None):
 
 
 @pytest.mark.parametrize("m", (None, 2, 5, 100, 300))
-def test_fp16_exact_integer(m, monkeypatch):
+def test_fp16_exact_integer(m, qmm_override):
     # Integer weights in [-8, 8] and activations in [-2, 2]: every partial
     # sum is an integer below 2^24, so GEMV and GEMM are exact.
     n, k = 333, 2048
@@ -63,13 +63,13 @@ def test_fp16_gemv_one_hot():
 
 
 @pytest.mark.parametrize("tile", (32, 64, 128))
-def test_fp16_gemm_identity_rows(tile, monkeypatch):
+def test_fp16_gemm_identity_rows(tile, qmm_override):
     # X = the first rows of I_K: row i of Y is column i of W, exactly.
     n, k, m = 200, 256, 70
     q = inputs.quantized_matrix(n, k, 16, 64, key=(92,))
     x = np.eye(m, k, dtype=np.float16)
     announce("fp16-identity", tile)
-    y = _run(q, x, m, tile, monkeypatch)
+    y = _run(q, x, m, tile, qmm_override)
     y_ref, _ = oracle.qmm(q["w"], None, None, x, n, k, 16, 64)
     assert np.array_equal(y.astype(np.float64), y_ref)
 

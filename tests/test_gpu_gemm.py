@@ -42,9 +42,9 @@ def test_gemm_parity(bits, m, n, k, group):
 @pytest.mark.parametrize("bits", PARITY_BITS)
 @pytest.mark.parametrize("tile", (32, 64, 128))
 @pytest.mark.parametrize("m,n,k", [(100, 300, 1024), (130, 257, 320), (257, 384, 2048)])
-def test_gemm_parity_every_tile(monkeypatch, bits, tile, m, n, k):
+def test_gemm_parity_every_tile(qmm_override, bits, tile, m, n, k):
     # Each tile height on shapes the planner would give another one.
-    monkeypatch.setenv("QMM_GEMM_TILE_M", str(tile))
+    qmm_override("QMM_GEMM_TILE_M", tile)
     q = inputs.quantized_matrix(n, k, bits, 64, key=(62, m, n, k, bits))
     x = inputs.activation_rows(m, k, key=(62, m, n, k, bits))
     announce("gemm-tile", tile, bits, m, n, k)
@@ -189,8 +189,8 @@ def _run_gemm_f16(q, x, workspace="auto"):
 @pytest.mark.parametrize("tile", (32, 64, 128))
 @pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (2, 129, 512), (100, 300, 1024), (257, 384, 2048),
                                    (130, 640, 4096)])
-def test_gemm_f16out_parity(monkeypatch, bits, tile, m, n, k):
-    monkeypatch.setenv("QMM_GEMM_TILE_M", str(tile))
+def test_gemm_f16out_parity(qmm_override, bits, tile, m, n, k):
+    qmm_override("QMM_GEMM_TILE_M", tile)
     q = inputs.quantized_matrix(n, k, bits, 64, key=(63, m, n, k, bits))
     x = inputs.activation_rows(m, k, key=(63, m, n, k, bits))
     announce("gemm-f16out", tile, bits, m, n, k)
@@ -203,10 +203,10 @@ def test_gemm_f16out_parity(monkeypatch, bits, tile, m, n, k):
 
 @pytest.mark.parametrize("bits", (4, 16))
 @pytest.mark.parametrize("split", (1, 3))
-def test_gemm_f16out_is_the_rounded_fp32_result(monkeypatch, bits, split):
+def test_gemm_f16out_is_the_rounded_fp32_result(qmm_override, bits, split):
     # Same plan, same sums: the fp16 output is the fp32 output rounded to
     # nearest even, bit for bit (with and without a K split).
-    monkeypatch.setenv("QMM_GEMM_SPLIT", str(split))
+    qmm_override("QMM_GEMM_SPLIT", split)
     m, n, k = 200, 520, 3072
     q = inputs.quantized_matrix(n, k, bits, 64, key=(64, bits))
     x = inputs.activation_rows(m, k, key=(64, bits))
@@ -241,11 +241,11 @@ def test_gemm_long_prefill_sampled(proj, out_fp16):
 @pytest.mark.parametrize("bits", (2, 4, 5, 8, 16))
 @pytest.mark.parametrize("tile", (64, 128))
 @pytest.mark.parametrize("m,n,k", [(100, 300, 1024), (257, 600, 2048), (130, 520, 3072)])
-def test_gemm_parity_wide_tile(monkeypatch, bits, tile, m, n, k):
+def test_gemm_parity_wide_tile(qmm_override, bits, tile, m, n, k):
     # 256-column tiles (eight waves along N taking whole steps), with and
     # without the wide scale loads (K a multiple of 512 or not).
-    monkeypatch.setenv("QMM_GEMM_TILE_M", str(tile))
-    monkeypatch.setenv("QMM_GEMM_TILE_N", "256")
+    qmm_override("QMM_GEMM_TILE_M", tile)
+    qmm_override("QMM_GEMM_TILE_N", 256)
     q = inputs.quantized_matrix(n, k, bits, 64, key=(65, m, n, k, bits))
     x = inputs.activation_rows(m, k, key=(65, m, n, k, bits))
     announce("gemm-wide-tile", tile, bits, m, n, k)

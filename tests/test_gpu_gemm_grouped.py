@@ -53,12 +53,12 @@ def test_grouped_parity(bits, m, ns, k):
 @pytest.mark.parametrize("force_one_launch", [False, True])
 @pytest.mark.parametrize("m", tuple(configs.PREFILL_M) + (2048,))
 @pytest.mark.parametrize("group", ["qkv", "gate_up"])
-def test_grouped_prefill_layer_sampled(monkeypatch, m, group, force_one_launch):
+def test_grouped_prefill_layer_sampled(qmm_override, m, group, force_one_launch):
     """The Llama-3.2-1B layer's q|k|v and gate|up groups at full size, as the
     benchmark launches them (and forced into one launch where the library
     would launch the members separately); sampled outputs of every member."""
     if force_one_launch:
-        monkeypatch.setenv("QMM_GEMM_GROUPED", "1")
+        qmm_override("QMM_GEMM_GROUPED", 1)
     names = ["q_proj", "k_proj", "v_proj"] if group == "qkv" else ["gate_proj", "up_proj"]
     projs = {p[0]: (j, p) for j, p in enumerate(configs.LLAMA32_1B_PROJ)}
     qs = []
