@@ -21,7 +21,8 @@ __all__ = [
     "qmm_gemv_batch_prepare", "qmm_gemv_batched", "GemvDesc", "GemmMember", "qmm_gemv_swiglu",
     "qmm_gemm_f16out",
     "qmm_moe_swiglu", "qmm_gemv_residual", "qmm_moe_combine", "qmm_gemm_grouped",
-    "qmm_gemm_grouped_workspace_bytes", "qmm_set_override", "overrides",
+    "qmm_gemm_grouped_workspace_bytes", "qmm_gemm_noalloc", "qmm_set_override", "overrides",
+    "QMM_NOALLOC_SCRATCH_BYTES",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
     "QMM_OK", "QMM_ERR_INVALID_ARGUMENT", "QMM_ERR_UNSUPPORTED", "QMM_ERR_MISALIGNED",
     "QMM_ERR_DEVICE", "EXPORTED_SYMBOLS",
@@ -32,12 +33,13 @@ QMM_ERR_INVALID_ARGUMENT = 1
 QMM_ERR_UNSUPPORTED = 2
 QMM_ERR_MISALIGNED = 3
 QMM_ERR_DEVICE = 4
+QMM_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # include/qmm.h
 
 EXPORTED_SYMBOLS = (
     "qmm_gemv", "qmm_gemm", "qmm_gemm_workspace_bytes", "qmm_moe_gemm", "qmm_unpack",
     "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out",
     "qmm_moe_swiglu", "qmm_gemv_residual", "qmm_moe_combine", "qmm_gemm_grouped",
-    "qmm_gemm_grouped_workspace_bytes", "qmm_set_override",
+    "qmm_gemm_grouped_workspace_bytes", "qmm_gemm_noalloc", "qmm_set_override",
     "qmm_get_plan", "qmm_status_string", "qmm_last_error", "qmm_abi_version",
 )
 
@@ -125,6 +127,7 @@ def load():
     lib.qmm_gemv_swiglu.argtypes = [p, p, p, p, p, p, p, p, i64, i64, ci, ci, p]
     lib.qmm_gemv_residual.argtypes = [p, p, p, p, p, p, i64, i64, ci, ci, p]
     lib.qmm_gemm_f16out.argtypes = [p, p, p, p, p, i64, i64, i64, ci, ci, p, sz, p]
+    lib.qmm_gemm_noalloc.argtypes = [p, p, p, p, p, i64, i64, i64, ci, ci, p]
     lib.qmm_set_override.argtypes = [ctypes.c_char_p, ci]
     lib.qmm_gemm_workspace_bytes.argtypes = [i64, i64, i64, ci, ci]
     lib.qmm_gemm_workspace_bytes.restype = sz
@@ -140,7 +143,7 @@ def load():
     lib.qmm_get_plan.argtypes = [ci, i64, i64, i64, ci, ci, ci, sz, ctypes.POINTER(_Plan)]
     for f in ("qmm_gemv", "qmm_gemm", "qmm_moe_gemm", "qmm_unpack", "qmm_get_plan",
               "qmm_gemv_batch_prepare", "qmm_gemv_batched", "qmm_gemv_swiglu", "qmm_gemm_f16out", "qmm_moe_swiglu",
-              "qmm_gemv_residual", "qmm_moe_combine", "qmm_gemm_grouped",
+              "qmm_gemv_residual", "qmm_moe_combine", "qmm_gemm_grouped", "qmm_gemm_noalloc",
               "qmm_set_override"):
         getattr(lib, f).restype = ci
     lib.qmm_status_string.argtypes = [ci]
@@ -227,6 +230,14 @@ def qmm_gemm(w_packed, scales, mins, x, y, m, n, k, bits, group_size, workspace=
                            int(m), int(n), int(k), int(bits), int(group_size), _addr(workspace),
                            int(workspace_bytes), _stream(stream)),
            "qmm_gemm")
+
+
+def qmm_gemm_noalloc(w_packed, scales, mins, x, y, m, n, k, bits, group_size, stream=None) -> None:
+    """As qmm_gemm with no workspace: the library's own fixed scratch array
+    holds any K-split partial sums; asynchronous."""
+    _check(load().qmm_gemm_noalloc(_addr(w_packed), _addr(scales), _addr(mins), _addr(x), _addr(y),
+                                   int(m), int(n), int(k), int(bits), int(group_size), _stream(stream)),
+           "qmm_gemm_noalloc")
 
 
 def qmm_set_override(name: str, value: int) -> None:

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/qmm.h"
 #include "qmm_kernels.h"
@@ -500,12 +501,56 @@ size_t qmm_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits, int g
 
 namespace {
 
+// ---- scratch of qmm_gemm_noalloc ---------------------------------------------
+// K-split partial sums and arrival counters of the allocation-free GEMM: one
+// array per GPU, part of the library's code object, held until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: each device's own copy is found once with hipGetSymbolAddress
+// (with that device current) and only that address is passed on.
+static __device__ __align__(256) unsigned char scratch[QMM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> g_scratch_addr[MAX_DEVICES];
+std::mutex g_scratch_mutex;
+
+qmm_status device_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(QMM_ERR_DEVICE, "no HIP device available");
+    }
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(QMM_ERR_UNSUPPORTED, "device %d beyond %d", dev, MAX_DEVICES);
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return fail(QMM_ERR_DEVICE, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+            }
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return QMM_OK;
+}
+
+// Zero `count` ints (a kernel rather than a memset node, so the call stays
+// safe to capture into a graph).
+__global__ void clear_ints_kernel(int* __restrict__ p, int count) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = 0;
+}
+
 // qmm_gemm and qmm_gemm_f16out.  fp16 output always takes the MFMA kernel
 // (its epilogue does the rounding); fp32 output routes m <= 2 to the GEMV
 // kernels.
 qmm_status gemm_common(const void* w_packed, const void* scales, const void* mins, const void* x,
                        void* y, int64_t m, int64_t n, int64_t k, int bits, int group_size,
-                       void* workspace, size_t workspace_bytes, void* stream, bool out16) {
+                       void* workspace, size_t workspace_bytes, void* stream, bool out16,
+                       bool noalloc = false) {
     qmm_status st = check_format(n, k, bits, group_size);
     if (st != QMM_OK) return st;
     if (m < 0) return fail(QMM_ERR_INVALID_ARGUMENT, "m=%lld is negative", (long long)m);
@@ -537,6 +582,18 @@ qmm_status gemm_common(const void* w_packed, const void* scales, const void* min
         RowsArgs a{w, s, mn, xx, nullptr, (int)m, nullptr, 1, (int)m, yf, (int)n, (int)k, group_size, bits};
         return launched(launch_rows(a, sh, as_stream(stream)), "qmm_gemm (rows)");
     }
+    if (noalloc) {
+        // The plan qmm_gemm takes with its preferred workspace, on the
+        // library's own scratch array.
+        size_t need = 0;
+        (void)plan_gemm(m, n, k, group_size, cus, (size_t)-1, &need);
+        if (need > (size_t)QMM_NOALLOC_SCRATCH_BYTES)
+            return fail(QMM_ERR_UNSUPPORTED,
+                        "m=%lld n=%lld k=%lld needs %zu bytes of scratch, more than the %zu this entry point holds",
+                        (long long)m, (long long)n, (long long)k, need, (size_t)QMM_NOALLOC_SCRATCH_BYTES);
+        if ((st = device_scratch(&workspace)) != QMM_OK) return st;
+        workspace_bytes = need;
+    }
     const GemmShape sh = plan_gemm(m, n, k, group_size, cus, workspace ? workspace_bytes : 0, nullptr);
     float* partial = nullptr;
     int* counters = nullptr;
@@ -546,8 +603,18 @@ qmm_status gemm_common(const void* w_packed, const void* scales, const void* min
             (int64_t)sh.grid_m * sh.grid_n <= GEMM_COUNTER_TILES)
             counters = static_cast<int*>(workspace);
     }
+    if (noalloc && counters) {
+        // The shared array keeps whatever the last call left: the arrival
+        // counters this launch uses start from zero.
+        const int used = sh.grid_m * sh.grid_n;
+        hipLaunchKernelGGL(clear_ints_kernel, dim3((used + 255) / 256), dim3(256), 0, as_stream(stream), counters,
+                           used);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess)
+            return fail(QMM_ERR_DEVICE, "qmm_gemm_noalloc: counter reset failed: %s", hipGetErrorString(e));
+    }
     GemmArgs a{w, s, mn, xx, yf, partial, counters, (int)m, (int)n, (int)k, group_size, bits, out16 ? 1 : 0};
-    return launched(launch_gemm(a, sh, as_stream(stream)), out16 ? "qmm_gemm_f16out" : "qmm_gemm");
+    return launched(launch_gemm(a, sh, as_stream(stream)),
+                    noalloc ? "qmm_gemm_noalloc" : out16 ? "qmm_gemm_f16out" : "qmm_gemm");
 }
 
 }  // namespace
@@ -695,6 +762,13 @@ qmm_status qmm_gemm_f16out(const void* w_packed, const void* scales, const void*
                            void* workspace, size_t workspace_bytes, void* stream) {
     return gemm_common(w_packed, scales, mins, x, y, m, n, k, bits, group_size, workspace,
                        workspace_bytes, stream, true);
+}
+
+qmm_status qmm_gemm_noalloc(const void* w_packed, const void* scales, const void* mins, const void* x,
+                            float* y, int64_t m, int64_t n, int64_t k, int bits, int group_size,
+                            void* stream) {
+    return gemm_common(w_packed, scales, mins, x, y, m, n, k, bits, group_size, nullptr, 0, stream, false,
+                       true);
 }
 
 qmm_status qmm_set_override(const char* name, int value) {

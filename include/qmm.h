@@ -54,7 +54,8 @@
  *   deterministic -- every output element is summed in a fixed order that
  *   depends only on the shape and the launch plan -- except for
  *   qmm_moe_combine, whose float atomic adds into a token's row happen in
- *   no fixed order.
+ *   no fixed order.  The one exception to "allocates nothing" is
+ *   qmm_gemm_noalloc's fixed scratch array (see there).
  *   The launch plan (kernel variant, tiles, splits, grids) depends on the
  *   shape, the bit width and the device's compute-unit count, and on the
  *   overrides of qmm_set_override, which the library reads from the
@@ -175,6 +176,26 @@ QMM_API qmm_status qmm_gemm_f16out(const void *w_packed, const void *scales,
                                    const void *mins, const void *x, void *y, int64_t m,
                                    int64_t n, int64_t k, int bits, int group_size,
                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Prefill GEMM that allocates nothing, for callers that cannot call
+ * hipMalloc or take a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.
+ * Same arguments and result as qmm_gemm without the workspace: it runs the
+ * plan qmm_gemm takes with its preferred workspace (qmm_gemm_workspace_bytes),
+ * so y is bit-identical to that call's.  The K-split partial sums and
+ * arrival counters live in a static device array of
+ * QMM_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; a shape that would need more (qmm_gemm_workspace_bytes
+ * above that) returns QMM_ERR_UNSUPPORTED and launches nothing.  Each call
+ * resets the counters it uses with a small kernel before the GEMM (no
+ * memset, no allocation).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other host threads) race
+ * and give wrong results; calls ordered on one stream are safe.           */
+#define QMM_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+
+QMM_API qmm_status qmm_gemm_noalloc(const void *w_packed, const void *scales, const void *mins,
+                                    const void *x, float *y, int64_t m, int64_t n, int64_t k,
+                                    int bits, int group_size, void *stream);
 
 /* Grouped prefill GEMM: up to 4 weight matrices that share the activations
  * x [m][k] (the q, k and v projections of a layer, or gate and up), one

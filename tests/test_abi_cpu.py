@@ -103,6 +103,12 @@ def test_gemm_and_moe_argument_checks(lib):
         qmm.QMM_ERR_INVALID_ARGUMENT  # bytes without a buffer
     assert g(p(A16), p(A16), p(A16), p(A16), p(A16), 8, 64, 128, 4, 64, p(A16 + 4), 64, None) == \
         qmm.QMM_ERR_MISALIGNED
+    na = lib.qmm_gemm_noalloc
+    assert na(p(A16), p(A16), p(A16), p(A16), p(A16), -1, 64, 128, 4, 64, None) == qmm.QMM_ERR_INVALID_ARGUMENT
+    assert na(p(A16), p(A16), p(A16), p(A16), p(A16), 0, 64, 128, 4, 64, None) == qmm.QMM_OK
+    assert na(p(A16), p(A16), p(A16), p(A16), p(A16 + 4), 8, 64, 128, 4, 64, None) == qmm.QMM_ERR_MISALIGNED
+    assert na(p(A16), p(A16), p(A16), None, p(A16), 8, 64, 128, 4, 64, None) == qmm.QMM_ERR_INVALID_ARGUMENT
+    assert na(p(A16), p(A16), p(A16), p(A16), p(A16), 8, 64, 128, 7, 64, None) == qmm.QMM_ERR_UNSUPPORTED
     mo = lib.qmm_moe_gemm
     assert mo(p(A16), p(A16), p(A16), p(A16), None, 4, p(A16), p(A16), 8, 2, 64, 128, 4, 64, None) == \
         qmm.QMM_ERR_INVALID_ARGUMENT  # no index and too few x rows
