@@ -40,8 +40,7 @@
 // tile inside this kernel, more by a second kernel.  Work-group ids are
 // remapped so that each XCD (and its L2) takes a contiguous range of tiles.
 // A grouped launch runs several weight matrices that share X as one grid.
-#include "qmm_device.h"
-#include "qmm_kernels.h"
+#include "gemm_common.h"
 
 #include <type_traits>
 
@@ -52,14 +51,6 @@ static_assert(BK % 128 == 0, "each of two waves along K takes whole 64-code chun
 constexpr int BN = 128;         // columns per work-group (default tile width)
 constexpr int XPAD = 8;         // halves of padding per LDS row (conflict-free 16-byte reads)
 constexpr int XROW = BK + XPAD; // halves per LDS row
-
-// Slot order of a 32-code chunk: slot 2i holds code ka(i) and slot 2i+1 code
-// kb(i) of the pair format, i.e. exactly the order in which the dequantized
-// pairs sit in registers.
-template <int B>
-constexpr int slot_k(int p) {
-    return (p & 1) ? PairFmt<B>::kb(p >> 1) : PairFmt<B>::ka(p >> 1);
-}
 
 // Halves of X reordered as one unit: every format keeps each aligned block
 // of XH slots inside the same XH codes, with the same pattern in every block
@@ -94,53 +85,6 @@ __device__ __forceinline__ void to_slot_order(const u32 (&in)[x_unit_halves<B>()
     }
 }
 
-// One 32-code chunk (b words) -> 16 fp16 pairs s*q + m in slot order.
-template <int B>
-__device__ __forceinline__ void dequant_pairs(const u32 (&w)[B], u32 s_bits, u32 m_bits,
-                                              f16x2 (&out)[16]) {
-    using F = PairFmt<B>;
-    if constexpr (!has_affine<B>()) {
-        // fp16 weights: the words are the operand pairs already.
-#pragma unroll
-        for (int i = 0; i < 16; ++i) out[i] = as_h2(w[i]);
-        return;
-    }
-    u32 p[16];
-    F::extract(w, p);
-    const f16 s = __builtin_bit_cast(f16, (uint16_t)s_bits);
-    const f16 m = __builtin_bit_cast(f16, (uint16_t)m_bits);
-    const f16x2 s2 = {s, s}, m2 = {m, m};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const f16 inv = (f16)F::inv_factor(F::acc(i));
-        const f16 off = (f16)(-1024.0f * F::inv_factor(F::acc(i)));
-        const f16x2 inv2 = {inv, inv}, off2 = {off, off};
-        // (1024 + f q) * (1/f) - 1024/f is exactly q (f a power of two).
-        const f16x2 q2 = __builtin_elementwise_fma(as_h2(p[i]), inv2, off2);
-        // s*q + m, fused: one rounding of the exact value to fp16.
-        out[i] = __builtin_elementwise_fma(q2, s2, m2);
-    }
-}
-
-// Steps U..N-1 of one pass of the unrolled main loop: all of them, or (for
-// the remainder after the loop) only those before st1.
-template <int U, int N, class F>
-__device__ __forceinline__ void all_steps(F& f, int st) {
-    if constexpr (U < N) {
-        f(std::integral_constant<int, U>{}, st + U);
-        all_steps<U + 1, N>(f, st);
-    }
-}
-template <int U, int N, class F>
-__device__ __forceinline__ void unrolled_steps(F& f, int st, int st1) {
-    if constexpr (U < N) {
-        if (st + U < st1) {
-            f(std::integral_constant<int, U>{}, st + U);
-            unrolled_steps<U + 1, N>(f, st, st1);
-        }
-    }
-}
-
 // Prefetch distance (steps between a step's loads and its matrix work) and
 // the occupancy target (work-groups per CU the register allocation must
 // allow).
@@ -149,6 +93,12 @@ __device__ __forceinline__ void unrolled_steps(F& f, int st, int st1) {
 #endif
 #ifndef GEMM_MINB
 #define GEMM_MINB 2
+#endif
+#ifndef GEMM_SCHED
+#define GEMM_SCHED 0
+#endif
+#ifndef GEMM_SCHED_V
+#define GEMM_SCHED_V 4
 #endif
 constexpr int PD = GEMM_PD;
 static_assert(PD >= 2 && PD <= 4, "prefetch distance");
@@ -181,87 +131,6 @@ static_assert(UNROLL_SW % SW_STEPS == 0 && UNROLL_SW % UNROLL == 0, "wide-scale 
 // splits for all of them before adding, so the latencies overlap; loads past
 // the last split or outside the matrix read zeros, and stores outside it are
 // dropped (buffer range checks).  N % 4 != 0 takes single columns.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-// Cache policy of the split-K partial sums: sc0 | sc1 (system coherence), so
-// stores write through to memory and loads fetch from it, past every cache.
-constexpr int CPOL_COHERENT = 1 | 16;
-// s_waitcnt with vmcnt = 0 (expcnt and lgkmcnt at their maxima, not waited on).
-constexpr int WAITCNT_VM0 = 0x0F70;
-template <int TILE_M, int TN, int THREADS>
-__device__ __forceinline__ void reduce_tile(const float* P, float* Y, int M, int N, int split, int m0, int n0,
-                                            int tid, int out16) {
-    const uint32_t mn = (uint32_t)M * (uint32_t)N;  // floats per split
-    const uint32_t p_bytes = mn * 4u * (uint32_t)split;  // < 2^32: checked on the host
-    const uint32_t y_bytes = mn * (out16 ? 2u : 4u);
-    const rsrc_t pr = make_rsrc(P, p_bytes);
-    const rsrc_t yr = make_rsrc(Y, y_bytes);
-    auto sum_groups = [&](auto vec_c) {
-        constexpr int V = decltype(vec_c)::value;      // columns per group: 4 or 1
-        constexpr int GROUPS = TILE_M * TN / V;          // groups in the tile
-        static_assert(GROUPS % THREADS == 0, "tile reduction layout");
-        constexpr int PER = GROUPS / THREADS;
-        constexpr int E = PER < 4 ? PER : 4;
-        using vec = std::conditional_t<V == 4, f32x4, float>;
-#pragma unroll 1
-        for (int e0 = 0; e0 < PER; e0 += E) {
-            uint32_t off[E];
-            bool ok[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int q = (e0 + e) * THREADS + tid;
-                const int r = m0 + q / (TN / V), c = n0 + V * (q % (TN / V));
-                ok[e] = r < M && c < N;
-                off[e] = (uint32_t)r * (uint32_t)N + (uint32_t)c;  // element index
-            }
-            vec acc[E];
-#pragma unroll 1
-            for (int s0 = 0; s0 < split; s0 += 4) {
-                vec v[4][E];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const uint32_t o = (ok[e] && s0 + j < split) ? ((uint32_t)(s0 + j) * mn + off[e]) * 4u : p_bytes;
-                        if constexpr (V == 4)
-                            v[j][e] = __builtin_bit_cast(
-                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, o, 0, CPOL_COHERENT));
-                        else
-                            v[j][e] = __builtin_bit_cast(
-                                float, __builtin_amdgcn_raw_buffer_load_b32(pr, o, 0, CPOL_COHERENT));
-                    }
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int e = 0; e < E; ++e) acc[e] = (s0 == 0 && j == 0) ? v[j][e] : acc[e] + v[j][e];
-            }
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                if (out16) {
-                    const uint32_t o = ok[e] ? off[e] * 2u : y_bytes;
-                    if constexpr (V == 4) {
-                        const f16 h[4] = {(f16)acc[e][0], (f16)acc[e][1], (f16)acc[e][2], (f16)acc[e][3]};
-                        u32x2 w;
-                        __builtin_memcpy(&w, h, 8);
-                        __builtin_amdgcn_raw_buffer_store_b64(w, yr, o, 0, 0);
-                    } else {
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (f16)acc[e]), yr, o, 0, 0);
-                    }
-                } else {
-                    const uint32_t o = ok[e] ? off[e] * 4u : y_bytes;
-                    if constexpr (V == 4)
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[e]), yr, o, 0, 0);
-                    else
-                        buffer_store_f32(acc[e], yr, o);
-                }
-            }
-        }
-    };
-    if (N % 4 == 0)
-        sum_groups(std::integral_constant<int, 4>{});
-    else
-        sum_groups(std::integral_constant<int, 1>{});
-}
-
 constexpr int gemm_min_blocks(int wn) { return GEMM_MINB * 2 / wn > 0 ? GEMM_MINB * 2 / wn : 1; }
 
 //
@@ -561,6 +430,24 @@ __global__ __launch_bounds__(64 * WN * KW, gemm_min_blocks(WN)) void gemm_kernel
             sm_of_block(std::integral_constant<int, (U + 1) % SW_STEPS>{}, sq[NEXT], mq[NEXT]);
         }
         dequant(wq[NEXT], sq[NEXT], mq[NEXT], wv[BUF ^ 1]);
+#if GEMM_SCHED
+        // Interleave: the X staging writes first, then per matrix
+        // instruction one A-fragment read (the reads run one substep ahead
+        // of their use) and a share of the dequantization.
+        {
+            constexpr int NM = MS * NS * CH * 4;   // matrix instructions per step
+            constexpr int NR = MS * CH * 4;        // A-fragment reads per step
+            constexpr int XWR = XU * XW / 4;       // X staging writes
+            __builtin_amdgcn_sched_group_barrier(0x200, XWR, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i * NR / NM + MS < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, GEMM_SCHED_V, 0);
+            }
+        }
+#endif
         __syncthreads();
     };
     // Whole passes in the loop, the remainder after it: an exit from the
@@ -678,18 +565,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         Y[i] = v;
 }
 
-// floor(n / d) = (n * mul) >> shift for every n < 2^31: shift = 31 + ceil(log2 d),
-// mul = ceil(2^shift / d) (Granlund and Montgomery, "Division by invariant
-// integers using multiplication", 1994, the N+1-bit multiplier case).
-struct DivMagic {
-    uint64_t mul;
-    int shift;
-};
-static DivMagic div_magic(int d) {
-    int l = 0;
-    while ((1LL << l) < d) ++l;
-    const int shift = 31 + l;
-    return {((1ULL << shift) + (uint64_t)d - 1) / (uint64_t)d, shift};
+hipError_t launch_splitk_reduce(const float* partial, void* y, int64_t count, int split, int out16,
+                                hipStream_t st) {
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, partial,
+                       static_cast<float*>(y), count, split, out16);
+    return hipGetLastError();
 }
 
 template <int B, int MS, int WN, int KW = 2, int TN = BN>
@@ -743,10 +623,7 @@ static hipError_t launch_gemm_t(const GemmArgs& a, const GemmShape& sh, hipStrea
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || sh.split == 1 || red) return err;
-    const int64_t count = (int64_t)a.m_rows * a.n;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st,
-                       a.partial, a.y, count, sh.split, a.out16);
-    return hipGetLastError();
+    return launch_splitk_reduce(a.partial, a.y, (int64_t)a.m_rows * a.n, sh.split, a.out16, st);
 }
 
 template <int B>
@@ -768,6 +645,7 @@ static hipError_t launch_gemm_b(const GemmArgs& a, const GemmShape& sh, hipStrea
 }
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmShape& sh, hipStream_t st) {
+    if (sh.kernel == 1) return launch_gemm_wl(a, sh, st);
     switch (a.bits) {
         case 2: return launch_gemm_b<2>(a, sh, st);
         case 3: return launch_gemm_b<3>(a, sh, st);

@@ -152,12 +152,12 @@ qmm_status device_cus(int* cus) {
 enum OverrideId {
     OV_UNIT, OV_GEMV_LPR, OV_GEMV_XC, OV_GEMV_U, OV_GEMV_WAVES_PER_CU, OV_BATCH_U, OV_ROWS_MR,
     OV_ROWS_WAVES_PER_CU, OV_GEMM_TILE_M, OV_GEMM_TILE_N, OV_GEMM_SPLIT, OV_GEMM_WIDE_SCALES,
-    OV_GEMM_ORDER, OV_GEMM_GROUPED, OV_COUNT
+    OV_GEMM_ORDER, OV_GEMM_GROUPED, OV_GEMM_KERNEL, OV_COUNT
 };
 const char* const OVERRIDE_NAMES[OV_COUNT] = {
     "QMM_UNIT", "QMM_GEMV_LPR", "QMM_GEMV_XC", "QMM_GEMV_U", "QMM_GEMV_WAVES_PER_CU", "QMM_BATCH_U",
     "QMM_ROWS_MR", "QMM_ROWS_WAVES_PER_CU", "QMM_GEMM_TILE_M", "QMM_GEMM_TILE_N", "QMM_GEMM_SPLIT",
-    "QMM_GEMM_WIDE_SCALES", "QMM_GEMM_ORDER", "QMM_GEMM_GROUPED"};
+    "QMM_GEMM_WIDE_SCALES", "QMM_GEMM_ORDER", "QMM_GEMM_GROUPED", "QMM_GEMM_KERNEL"};
 std::atomic<int> g_override[OV_COUNT];
 
 struct OverridesFromEnvironment {
@@ -336,8 +336,73 @@ constexpr int64_t GEMM_COUNTER_TILES = GEMM_COUNTER_BYTES / sizeof(int);
 // tiles128: 128-column tiles (per member, summed); grouped launches keep
 // 128-column tiles and split K only where the kernel reduces the split
 // itself (32/64-row tiles, counters for every tile).
+// Workspace for a split plan: the arrival counters, then the partial sums
+// (their byte offsets must stay below 2^32).  Shrinks the split to what the
+// caller's workspace holds.
+int fit_split(int split, int64_t m, int64_t n, size_t ws_bytes, size_t* ws_need) {
+    const size_t per_split = (size_t)m * n * sizeof(float);
+    const size_t cnt_bytes = GEMM_COUNTER_BYTES;
+    if (per_split && split > 1 && per_split * split > 0xFFFFFFFFull) split = (int)(0xFFFFFFFFull / per_split);
+    if (ws_need) *ws_need = split > 1 ? cnt_bytes + per_split * split : 0;
+    if (split > 1 && ws_bytes < cnt_bytes + per_split * split) {
+        split = (per_split && ws_bytes > cnt_bytes) ? (int)((ws_bytes - cnt_bytes) / per_split) : 1;
+        if (split < 2) split = 1;
+    }
+    return split;
+}
+
+// The LDS-dequantizing kernel (gemm_wl.hip).  Its 256 x 256 tiles read the
+// fewest LDS bytes per matrix instruction (the limit of both kernels once
+// the dequantization is off the matrix waves): measured 76.3 vs 82.8 us on
+// the 8192 x 2048 projections at 2048 tokens.  It takes the shapes whose
+// 256 x 256 grid alone fills the CUs; the override QMM_GEMM_KERNEL = 1
+// forces it elsewhere (tiles 256 x 128 above 128 rows, else 128 x 128,
+// unless QMM_GEMM_TILE_M / _N say otherwise).
+bool wl_fills(int64_t m, int64_t n, int cus) { return (m + 255) / 256 * ((n + 255) / 256) >= cus; }
+
+GemmShape plan_gemm_wl(int64_t m, int64_t n, int64_t k, int cus, size_t ws_bytes, size_t* ws_need) {
+    GemmShape sh{};
+    sh.kernel = 1;
+    const bool forced = override_or(OV_GEMM_KERNEL, 0) == 1;
+    sh.tile_m = forced ? (m > 128 ? 256 : 128) : 256;
+    sh.tile_n = forced ? 128 : 256;
+    const int etm = override_or(OV_GEMM_TILE_M, 0);
+    if (etm == 128 || etm == 256) sh.tile_m = etm;
+    const int etn = override_or(OV_GEMM_TILE_N, 0);
+    if (etn == 128 || etn == 256) sh.tile_n = etn;
+    sh.grid_m = (int)((m + sh.tile_m - 1) / sh.tile_m);
+    sh.grid_n = (int)((n + sh.tile_n - 1) / sh.tile_n);
+    const int k_tiles = (int)((k + gemm_wl_step_codes(sh.tile_n) - 1) / gemm_wl_step_codes(sh.tile_n));
+    const int64_t tiles = (int64_t)sh.grid_m * sh.grid_n;
+    int split = 1;
+    if (tiles < cus) {
+        split = (int)((cus + tiles - 1) / tiles);
+        const int by_k = k_tiles / 2 > 1 ? k_tiles / 2 : 1;
+        if (split > by_k) split = by_k;
+    }
+    const int es = override_or(OV_GEMM_SPLIT, 0);
+    if (es > 0) split = es < k_tiles ? es : k_tiles;
+    if (split > 16) split = 16;
+    split = fit_split(split, m, n, ws_bytes, ws_need);
+    sh.k_tiles_per_split = (k_tiles + split - 1) / split;
+    sh.split = (k_tiles + sh.k_tiles_per_split - 1) / sh.k_tiles_per_split;
+    sh.wide_scales = false;
+    // Tile order: an XCD's consecutive tiles share X rows (column tile
+    // fastest) or W columns (row tile fastest); take the order that moves
+    // fewer bytes into the XCDs: X once plus W once per row tile, or W once
+    // plus X once per column tile.
+    const double xb = 2.0 * (double)m * (double)k, wb = 0.5 * (double)n * (double)k;
+    const bool col_fastest = xb + sh.grid_m * wb <= wb + sh.grid_n * xb;
+    const int eo = override_or(OV_GEMM_ORDER, 0);
+    sh.n_fast = eo == 1 ? true : eo == 2 ? false : col_fastest;
+    return sh;
+}
+
 GemmShape plan_gemm_impl(int64_t m, int64_t n, int64_t tiles128, bool grouped, int64_t k, int group, int cus,
                          size_t ws_bytes, size_t* ws_need) {
+    const int ek = override_or(OV_GEMM_KERNEL, 0);
+    if (!grouped && (ek == 1 || (ek != 2 && m > 128 && wl_fills(m, n, cus))))
+        return plan_gemm_wl(m, n, k, cus, ws_bytes, ws_need);
     GemmShape sh{};
     const int k_tiles = (int)((k + GEMM_BK - 1) / GEMM_BK);
     const int64_t grid_n = tiles128;
@@ -370,16 +435,7 @@ GemmShape plan_gemm_impl(int64_t m, int64_t n, int64_t tiles128, bool grouped, i
     if (es > 0) split = es < k_tiles ? es : k_tiles;
     if (split > 16) split = 16;  // the reduction handles at most 16 splits
     if (grouped && (sh.tile_m > 64 || tiles > GEMM_COUNTER_TILES)) split = 1;
-    // Workspace: the tiles' arrival counters, then the partial sums (their
-    // byte offsets must stay below 2^32).
-    const size_t per_split = (size_t)m * n * sizeof(float);
-    const size_t cnt_bytes = GEMM_COUNTER_BYTES;
-    if (per_split && split > 1 && per_split * split > 0xFFFFFFFFull) split = (int)(0xFFFFFFFFull / per_split);
-    if (ws_need) *ws_need = split > 1 ? cnt_bytes + per_split * split : 0;
-    if (split > 1 && ws_bytes < cnt_bytes + per_split * split) {
-        split = (per_split && ws_bytes > cnt_bytes) ? (int)((ws_bytes - cnt_bytes) / per_split) : 1;
-        if (split < 2) split = 1;
-    }
+    split = fit_split(split, m, n, ws_bytes, ws_need);
     sh.k_tiles_per_split = (k_tiles + split - 1) / split;
     // Wide scale loads need splits that start at multiples of four steps.
     const bool wide = group == 64 && GEMM_BK == 128 && k % 512 == 0 && override_or(OV_GEMM_WIDE_SCALES, 1) != 0;
@@ -392,6 +448,14 @@ GemmShape plan_gemm_impl(int64_t m, int64_t n, int64_t tiles128, bool grouped, i
     const int eo = override_or(OV_GEMM_ORDER, 0);
     sh.n_fast = eo == 1 ? true : eo == 2 ? false : (sh.grid_m >= 16 && sh.grid_n <= sh.grid_m);
     return sh;
+}
+
+// Splits summed inside the GEMM kernel (arrival counters in the workspace):
+// two-way splits of the tiles that have that reduction.
+bool reduces_in_kernel(const GemmShape& sh) {
+    if (sh.split < 2 || sh.split > GEMM_INKERNEL_REDUCE_MAX_SPLIT) return false;
+    if ((int64_t)sh.grid_m * sh.grid_n > GEMM_COUNTER_TILES) return false;
+    return sh.kernel == 1 || (sh.tile_m <= 64 && sh.tile_n == 128);
 }
 
 GemmShape plan_gemm(int64_t m, int64_t n, int64_t k, int group, int cus, size_t ws_bytes, size_t* ws_need) {
@@ -599,9 +663,7 @@ qmm_status gemm_common(const void* w_packed, const void* scales, const void* min
     int* counters = nullptr;
     if (sh.split > 1) {
         partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + GEMM_COUNTER_BYTES);
-        if (sh.split <= GEMM_INKERNEL_REDUCE_MAX_SPLIT && sh.tile_m <= 64 && sh.tile_n == 128 &&
-            (int64_t)sh.grid_m * sh.grid_n <= GEMM_COUNTER_TILES)
-            counters = static_cast<int*>(workspace);
+        if (reduces_in_kernel(sh)) counters = static_cast<int*>(workspace);
     }
     if (noalloc && counters) {
         // The shared array keeps whatever the last call left: the arrival
@@ -1006,8 +1068,8 @@ qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits, int g
     }
     if (op == 1) {
         const GemmShape sh = plan_gemm(m, n, k, group_size, cus, workspace_bytes, nullptr);
-        plan->variant = 2;
-        plan->block = gemm_threads(sh.tile_m);
+        plan->variant = sh.kernel == 1 ? 4 : 2;
+        plan->block = sh.kernel == 1 ? gemm_wl_threads(sh.tile_m) : gemm_threads(sh.tile_m);
         plan->split_k = sh.split;
         plan->tile_m = sh.tile_m;
         plan->tile_n = sh.tile_n;

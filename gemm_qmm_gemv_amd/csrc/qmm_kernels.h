@@ -133,6 +133,7 @@ struct GemmArgs {
 };
 
 struct GemmShape {
+    int kernel;        // 0: weights dequantized into registers (gemm.hip), 1: into LDS (gemm_wl.hip)
     int tile_m, tile_n;
     int split;        // K split
     int k_tiles_per_split;
@@ -237,6 +238,15 @@ QMM_DECLARE_BITS(16)
 #undef QMM_DECLARE_BITS
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmShape& sh, hipStream_t st);
+hipError_t launch_gemm_wl(const GemmArgs& a, const GemmShape& sh, hipStream_t st);
+// y = the sum over `split` partial-sum blocks of `count` floats each, in split
+// order (fp32, or rounded once to fp16 when out16).
+hipError_t launch_splitk_reduce(const float* partial, void* y, int64_t count, int split, int out16,
+                                hipStream_t st);
+// K per step of the LDS-dequantizing GEMM.
+constexpr int gemm_wl_step_codes(int) { return 64; }
+// Threads of its work-groups: 64 per consumer wave (4 or 8) plus 4 producer waves.
+constexpr int gemm_wl_threads(int tile_m) { return 64 * (tile_m / 64 * 2 + 4); }
 #ifndef GEMM_BK_STEP
 #define GEMM_BK_STEP 128
 #endif

@@ -359,8 +359,9 @@ QMM_API qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bit
  * is ignored).  name is one of QMM_UNIT, QMM_GEMV_LPR, QMM_GEMV_XC,
  * QMM_GEMV_U, QMM_GEMV_WAVES_PER_CU, QMM_BATCH_U, QMM_ROWS_MR,
  * QMM_ROWS_WAVES_PER_CU, QMM_GEMM_TILE_M, QMM_GEMM_TILE_N, QMM_GEMM_SPLIT,
- * QMM_GEMM_WIDE_SCALES, QMM_GEMM_ORDER, QMM_GEMM_GROUPED; value < 0 removes
- * the override.  The same names are read from the environment once, when
+ * QMM_GEMM_WIDE_SCALES, QMM_GEMM_ORDER, QMM_GEMM_GROUPED, QMM_GEMM_KERNEL
+ * (1: the prefill GEMM that dequantizes into LDS, 2: the one that
+ * dequantizes into registers); value < 0 removes the override.  The same names are read from the environment once, when
  * the library is loaded.  Unknown name: QMM_ERR_INVALID_ARGUMENT.          */
 QMM_API qmm_status qmm_set_override(const char *name, int value);
 
