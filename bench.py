@@ -153,6 +153,24 @@ class Timer:
         return a.elapsed_time(b) / replays
 
 
+# Working sets of at least this many bytes per timing loop keep every HBM
+# rate honest: twice the 256 MB last-level cache, so no replay finds its
+# weights still cached from the previous one.
+CACHE_BUST_BYTES = 540 * 2**20
+
+
+def copies_for(nbytes: int, cap: int = 4096) -> int:
+    """Device copies of an nbytes working set that together exceed CACHE_BUST_BYTES."""
+    return max(2, min(cap, -(-CACHE_BUST_BYTES // max(nbytes, 1))))
+
+
+def device_copies(dq: dict, count: int) -> list:
+    """dq plus count - 1 device-side clones of its weight, scale and min tensors."""
+    clone = lambda t: None if t is None else t.clone()
+    return [dq] + [{**dq, "w": dq["w"].clone(), "scales": clone(dq["scales"]), "mins": clone(dq["mins"])}
+                   for _ in range(count - 1)]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -394,43 +412,52 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
         "GBps": round(set_bytes / ms / 1e6, 1), "projection_tok_per_s": round(1e3 / ms, 1)}
     log("dependent-stage graph: %.1f us" % (ms * 1e3))
 
-    # LM head alone, four rotating copies (352 MB > the 256 MB last-level cache).
+    # LM head alone, rotating device copies (CACHE_BUST_BYTES in all).
     name, n, k = configs.QWEN3_06B_LM_HEAD
-    copies = [mats[-1][2]] + [tensors.upload_matrix(inputs.quantized_matrix(n, k, 4, G, key=(90, c)))
-                              for c in range(3)]
+    b = configs.gemv_bytes(n, k, 4)
+    copies = device_copies(mats[-1][2], copies_for(b))
     yl = torch.empty(n, dtype=torch.float32, device="cuda")
     idx = [0]
 
     def lm_call():
-        tensors.gemv(copies[idx[0] % 4], xs[-1], yl)
+        tensors.gemv(copies[idx[0] % len(copies)], xs[-1], yl)
         idx[0] += 1
-    ms = timer(lm_call, reps=40)
-    b = configs.gemv_bytes(n, k, 4)
+    ms = timer(lm_call, reps=len(copies) * 4)
     out["lm_head_151936x1024_q4"] = {"us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1),
-                                     "pct_peak": round(100 * b / ms / 1e6 / HBM_PEAK_GBS, 1)}
+                                     "pct_peak": round(100 * b / ms / 1e6 / HBM_PEAK_GBS, 1),
+                                     "copies": len(copies)}
     del copies
     log("lm head: %.1f us" % (ms * 1e3))
 
-    # Single 3072 x 1024 Q4 GEMV.
+    # Single 3072 x 1024 Q4 GEMV, rotating device copies.
     c = configs.SINGLE_Q4
     q = inputs.quantized_matrix(c["n"], c["k"], 4, G, key=(configs.CFG_SINGLE, 0, 0, 4))
-    dq = tensors.upload_matrix(q)
+    b = configs.gemv_bytes(c["n"], c["k"], 4)
+    copies = device_copies(tensors.upload_matrix(q), copies_for(b))
     x = tensors.device_tensor(inputs.activation_rows(1, c["k"], key=(configs.CFG_SINGLE, 0, 0, 4))[0])
     y = torch.empty(c["n"], dtype=torch.float32, device="cuda")
-    ms = timer(lambda: tensors.gemv(dq, x, y), reps=100)
-    b = configs.gemv_bytes(c["n"], c["k"], 4)
+    idx = [0]
+
+    def single_call():
+        tensors.gemv(copies[idx[0] % len(copies)], x, y)
+        idx[0] += 1
+    ms = timer(single_call, reps=len(copies))
     out["single_3072x1024_q4"] = {"us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1),
-                                  "pct_peak": round(100 * b / ms / 1e6 / HBM_PEAK_GBS, 2)}
+                                  "pct_peak": round(100 * b / ms / 1e6 / HBM_PEAK_GBS, 2),
+                                  "copies": len(copies)}
+    del copies
 
     # Per-shape single launches of the Qwen3-0.6B projections: the 28 layers'
-    # own matrices of each shape in turn (one launch each, graph-replayed).
-    # The 28 matrices of one shape total 29-50 MB, which the 256 MB last-level
-    # cache can hold between replays, so these rates are upper bounds of what
-    # a decode step sees; at 0.6-1.8 MB a launch is too short to reach a
+    # own matrices of each shape in turn, plus device copies of them until
+    # the rotation exceeds CACHE_BUST_BYTES (one launch each,
+    # graph-replayed).  At 0.6-1.8 MB a launch is too short to reach a
     # steady stream (it is dominated by its fixed start-up cost).
     per_shape = {}
     for pname, n, k in configs.QWEN3_06B_PROJ:
-        sel = [(d, x, y) for (layer, name, d), x, y in zip(mats, xs, ys) if name == pname]
+        own = [(d, x, y) for (layer, name, d), x, y in zip(mats, xs, ys) if name == pname]
+        rounds = copies_for(len(own) * configs.gemv_bytes(n, k, 4))
+        sel = [(cp, x, y) for r in range(rounds) for d, x, y in own
+               for cp in ([d] if r == 0 else device_copies(d, 2)[1:])]
         jj = [0]
 
         def shape_call():
@@ -440,19 +467,22 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
         ms = timer(shape_call, reps=len(sel))
         b = configs.gemv_bytes(n, k, 4)
         per_shape[pname] = {"n": n, "k": k, "us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1),
-                            "pct_peak": round(100 * b / ms / 1e6 / HBM_PEAK_GBS, 2)}
+                            "pct_peak": round(100 * b / ms / 1e6 / HBM_PEAK_GBS, 2), "copies": len(sel)}
+        del sel
     out["qwen3_0.6b_per_shape_q4"] = per_shape
     log("qwen3 per shape: " + ", ".join("%s %.2f us" % (k2, v["us"]) for k2, v in per_shape.items()))
 
-    # Bit-width sweep on Llama-3.2-3B shapes (rotating 2 copies of each).
+    # Bit-width sweep on Llama-3.2-3B shapes (rotating device copies of each
+    # matrix, CACHE_BUST_BYTES in all).
     sweep = {}
     for bits in configs.SWEEP_BITS:
         row = {}
         for j, (pname, n, k) in enumerate(configs.LLAMA32_3B_PROJ):
             if pname in ("k_proj", "o_proj", "up_proj"):
                 continue  # same shapes as v, q and gate
-            cps = [tensors.upload_matrix(inputs.quantized_matrix(n, k, bits, G, key=(configs.CFG_SWEEP, r, j, bits)))
-                   for r in range(2 if pname == "lm_head" else 4)]
+            b = configs.gemv_bytes(n, k, bits)
+            base = tensors.upload_matrix(inputs.quantized_matrix(n, k, bits, G, key=(configs.CFG_SWEEP, 0, j, bits)))
+            cps = device_copies(base, copies_for(b))
             xv = tensors.device_tensor(inputs.activation_rows(1, k, key=(configs.CFG_SWEEP, 0, j, bits))[0])
             yv = torch.empty(n, dtype=torch.float32, device="cuda")
             ii = [0]
@@ -460,10 +490,9 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
             def call():
                 tensors.gemv(cps[ii[0] % len(cps)], xv, yv)
                 ii[0] += 1
-            ms = timer(call, reps=20)
-            b = configs.gemv_bytes(n, k, bits)
-            row[pname] = {"us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1)}
-            del cps
+            ms = timer(call, reps=max(len(cps), 20))
+            row[pname] = {"us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1), "copies": len(cps)}
+            del cps, base
         # Per-token projection time: 28 layers of q, k, v, o, gate, up, down
         # (k as v, o as q, up as gate: same shapes) plus the LM head, from the
         # per-launch times above.
@@ -492,29 +521,30 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
     # from HBM).
     glu = {}
     for label, n, k in (("qwen3_0.6b_gate_up", 3072, 1024), ("llama3.2_3b_gate_up", 8192, 3072)):
-        pairs = [(tensors.upload_matrix(inputs.quantized_matrix(n, k, 4, G, key=(configs.CFG_SWEEP, 90, r, 0))),
-                  tensors.upload_matrix(inputs.quantized_matrix(n, k, 4, G, key=(configs.CFG_SWEEP, 90, r, 1))))
-                 for r in range(8)]
+        b = 2 * configs.weight_bytes(n, k, 4) + 2 * k + 4 * n
+        dg0 = tensors.upload_matrix(inputs.quantized_matrix(n, k, 4, G, key=(configs.CFG_SWEEP, 90, 0, 0)))
+        du0 = tensors.upload_matrix(inputs.quantized_matrix(n, k, 4, G, key=(configs.CFG_SWEEP, 90, 0, 1)))
+        npair = copies_for(b)
+        pairs = list(zip(device_copies(dg0, npair), device_copies(du0, npair)))
         xg = tensors.device_tensor(inputs.activation_rows(1, k, key=(configs.CFG_SWEEP, 90, k))[0])
         hg = torch.empty(n, dtype=torch.float32, device="cuda")
         yg2 = torch.empty(n, dtype=torch.float32, device="cuda")
         ii = [0]
 
         def fused():
-            dg, du = pairs[ii[0] % 8]
+            dg, du = pairs[ii[0] % npair]
             tensors.gemv_swiglu(dg, du, xg, hg)
             ii[0] += 1
 
         def separate():
-            dg, du = pairs[ii[0] % 8]
+            dg, du = pairs[ii[0] % npair]
             tensors.gemv(dg, xg, hg)
             tensors.gemv(du, xg, yg2)
             ii[0] += 1
-        ms_f = timer(fused, reps=40)
-        ms_s = timer(separate, reps=40)
-        b = 2 * configs.weight_bytes(n, k, 4) + 2 * k + 4 * n
+        ms_f = timer(fused, reps=npair)
+        ms_s = timer(separate, reps=npair)
         glu[label] = {"fused_us": round(ms_f * 1e3, 2), "two_gemvs_us": round(ms_s * 1e3, 2),
-                      "fused_GBps": round(b / ms_f / 1e6, 1)}
+                      "fused_GBps": round(b / ms_f / 1e6, 1), "copies": npair}
         del pairs
         log("swiglu %s: fused %.1f us, two gemvs %.1f us" % (label, ms_f * 1e3, ms_s * 1e3))
     out["swiglu_fusion_q4"] = glu
@@ -523,77 +553,98 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
     # against the plain GEMV followed by a separate add launch.
     resid = {}
     for label, n, k in (("qwen3_0.6b_o_proj", 1024, 2048), ("llama3.2_3b_down", 3072, 8192)):
-        mats = [tensors.upload_matrix(inputs.quantized_matrix(n, k, 4, G, key=(configs.CFG_SWEEP, 91, r)))
-                for r in range(8)]
+        nm = copies_for(configs.gemv_bytes(n, k, 4))
+        mats = device_copies(tensors.upload_matrix(inputs.quantized_matrix(n, k, 4, G, key=(configs.CFG_SWEEP, 91, 0))),
+                             nm)
         xr = tensors.device_tensor(inputs.activation_rows(1, k, key=(configs.CFG_SWEEP, 91, k))[0])
         hr = torch.zeros(n, dtype=torch.float32, device="cuda")
         yr = torch.empty(n, dtype=torch.float32, device="cuda")
         ii = [0]
 
         def fused_res():
-            tensors.gemv_residual(mats[ii[0] % 8], xr, hr, hr)
+            tensors.gemv_residual(mats[ii[0] % nm], xr, hr, hr)
             ii[0] += 1
 
         def gemv_then_add():
-            tensors.gemv(mats[ii[0] % 8], xr, yr)
+            tensors.gemv(mats[ii[0] % nm], xr, yr)
             hr.add_(yr)
             ii[0] += 1
-        ms_f = timer(fused_res, reps=40)
-        ms_s = timer(gemv_then_add, reps=40)
-        resid[label] = {"fused_us": round(ms_f * 1e3, 2), "gemv_plus_add_us": round(ms_s * 1e3, 2)}
+        ms_f = timer(fused_res, reps=nm)
+        ms_s = timer(gemv_then_add, reps=nm)
+        resid[label] = {"fused_us": round(ms_f * 1e3, 2), "gemv_plus_add_us": round(ms_s * 1e3, 2),
+                        "copies": nm}
         del mats
         log("residual %s: fused %.1f us, gemv + add %.1f us" % (label, ms_f * 1e3, ms_s * 1e3))
     out["residual_fusion_q4"] = resid
 
-    # MoE expert projections (Qwen3-30B-A3B shapes).
+    # MoE expert projections (Qwen3-30B-A3B shapes).  Every timing loop
+    # rotates over device copies of the expert stacks and over routings drawn
+    # with different seeds, so the experts a call touches are not still
+    # cached from the previous calls (at one token a call reads 7 MB per
+    # projection; the loop reads more than CACHE_BUST_BYTES).
     moe = {}
     e, top = configs.MOE["n_experts"], configs.MOE["top_k"]
+    n_stack = 6
     stacks = {}
     for j, (pname, n, k) in enumerate(configs.MOE_PROJ):
-        stacks[pname] = tensors.upload_matrix(inputs.stacked_experts(e, n, k, 4, G, key=(configs.CFG_MOE, j)))
+        base = tensors.upload_matrix(inputs.stacked_experts(e, n, k, 4, G, key=(configs.CFG_MOE, j)))
+        stacks[pname] = device_copies(base, n_stack)
     for tokens in configs.MOE["tokens"]:
-        r = inputs.routing(tokens, e, top, key=(configs.CFG_MOE, tokens))
+        n_route = 32 if tokens == 1 else 4
+        routes = [inputs.routing(tokens, e, top, key=(configs.CFG_MOE, tokens) + ((r,) if r else ()))
+                  for r in range(n_route)]
         p = tokens * top
-        distinct = int((np.diff(r["offsets"]) > 0).sum())
-        off = tensors.device_tensor(r["offsets"])
-        rows = tensors.device_tensor(r["pair_token"])
+        distinct = float(np.mean([(np.diff(r["offsets"]) > 0).sum() for r in routes]))
+        off = [tensors.device_tensor(r["offsets"]) for r in routes]
+        rows = [tensors.device_tensor(r["pair_token"]) for r in routes]
+        pw = [tensors.device_tensor(r["pair_weight"]) for r in routes]
+        pt64 = [rw.long() for rw in rows]
+        combos = [(c, ri) for ri in range(n_route) for c in range(n_stack)]
         x_tok = tensors.device_tensor(inputs.activation_rows(tokens, 2048, key=(configs.CFG_MOE, tokens)))
         x_pair = tensors.device_tensor(inputs.activation_rows(p, 768, key=(configs.CFG_MOE, tokens, 9)))
+        ii = [0]
+
+        def rotating(fn):
+            def call():
+                c, ri = combos[ii[0] % len(combos)]
+                fn(c, ri)
+                ii[0] += 1
+            return call
         row = {}
         tot_b, tot_ms = 0, 0.0
         for pname, n, k in configs.MOE_PROJ:
-            st = stacks[pname]
             yo = torch.empty((p, n), dtype=torch.float32, device="cuda")
             if pname == "down_proj":
-                fn = lambda: tensors.moe(st, x_pair, None, off, p, y=yo)
+                fn = rotating(lambda c, ri: tensors.moe(stacks["down_proj"][c], x_pair, None, off[ri], p, y=yo))
             else:
-                fn = lambda: tensors.moe(st, x_tok, rows, off, p, y=yo)
-            ms = timer(fn, reps=30)
+                fn = rotating(lambda c, ri, pname=pname: tensors.moe(stacks[pname][c], x_tok, rows[ri], off[ri],
+                                                                     p, y=yo))
+            ms = timer(fn, reps=len(combos))
             b = distinct * configs.weight_bytes(n, k, 4) + 2 * p * k + 4 * p * n
             row[pname] = {"us": round(ms * 1e3, 2), "GBps": round(b / ms / 1e6, 1)}
             tot_b += b
             tot_ms += ms
         # Gate and up fused with the SiLU-gated product (one launch), then down.
         ho = torch.empty((p, 768), dtype=torch.float32, device="cuda")
-        ms_glu = timer(lambda: tensors.moe_swiglu(stacks["gate_proj"], stacks["up_proj"], x_tok, rows,
-                                                  off, p, h=ho), reps=30)
+        ms_glu = timer(rotating(lambda c, ri: tensors.moe_swiglu(stacks["gate_proj"][c], stacks["up_proj"][c],
+                                                                 x_tok, rows[ri], off[ri], p, h=ho)),
+                       reps=len(combos))
         ms_fused = ms_glu + row["down_proj"]["us"] * 1e-3
         # Down projection with the routing-weighted combine into the token
         # rows (one launch), against the plain down projection followed by a
         # weighted scatter-add in torch.
-        pt = tensors.device_tensor(r["pair_token"])
-        pt64 = pt.long()
-        pw = tensors.device_tensor(r["pair_weight"])
         yc = torch.zeros((tokens, 2048), dtype=torch.float32, device="cuda")
-        ms_cmb = timer(lambda: tensors.moe_combine(stacks["down_proj"], x_pair, None, off, pt, pw, p, yc),
-                       reps=30)
-
-        def down_then_scatter():
-            tensors.moe(stacks["down_proj"], x_pair, None, off, p, y=yo_down)
-            yc.index_add_(0, pt64, yo_down * pw[:, None])
+        ms_cmb = timer(rotating(lambda c, ri: tensors.moe_combine(stacks["down_proj"][c], x_pair, None, off[ri],
+                                                                  rows[ri], pw[ri], p, yc)),
+                       reps=len(combos))
         yo_down = torch.empty((p, 2048), dtype=torch.float32, device="cuda")
-        ms_scatter = timer(down_then_scatter, reps=30)
-        moe["t%d" % tokens] = {"distinct_experts": distinct, "us": round(tot_ms * 1e3, 2),
+
+        def down_then_scatter(c, ri):
+            tensors.moe(stacks["down_proj"][c], x_pair, None, off[ri], p, y=yo_down)
+            yc.index_add_(0, pt64[ri], yo_down * pw[ri][:, None])
+        ms_scatter = timer(rotating(down_then_scatter), reps=len(combos))
+        moe["t%d" % tokens] = {"distinct_experts": round(distinct, 1), "routings": n_route,
+                               "stack_copies": n_stack, "us": round(tot_ms * 1e3, 2),
                                "GBps": round(tot_b / tot_ms / 1e6, 1), "proj": row,
                                "fused_gate_up_us": round(ms_glu * 1e3, 2),
                                "us_with_fused_gate_up": round(ms_fused * 1e3, 2),
@@ -602,6 +653,7 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
                                "us_fully_fused": round((ms_glu + ms_cmb) * 1e3, 2)}
         log("moe T=%d: %.1f us (gate|up fused: %.1f us; + fused combine: %.1f us)"
             % (tokens, tot_ms * 1e3, ms_fused * 1e3, (ms_glu + ms_cmb) * 1e3))
+    del stacks
     out["moe_qwen3_30b_a3b_q4"] = moe
     return out
 
@@ -624,13 +676,10 @@ def prefill_layers(torch, qmm, configs, inputs, tensors, timer, bits, ms_list, o
             need = qmm.qmm_gemm_workspace_bytes(m, n, k, bits, G)
             ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
             # Device-side copies of the same matrix, rotated so that the
-            # weights come from HBM (total above twice the 256 MB last-level
-            # cache, at most 64 copies).
+            # weights come from HBM (CACHE_BUST_BYTES in all).
             wb = configs.weight_bytes(n, k, bits)
-            ncp = max(4, min(64, -(-512 * 2**20 // wb)))
-            clone = lambda t: None if t is None else t.clone()
-            cps = [dq] + [{**dq, "w": dq["w"].clone(), "scales": clone(dq["scales"]),
-                           "mins": clone(dq["mins"])} for _ in range(ncp - 1)]
+            ncp = copies_for(wb, cap=1024)
+            cps = device_copies(dq, ncp)
             ii = [0]
 
             def call():
@@ -668,10 +717,8 @@ def prefill_layers(torch, qmm, configs, inputs, tensors, timer, bits, ms_list, o
                 bases = [tensors.upload_matrix(inputs.quantized_matrix(n, k, bits, G, key=(configs.CFG_PREFILL, 0, j, bits)))
                          for j, n, _ in sel]
                 wb = sum(configs.weight_bytes(n, k, bits) for _, n, _ in sel)
-                ncp = max(4, min(64, -(-512 * 2**20 // wb)))
-                clone = lambda t: None if t is None else t.clone()
-                sets = [bases] + [[{**d, "w": d["w"].clone(), "scales": clone(d["scales"]), "mins": clone(d["mins"])}
-                                   for d in bases] for _ in range(ncp - 1)]
+                ncp = copies_for(wb, cap=1024)
+                sets = [bases] + [[device_copies(d, 2)[1] for d in bases] for _ in range(ncp - 1)]
                 xg = tensors.device_tensor(inputs.activation_rows(m, k, key=(configs.CFG_PREFILL, 0, sel[0][0], 4, m)))
                 ysg = [torch.empty((m, n), dtype=torch.float32, device="cuda") for _, n, _ in sel]
                 members = [(d["w"], d["scales"], d["mins"], y, d["n"]) for d, y in zip(bases, ysg)]
@@ -696,6 +743,18 @@ def prefill_layers(torch, qmm, configs, inputs, tensors, timer, bits, ms_list, o
         log("prefill b%d m=%d%s: %.1f TFLOP/s (layer %.1f us, dense fp16 %.1f us)%s"
             % (bits, m, " fp16-out" if out_fp16 else "", tf, tot_ms * 1e3, dense_ms * 1e3, msg))
     return pre
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(np, configs, inputs, set_bytes):
@@ -727,6 +786,7 @@ def cpu_baseline(np, configs, inputs, set_bytes):
     gbs = reps * b / el / 1e9
     cores = oracle.threads()
     result = {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+              "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
               "sample": "layer 0's 7 Q4 projections + LM head rows 0..8191 (%d bytes), %d passes in %.1f s"
                         % (b, reps, el),
               "seconds_per_decode_set": round(set_bytes / (gbs * 1e9), 2)}

@@ -13,6 +13,7 @@ PARITY_BITS = BITS + (16,)  # 16: fp16 weights
 
 
 def _run_gemm(q, x, workspace="auto"):
+    # Outputs start as NaN, so a tile the kernel never writes cannot pass.
     import torch
     from gemm_qmm_gemv_amd import tensors
     dq = tensors.upload_matrix(q)
@@ -20,7 +21,8 @@ def _run_gemm(q, x, workspace="auto"):
     ws = None if workspace == "auto" else workspace
     if workspace is None:
         ws = torch.empty(0, dtype=torch.uint8, device="cuda")
-    y = tensors.gemm(dq, xd, workspace=ws)
+    y = torch.full((x.shape[0], q["n"]), float("nan"), dtype=torch.float32, device="cuda")
+    tensors.gemm(dq, xd, y=y, workspace=ws)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
@@ -180,7 +182,8 @@ def _run_gemm_f16(q, x, workspace="auto"):
     ws = None if workspace == "auto" else workspace
     if workspace is None:
         ws = torch.empty(0, dtype=torch.uint8, device="cuda")
-    y = tensors.gemm(dq, xd, workspace=ws, out_fp16=True)
+    y = torch.full((x.shape[0], q["n"]), float("nan"), dtype=torch.float16, device="cuda")
+    tensors.gemm(dq, xd, y=y, workspace=ws, out_fp16=True)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 

@@ -18,7 +18,9 @@ def _run(qs, x, workspace=None):
     import torch
     from gemm_qmm_gemv_amd import tensors
     dqs = [tensors.upload_matrix(q) for q in qs]
-    ys = tensors.gemm_grouped(dqs, tensors.device_tensor(x), workspace=workspace)
+    # Outputs start as NaN, so a tile no member's work-group writes cannot pass.
+    ys = [torch.full((x.shape[0], q["n"]), float("nan"), dtype=torch.float32, device="cuda") for q in qs]
+    tensors.gemm_grouped(dqs, tensors.device_tensor(x), ys=ys, workspace=workspace)
     torch.cuda.synchronize()
     return [y.cpu().numpy() for y in ys]
 
