@@ -10,34 +10,36 @@
 //
 // Y[M][N] = X[M][K] * W^T with W = s*q + m, on v_mfma_f32_32x32x16_f16.
 //
-// Work-group: eight waves, four along M and two along N; each wave owns a
-// (32 MS) x (32 NS) block of Y, so the work-group tile is (128 MS) x (64 NS).
-// K advances in steps of NB = 8 / NS blocks of 32 codes, which makes the
-// step's W tile exactly one 32-code chunk per thread.
+// Warp-specialized work-group: WM x 2 consumer waves and four producer
+// waves share a ring of LDS stages (three for 128-column tiles, two for
+// 256-column tiles); K advances 64 codes per step and every step ends at
+// one work-group barrier.
 //
-//   * W: thread t dequantizes chunk (column t / NB, block t % NB) of the
-//     step's tile: it loads the chunk's b words (consecutive threads read
-//     consecutive chunks of one row), turns them into sixteen fp16 values
-//     s*q + m (exact code through the fp16 mantissa, then one rounding),
-//     puts them in natural k order with one byte permute per pair and writes
-//     64 bytes to LDS.  Every weight is dequantized once per work-group, and
-//     only the compressed bytes come from memory.  The LDS tile is double
-//     buffered: one barrier per step.
-//   * X: each wave loads its own rows straight into registers as matrix-core
-//     A fragments (no LDS, no reordering).  For 32-code block p, lane l (row
-//     l % 32, half h = l / 32) holds X[row][32p + 16h .. 32p + 16h + 15]; its
-//     two 16-deep matrix steps take halves 0..7 and 8..15.  The B fragments
-//     read from LDS use the same assignment of k to (lane half, step,
-//     element), so every k of the block meets its own weight.  A ring of NB
-//     blocks keeps the loads of the next step in flight.
-//   * Per step: the W codes of the step after next are loaded, the B
-//     fragments of the next block are read from LDS while the matrix
-//     instructions of the current block run, and the next step's W tile is
-//     dequantized into the other LDS buffer -- independent instruction
-//     streams that the wave interleaves.
+//   * Producers, X: the step's X tile goes from memory straight into LDS
+//     with the direct global-to-LDS buffer loads (one kilobyte per wave and
+//     instruction, no registers, no reordering).
+//   * Producers, W: each thread owns one or two 32-code chunks of the step's
+//     W tile: it loads the chunk's b words and the group's scale and min two
+//     steps ahead, then dequantizes the chunk into 32 fp16 values s*q + m
+//     (exact code through the fp16 mantissa, one rounding), puts them in
+//     natural k order with one byte permute per pair and writes them to the
+//     stage.  Every weight is dequantized once per work-group, and only the
+//     compressed bytes come from memory.
+//   * Consumers: read A (X rows) and B (dequantized W columns) fragments
+//     from the stage and issue the matrix instructions; no global loads and
+//     no dequantization, so the matrix pipe is fed by LDS alone.  Each
+//     consumer wave owns a 64 x 32 NS block of Y (NS = 2 or 4).
+//   * LDS rows are 128 bytes of eight 16-byte pieces, XOR-swizzled so that
+//     the producers' stores and the consumers' 16-byte fragment reads are
+//     free of bank conflicts.
+//   * The barrier closing a step waits for the stage it hands over and for
+//     nothing newer: the producers' direct loads are not tracked by the
+//     compiler, so the wait counts them explicitly (scheduling barriers fix
+//     the order of the loads it counts).
 //
-// K splits, the in-kernel reduction of two splits, the XCD-aware tile order
-// and grouped launches work as in gemm.hip.
+// K splits (partial sums summed in the kernel by the last work-group of a
+// tile), the XCD-aware tile order and grouped launches (several matrices
+// sharing X, their column tiles concatenated) work as in gemm.hip.
 #include "gemm_common.h"
 
 namespace qmm {

@@ -810,30 +810,44 @@ __device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const 
 }
 
 template <int B, int UNIT, int XC, int U>
-__global__ __launch_bounds__(256) void gemv_batched_kernel(const BatchDesc* __restrict__ D, int count,
-                                                           int64_t total, int group) {
+__global__ __launch_bounds__(256) void gemv_batched_kernel(BatchCoarse coarse, const BatchDesc* __restrict__ D,
+                                                           int count, int per_wave, int extra, int group,
+                                                           int stride) {
+    (void)coarse;  // read through the kernel-argument segment pointer below
     __shared__ float ystage_all[4][YSTAGE];
     const int lane = threadIdx.x & 63;
+    // The coarse index loads depend on nothing, so they go out first.
+    typedef const __attribute__((address_space(4))) int kernarg_int;
+    kernarg_int* kc = (kernarg_int*)__builtin_amdgcn_kernarg_segment_ptr();
+    int ci[BATCH_COARSE / 64];
+#pragma unroll
+    for (int r = 0; r < BATCH_COARSE / 64; ++r) ci[r] = kc[64 * r + lane];
     const int waves_per_block = blockDim.x >> 6;
     const int wave = blockIdx.x * waves_per_block + (threadIdx.x >> 6);
-    const int nwaves = gridDim.x * waves_per_block;
     float* ystage = ystage_all[threadIdx.x >> 6];
-    const int64_t i0 = total * wave / nwaves;
-    const int64_t i1 = total * (wave + 1) / nwaves;
-    if (i0 >= i1) return;
+    // Items [i0, i1): per_wave = total / waves, and the first extra = total
+    // mod waves waves take one more (32-bit arithmetic, no division).
+    const int i0 = per_wave * wave + (wave < extra ? wave : extra);
+    const int i1 = i0 + per_wave + (wave < extra ? 1 : 0);
 
-    // Last descriptor whose first item is <= i0, in two rounds of 64 lanes:
-    // every S-th descriptor first (S = ceil(count / 64)), then the S after the
-    // chosen one, each lane holding a whole candidate descriptor so that the
-    // chosen one needs no further load.  Two dependent loads instead of a
-    // binary search's log2(count) and a reload, which had delayed every
-    // wave's first weight load.  first is non-decreasing and D[0].first = 0
-    // <= i0, so both ballots are non-empty.
-    const int S = (count + 63) / 64;
-    const bool in1 = lane * S < count;
-    const int64_t f1 = D[in1 ? lane * S : 0].first;
-    const uint64_t m1 = __ballot(in1 && f1 <= i0);
-    const int base = (63 - __clzll((long long)m1)) * S;
+    // Last descriptor whose first item is <= i0.  The coarse index (every
+    // stride-th descriptor's first item) is the kernel's first argument:
+    // lanes read it straight from the argument segment, with loads that
+    // depend on nothing, so they overlap the waves' own argument loads.
+    // Counting the entries <= i0 (non-decreasing, entry 0 is 0) gives the
+    // coarse block; one round of 64 lanes then reads the stride candidate
+    // descriptors of that block whole, so the chosen one needs no further
+    // load.  (One dependent descriptor load before the first weight load,
+    // where a search over the descriptors in memory took two.)  A block
+    // wider than 64 descriptors is finished by the forward walk below.
+    int below = 0;
+#pragma unroll
+    for (int r = 0; r < BATCH_COARSE / 64; ++r) below += __popcll(__ballot(ci[r] <= i0));
+    // (The exit of waves without items comes after the compare, so that the
+    // compiler keeps the coarse loads at the top instead of sinking them.)
+    if (i0 >= i1) return;
+    const int S = stride;
+    const int base = (below - 1) * S;
     const bool in2 = lane < S && base + lane < count;
     const BatchDesc cand = D[in2 ? base + lane : base];
     const uint64_t m2 = __ballot(in2 && cand.first <= i0);
@@ -910,7 +924,9 @@ template <int B, int UNIT, int XC, int U>
 hipError_t launch_batched_t(const BatchArgs& a, const GemvShape& sh, hipStream_t st) {
     constexpr auto kern = gemv_batched_kernel<B, UNIT, XC, U>;
     const int grid = persistent_grid(sh.work, sh.cus, blocks_per_cu<kern>(), sh.waves_per_cu);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, a.descs, a.count, a.total_items, a.group);
+    const int64_t waves = (int64_t)grid * 4;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, a.coarse, a.descs, a.count, (int)(a.total_items / waves),
+                       (int)(a.total_items % waves), a.group, a.stride);
     return hipGetLastError();
 }
 

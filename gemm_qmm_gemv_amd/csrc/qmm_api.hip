@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <climits>
 #include <cstring>
 #include <mutex>
 
@@ -360,7 +361,10 @@ int fit_split(int split, int64_t m, int64_t n, size_t ws_bytes, size_t* ws_need)
 // unless QMM_GEMM_TILE_M / _N say otherwise).
 bool wl_fills(int64_t m, int64_t n, int cus) { return (m + 255) / 256 * ((n + 255) / 256) >= cus; }
 
-GemmShape plan_gemm_wl(int64_t m, int64_t n, int64_t k, int cus, size_t ws_bytes, size_t* ws_need) {
+// member_n / members: a grouped launch's column counts; its column tiles are
+// counted per member (each member's last tile may be partial).
+GemmShape plan_gemm_wl(int64_t m, int64_t n, int64_t k, int cus, size_t ws_bytes, size_t* ws_need,
+                       const int64_t* member_n = nullptr, int members = 0) {
     GemmShape sh{};
     sh.kernel = 1;
     const bool forced = override_or(OV_GEMM_KERNEL, 0) == 1;
@@ -371,7 +375,13 @@ GemmShape plan_gemm_wl(int64_t m, int64_t n, int64_t k, int cus, size_t ws_bytes
     const int etn = override_or(OV_GEMM_TILE_N, 0);
     if (etn == 128 || etn == 256) sh.tile_n = etn;
     sh.grid_m = (int)((m + sh.tile_m - 1) / sh.tile_m);
-    sh.grid_n = (int)((n + sh.tile_n - 1) / sh.tile_n);
+    if (members) {
+        int64_t t = 0;
+        for (int j = 0; j < members; ++j) t += (member_n[j] + sh.tile_n - 1) / sh.tile_n;
+        sh.grid_n = (int)t;
+    } else {
+        sh.grid_n = (int)((n + sh.tile_n - 1) / sh.tile_n);
+    }
     const int k_tiles = (int)((k + gemm_wl_step_codes(sh.tile_n) - 1) / gemm_wl_step_codes(sh.tile_n));
     const int64_t tiles = (int64_t)sh.grid_m * sh.grid_n;
     int split = 1;
@@ -383,6 +393,8 @@ GemmShape plan_gemm_wl(int64_t m, int64_t n, int64_t k, int cus, size_t ws_bytes
     const int es = override_or(OV_GEMM_SPLIT, 0);
     if (es > 0) split = es < k_tiles ? es : k_tiles;
     if (split > 16) split = 16;
+    // A grouped launch reduces its splits in the kernel: one counter per tile.
+    if (members && tiles > GEMM_COUNTER_TILES) split = 1;
     split = fit_split(split, m, n, ws_bytes, ws_need);
     sh.k_tiles_per_split = (k_tiles + split - 1) / split;
     sh.split = (k_tiles + sh.k_tiles_per_split - 1) / sh.k_tiles_per_split;
@@ -731,6 +743,20 @@ static bool members_fill_alone(const qmm_gemm_member* members, const int64_t* id
     return true;
 }
 
+// The plan of one grouped launch: the LDS-dequantizing kernel where
+// QMM_GEMM_KERNEL = 1 asks for it, else the register-dequantizing kernel's
+// 128-column tiles.
+static GemmShape plan_grouped(const qmm_gemm_member* members, const int64_t* idx, int kept, int64_t m,
+                              int64_t k, int group_size, int cus, int64_t n_sum, int64_t tiles128,
+                              size_t ws_bytes, size_t* ws_need) {
+    if (override_or(OV_GEMM_KERNEL, 0) == 1) {
+        int64_t ns[GEMM_GROUP_MAX];
+        for (int j = 0; j < kept; ++j) ns[j] = members[idx[j]].n;
+        return plan_gemm_wl(m, n_sum, k, cus, ws_bytes, ws_need, ns, kept);
+    }
+    return plan_gemm_impl(m, n_sum, tiles128, true, k, group_size, cus, ws_bytes, ws_need);
+}
+
 size_t qmm_gemm_grouped_workspace_bytes(const qmm_gemm_member* members, int count, int64_t m, int64_t k,
                                         int bits, int group_size) {
     int64_t idx[GEMM_GROUP_MAX];
@@ -751,7 +777,7 @@ size_t qmm_gemm_grouped_workspace_bytes(const qmm_gemm_member* members, int coun
         }
         return need;
     }
-    (void)plan_gemm_impl(m, n_sum, tiles128, true, k, group_size, cus, (size_t)-1, &need);
+    (void)plan_grouped(members, idx, kept, m, k, group_size, cus, n_sum, tiles128, (size_t)-1, &need);
     return need;
 }
 
@@ -782,8 +808,9 @@ qmm_status qmm_gemm_grouped(const qmm_gemm_member* members, int count, const voi
         }
         return ok();
     }
-    const GemmShape sh =
-        plan_gemm_impl(m, n_sum, tiles128, true, k, group_size, cus, workspace ? workspace_bytes : 0, nullptr);
+    const GemmShape sh = plan_grouped(members, idx, kept, m, k, group_size, cus, n_sum, tiles128,
+                                      workspace ? workspace_bytes : 0, nullptr);
+    const int tile_n = sh.kernel == 1 ? sh.tile_n : 128;
     GemmGroupArgs g{};
     g.count = kept;
     int tile = 0, col = 0;
@@ -797,7 +824,7 @@ qmm_status qmm_gemm_grouped(const qmm_gemm_member* members, int count, const voi
         g.col0[j] = col;
         g.tile0[j] = tile;
         col += (int)mb.n;
-        tile += (int)((mb.n + 127) / 128);
+        tile += (int)((mb.n + tile_n - 1) / tile_n);
     }
     for (int j = kept; j <= GEMM_GROUP_MAX; ++j) g.tile0[j] = tile;
     float* partial = nullptr;
@@ -992,6 +1019,7 @@ qmm_status qmm_gemv_batched(const qmm_gemv_desc* descs_device, const qmm_gemv_de
                         "descriptor %lld not prepared for this batch (call qmm_gemv_batch_prepare)", (long long)i);
         first += batched_items(sh, descs_host[i].n, descs_host[i].k);
     }
+    if (first > INT_LIMIT) return fail(QMM_ERR_UNSUPPORTED, "more than 2^31-1 row batches in one batched launch");
     int cus = 0;
     if ((st = device_cus(&cus)) != QMM_OK) return st;
     sh.work = first;
@@ -1002,6 +1030,11 @@ qmm_status qmm_gemv_batched(const qmm_gemv_desc* descs_device, const qmm_gemv_de
     // so the last ones queue) is 6 % slower.
     sh.waves_per_cu = override_or(OV_GEMV_WAVES_PER_CU, BATCHED_WAVES_PER_CU);
     BatchArgs a{reinterpret_cast<const BatchDesc*>(descs_device), (int)count, first, group_size, bits};
+    a.stride = (int)((count + BATCH_COARSE - 1) / BATCH_COARSE);
+    for (int j = 0; j < BATCH_COARSE; ++j) {
+        const int64_t d = (int64_t)j * a.stride;
+        a.coarse.first[j] = d < count ? (int)descs_host[d].first_item : INT_MAX;
+    }
     return launched(launch_batched(a, sh, as_stream(stream)), "qmm_gemv_batched");
 }
 

@@ -154,11 +154,22 @@ struct BatchDesc {
 };
 static_assert(sizeof(BatchDesc) == 64, "descriptor layout");
 
+// Coarse index of a batched launch's work list, passed by value as the
+// kernel's first argument (so it sits at offset 0 of the kernel-argument
+// segment, which the waves read at start-up anyway): entry j is the first
+// item of descriptor j * stride, INT_MAX past the last descriptor.
+constexpr int BATCH_COARSE = 256;
+struct BatchCoarse {
+    int first[BATCH_COARSE];
+};
+
 struct BatchArgs {
     const BatchDesc* descs;  // device memory
     int count;
-    int64_t total_items;
+    int64_t total_items;     // below 2^31
     int group, bits;
+    int stride;              // descriptors per coarse entry
+    BatchCoarse coarse;
 };
 
 // Kernel shapes compiled for each bit width and unit: (lanes per row, units

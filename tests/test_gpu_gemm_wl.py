@@ -141,3 +141,30 @@ def test_wl_prefill_config_sampled(qmm_override, m, proj):
     rn[:4] = [0, 0, n - 1, n - 1]
     y_ref, a_ref = oracle.qmm_sample(q["w"], q["scales"], q["mins"], x, k, 4, configs.GROUP, rm, rn)
     assert_within(y[rm, rn], y_ref, a_ref, "gemm-wl prefill m%d %s" % (m, name))
+
+
+@pytest.mark.parametrize("bits", (2, 4, 5, 16))
+@pytest.mark.parametrize("tm,tn", TILES)
+@pytest.mark.parametrize("m,ns,k", [(200, [300, 77, 130], 1024), (64, [512, 128, 128], 2048),
+                                    (300, [256, 520], 512)])
+def test_wl_grouped_parity(qmm_override, bits, tm, tn, m, ns, k):
+    """Grouped launches on the LDS kernel (one launch forced): every member
+    against the oracle, K splits summed in the kernel, outputs NaN-prefilled."""
+    import torch
+    from gemm_qmm_gemv_amd import tensors
+    _force(qmm_override, tm, tn)
+    qmm_override("QMM_GEMM_GROUPED", 1)
+    qs = [inputs.quantized_matrix(n, k, bits, 64, key=(74, m, k, bits, i, n)) for i, n in enumerate(ns)]
+    x = inputs.activation_rows(m, k, key=(74, m, k, bits))
+    announce("gemm-wl-grouped", tm, tn, bits, m, ns, k)
+    dqs = [tensors.upload_matrix(q) for q in qs]
+    ys = [torch.full((m, q["n"]), float("nan"), dtype=torch.float32, device="cuda") for q in qs]
+    tensors.gemm_grouped(dqs, tensors.device_tensor(x), ys=ys)
+    ys2 = [torch.full((m, q["n"]), float("nan"), dtype=torch.float32, device="cuda") for q in qs]
+    tensors.gemm_grouped(dqs, tensors.device_tensor(x), ys=ys2)
+    torch.cuda.synchronize()
+    for i, (q, y, y2) in enumerate(zip(qs, ys, ys2)):
+        yh = y.cpu().numpy()
+        assert np.array_equal(yh, y2.cpu().numpy()), "member %d not deterministic" % i
+        y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, q["n"], k, bits, 64)
+        assert_within(yh, y_ref, a_ref, "gemm-wl grouped %dx%d b%d member %d" % (tm, tn, bits, i))
