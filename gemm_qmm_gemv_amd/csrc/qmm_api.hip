@@ -364,12 +364,12 @@ bool wl_fills(int64_t m, int64_t n, int cus) { return (m + 255) / 256 * ((n + 25
 // member_n / members: a grouped launch's column counts; its column tiles are
 // counted per member (each member's last tile may be partial).
 GemmShape plan_gemm_wl(int64_t m, int64_t n, int64_t k, int cus, size_t ws_bytes, size_t* ws_need,
-                       const int64_t* member_n = nullptr, int members = 0) {
+                       const int64_t* member_n = nullptr, int members = 0, int tile_n = 256) {
     GemmShape sh{};
     sh.kernel = 1;
     const bool forced = override_or(OV_GEMM_KERNEL, 0) == 1;
     sh.tile_m = forced ? (m > 128 ? 256 : 128) : 256;
-    sh.tile_n = forced ? 128 : 256;
+    sh.tile_n = forced ? 128 : tile_n;
     const int etm = override_or(OV_GEMM_TILE_M, 0);
     if (etm == 128 || etm == 256) sh.tile_m = etm;
     const int etn = override_or(OV_GEMM_TILE_N, 0);
@@ -728,6 +728,23 @@ static qmm_status check_group(const qmm_gemm_member* members, int count, int64_t
     return QMM_OK;
 }
 
+// Column tiles of a grouped launch at tile width tn (per member).
+static int64_t grouped_tiles(const qmm_gemm_member* members, const int64_t* idx, int kept, int64_t tn) {
+    int64_t t = 0;
+    for (int j = 0; j < kept; ++j) t += (members[idx[j]].n + tn - 1) / tn;
+    return t;
+}
+
+// Whether one grouped launch of the LDS-dequantizing kernel (256-row tiles)
+// fills the CUs without a K split: then it beats both separate launches and
+// the register kernel's grouped launch (gate|up at 512 tokens: 46.3 us
+// against 51.7 for two launches; q|k|v, whose grids stay below the CU
+// count, lose 2-3x on it through their K splits).
+static bool grouped_wl_fills(const qmm_gemm_member* members, const int64_t* idx, int kept, int64_t m, int cus) {
+    if (m <= 128) return false;
+    return (m + 255) / 256 * grouped_tiles(members, idx, kept, 128) >= cus;
+}
+
 // A grouped launch pays where the members underfill the GPU on their own
 // (q|k|v, and gate|up at 128 tokens: 11.5 vs 27.8 us and 17.9 vs 28.0 us);
 // where every member's own tile grid already fills it, separate launches
@@ -736,23 +753,32 @@ static qmm_status check_group(const qmm_gemm_member* members, int count, int64_t
 static bool members_fill_alone(const qmm_gemm_member* members, const int64_t* idx, int kept, int64_t m,
                                int64_t k, int group_size, int cus) {
     if (override_or(OV_GEMM_GROUPED, 0) == 1) return false;  // always one launch (for measurements)
+    bool all_wl = true;
     for (int j = 0; j < kept; ++j) {
         const GemmShape sh = plan_gemm(m, members[idx[j]].n, k, group_size, cus, 0, nullptr);
         if ((int64_t)sh.grid_m * sh.grid_n < cus) return false;
+        all_wl = all_wl && sh.kernel == 1;
     }
+    // Members that fill the GPU only with the register kernel's tiles go
+    // into one launch of the LDS kernel where that launch fills it too.
+    if (!all_wl && override_or(OV_GEMM_KERNEL, 0) != 2 && grouped_wl_fills(members, idx, kept, m, cus))
+        return false;
     return true;
 }
 
 // The plan of one grouped launch: the LDS-dequantizing kernel where
-// QMM_GEMM_KERNEL = 1 asks for it, else the register-dequantizing kernel's
-// 128-column tiles.
+// QMM_GEMM_KERNEL = 1 asks for it or where its grouped grid fills the CUs
+// (256 x 256 tiles if those fill them, else 256 x 128), else the register-
+// dequantizing kernel's 128-column tiles.
 static GemmShape plan_grouped(const qmm_gemm_member* members, const int64_t* idx, int kept, int64_t m,
                               int64_t k, int group_size, int cus, int64_t n_sum, int64_t tiles128,
                               size_t ws_bytes, size_t* ws_need) {
-    if (override_or(OV_GEMM_KERNEL, 0) == 1) {
+    const int ek = override_or(OV_GEMM_KERNEL, 0);
+    if (ek == 1 || (ek != 2 && grouped_wl_fills(members, idx, kept, m, cus))) {
         int64_t ns[GEMM_GROUP_MAX];
         for (int j = 0; j < kept; ++j) ns[j] = members[idx[j]].n;
-        return plan_gemm_wl(m, n_sum, k, cus, ws_bytes, ws_need, ns, kept);
+        const bool wide = (m + 255) / 256 * grouped_tiles(members, idx, kept, 256) >= cus;
+        return plan_gemm_wl(m, n_sum, k, cus, ws_bytes, ws_need, ns, kept, wide ? 256 : 128);
     }
     return plan_gemm_impl(m, n_sum, tiles128, true, k, group_size, cus, ws_bytes, ws_need);
 }

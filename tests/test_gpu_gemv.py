@@ -150,3 +150,31 @@ def test_gemv_zero_rows_is_noop():
     qmm_gemv(w, s, s, x, y, 0, 64, 4, 64)
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
+
+
+@pytest.mark.parametrize("bits", PARITY_BITS)
+@pytest.mark.parametrize("n,k", [(257, 3072), (64, 768), (33, 6144)])
+def test_gemv_three_units_per_lane(qmm_override, bits, n, k):
+    """16 lanes per row with three units each (forced): parity, and exact
+    integers bit for bit."""
+    import gemm_qmm_gemv_amd as qmm
+    qmm_override("QMM_GEMV_LPR", 16)
+    qmm_override("QMM_GEMV_XC", 3)
+    pl = qmm.qmm_get_plan(0, 1, n, k, bits, 64)
+    assert (pl["lanes_per_row"], pl["units_per_lane"]) == (16, 3)
+    q = inputs.quantized_matrix(n, k, bits, 64, key=(54, n, k, bits))
+    x = inputs.activation_rows(1, k, key=(54, n, k, bits))[0]
+    announce("gemv-16x3", bits, n, k, "multipass", pl["multipass"])
+    y = _run_gemv(q, x)
+    y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, 64)
+    assert_within(y, y_ref, a_ref, "gemv 16x3 b%d %dx%d" % (bits, n, k))
+    if bits != 16:
+        rng = inputs.rng_for(55, n, k, bits)
+        w = inputs.packed_words(rng, n, k, bits)
+        s = np.ones((n, k // 64), dtype=np.float16)
+        mn = np.zeros((n, k // 64), dtype=np.float16)
+        xi = rng.integers(-2, 3, size=k).astype(np.float16)
+        qe = {"w": w, "scales": s, "mins": mn, "n": n, "k": k, "bits": bits, "group": 64}
+        ye = _run_gemv(qe, xi)
+        y_ref, _ = oracle.qmm(w, s, mn, xi, n, k, bits, 64)
+        assert np.array_equal(ye.astype(np.float64), y_ref)
