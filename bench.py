@@ -15,8 +15,8 @@ Also measured (outside the timed region, reported in the same JSON line):
   * the same set as 197 separate qmm_gemv launches replayed from a HIP graph;
   * the set in decode dependency order (per layer: q|k|v, o, gate|up, down;
     then the LM head) replayed from a HIP graph: per-token projection time,
-    also with the epilogues fused (o and down adding the residual, gate/up
-    as one SiLU-gated launch);
+    also as a fused decode step (q|k|v stored as one matrix, o and down
+    adding the residual, gate/up as one SiLU-gated launch);
   * the LM head alone with four rotating copies (steady state);
   * the single 3072 x 1024 Q4 GEMV;
   * the Llama-3.2-3B-shaped bit-width sweep (Q2/Q3/Q4/Q5/Q6/Q8 and fp16
@@ -415,20 +415,25 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
     log("dependent-stage graph: %.1f us" % (ms * 1e3))
 
     # The same decode step with its epilogues fused as a decoder layer runs
-    # them: q|k|v batched, o with the residual add (y = r + W x), gate/up as
-    # one SiLU-gated launch, down with the residual add; then the LM head.
-    qkv_batches = []
+    # them: q|k|v as one GEMV over the three matrices stored as one [q; k; v]
+    # matrix (they share x; the same bytes, one plain launch), o with the
+    # residual add (y = r + W x), gate/up as one SiLU-gated launch, down with
+    # the residual add; then the LM head.
+    qkv_mats = []
     for layer in range(configs.QWEN3_06B_LAYERS):
         base = layer * per_layer
-        qkv_batches.append(tensors.GemvBatch([(mats[base + i][2], xs[base + i], ys[base + i]) for i in (0, 1, 2)],
-                                             4, G))
+        parts = [mats[base + i][2] for i in (0, 1, 2)]
+        qkv_mats.append(dict(parts[0], n=sum(p["n"] for p in parts),
+                             w=torch.cat([p["w"] for p in parts]), scales=torch.cat([p["scales"] for p in parts]),
+                             mins=torch.cat([p["mins"] for p in parts])))
+    qkv_out = torch.empty(qkv_mats[0]["n"], dtype=torch.float32, device="cuda")
     resid = torch.zeros(configs.QWEN3_06B_PROJ[3][1], dtype=torch.float32, device="cuda")
     hbuf = torch.empty(configs.QWEN3_06B_PROJ[4][1], dtype=torch.float32, device="cuda")
 
     def dependent_fused():
         for layer in range(configs.QWEN3_06B_LAYERS):
             base = layer * per_layer
-            qkv_batches[layer]()
+            tensors.gemv(qkv_mats[layer], xs[base], qkv_out)
             tensors.gemv_residual(mats[base + 3][2], xs[base + 3], resid, resid)
             tensors.gemv_swiglu(mats[base + 4][2], mats[base + 5][2], xs[base + 4], hbuf)
             tensors.gemv_residual(mats[base + 6][2], xs[base + 6], resid, resid)
@@ -442,7 +447,7 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
     out["decode_dependent_fused_graph"] = {
         "launches": 4 * configs.QWEN3_06B_LAYERS + 1, "per_token_us": round(ms * 1e3, 2),
         "GBps": round(set_bytes / ms / 1e6, 1), "projection_tok_per_s": round(1e3 / ms, 1),
-        "epilogues": "o and down add the residual, gate/up write silu(g)*u"}
+        "epilogues": "q|k|v one [q;k;v] matrix, o and down add the residual, gate/up write silu(g)*u"}
     log("dependent fused graph: %.1f us" % (ms * 1e3))
 
     # LM head alone, rotating device copies (CACHE_BUST_BYTES in all).

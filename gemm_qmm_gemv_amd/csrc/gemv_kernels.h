@@ -37,6 +37,19 @@ namespace qmm {
 // scales and mins arrive instead as one 32-bit word per lane of the batch's
 // contiguous scale block (and min block) and are handed out to the lanes
 // that need them with cross-lane permutes.
+// Every GEMV-family launch uses 256-thread work-groups (the launch bounds
+// below); a compile-time count saves a kernel-argument load.
+constexpr int GEMV_WAVES_PER_BLOCK = 4;
+
+// a / group for the group size, a wave-uniform kernel argument: a shift for
+// the usual power-of-two sizes (a uniform branch), a division otherwise.
+// The division's set-up had put dozens of instructions between the
+// argument loads and the first weight load of every launch.
+__device__ __forceinline__ int div_group(int a, int group) {
+    if ((group & (group - 1)) == 0) return a >> __builtin_ctz((unsigned)group);
+    return a / group;
+}
+
 template <int B, int UNIT, int XC, int U>
 struct RowBatch {
     static constexpr int WPU = UNIT * B / 32;
@@ -187,12 +200,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
     constexpr int SLOTS = 64 / LPR;
     const int lane = threadIdx.x & 63;
     const int slot = lane / LPR, j = lane % LPR;
-    const int waves_per_block = blockDim.x >> 6;
+    constexpr int waves_per_block = GEMV_WAVES_PER_BLOCK;  // every launch: 256 threads
     const int wave = blockIdx.x * waves_per_block + (threadIdx.x >> 6);
     const int nwaves = gridDim.x * waves_per_block;
     const int nu = k / UNIT;
     const int wpr = k / 32 * B;
-    const int gpr = k / group;
+    const int gpr = div_group(k, group);
     const int stride = nwaves * SLOTS * U;
     const MatRsrc mr = mat_rsrc<B>(W, S, Mn, n, wpr, gpr);
     const rsrc_t xr = make_rsrc(X, (uint32_t)k * 2u);
@@ -217,7 +230,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
 #pragma unroll
         for (int c = 0; c < XC; ++c) {
             unit[c] = (pass * XC + c) * LPR + j;
-            gidx[c] = unit[c] < nu ? (unit[c] * UNIT) / group : 0;
+            gidx[c] = unit[c] < nu ? div_group(unit[c] * UNIT, group) : 0;
         }
     };
     // Units past the row read zeros (offset at the end of x), which gives the
@@ -315,12 +328,12 @@ __global__ __launch_bounds__(256) void gemv_glu_kernel(
     constexpr int SLOTS = 64 / LPR;
     const int lane = threadIdx.x & 63;
     const int slot = lane / LPR, j = lane % LPR;
-    const int waves_per_block = blockDim.x >> 6;
+    constexpr int waves_per_block = GEMV_WAVES_PER_BLOCK;  // every launch: 256 threads
     const int wave = blockIdx.x * waves_per_block + (threadIdx.x >> 6);
     const int nwaves = gridDim.x * waves_per_block;
     const int nu = k / UNIT;
     const int wpr = k / 32 * B;
-    const int gpr = k / group;
+    const int gpr = div_group(k, group);
     const int stride = nwaves * SLOTS;
     const MatRsrc mg = mat_rsrc<B>(Wg, Sg, Mg, n, wpr, gpr);
     const MatRsrc mu = mat_rsrc<B>(Wu, Su, Mu, n, wpr, gpr);
@@ -330,7 +343,7 @@ __global__ __launch_bounds__(256) void gemv_glu_kernel(
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
         unit[c] = c * LPR + j;
-        gidx[c] = unit[c] < nu ? (unit[c] * UNIT) / group : 0;
+        gidx[c] = unit[c] < nu ? div_group(unit[c] * UNIT, group) : 0;
     }
     XUnit<B, UNIT> xu[XC];
 
@@ -448,12 +461,12 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
     constexpr int ALIGN = unit_align(B, UNIT);
     const int lane = threadIdx.x & 63;
     const int slot = lane / LPR, j = lane % LPR;
-    const int waves_per_block = blockDim.x >> 6;
+    constexpr int waves_per_block = GEMV_WAVES_PER_BLOCK;  // every launch: 256 threads
     const int wave = blockIdx.x * waves_per_block + (threadIdx.x >> 6);
     const int nwaves = gridDim.x * waves_per_block;
     const int nu = k / UNIT;
     const int wpr = k / 32 * B;
-    const int gpr = k / group;
+    const int gpr = div_group(k, group);
     const int passes = MP ? (nu + LPR * XC - 1) / (LPR * XC) : 1;
 
     // A work-group row handles one (segment, MR-row batch) pair at a time:
@@ -607,7 +620,7 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
                                                      live ? ((uint32_t)row * (uint32_t)wpr + (uint32_t)(u * WPU)) * 4u
                                                           : mr.wbytes,
                                                      wv[c]);
-                            const uint32_t so = live ? ((uint32_t)row * (uint32_t)gpr + (uint32_t)((u * UNIT) / group)) * 2u
+                            const uint32_t so = live ? ((uint32_t)row * (uint32_t)gpr + (uint32_t)div_group(u * UNIT, group)) * 2u
                                                      : mr.sbytes;
                             sv[c] = buffer_u16(mr.s, so);
                             mv[c] = buffer_u16(mr.m, so);
@@ -630,7 +643,7 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(
 #pragma unroll
             for (int c = 0; c < XC; ++c) {
                 unit[c] = c * LPR + j;
-                gidx[c] = unit[c] < nu ? (unit[c] * UNIT) / group : 0;
+                gidx[c] = unit[c] < nu ? div_group(unit[c] * UNIT, group) : 0;
             }
             const int stride = nwaves * SLOTS;
             auto body = [&](auto wide_c) {
@@ -722,7 +735,7 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
     const int slot = lane / LPR, j = lane % LPR;
     const int nu = k / UNIT;
     const int wpr = k / 32 * B;
-    const int gpr = k / group;
+    const int gpr = div_group(k, group);
     const MatRsrc mr = mat_rsrc<B>(W, S, Mn, n, wpr, gpr);
     const rsrc_t xr = make_rsrc(X, (uint32_t)k * 2u);
     const rsrc_t yr = make_rsrc(Y, (uint32_t)n * 4u);
@@ -730,7 +743,7 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
         unit[c] = c * LPR + j;
-        gidx[c] = unit[c] < nu ? (unit[c] * UNIT) / group : 0;
+        gidx[c] = unit[c] < nu ? div_group(unit[c] * UNIT, group) : 0;
     }
     RowBatch<B, UNIT, XC, U> ba, bb;
     load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, b0 * ROWS, true, wpr, gpr, slot, unit, gidx, nu, lane);
@@ -803,7 +816,7 @@ template <int B, int UNIT, int LPR, int XC, int U>
 __device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const uint16_t* Mn,
                                          const uint16_t* X, float* Y, int n, int k, int group, int b0,
                                          int b1, int lane, float* ystage) {
-    if (wide_scales_ok<LPR, U>(S, Mn, k / group))
+    if (wide_scales_ok<LPR, U>(S, Mn, div_group(k, group)))
         gemv_run_w<B, UNIT, LPR, XC, U, true>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage);
     else
         gemv_run_w<B, UNIT, LPR, XC, U, false>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage);
@@ -814,7 +827,7 @@ __global__ __launch_bounds__(256) void gemv_batched_kernel(BatchCoarse coarse, c
                                                            int count, int per_wave, int extra, int group,
                                                            int stride) {
     (void)coarse;  // read through the kernel-argument segment pointer below
-    __shared__ float ystage_all[4][YSTAGE];
+    __shared__ float ystage_all[GEMV_WAVES_PER_BLOCK][YSTAGE];
     const int lane = threadIdx.x & 63;
     // The coarse index loads depend on nothing, so they go out first.
     typedef const __attribute__((address_space(4))) int kernarg_int;
@@ -822,7 +835,7 @@ __global__ __launch_bounds__(256) void gemv_batched_kernel(BatchCoarse coarse, c
     int ci[BATCH_COARSE / 64];
 #pragma unroll
     for (int r = 0; r < BATCH_COARSE / 64; ++r) ci[r] = kc[64 * r + lane];
-    const int waves_per_block = blockDim.x >> 6;
+    constexpr int waves_per_block = GEMV_WAVES_PER_BLOCK;  // every launch: 256 threads
     const int wave = blockIdx.x * waves_per_block + (threadIdx.x >> 6);
     float* ystage = ystage_all[threadIdx.x >> 6];
     // Items [i0, i1): per_wave = total / waves, and the first extra = total
@@ -906,7 +919,7 @@ __global__ __launch_bounds__(256) void gemv_batched_kernel(BatchCoarse coarse, c
 template <auto Kernel>
 hipError_t launch_gemv_k(const GemvArgs& a, const GemvShape& sh, hipStream_t st) {
     const int grid = persistent_grid(sh.work, sh.cus, blocks_per_cu<Kernel>(), sh.waves_per_cu);
-    hipLaunchKernelGGL(Kernel, dim3(grid), dim3(256), 0, st, a.w, a.s, a.m, a.x, a.y, a.n, a.k, a.group, a.r);
+    hipLaunchKernelGGL(Kernel, dim3(grid), dim3(64 * GEMV_WAVES_PER_BLOCK), 0, st, a.w, a.s, a.m, a.x, a.y, a.n, a.k, a.group, a.r);
     return hipGetLastError();
 }
 
@@ -924,8 +937,8 @@ template <int B, int UNIT, int XC, int U>
 hipError_t launch_batched_t(const BatchArgs& a, const GemvShape& sh, hipStream_t st) {
     constexpr auto kern = gemv_batched_kernel<B, UNIT, XC, U>;
     const int grid = persistent_grid(sh.work, sh.cus, blocks_per_cu<kern>(), sh.waves_per_cu);
-    const int64_t waves = (int64_t)grid * 4;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, a.coarse, a.descs, a.count, (int)(a.total_items / waves),
+    const int64_t waves = (int64_t)grid * GEMV_WAVES_PER_BLOCK;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * GEMV_WAVES_PER_BLOCK), 0, st, a.coarse, a.descs, a.count, (int)(a.total_items / waves),
                        (int)(a.total_items % waves), a.group, a.stride);
     return hipGetLastError();
 }
@@ -944,7 +957,7 @@ inline dim3 rows_grid(const RowsShape& sh) {
 
 template <auto Kernel>
 hipError_t launch_rows_k(const RowsArgs& a, const RowsShape& sh, hipStream_t st, bool second_stack) {
-    hipLaunchKernelGGL(Kernel, rows_grid<Kernel>(sh), dim3(256), 0, st, a.w, a.s, a.m,
+    hipLaunchKernelGGL(Kernel, rows_grid<Kernel>(sh), dim3(64 * GEMV_WAVES_PER_BLOCK), 0, st, a.w, a.s, a.m,
                        second_stack ? a.w2 : a.w, second_stack ? a.s2 : a.s, second_stack ? a.m2 : a.m, a.x,
                        a.x_rows, a.x_count, a.offsets, a.n_seg, a.m_total, a.y, a.n, a.k, a.group, sh.pairs,
                        a.pair_token, a.pair_weight, a.n_tokens);
@@ -969,7 +982,7 @@ template <int B, int UNIT, int LPR, int XC>
 hipError_t launch_glu_t(const GluArgs& a, const GemvShape& sh, hipStream_t st) {
     constexpr auto kern = gemv_glu_kernel<B, UNIT, LPR, XC>;
     const int grid = persistent_grid(sh.work, sh.cus, blocks_per_cu<kern>(), sh.waves_per_cu);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, a.wg, a.sg, a.mg, a.wu, a.su, a.mu, a.x, a.h,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * GEMV_WAVES_PER_BLOCK), 0, st, a.wg, a.sg, a.mg, a.wu, a.su, a.mu, a.x, a.h,
                        a.n, a.k, a.group);
     return hipGetLastError();
 }
