@@ -33,7 +33,7 @@ Also measured (outside the timed region, reported in the same JSON line):
   * measured ceilings (a plain streaming read and an fp16 MFMA loop built
     here), reported beside the spec peaks as second denominators.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick | --decode-graphs]
 """
 from __future__ import annotations
 
@@ -181,6 +181,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--quick", action="store_true", help="headline only (for profiler runs)")
+    ap.add_argument("--decode-graphs", action="store_true",
+                    help="headline plus the decode-order graphs only (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (counter scale reference)")
@@ -299,7 +301,10 @@ def main():
         },
     }
 
-    if not args.quick:
+    if args.decode_graphs:
+        result["extras"] = extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_bytes,
+                                  decode_graphs_only=True)
+    elif not args.quick:
         ceil = measured_ceilings(torch, set_bytes)
         result["measured_ceilings"] = ceil
         result["roofline"]["measured_peak"] = ceil["hbm_read_GBps"]
@@ -313,7 +318,7 @@ def main():
                     if "grouped" in row:
                         row["grouped"]["pct_of_measured_mfma"] = round(
                             100 * row["grouped"]["TFLOPs"] / ceil["mfma_f16_TFLOPs"], 2)
-    if not args.no_cpu_baseline and not args.quick:
+    if not args.no_cpu_baseline and not args.quick and not args.decode_graphs:
         result["cpu_baseline"] = cpu_baseline(np, configs, inputs, set_bytes)
     print(json.dumps(result), flush=True)
 
@@ -371,7 +376,7 @@ def measured_ceilings(torch, set_bytes):
     return out
 
 
-def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_bytes):
+def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_bytes, decode_graphs_only=False):
     G = configs.GROUP
     out = {}
 
@@ -449,6 +454,8 @@ def extras(torch, np, qmm, configs, inputs, tensors, timer, mats, xs, ys, set_by
         "GBps": round(set_bytes / ms / 1e6, 1), "projection_tok_per_s": round(1e3 / ms, 1),
         "epilogues": "q|k|v one [q;k;v] matrix, o and down add the residual, gate/up write silu(g)*u"}
     log("dependent fused graph: %.1f us" % (ms * 1e3))
+    if decode_graphs_only:
+        return out
 
     # LM head alone, rotating device copies (CACHE_BUST_BYTES in all).
     name, n, k = configs.QWEN3_06B_LM_HEAD
