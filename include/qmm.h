@@ -236,7 +236,11 @@ QMM_API size_t qmm_gemm_grouped_workspace_bytes(const qmm_gemm_member *members, 
  * Apple Silicon via Native Metal", section "Metodologia" (low-overhead
  * dispatch without per-operation scheduling).
  * Every descriptor is one qmm_gemv (same bits and group_size for all; each
- * k at most 64*3*64 codes for 64-multiple groups).  first_item is owned by
+ * k at most 8192 codes for 64-multiple groups, 4096 otherwise and at 16
+ * bits, else QMM_ERR_UNSUPPORTED; the whole batch below 2^31 row batches,
+ * likewise).  Launch start-up reads a 256-entry index of the work list from
+ * the kernel arguments, so finding a wave's first descriptor costs one
+ * dependent load of the device copy whatever the count.  first_item is owned by
  * the library: qmm_gemv_batch_prepare fills it in a host array, the caller
  * copies the array to device memory (once; it can be reused for every
  * later call with the same shapes and pointers) and passes both copies to

@@ -223,14 +223,18 @@ def test_gemv_plan_small_vs_large(lib):
 
 def _expected_tile(m, n, k, cus=256):
     # 64-row tiles unless they would need more work-groups than CUs, or K is
-    # long (64 steps of 128 or more) with more than one 128-row tile.
+    # long (64 steps of 128 or more) with more than one 128-row tile; above
+    # 64 rows, 32-row tiles where the 64-row grid underfills the CUs and K
+    # is short.
     if m <= 32:
         return 32
     if m <= 64:
         return 64
     tiles64 = -(-m // 64) * -(-n // 128)
-    long_k = -(-k // 128) >= 64 and m > 128
-    return 64 if tiles64 <= cus and not long_k else 128
+    long_k = -(-k // 128) >= 64
+    if tiles64 <= cus and not (long_k and m > 128):
+        return 32 if tiles64 < cus and not long_k else 64
+    return 128
 
 
 @pytest.mark.parametrize("m", (3, 64, 128, 512, 1000))
@@ -257,8 +261,8 @@ def test_gemm_plan(lib, m, n, k):
 
 def test_gemm_plan_on_the_prefill_shapes(lib):
     # The measured choices: (m, n, k) -> (tile_m, split_k).
-    want = {(128, 2048, 2048): (64, 4), (128, 512, 2048): (64, 4), (128, 8192, 2048): (64, 2),
-            (128, 2048, 8192): (64, 8), (512, 2048, 2048): (64, 2), (512, 512, 2048): (64, 4),
+    want = {(128, 2048, 2048): (32, 4), (128, 512, 2048): (32, 4), (128, 8192, 2048): (32, 1),
+            (128, 2048, 8192): (64, 8), (512, 2048, 2048): (32, 1), (512, 512, 2048): (32, 4),
             (512, 8192, 2048): (128, 1), (512, 2048, 8192): (128, 4)}
     for (m, n, k), (tile, split) in want.items():
         pl = qmm.qmm_get_plan(1, m, n, k, 4, 64, cu_count=256, workspace_bytes=1 << 40)
@@ -376,9 +380,10 @@ def test_grouped_argument_checks(lib):
 def test_grouped_workspace_follows_the_launch_decision(lib):
     # Without a device the planner assumes 256 compute units.  q|k|v of a
     # Llama-3.2-1B layer at 128 tokens underfill the GPU alone: one grouped
-    # launch of 2 x 24 tiles, K split in four (counters, then the partial
-    # sums of all three members).  gate|up at 2048 tokens fill it alone:
-    # separate launches without a split need no workspace.
+    # launch of 4 x 24 tiles (32 rows), K split in two (three fitted, two
+    # after rounding each split to whole blocks of four steps; counters,
+    # then the partial sums of all three members).  gate|up at 2048 tokens
+    # fill it alone: separate launches without a split need no workspace.
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
@@ -386,7 +391,7 @@ def test_grouped_workspace_follows_the_launch_decision(lib):
     def members(ns):
         return [(A16, A16, A16, A16, n) for n in ns]
     need = qmm.qmm_gemm_grouped_workspace_bytes(members([2048, 512, 512]), 128, 2048, 4, 64)
-    assert need == 4096 + 4 * 128 * 3072 * 4
+    assert need == 4096 + 2 * 128 * 3072 * 4
     assert qmm.qmm_gemm_grouped_workspace_bytes(members([8192, 8192]), 2048, 2048, 4, 64) == 0
     # A member with n = 0 is skipped; an empty group needs nothing.
     assert qmm.qmm_gemm_grouped_workspace_bytes(members([2048, 0, 512, 512]), 128, 2048, 4, 64) == need

@@ -58,6 +58,28 @@ def test_batched_mixed_k_one_launch(bits):
         assert_within(y[:n], y_ref, a_ref, "batched mixed-k b%d %dx%d" % (bits, n, k))
 
 
+@pytest.mark.parametrize("count", (257, 3000, 17000))
+def test_batched_many_descriptors(count):
+    # The launch finds each wave's first descriptor through a 256-entry
+    # index of the work list: one descriptor per entry up to 256, a block of
+    # ceil(count / 256) per entry above (searched by one round of 64 lanes),
+    # and past 16384 blocks wider than a round (finished by the walk from
+    # descriptor to descriptor).  Small matrices of mixed K, empty ones
+    # among them; every row of every output checked.
+    rng = np.random.default_rng(count)
+    ks = (64, 1024, 2048, 3072)
+    shapes = [(int(rng.integers(0, 9)) if i % 7 else 0, int(ks[rng.integers(0, 4)])) for i in range(count)]
+    shapes[-1] = (5, 1024)
+    announce("batched-many", count)
+    qs, ys = _run_batch(shapes, 4, 64, 5)
+    for i, ((q, x), y, (n, k)) in enumerate(zip(qs, ys, shapes)):
+        if n == 0:
+            assert np.all(y == -3.0), i
+            continue
+        y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, 4, 64)
+        assert_within(y[:n], y_ref, a_ref, "batched many %d: descriptor %d" % (count, i))
+
+
 @pytest.mark.parametrize("k", (2048, 3072))
 def test_batched_layer_like(k):
     # Many matrices of one K, as in one launch of the decode set.

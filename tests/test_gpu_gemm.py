@@ -84,8 +84,8 @@ def test_gemm_split_workspace_reuse():
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
     # Splits of 2 are added up inside the GEMM kernel, larger ones by a
     # separate reduction kernel: both kinds, and odd N, in one sequence.
-    cases = [(128, 8192, 2048, 4), (128, 2048, 2048, 4), (512, 2048, 2048, 3), (64, 512, 8192, 4),
-             (128, 2048, 8192, 8), (96, 300, 1024, 4), (128, 8196, 2048, 5), (128, 2052, 2048, 4),
+    cases = [(128, 4096, 2048, 4), (128, 2048, 2048, 4), (512, 1024, 2048, 3), (64, 512, 8192, 4),
+             (128, 2048, 8192, 8), (96, 300, 1024, 4), (128, 4100, 2048, 5), (128, 2052, 2048, 4),
              (200, 1000, 4096, 2)]
     for m, n, k, bits in cases:
         pl = qmm.qmm_get_plan(1, m, n, k, bits, 64, workspace_bytes=ws.numel())

@@ -18,10 +18,10 @@ BITS, GROUP = 4, 64
 
 # (first call, second call): each (m, n, k); the second is smaller.
 SEQUENCES = [
-    ((128, 8192, 2048), (96, 2048, 1024)),    # two-way split summed in the kernel, then a smaller one
+    ((128, 4096, 2048), (96, 2048, 1024)),    # two-way split summed in the kernel, then a smaller one
     ((128, 2048, 2048), (64, 512, 2048)),     # split summed by a second kernel
     ((512, 8192, 2048), (2, 256, 1024)),      # no split, then the multi-row GEMV route
-    ((2048, 512, 2048), (200, 1024, 3072)),   # in-kernel split at 2048 tokens, then a ragged m
+    ((2048, 256, 2048), (200, 1024, 3072)),   # in-kernel split at 2048 tokens, then a ragged m
 ]
 
 
