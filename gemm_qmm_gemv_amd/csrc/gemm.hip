@@ -94,12 +94,6 @@ __device__ __forceinline__ void to_slot_order(const u32 (&in)[x_unit_halves<B>()
 #ifndef GEMM_MINB
 #define GEMM_MINB 2
 #endif
-#ifndef GEMM_SCHED
-#define GEMM_SCHED 0
-#endif
-#ifndef GEMM_SCHED_V
-#define GEMM_SCHED_V 4
-#endif
 constexpr int PD = GEMM_PD;
 static_assert(PD >= 2 && PD <= 4, "prefetch distance");
 // The main loop is unrolled so that every ring index is a compile-time
@@ -430,24 +424,6 @@ __global__ __launch_bounds__(64 * WN * KW, gemm_min_blocks(WN)) void gemm_kernel
             sm_of_block(std::integral_constant<int, (U + 1) % SW_STEPS>{}, sq[NEXT], mq[NEXT]);
         }
         dequant(wq[NEXT], sq[NEXT], mq[NEXT], wv[BUF ^ 1]);
-#if GEMM_SCHED
-        // Interleave: the X staging writes first, then per matrix
-        // instruction one A-fragment read (the reads run one substep ahead
-        // of their use) and a share of the dequantization.
-        {
-            constexpr int NM = MS * NS * CH * 4;   // matrix instructions per step
-            constexpr int NR = MS * CH * 4;        // A-fragment reads per step
-            constexpr int XWR = XU * XW / 4;       // X staging writes
-            __builtin_amdgcn_sched_group_barrier(0x200, XWR, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);
-#pragma unroll
-            for (int i = 0; i < NM; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (i * NR / NM + MS < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, GEMM_SCHED_V, 0);
-            }
-        }
-#endif
         __syncthreads();
     };
     // Whole passes in the loop, the remainder after it: an exit from the
