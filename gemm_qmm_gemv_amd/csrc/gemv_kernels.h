@@ -41,6 +41,20 @@ namespace qmm {
 // below); a compile-time count saves a kernel-argument load.
 constexpr int GEMV_WAVES_PER_BLOCK = 4;
 
+// Output staging.  Stores and loads share one in-order completion counter on
+// this architecture, so a store issued inside the pipelined loop makes the
+// next wait for a load also wait for that store's write to complete.  The
+// row sums are therefore parked in LDS (a per-wave area of YSTAGE floats) and
+// written out with coalesced stores once per run, or when the area is full.
+// (Both the batched launch and the single GEMV run their rows this way.)
+constexpr int YSTAGE = 256;
+
+template <int B, int UNIT, int LPR, int XC, int U, bool RES>
+__device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const uint16_t* Mn,
+                                         const uint16_t* X, float* Y, int n, int k, int group, int b0,
+                                         int b1, int lane, float* ystage, int base, int bstride,
+                                         const float* R);
+
 // a / group for the group size, a wave-uniform kernel argument: a shift for
 // the usual power-of-two sizes (a uniform branch), a division otherwise.
 // The division's set-up had put dozens of instructions between the
@@ -176,12 +190,17 @@ __device__ __forceinline__ void store_batch(float (&yacc)[U], rsrc_t yr, int rb,
     }
 }
 
-// Decode GEMV.  Single pass (k <= LPR*XC*UNIT): the activation units stay in
-// registers for the whole kernel, and the loop is software-pipelined -- the
-// next row batch's loads are issued before the current batch's arithmetic, and
-// the first batch's loads before the activation set-up, so memory latency
-// overlaps both.  Multi-pass (MP, larger k): each row batch walks k in passes
-// and rebuilds the activation units per pass (no pipelining).
+// Decode GEMV.  Single pass (k <= LPR*XC*UNIT): each wave takes row batches
+// wave, wave + waves, ... (all waves read neighbouring rows at a time); the
+// activation units stay in registers for the whole kernel, and the loop is
+// software-pipelined -- the next row batch's loads are issued before the
+// current batch's arithmetic, and the first batch's loads before the
+// activation set-up, so memory latency overlaps both.  STG: the same sweep
+// through gemv_run, with the row sums staged in LDS and stored outside the
+// loop (for 64-lane rows and several batches per wave; a launch with one
+// batch per wave pays the staging round trip for nothing).  Multi-pass (MP,
+// larger k): each row batch walks k in passes and rebuilds the activation
+// units per pass (no pipelining).
 //
 // The output pointer is restrict-qualified unless the residual may alias it.
 template <bool RES>
@@ -191,12 +210,13 @@ using out_ptr = std::conditional_t<RES, float*, float* __restrict__>;
 // may be y itself: each row's residual is read, by the lanes of that row's
 // slot, before the row is written.  Without RES, R is ignored and the
 // kernel issues no residual loads.
-template <int B, int UNIT, int LPR, int XC, int U, bool MP, bool RES = false>
+template <int B, int UNIT, int LPR, int XC, int U, bool MP, bool RES = false, bool STG = false>
 __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
                                                    const uint16_t* __restrict__ S,
                                                    const uint16_t* __restrict__ Mn,
                                                    const uint16_t* __restrict__ X,
                                                    out_ptr<RES> Y, int n, int k, int group, const float* R) {
+    __shared__ float ystage_all[GEMV_WAVES_PER_BLOCK][STG ? YSTAGE : 1];
     constexpr int SLOTS = 64 / LPR;
     const int lane = threadIdx.x & 63;
     const int slot = lane / LPR, j = lane % LPR;
@@ -262,7 +282,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
                 }
                 store_batch<LPR, U>(yacc, yr, rb, n, slot, j, res);
             }
-        } else {
+        } else if constexpr (!STG) {
             units_of_pass(0);
             int rb = wave * SLOTS * U;
             if (rb >= n) return;
@@ -297,10 +317,20 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
             }
         }
     };
-    if (wide_scales_ok<LPR, U>(S, Mn, gpr))
+    if constexpr (STG) {
+        // This wave's grid-strided row batches through the pipelined run
+        // with its row sums staged in LDS (stores leave the loop).
+        constexpr int ROWS = SLOTS * U;
+        const int batches = (n + ROWS - 1) / ROWS;
+        if (wave >= batches) return;
+        const int nb = (batches - wave + nwaves - 1) / nwaves;
+        gemv_run<B, UNIT, LPR, XC, U, RES>(W, S, Mn, X, Y, n, k, group, 0, nb, lane, ystage_all[threadIdx.x >> 6],
+                                           wave, nwaves, R);
+    } else if (wide_scales_ok<LPR, U>(S, Mn, gpr)) {
         body(std::true_type{});
-    else
+    } else {
         body(std::false_type{});
+    }
 }
 
 // Fused gate/up projection of a feed-forward block: h[n] = silu(g[n]) * u[n]
@@ -717,21 +747,22 @@ __device__ __forceinline__ int batched_lanes_per_row(int nu) {
     return lpr;
 }
 
-// Output staging.  Stores and loads share one in-order completion counter on
-// this architecture, so a store issued inside the pipelined loop makes the
-// next wait for a load also wait for that store's write to complete.  The
-// row sums are therefore parked in LDS (a per-wave area of YSTAGE floats) and
-// written out with coalesced stores once per run, or when the area is full.
-constexpr int YSTAGE = 256;
 
 // Row batches [b0, b1) of one matrix (all arguments wave-uniform), with the
-// scale layout fixed at compile time.  ystage: this wave's LDS area.
-template <int B, int UNIT, int LPR, int XC, int U, bool WIDE>
+// scale layout fixed at compile time; batch b holds rows (base + b * bstride)
+// * ROWS onwards (contiguous batches: base 0, bstride 1; a grid-strided
+// sweep: base = the wave, bstride = the grid's waves).  ystage: this wave's
+// LDS area.  RES: R holds an fp32 residual [n] added to every output at the
+// flush (R may be Y: a row's residual is read by the lane that then writes
+// the row).
+template <int B, int UNIT, int LPR, int XC, int U, bool WIDE, bool RES>
 __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, const uint16_t* Mn,
                                            const uint16_t* X, float* Y, int n, int k, int group,
-                                           int b0, int b1, int lane, float* ystage) {
+                                           int b0, int b1, int lane, float* ystage, int base, int bstride,
+                                           const float* R) {
     constexpr int SLOTS = 64 / LPR;
     constexpr int ROWS = SLOTS * U;
+    auto row_of = [&](int b) { return (base + b * bstride) * ROWS; };
     const int slot = lane / LPR, j = lane % LPR;
     const int nu = k / UNIT;
     const int wpr = k / 32 * B;
@@ -739,6 +770,7 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
     const MatRsrc mr = mat_rsrc<B>(W, S, Mn, n, wpr, gpr);
     const rsrc_t xr = make_rsrc(X, (uint32_t)k * 2u);
     const rsrc_t yr = make_rsrc(Y, (uint32_t)n * 4u);
+    const rsrc_t rr = make_rsrc(R, RES ? (uint32_t)n * 4u : 0u);
     int unit[XC], gidx[XC];
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
@@ -746,7 +778,7 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
         gidx[c] = unit[c] < nu ? div_group(unit[c] * UNIT, group) : 0;
     }
     RowBatch<B, UNIT, XC, U> ba, bb;
-    load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, b0 * ROWS, true, wpr, gpr, slot, unit, gidx, nu, lane);
+    load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, row_of(b0), true, wpr, gpr, slot, unit, gidx, nu, lane);
     // The first batch's weight loads go out before the activation loads and
     // their set-up arithmetic, which the scheduler would otherwise hoist.
     __builtin_amdgcn_sched_barrier(0);
@@ -775,9 +807,11 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
         const int cnt = (be - bf) * ROWS;
         for (int i0 = 0; i0 < cnt; i0 += 64) {
             const int i = i0 + lane;
-            const int row = bf * ROWS + i;
-            const float v = ystage[i < YSTAGE ? i : 0];
-            buffer_store_f32(v, yr, (i < cnt && row < n) ? (uint32_t)row * 4u : (uint32_t)n * 4u);
+            const int row = row_of(bf + i / ROWS) + i % ROWS;
+            float v = ystage[i < YSTAGE ? i : 0];
+            const uint32_t off = (i < cnt && row < n) ? (uint32_t)row * 4u : (uint32_t)n * 4u;
+            if constexpr (RES) v += __builtin_bit_cast(float, buffer_u32(rr, off));
+            buffer_store_f32(v, yr, off);
         }
         bf = be;
     };
@@ -801,10 +835,10 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
     for (int c0 = b0; c0 < b1; c0 += CAP) {
         const int c1 = c0 + CAP < b1 ? c0 + CAP : b1;
         for (int b = c0; b < c1; b += 2) {
-            load_batch<B, UNIT, LPR, XC, U, WIDE>(bb, mr, (b + 1) * ROWS, b + 1 < b1, wpr, gpr, slot, unit, gidx, nu, lane);
+            load_batch<B, UNIT, LPR, XC, U, WIDE>(bb, mr, row_of(b + 1), b + 1 < b1, wpr, gpr, slot, unit, gidx, nu, lane);
             __builtin_amdgcn_sched_barrier(0);
             finish(ba, b);
-            load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, (b + 2) * ROWS, b + 2 < b1, wpr, gpr, slot, unit, gidx, nu, lane);
+            load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, row_of(b + 2), b + 2 < b1, wpr, gpr, slot, unit, gidx, nu, lane);
             __builtin_amdgcn_sched_barrier(0);
             finish(bb, b + 1);
         }
@@ -812,14 +846,17 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
     }
 }
 
-template <int B, int UNIT, int LPR, int XC, int U>
+template <int B, int UNIT, int LPR, int XC, int U, bool RES>
 __device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const uint16_t* Mn,
                                          const uint16_t* X, float* Y, int n, int k, int group, int b0,
-                                         int b1, int lane, float* ystage) {
+                                         int b1, int lane, float* ystage, int base, int bstride,
+                                         const float* R) {
     if (wide_scales_ok<LPR, U>(S, Mn, div_group(k, group)))
-        gemv_run_w<B, UNIT, LPR, XC, U, true>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage);
+        gemv_run_w<B, UNIT, LPR, XC, U, true, RES>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage, base,
+                                                   bstride, R);
     else
-        gemv_run_w<B, UNIT, LPR, XC, U, false>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage);
+        gemv_run_w<B, UNIT, LPR, XC, U, false, RES>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage, base,
+                                                    bstride, R);
 }
 
 template <int B, int UNIT, int XC, int U>
@@ -894,11 +931,14 @@ __global__ __launch_bounds__(256) void gemv_batched_kernel(BatchCoarse coarse, c
             const int b0 = (int)(i - first);
             const int b1 = (int)((i1 < end ? i1 : end) - first);
             if (lpr == 16)
-                gemv_run<B, UNIT, 16, XC, U>(bd.w, bd.s, bd.m, bd.x, bd.y, n, k, group, b0, b1, lane, ystage);
+                gemv_run<B, UNIT, 16, XC, U, false>(bd.w, bd.s, bd.m, bd.x, bd.y, n, k, group, b0, b1, lane, ystage,
+                                                    0, 1, nullptr);
             else if (lpr == 32)
-                gemv_run<B, UNIT, 32, XC, U>(bd.w, bd.s, bd.m, bd.x, bd.y, n, k, group, b0, b1, lane, ystage);
+                gemv_run<B, UNIT, 32, XC, U, false>(bd.w, bd.s, bd.m, bd.x, bd.y, n, k, group, b0, b1, lane, ystage,
+                                                    0, 1, nullptr);
             else
-                gemv_run<B, UNIT, 64, XC, U>(bd.w, bd.s, bd.m, bd.x, bd.y, n, k, group, b0, b1, lane, ystage);
+                gemv_run<B, UNIT, 64, XC, U, false>(bd.w, bd.s, bd.m, bd.x, bd.y, n, k, group, b0, b1, lane, ystage,
+                                                    0, 1, nullptr);
             i = first + b1;
         }
         if (++d >= count || i >= i1) break;
@@ -928,6 +968,12 @@ hipError_t launch_gemv_t(const GemvArgs& a, const GemvShape& sh, hipStream_t st)
     if (sh.multipass) {
         if (a.r) return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, true, true>>(a, sh, st);
         return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, true, false>>(a, sh, st);
+    }
+    if constexpr (LPR == 64) {
+        if (sh.staged) {
+            if (a.r) return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, false, true, true>>(a, sh, st);
+            return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, false, false, true>>(a, sh, st);
+        }
     }
     if (a.r) return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, false, true>>(a, sh, st);
     return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, false, false>>(a, sh, st);

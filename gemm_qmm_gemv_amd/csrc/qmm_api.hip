@@ -238,6 +238,13 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     // more batches through its pipelined loop); larger ones, the LM heads,
     // keep the occupancy-sized grid.
     const int wpc_default = batches <= (int64_t)16 * cus ? 8 : 0;
+    // 64-lane rows with at least 16 batches per CU stage their row sums in
+    // LDS (Llama-3.2-3B shapes at Q4: the 128256 x 3072 LM head 41.7 -> 41.4
+    // us, 8192 x 3072 6.54 -> 6.15 us; Q2 31.9 -> 30.6 and 6.35 -> 6.05 us);
+    // with fewer batches per wave the staging round trip costs more than
+    // the stores it moves (1024 x 3072: 3.9 -> 4.3 us), and 16-lane rows
+    // lose by it too (151936 x 1024: 17.6 -> 18.2 us).
+    sh.staged = !sh.multipass && sh.lpr == 64 && batches >= (int64_t)16 * cus;
     sh.waves_per_cu = override_or(OV_GEMV_WAVES_PER_CU, wpc_default);
     // Reported grid: the cap assumes 16 resident waves per CU; the launch
     // uses the kernel's real occupancy.
@@ -1115,6 +1122,7 @@ qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits, int g
         plan->unit_codes = sh.unit;
         plan->grid = sh.grid;
         plan->reserved[0] = sh.multipass;
+        plan->reserved[1] = sh.staged;
         return ok();
     }
     if (op == 3) {

@@ -350,7 +350,8 @@ typedef struct qmm_plan {
     int32_t tile_m, tile_n;/* GEMM: block tile                              */
     int64_t grid;          /* work-groups launched                          */
     int32_t block;         /* threads per work-group                        */
-    int32_t reserved[5];
+    int32_t reserved[5];   /* GEMV: [0] multi-pass rows, [1] row sums staged
+                              in LDS; the rest zero                          */
 } qmm_plan;
 
 QMM_API qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits,

@@ -218,3 +218,29 @@ def test_residual_exact(bits):
     torch.cuda.synchronize()
     y_ref, _ = oracle.qmm(qe["w"], qe["scales"], qe["mins"], xe, n, k, bits, 64)
     assert np.array_equal(ye.cpu().numpy().astype(np.float64), y_ref.reshape(-1) + r.astype(np.float64))
+
+
+@pytest.mark.parametrize("bits", (2, 3, 4, 8))
+def test_staged_single_gemv_exact_and_residual(bits):
+    # 64-lane rows with many batches per wave take the LDS-staged sweep:
+    # exact integers bit for bit, the fused residual added at the flush
+    # (in place), ragged row count.
+    import torch
+    import gemm_qmm_gemv_amd as qmm
+    from gemm_qmm_gemv_amd import tensors
+    n, k = 8195, 3072
+    pl = qmm.qmm_get_plan(0, 1, n, k, bits, 64, cu_count=256)
+    assert pl["staged"] and pl["lanes_per_row"] == 64
+    qe = _exact_matrix(n, k, bits, (105, bits))
+    xe = _int_x(1, k, (106, bits))[0]
+    announce("staged-exact", bits)
+    dq, xd = tensors.upload_matrix(qe), tensors.device_tensor(xe)
+    y = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    tensors.gemv(dq, xd, y)
+    r = inputs.rng_for(107, bits).integers(-1000, 1000, size=n).astype(np.float32)
+    rd = tensors.device_tensor(r)
+    tensors.gemv_residual(dq, xd, rd, rd)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.qmm(qe["w"], qe["scales"], qe["mins"], xe, n, k, bits, 64)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), y_ref.reshape(-1))
+    assert np.array_equal(rd.cpu().numpy().astype(np.float64), y_ref.reshape(-1) + r.astype(np.float64))
