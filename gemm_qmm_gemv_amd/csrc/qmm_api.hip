@@ -153,12 +153,12 @@ qmm_status device_cus(int* cus) {
 enum OverrideId {
     OV_UNIT, OV_GEMV_LPR, OV_GEMV_XC, OV_GEMV_U, OV_GEMV_WAVES_PER_CU, OV_BATCH_U, OV_ROWS_MR,
     OV_ROWS_WAVES_PER_CU, OV_GEMM_TILE_M, OV_GEMM_TILE_N, OV_GEMM_SPLIT, OV_GEMM_WIDE_SCALES,
-    OV_GEMM_ORDER, OV_GEMM_GROUPED, OV_GEMM_KERNEL, OV_COUNT
+    OV_GEMM_ORDER, OV_GEMM_GROUPED, OV_GEMM_KERNEL, OV_GEMV_STAGED, OV_COUNT
 };
 const char* const OVERRIDE_NAMES[OV_COUNT] = {
     "QMM_UNIT", "QMM_GEMV_LPR", "QMM_GEMV_XC", "QMM_GEMV_U", "QMM_GEMV_WAVES_PER_CU", "QMM_BATCH_U",
     "QMM_ROWS_MR", "QMM_ROWS_WAVES_PER_CU", "QMM_GEMM_TILE_M", "QMM_GEMM_TILE_N", "QMM_GEMM_SPLIT",
-    "QMM_GEMM_WIDE_SCALES", "QMM_GEMM_ORDER", "QMM_GEMM_GROUPED", "QMM_GEMM_KERNEL"};
+    "QMM_GEMM_WIDE_SCALES", "QMM_GEMM_ORDER", "QMM_GEMM_GROUPED", "QMM_GEMM_KERNEL", "QMM_GEMV_STAGED"};
 std::atomic<int> g_override[OV_COUNT];
 
 struct OverridesFromEnvironment {
@@ -245,6 +245,8 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     // the stores it moves (1024 x 3072: 3.9 -> 4.3 us), and 16-lane rows
     // lose by it too (151936 x 1024: 17.6 -> 18.2 us).
     sh.staged = !sh.multipass && sh.lpr == 64 && batches >= (int64_t)16 * cus;
+    const int es = override_or(OV_GEMV_STAGED, -1);
+    if (es >= 0) sh.staged = es == 1 && !sh.multipass && sh.lpr == 64;
     sh.waves_per_cu = override_or(OV_GEMV_WAVES_PER_CU, wpc_default);
     // Reported grid: the cap assumes 16 resident waves per CU; the launch
     // uses the kernel's real occupancy.

@@ -366,7 +366,9 @@ QMM_API qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bit
  * QMM_ROWS_WAVES_PER_CU, QMM_GEMM_TILE_M, QMM_GEMM_TILE_N, QMM_GEMM_SPLIT,
  * QMM_GEMM_WIDE_SCALES, QMM_GEMM_ORDER, QMM_GEMM_GROUPED, QMM_GEMM_KERNEL
  * (1: the prefill GEMM that dequantizes into LDS, 2: the one that
- * dequantizes into registers); value < 0 removes the override.  The same names are read from the environment once, when
+ * dequantizes into registers), QMM_GEMV_STAGED (1/0: single GEMVs with
+ * 64-lane rows do / do not stage their row sums in LDS); value < 0 removes
+ * the override.  The same names are read from the environment once, when
  * the library is loaded.  Unknown name: QMM_ERR_INVALID_ARGUMENT.          */
 QMM_API qmm_status qmm_set_override(const char *name, int value);
 
