@@ -211,10 +211,13 @@ QMM_API qmm_status qmm_gemm_noalloc(const void *w_packed, const void *scales, co
  *     qmm_gemm_grouped_workspace_bytes gives the preferred size (it reads
  *     the members' n only; sized for the current device, or for 256
  *     compute units where no device can be queried).
- * The members go into one launch where they underfill the GPU on their own;
- * where each member's own tile grid fills it, they are launched one after
- * another as qmm_gemm would (same stream, same workspace).  Either way each
- * y_i is member i's product to qmm_gemm's accuracy.                       */
+ * The library chooses between one launch and one launch per member (as
+ * qmm_gemm would, same stream, same workspace) from the shapes: one launch
+ * where the members underfill the GPU on their own, or where their tiles
+ * together fill it without a K split; separate launches where each
+ * member's own tile grid fills it.  Either way each y_i is member i's
+ * product to qmm_gemm's accuracy.  A grouped launch sums any K split
+ * inside the kernel, as described for two-way splits under qmm_gemm.      */
 typedef struct {
     const void *w_packed;
     const void *scales;
