@@ -4,10 +4,13 @@ product is computed by the library's kernels.
 """
 from __future__ import annotations
 
+import ctypes
+import functools
+
 import numpy as np
 import torch
 
-from . import (GemvDesc, qmm_gemm, qmm_gemm_f16out, qmm_gemm_workspace_bytes, qmm_gemv, qmm_gemv_batch_prepare,
+from . import (QMM_OK, GemvDesc, _check, _stream, load, qmm_gemm, qmm_gemm_f16out, qmm_gemm_workspace_bytes, qmm_gemv, qmm_gemv_batch_prepare,
                qmm_gemv_swiglu, qmm_moe_swiglu, qmm_gemv_residual, qmm_moe_combine, qmm_gemm_grouped,
                qmm_gemm_grouped_workspace_bytes,
                qmm_gemv_batched, qmm_moe_gemm, qmm_unpack)
@@ -156,6 +159,13 @@ class GemvBatch:
         raw = np.frombuffer(bytes(self.host), dtype=np.uint8).copy()
         self.device = torch.from_numpy(raw).to(device)
         self.keep = items  # the buffers must outlive the batch
+        # The call's fixed arguments, converted once: a launch then costs one
+        # foreign call (the host time before the first launch of a timed
+        # region counts in it).
+        self._launch = functools.partial(load().qmm_gemv_batched, self.device.data_ptr(),
+                                         ctypes.addressof(self.host), len(self.host), bits, group)
 
     def __call__(self, stream=None) -> None:
-        qmm_gemv_batched(self.device, self.host, self.bits, self.group, stream=stream)
+        status = self._launch(_stream(stream))
+        if status != QMM_OK:
+            _check(status, "qmm_gemv_batched")
