@@ -176,6 +176,78 @@ __device__ __forceinline__ void accumulate_batch(const RowBatch<B, UNIT, XC, U>&
         }
 }
 
+// Activation units held once per work-group in LDS (XUNIT_LDS_WORDS words
+// per unit: the UNIT/2 pair words, the offset constant, the plain sum, two
+// words of padding).  A stride of 36 words puts the 16 units that the 16
+// lanes of a slot read at distinct bank quadruples, so the 16-byte reads are
+// conflict-free; the slots of a wave read the same units (broadcast).
+constexpr int XUNIT_LDS_WORDS = 36;
+template <int B, int UNIT>
+__device__ __forceinline__ void store_xunit_lds(const XUnit<B, UNIT>& xu, u32* dst) {
+    static_assert(UNIT / 2 + 2 <= XUNIT_LDS_WORDS, "unit layout");
+#pragma unroll
+    for (int i = 0; i < UNIT / 2; i += 4)
+        *reinterpret_cast<u32x4*>(dst + i) = u32x4{as_u32(xu.xp[i]), as_u32(xu.xp[i + 1]), as_u32(xu.xp[i + 2]),
+                                                    as_u32(xu.xp[i + 3])};
+    *reinterpret_cast<u32x4*>(dst + UNIT / 2) =
+        u32x4{__builtin_bit_cast(u32, xu.corr), __builtin_bit_cast(u32, xu.xsum), 0u, 0u};
+}
+template <int B, int UNIT>
+__device__ __forceinline__ void load_xunit_lds(const u32* src, XUnit<B, UNIT>& xu) {
+#pragma unroll
+    for (int i = 0; i < UNIT / 2; i += 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + i);
+        xu.xp[i] = as_h2(v[0]); xu.xp[i + 1] = as_h2(v[1]); xu.xp[i + 2] = as_h2(v[2]); xu.xp[i + 3] = as_h2(v[3]);
+    }
+    const u32x4 t = *reinterpret_cast<const u32x4*>(src + UNIT / 2);
+    // Elements go through plain scalars: this compiler resolves a bit cast
+    // of a vector element expression to element 0.
+    const u32 c0 = t[0], c1 = t[1];
+    xu.corr = __builtin_bit_cast(float, c0);
+    xu.xsum = __builtin_bit_cast(float, c1);
+}
+
+// accumulate_batch with the lane's activation units read from LDS (xl: the
+// work-group's units, unit u at xl + u * XUNIT_LDS_WORDS), one unit at a
+// time, so a lane never holds more than one unit's pairs.
+template <int B, int UNIT, int LPR, int XC, int U, bool WIDE>
+__device__ __forceinline__ void accumulate_batch_lds(const RowBatch<B, UNIT, XC, U>& bt, const u32* xl,
+                                                     const int (&unit)[XC], float (&yacc)[U], int slot, int gpr,
+                                                     const int (&gidx)[XC]) {
+    constexpr int SLOTS = 64 / LPR;
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+        XUnit<B, UNIT> xu;
+        load_xunit_lds<B, UNIT>(xl + unit[c] * XUNIT_LDS_WORDS, xu);
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            u32 sb = 0, mb = 0;
+            if constexpr (!has_affine<B>()) {
+            } else if constexpr (!WIDE) {
+                sb = bt.s[r][c];
+                mb = bt.m[r][c];
+            } else {
+                const int off = (r * SLOTS + slot) * gpr + gidx[c];
+                const int src = (off >> 1) << 2;
+                const u32 sw = (u32)__builtin_amdgcn_ds_bpermute(src, (int)bt.sblk);
+                const u32 mw = (u32)__builtin_amdgcn_ds_bpermute(src, (int)bt.mblk);
+                const u32 sh = (off & 1) << 4;
+                sb = (sw >> sh) & 0xFFFFu;
+                mb = (mw >> sh) & 0xFFFFu;
+            }
+            const float t = unit_qx<B, UNIT>(bt.w[r][c], xu);
+            if constexpr (has_affine<B>())
+                yacc[r] = __builtin_fmaf(scale_value<B>(sb), t,
+                                         __builtin_fmaf(half_bits_to_float((uint16_t)mb), xu.xsum, yacc[r]));
+            else
+                yacc[r] += t;
+        }
+        // One unit's pairs at a time: left alone, the scheduler hoists all
+        // three units' reads and the registers they were meant to save.
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Reduce the U row sums over the LPR lanes of each slot and store them.  The
 // store is unconditional: lanes with nothing to write aim past the end of y.
 template <int LPR, int U>
@@ -217,6 +289,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
                                                    const uint16_t* __restrict__ X,
                                                    out_ptr<RES> Y, int n, int k, int group, const float* R) {
     __shared__ float ystage_all[GEMV_WAVES_PER_BLOCK][STG ? YSTAGE : 1];
+    // Three units per lane (16 lanes x 3 units: rows of up to 48 units with
+    // no idle lane): the activation units live in LDS, built once per
+    // work-group, instead of three units' pairs in every lane's registers.
+    constexpr bool XL = XC == 3 && !MP && !STG;
+    __shared__ __attribute__((aligned(16))) u32 xl_all[XL ? LPR * XC * XUNIT_LDS_WORDS : 4];
     constexpr int SLOTS = 64 / LPR;
     const int lane = threadIdx.x & 63;
     const int slot = lane / LPR, j = lane % LPR;
@@ -284,6 +361,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
             }
         } else if constexpr (!STG) {
             units_of_pass(0);
+            if constexpr (XL) {
+                // Unit u (< LPR * XC) built by thread u; units past the row
+                // are zero.  Every wave reaches the barrier before any exits.
+                const int u = threadIdx.x;
+                if (u < LPR * XC) {
+                    XUnit<B, UNIT> t;
+                    prep_xunit<B, UNIT>(xr, u < nu ? (uint32_t)(u * UNIT * 2) : (uint32_t)k * 2u, t);
+                    store_xunit_lds<B, UNIT>(t, xl_all + u * XUNIT_LDS_WORDS);
+                }
+                __syncthreads();
+            }
             int rb = wave * SLOTS * U;
             if (rb >= n) return;
             RowBatch<B, UNIT, XC, U> ba, bb;
@@ -293,7 +381,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
             // The first batch's weight loads go out before the activation
             // loads and their set-up arithmetic.
             __builtin_amdgcn_sched_barrier(0);
-            prep();
+            if constexpr (!XL) prep();
             while (true) {
                 float yacc[U];
                 int nxt = rb + stride;
@@ -301,7 +389,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
                 load_res(nxt, nxt < n, rb_res);
 #pragma unroll
                 for (int r = 0; r < U; ++r) yacc[r] = 0.f;
-                accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(ba, xu, yacc, slot, gpr, gidx);
+                if constexpr (XL)
+                    accumulate_batch_lds<B, UNIT, LPR, XC, U, WIDE>(ba, xl_all, unit, yacc, slot, gpr, gidx);
+                else
+                    accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(ba, xu, yacc, slot, gpr, gidx);
                 store_batch<LPR, U>(yacc, yr, rb, n, slot, j, ra);
                 rb = nxt;
                 if (rb >= n) break;
@@ -310,7 +401,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
                 load_res(nxt, nxt < n, ra);
 #pragma unroll
                 for (int r = 0; r < U; ++r) yacc[r] = 0.f;
-                accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(bb, xu, yacc, slot, gpr, gidx);
+                if constexpr (XL)
+                    accumulate_batch_lds<B, UNIT, LPR, XC, U, WIDE>(bb, xl_all, unit, yacc, slot, gpr, gidx);
+                else
+                    accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(bb, xu, yacc, slot, gpr, gidx);
                 store_batch<LPR, U>(yacc, yr, rb, n, slot, j, rb_res);
                 rb = nxt;
                 if (rb >= n) break;

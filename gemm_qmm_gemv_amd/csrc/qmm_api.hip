@@ -205,11 +205,22 @@ LaneSplit choose_split(int nu, int max_xc, bool (*supported)(int, int)) {
 bool gemv_split_ok(int lpr, int xc) { return gemv_shape_supported(lpr, xc, 1); }
 bool rows_split_ok(int lpr, int xc) { return rows_shape_supported(lpr, xc, 1); }
 
-GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
+// three_unit_rows: the 16 x 3 layout is open to the caller (the fused
+// gate/up kernel has no such shape).
+GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus, bool three_unit_rows = true) {
     GemvShape sh{};
     sh.unit = unit_codes(bits, group);
     const int nu = (int)(k / sh.unit);
     LaneSplit ls = choose_split(nu, 3, gemv_split_ok);
+    // Rows of 33 to 48 units (K = 3072 at 64-code units): 16 lanes with three
+    // units each, whose activation units the work-group keeps in LDS, leave
+    // no lane idle where 64-lane rows idle a quarter of the wave.  Measured
+    // on the Llama-3.2-3B shapes (K = 3072): LM head Q2 30.9 -> 27.3 us, Q3
+    // 39.4 -> 35.3, Q4 43.5 -> 42.6; 8192 x 3072 Q2/Q3/Q4 5.9/6.5/6.2 ->
+    // 5.3/5.5/5.8 us; 3072 x 3072 4.8/4.9/4.9 -> 4.3/4.2/4.3 us.
+    if (three_unit_rows && !ls.multipass && ls.lpr == 64 && ls.xc == 1 && nu > 32 && nu <= 48 &&
+        gemv_split_ok(16, 3))
+        ls = {16, 3, false};
     const int el = override_or(OV_GEMV_LPR, 0), ex = override_or(OV_GEMV_XC, 0);
     if (el > 0 && ex > 0 && gemv_split_ok(el, ex)) ls = {el, ex, el * ex < nu};
     sh.lpr = ls.lpr;
@@ -239,8 +250,9 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     // keep the occupancy-sized grid.
     const int wpc_default = batches <= (int64_t)16 * cus ? 8 : 0;
     // 64-lane rows with at least 16 batches per CU stage their row sums in
-    // LDS (Llama-3.2-3B shapes at Q4: the 128256 x 3072 LM head 41.7 -> 41.4
-    // us, 8192 x 3072 6.54 -> 6.15 us; Q2 31.9 -> 30.6 and 6.35 -> 6.05 us);
+    // LDS (measured when K = 3072 rows still took 64 lanes, at Q4: the
+    // 128256 x 3072 LM head 41.7 -> 41.4 us, 8192 x 3072 6.54 -> 6.15 us; Q2
+    // 31.9 -> 30.6 and 6.35 -> 6.05 us; they now take 16 x 3 above);
     // with fewer batches per wave the staging round trip costs more than
     // the stores it moves (1024 x 3072: 3.9 -> 4.3 us), and 16-lane rows
     // lose by it too (151936 x 1024: 17.6 -> 18.2 us).
@@ -571,7 +583,7 @@ qmm_status qmm_gemv_swiglu(const void* gate_w, const void* gate_scales, const vo
     if (!aligned(x, 16) || !aligned(h, 16)) return fail(QMM_ERR_MISALIGNED, "x or h not 16-byte aligned");
     int cus = 0;
     if ((st = device_cus(&cus)) != QMM_OK) return st;
-    GemvShape sh = plan_gemv(n, k, bits, group_size, cus);
+    GemvShape sh = plan_gemv(n, k, bits, group_size, cus, false);
     if (sh.multipass || !glu_shape_supported(sh.lpr, sh.xc))
         return fail(QMM_ERR_UNSUPPORTED, "k=%lld needs more than one pass of the fused gate/up kernel",
                     (long long)k);

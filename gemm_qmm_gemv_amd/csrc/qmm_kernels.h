@@ -177,7 +177,7 @@ struct BatchArgs {
 // per lane, rows per slot) for the GEMV kernels, (lanes, units, activation
 // rows) for the multi-row kernel.
 #define QMM_GEMV_SHAPES(X) \
-    X(16, 1, 1) X(16, 1, 2) X(16, 3, 1) \
+    X(16, 1, 1) X(16, 1, 2) X(16, 3, 1) X(16, 3, 2) \
     X(32, 1, 1) X(32, 1, 2) \
     X(64, 1, 1) X(64, 1, 2) \
     X(64, 2, 1)

@@ -228,7 +228,7 @@ def test_staged_single_gemv_exact_and_residual(bits):
     import torch
     import gemm_qmm_gemv_amd as qmm
     from gemm_qmm_gemv_amd import tensors
-    n, k = 8195, 3072
+    n, k = 8195, 4096
     pl = qmm.qmm_get_plan(0, 1, n, k, bits, 64, cu_count=256)
     assert pl["staged"] and pl["lanes_per_row"] == 64
     qe = _exact_matrix(n, k, bits, (105, bits))

@@ -178,3 +178,33 @@ def test_gemv_three_units_per_lane(qmm_override, bits, n, k):
         ye = _run_gemv(qe, xi)
         y_ref, _ = oracle.qmm(w, s, mn, xi, n, k, bits, 64)
         assert np.array_equal(ye.astype(np.float64), y_ref)
+
+
+@pytest.mark.parametrize("bits", (2, 3, 4, 8))
+def test_gemv_k3072_takes_16x3_exact_and_residual(bits):
+    """K = 3072 rows (48 units) are planned as 16 lanes x 3 units with the
+    activation units in LDS: exact integers bit for bit, and the fused
+    residual added in place, on a ragged row count."""
+    import gemm_qmm_gemv_amd as qmm
+    torch = _torch()
+    from gemm_qmm_gemv_amd import tensors
+    n, k = 1029, 3072
+    pl = qmm.qmm_get_plan(0, 1, n, k, bits, 64)
+    assert (pl["lanes_per_row"], pl["units_per_lane"], pl["multipass"]) == (16, 3, False)
+    rng = inputs.rng_for(56, n, k, bits)
+    w = inputs.packed_words(rng, n, k, bits)
+    s = np.ones((n, k // 64), dtype=np.float16)
+    mn = np.zeros((n, k // 64), dtype=np.float16)
+    xi = rng.integers(-2, 3, size=k).astype(np.float16)
+    qe = {"w": w, "scales": s, "mins": mn, "n": n, "k": k, "bits": bits, "group": 64}
+    announce("gemv-k3072-16x3", bits, n, k)
+    dq, xd = tensors.upload_matrix(qe), tensors.device_tensor(xi)
+    y = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    tensors.gemv(dq, xd, y)
+    r = rng.integers(-1000, 1000, size=n).astype(np.float32)
+    rd = tensors.device_tensor(r)
+    tensors.gemv_residual(dq, xd, rd, rd)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.qmm(w, s, mn, xi, n, k, bits, 64)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), y_ref.reshape(-1))
+    assert np.array_equal(rd.cpu().numpy().astype(np.float64), y_ref.reshape(-1) + r.astype(np.float64))
