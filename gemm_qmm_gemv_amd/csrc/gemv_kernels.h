@@ -53,7 +53,7 @@ template <int B, int UNIT, int LPR, int XC, int U, bool RES>
 __device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const uint16_t* Mn,
                                          const uint16_t* X, float* Y, int n, int k, int group, int b0,
                                          int b1, int lane, float* ystage, int base, int bstride,
-                                         const float* R);
+                                         const float* R, const u32* xl = nullptr);
 
 // a / group for the group size, a wave-uniform kernel argument: a shift for
 // the usual power-of-two sizes (a uniform branch), a division otherwise.
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
     // Three units per lane (16 lanes x 3 units: rows of up to 48 units with
     // no idle lane): the activation units live in LDS, built once per
     // work-group, instead of three units' pairs in every lane's registers.
-    constexpr bool XL = XC == 3 && !MP && !STG;
+    constexpr bool XL = XC == 3 && !MP;
     __shared__ __attribute__((aligned(16))) u32 xl_all[XL ? LPR * XC * XUNIT_LDS_WORDS : 4];
     constexpr int SLOTS = 64 / LPR;
     const int lane = threadIdx.x & 63;
@@ -321,6 +321,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
         }
     };
 
+    if constexpr (XL) {
+        // Unit u (< LPR * XC) built by thread u; units past the row are
+        // zero.  Every wave reaches the barrier before any exits.
+        const int u = threadIdx.x;
+        if (u < LPR * XC) {
+            XUnit<B, UNIT> t;
+            prep_xunit<B, UNIT>(xr, u < nu ? (uint32_t)(u * UNIT * 2) : (uint32_t)k * 2u, t);
+            store_xunit_lds<B, UNIT>(t, xl_all + u * XUNIT_LDS_WORDS);
+        }
+        __syncthreads();
+    }
     XUnit<B, UNIT> xu[XC];
     int unit[XC], gidx[XC];
     auto units_of_pass = [&](int pass) {
@@ -361,17 +372,6 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
             }
         } else if constexpr (!STG) {
             units_of_pass(0);
-            if constexpr (XL) {
-                // Unit u (< LPR * XC) built by thread u; units past the row
-                // are zero.  Every wave reaches the barrier before any exits.
-                const int u = threadIdx.x;
-                if (u < LPR * XC) {
-                    XUnit<B, UNIT> t;
-                    prep_xunit<B, UNIT>(xr, u < nu ? (uint32_t)(u * UNIT * 2) : (uint32_t)k * 2u, t);
-                    store_xunit_lds<B, UNIT>(t, xl_all + u * XUNIT_LDS_WORDS);
-                }
-                __syncthreads();
-            }
             int rb = wave * SLOTS * U;
             if (rb >= n) return;
             RowBatch<B, UNIT, XC, U> ba, bb;
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
         if (wave >= batches) return;
         const int nb = (batches - wave + nwaves - 1) / nwaves;
         gemv_run<B, UNIT, LPR, XC, U, RES>(W, S, Mn, X, Y, n, k, group, 0, nb, lane, ystage_all[threadIdx.x >> 6],
-                                           wave, nwaves, R);
+                                           wave, nwaves, R, XL ? xl_all : nullptr);
     } else if (wide_scales_ok<LPR, U>(S, Mn, gpr)) {
         body(std::true_type{});
     } else {
@@ -853,7 +853,10 @@ template <int B, int UNIT, int LPR, int XC, int U, bool WIDE, bool RES>
 __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, const uint16_t* Mn,
                                            const uint16_t* X, float* Y, int n, int k, int group,
                                            int b0, int b1, int lane, float* ystage, int base, int bstride,
-                                           const float* R) {
+                                           const float* R, const u32* xl) {
+    // Three units per lane: the activation units come from the work-group's
+    // LDS copy (xl), one at a time, instead of the lane's registers.
+    constexpr bool XL = XC == 3;
     constexpr int SLOTS = 64 / LPR;
     constexpr int ROWS = SLOTS * U;
     auto row_of = [&](int b) { return (base + b * bstride) * ROWS; };
@@ -878,9 +881,11 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
     __builtin_amdgcn_sched_barrier(0);
     // Units past the row read zeros: the all-zero unit state, branch-free.
     XUnit<B, UNIT> xu[XC];
+    if constexpr (!XL) {
 #pragma unroll
-    for (int c = 0; c < XC; ++c)
-        prep_xunit<B, UNIT>(xr, unit[c] < nu ? (uint32_t)(unit[c] * UNIT * 2) : (uint32_t)k * 2u, xu[c]);
+        for (int c = 0; c < XC; ++c)
+            prep_xunit<B, UNIT>(xr, unit[c] < nu ? (uint32_t)(unit[c] * UNIT * 2) : (uint32_t)k * 2u, xu[c]);
+    }
     // The batch range is wave-uniform; saying so keeps the loop a scalar loop
     // (no per-lane exit masks).
     b0 = uniform(b0);
@@ -915,7 +920,10 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
         float yacc[U];
 #pragma unroll
         for (int r = 0; r < U; ++r) yacc[r] = 0.f;
-        accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(bt, xu, yacc, slot, gpr, gidx);
+        if constexpr (XL)
+            accumulate_batch_lds<B, UNIT, LPR, XC, U, WIDE>(bt, xl, unit, yacc, slot, gpr, gidx);
+        else
+            accumulate_batch<B, UNIT, LPR, XC, U, WIDE>(bt, xu, yacc, slot, gpr, gidx);
 #pragma unroll
         for (int r = 0; r < U; ++r) ystage[(b - bf) * ROWS + r * SLOTS + slot] = group_sum<LPR>(yacc[r]);
     };
@@ -944,13 +952,13 @@ template <int B, int UNIT, int LPR, int XC, int U, bool RES>
 __device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const uint16_t* Mn,
                                          const uint16_t* X, float* Y, int n, int k, int group, int b0,
                                          int b1, int lane, float* ystage, int base, int bstride,
-                                         const float* R) {
+                                         const float* R, const u32* xl) {
     if (wide_scales_ok<LPR, U>(S, Mn, div_group(k, group)))
         gemv_run_w<B, UNIT, LPR, XC, U, true, RES>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage, base,
-                                                   bstride, R);
+                                                   bstride, R, xl);
     else
         gemv_run_w<B, UNIT, LPR, XC, U, false, RES>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage, base,
-                                                    bstride, R);
+                                                    bstride, R, xl);
 }
 
 template <int B, int UNIT, int XC, int U>
@@ -1063,7 +1071,7 @@ hipError_t launch_gemv_t(const GemvArgs& a, const GemvShape& sh, hipStream_t st)
         if (a.r) return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, true, true>>(a, sh, st);
         return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, true, false>>(a, sh, st);
     }
-    if constexpr (LPR == 64) {
+    if constexpr (LPR == 64 || (LPR == 16 && XC == 3)) {
         if (sh.staged) {
             if (a.r) return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, false, true, true>>(a, sh, st);
             return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, false, false, true>>(a, sh, st);

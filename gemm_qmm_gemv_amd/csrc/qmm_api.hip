@@ -256,9 +256,15 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus, bool thr
     // with fewer batches per wave the staging round trip costs more than
     // the stores it moves (1024 x 3072: 3.9 -> 4.3 us), and 16-lane rows
     // lose by it too (151936 x 1024: 17.6 -> 18.2 us).
-    sh.staged = !sh.multipass && sh.lpr == 64 && batches >= (int64_t)16 * cus;
+    // 16 x 3 rows stage too, from Q4 up: the staged loop's extra registers
+    // (143 instead of 128 VGPRs: three waves per SIMD instead of four) cost
+    // more than the stores it moves where the weights are fewest bytes per
+    // instruction (the 128256 x 3072 LM head: Q4 43.1 -> 41.4 us staged, Q2
+    // 27.3 -> 28.9, Q3 35.3 -> 35.6).
+    const bool stageable = sh.lpr == 64 || (sh.lpr == 16 && sh.xc == 3 && bits >= 4);
+    sh.staged = !sh.multipass && stageable && batches >= (int64_t)16 * cus;
     const int es = override_or(OV_GEMV_STAGED, -1);
-    if (es >= 0) sh.staged = es == 1 && !sh.multipass && sh.lpr == 64;
+    if (es >= 0) sh.staged = es == 1 && !sh.multipass && stageable;
     sh.waves_per_cu = override_or(OV_GEMV_WAVES_PER_CU, wpc_default);
     // Reported grid: the cap assumes 16 resident waves per CU; the launch
     // uses the kernel's real occupancy.

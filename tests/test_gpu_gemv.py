@@ -208,3 +208,41 @@ def test_gemv_k3072_takes_16x3_exact_and_residual(bits):
     y_ref, _ = oracle.qmm(w, s, mn, xi, n, k, bits, 64)
     assert np.array_equal(y.cpu().numpy().astype(np.float64), y_ref.reshape(-1))
     assert np.array_equal(rd.cpu().numpy().astype(np.float64), y_ref.reshape(-1) + r.astype(np.float64))
+
+
+@pytest.mark.parametrize("bits", (2, 3, 4, 8))
+@pytest.mark.parametrize("staged", (0, 1))
+def test_gemv_16x3_staged_and_unstaged_exact(qmm_override, bits, staged):
+    """The 16 x 3 layout through both loops -- row sums staged in LDS (Q4 and
+    wider) and stored per batch -- with every output NaN-prefilled: exact
+    integers bit for bit, the residual added in place."""
+    import gemm_qmm_gemv_amd as qmm
+    torch = _torch()
+    from gemm_qmm_gemv_amd import tensors
+    qmm_override("QMM_GEMV_STAGED", staged)
+    n, k = 8195, 3072
+    pl = qmm.qmm_get_plan(0, 1, n, k, bits, 64)
+    assert (pl["lanes_per_row"], pl["units_per_lane"]) == (16, 3)
+    assert pl["staged"] == (bool(staged) and bits >= 4)
+    rng = inputs.rng_for(57, n, k, bits)
+    w = inputs.packed_words(rng, n, k, bits)
+    s = np.ones((n, k // 64), dtype=np.float16)
+    mn = np.zeros((n, k // 64), dtype=np.float16)
+    xi = rng.integers(-2, 3, size=k).astype(np.float16)
+    qe = {"w": w, "scales": s, "mins": mn, "n": n, "k": k, "bits": bits, "group": 64}
+    announce("gemv-16x3-staged", staged, bits)
+    dq, xd = tensors.upload_matrix(qe), tensors.device_tensor(xi)
+    y = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    tensors.gemv(dq, xd, y)
+    r = rng.integers(-1000, 1000, size=n).astype(np.float32)
+    rd = tensors.device_tensor(r)
+    tensors.gemv_residual(dq, xd, rd, rd)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.qmm(w, s, mn, xi, n, k, bits, 64)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), y_ref.reshape(-1))
+    assert np.array_equal(rd.cpu().numpy().astype(np.float64), y_ref.reshape(-1) + r.astype(np.float64))
+    q = inputs.quantized_matrix(n, k, bits, 64, key=(58, bits))
+    x = inputs.activation_rows(1, k, key=(58, bits))[0]
+    yq = _run_gemv(q, x)
+    y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, 64)
+    assert_within(yq, y_ref, a_ref, "gemv 16x3 staged=%d b%d" % (staged, bits))
