@@ -49,11 +49,29 @@ constexpr int GEMV_WAVES_PER_BLOCK = 4;
 // (Both the batched launch and the single GEMV run their rows this way.)
 constexpr int YSTAGE = 256;
 
-template <int B, int UNIT, int LPR, int XC, int U, bool RES>
+// XLDS: the activation units come from the work-group's LDS copy xl (see
+// gemv_kernel) instead of every lane's registers.
+template <int B, int UNIT, int LPR, int XC, int U, bool RES, bool XLDS = false>
 __device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const uint16_t* Mn,
                                          const uint16_t* X, float* Y, int n, int k, int group, int b0,
                                          int b1, int lane, float* ystage, int base, int bstride,
                                          const float* R, const u32* xl = nullptr);
+
+// Single GEMVs over quantized weights keep the row's activation units once
+// per work-group in LDS: building them in every lane (a strided read of the
+// whole of x per wave, and its conversion) costs more than reading them back
+// from LDS for each row batch, most where a wave has few batches.  Measured
+// (cache-busted, one launch, Q4 unless named): 3072 x 8192 8.1 -> 6.0 us
+// (Q2 7.6 -> 5.5, Q8 9.8 -> 8.1), 2048 x 8192 7.9 -> 5.3, 8192 x 2048 5.95 ->
+// 5.00, 4096 x 4096 5.91 -> 5.13, 3072 x 1024 3.97 -> 3.51, 1024 x 1024 3.82
+// -> 3.35, 151936 x 1024 Q2 13.4 -> 12.6; the staged 64 x 1 rows of the
+// larger matrices lose a little (8192 x 4096 6.6 -> 6.8, 65536 x 4096 27.2 ->
+// 27.6).  fp16 weights keep their registers except in 16 x 3 rows (in LDS,
+// 3072 x 3072 5.8 -> 6.1 us and 65536 x 3072 65.2 -> 66.6 at 64 x 2).
+template <int B, int LPR, int XC>
+constexpr bool xunits_in_lds() {
+    return XC == 3 || B < 16;
+}
 
 // a / group for the group size, a wave-uniform kernel argument: a shift for
 // the usual power-of-two sizes (a uniform branch), a division otherwise.
@@ -289,10 +307,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
                                                    const uint16_t* __restrict__ X,
                                                    out_ptr<RES> Y, int n, int k, int group, const float* R) {
     __shared__ float ystage_all[GEMV_WAVES_PER_BLOCK][STG ? YSTAGE : 1];
-    // Three units per lane (16 lanes x 3 units: rows of up to 48 units with
-    // no idle lane): the activation units live in LDS, built once per
-    // work-group, instead of three units' pairs in every lane's registers.
-    constexpr bool XL = XC == 3 && !MP;
+    // Two or three units per lane: the activation units live in LDS, built
+    // once per work-group, instead of each unit's pairs in every lane's
+    // registers.
+    constexpr bool XL = xunits_in_lds<B, LPR, XC>() && !MP;
     __shared__ __attribute__((aligned(16))) u32 xl_all[XL ? LPR * XC * XUNIT_LDS_WORDS : 4];
     constexpr int SLOTS = 64 / LPR;
     const int lane = threadIdx.x & 63;
@@ -418,8 +436,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
         const int batches = (n + ROWS - 1) / ROWS;
         if (wave >= batches) return;
         const int nb = (batches - wave + nwaves - 1) / nwaves;
-        gemv_run<B, UNIT, LPR, XC, U, RES>(W, S, Mn, X, Y, n, k, group, 0, nb, lane, ystage_all[threadIdx.x >> 6],
-                                           wave, nwaves, R, XL ? xl_all : nullptr);
+        gemv_run<B, UNIT, LPR, XC, U, RES, XL>(W, S, Mn, X, Y, n, k, group, 0, nb, lane,
+                                               ystage_all[threadIdx.x >> 6], wave, nwaves, R, xl_all);
     } else if (wide_scales_ok<LPR, U>(S, Mn, gpr)) {
         body(std::true_type{});
     } else {
@@ -849,14 +867,11 @@ __device__ __forceinline__ int batched_lanes_per_row(int nu) {
 // LDS area.  RES: R holds an fp32 residual [n] added to every output at the
 // flush (R may be Y: a row's residual is read by the lane that then writes
 // the row).
-template <int B, int UNIT, int LPR, int XC, int U, bool WIDE, bool RES>
+template <int B, int UNIT, int LPR, int XC, int U, bool WIDE, bool RES, bool XL>
 __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, const uint16_t* Mn,
                                            const uint16_t* X, float* Y, int n, int k, int group,
                                            int b0, int b1, int lane, float* ystage, int base, int bstride,
                                            const float* R, const u32* xl) {
-    // Three units per lane: the activation units come from the work-group's
-    // LDS copy (xl), one at a time, instead of the lane's registers.
-    constexpr bool XL = XC == 3;
     constexpr int SLOTS = 64 / LPR;
     constexpr int ROWS = SLOTS * U;
     auto row_of = [&](int b) { return (base + b * bstride) * ROWS; };
@@ -948,17 +963,17 @@ __device__ __forceinline__ void gemv_run_w(const u32* W, const uint16_t* S, cons
     }
 }
 
-template <int B, int UNIT, int LPR, int XC, int U, bool RES>
+template <int B, int UNIT, int LPR, int XC, int U, bool RES, bool XLDS>
 __device__ __forceinline__ void gemv_run(const u32* W, const uint16_t* S, const uint16_t* Mn,
                                          const uint16_t* X, float* Y, int n, int k, int group, int b0,
                                          int b1, int lane, float* ystage, int base, int bstride,
                                          const float* R, const u32* xl) {
     if (wide_scales_ok<LPR, U>(S, Mn, div_group(k, group)))
-        gemv_run_w<B, UNIT, LPR, XC, U, true, RES>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage, base,
-                                                   bstride, R, xl);
+        gemv_run_w<B, UNIT, LPR, XC, U, true, RES, XLDS>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage,
+                                                         base, bstride, R, xl);
     else
-        gemv_run_w<B, UNIT, LPR, XC, U, false, RES>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage, base,
-                                                    bstride, R, xl);
+        gemv_run_w<B, UNIT, LPR, XC, U, false, RES, XLDS>(W, S, Mn, X, Y, n, k, group, b0, b1, lane, ystage,
+                                                          base, bstride, R, xl);
 }
 
 template <int B, int UNIT, int XC, int U>
