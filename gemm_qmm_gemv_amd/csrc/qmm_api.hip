@@ -205,9 +205,7 @@ LaneSplit choose_split(int nu, int max_xc, bool (*supported)(int, int)) {
 bool gemv_split_ok(int lpr, int xc) { return gemv_shape_supported(lpr, xc, 1); }
 bool rows_split_ok(int lpr, int xc) { return rows_shape_supported(lpr, xc, 1); }
 
-// three_unit_rows: the 16 x 3 layout is open to the caller (the fused
-// gate/up kernel has no such shape).
-GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus, bool three_unit_rows = true) {
+GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     GemvShape sh{};
     sh.unit = unit_codes(bits, group);
     const int nu = (int)(k / sh.unit);
@@ -218,7 +216,7 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus, bool thr
     // on the Llama-3.2-3B shapes (K = 3072): LM head Q2 30.9 -> 27.3 us, Q3
     // 39.4 -> 35.3, Q4 43.5 -> 42.6; 8192 x 3072 Q2/Q3/Q4 5.9/6.5/6.2 ->
     // 5.3/5.5/5.8 us; 3072 x 3072 4.8/4.9/4.9 -> 4.3/4.2/4.3 us.
-    if (three_unit_rows && !ls.multipass && ls.lpr == 64 && ls.xc == 1 && nu > 32 && nu <= 48 &&
+    if (!ls.multipass && ls.lpr == 64 && ls.xc == 1 && nu > 32 && nu <= 48 &&
         gemv_split_ok(16, 3))
         ls = {16, 3, false};
     const int el = override_or(OV_GEMV_LPR, 0), ex = override_or(OV_GEMV_XC, 0);
@@ -589,7 +587,7 @@ qmm_status qmm_gemv_swiglu(const void* gate_w, const void* gate_scales, const vo
     if (!aligned(x, 16) || !aligned(h, 16)) return fail(QMM_ERR_MISALIGNED, "x or h not 16-byte aligned");
     int cus = 0;
     if ((st = device_cus(&cus)) != QMM_OK) return st;
-    GemvShape sh = plan_gemv(n, k, bits, group_size, cus, false);
+    GemvShape sh = plan_gemv(n, k, bits, group_size, cus);
     if (sh.multipass || !glu_shape_supported(sh.lpr, sh.xc))
         return fail(QMM_ERR_UNSUPPORTED, "k=%lld needs more than one pass of the fused gate/up kernel",
                     (long long)k);

@@ -186,7 +186,7 @@ struct BatchArgs {
 // compiled shapes are (units per lane, rows per slot).
 // (lanes per row, units per lane) of the fused gate/up kernel: single pass,
 // one row per slot and iteration (two with both matrices).
-#define QMM_GLU_SHAPES(X) X(16, 1) X(32, 1) X(64, 1) X(64, 2)
+#define QMM_GLU_SHAPES(X) X(16, 1) X(16, 3) X(32, 1) X(64, 1) X(64, 2)
 constexpr bool glu_shape_supported(int lpr, int xc) {
 #define X(L, C) if (lpr == L && xc == C) return true;
     QMM_GLU_SHAPES(X)

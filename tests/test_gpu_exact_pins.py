@@ -13,8 +13,9 @@ tolerance:
 
 Covered here: the batched launch (mixed K: 16, 32 and 64 lanes per row, two
 units per lane), the expert-rows kernel (one and two activation rows per
-batch), the m = 2 GEMM route (the same kernel), and the residual variant
-(r = 0 and integer r)."""
+batch), the m = 2 GEMM route (the same kernel), the residual variant
+(r = 0 and integer r), and the fused gate/up kernel (a gate sum of at least
+32, where silu is the identity in fp32)."""
 import numpy as np
 import pytest
 
@@ -244,3 +245,36 @@ def test_staged_single_gemv_exact_and_residual(bits):
     y_ref, _ = oracle.qmm(qe["w"], qe["scales"], qe["mins"], xe, n, k, bits, 64)
     assert np.array_equal(y.cpu().numpy().astype(np.float64), y_ref.reshape(-1))
     assert np.array_equal(rd.cpu().numpy().astype(np.float64), y_ref.reshape(-1) + r.astype(np.float64))
+
+
+# Fused gate/up: lanes per row x units per lane for each K.
+GLU_SHAPES = [(1029, 1024, (16, 1)), (1000, 2048, (32, 1)), (1029, 3072, (16, 3)), (515, 4096, (64, 1)),
+              (515, 8192, (64, 2))]
+
+
+@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6, 8))
+@pytest.mark.parametrize("n,k,layout", GLU_SHAPES)
+def test_swiglu_exact(bits, n, k, layout):
+    # Exact integers with non-negative activations x in {0, 1, 2}: both sums
+    # are integers below 2^24, and the gate sum is at least 32, where
+    # exp(-g) vanishes beside 1 in fp32, so silu(g) = g / 1 = g exactly and
+    # h = g * u rounds once: the fused kernel must match fp32(g * u) bit for
+    # bit.  A dropped or misplaced unit, group or row changes g or u by an
+    # integer and h by at least u or g.
+    import torch
+    import gemm_qmm_gemv_amd as qmm
+    from gemm_qmm_gemv_amd import tensors
+    pl = qmm.qmm_get_plan(0, 1, n, k, bits, 64, cu_count=256)
+    assert (pl["lanes_per_row"], pl["units_per_lane"], pl["multipass"]) == layout + (False,)
+    g = _exact_matrix(n, k, bits, (108, bits, k))
+    u = _exact_matrix(n, k, bits, (109, bits, k))
+    x = inputs.rng_for(110, bits, k).integers(0, 3, size=k).astype(np.float16)
+    g_ref, _ = oracle.qmm(g["w"], g["scales"], g["mins"], x, n, k, bits, 64)
+    u_ref, _ = oracle.qmm(u["w"], u["scales"], u["mins"], x, n, k, bits, 64)
+    assert g_ref.min() >= 32
+    announce("swiglu-exact", bits, n, k)
+    h = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    tensors.gemv_swiglu(tensors.upload_matrix(g), tensors.upload_matrix(u), tensors.device_tensor(x), h)
+    torch.cuda.synchronize()
+    h_ref = (g_ref.reshape(-1) * u_ref.reshape(-1)).astype(np.float32)
+    assert np.array_equal(h.cpu().numpy(), h_ref)
