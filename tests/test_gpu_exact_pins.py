@@ -14,8 +14,8 @@ tolerance:
 Covered here: the batched launch (mixed K: 16, 32 and 64 lanes per row, two
 units per lane), the expert-rows kernel (one and two activation rows per
 batch), the m = 2 GEMM route (the same kernel), the residual variant
-(r = 0 and integer r), and the fused gate/up kernel (a gate sum of at least
-32, where silu is the identity in fp32)."""
+(r = 0 and integer r), and the fused gate/up kernels, single and expert
+rows (a gate sum of at least 32, where silu is the identity in fp32)."""
 import numpy as np
 import pytest
 
@@ -278,3 +278,31 @@ def test_swiglu_exact(bits, n, k, layout):
     torch.cuda.synchronize()
     h_ref = (g_ref.reshape(-1) * u_ref.reshape(-1)).astype(np.float32)
     assert np.array_equal(h.cpu().numpy(), h_ref)
+
+
+@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6, 8))
+@pytest.mark.parametrize("k", (1024, 2048))
+@pytest.mark.parametrize("per_expert", (1, 3), ids=("one_row", "rows_pairs"))
+def test_moe_swiglu_exact(bits, k, per_expert):
+    # The fused gate/up rows with exact integers and activations in {0, 1, 2}:
+    # every gate sum is at least 32, where silu is the identity in fp32, so
+    # each output must equal fp32(g * u) bit for bit (16 and 32 lanes per
+    # row; one and two activation rows per batch, a ragged last batch).
+    import torch
+    from gemm_qmm_gemv_amd import tensors
+    e, n = 6, 130
+    gs = _exact_stack(e, n, k, bits, (111, bits, k))
+    us = _exact_stack(e, n, k, bits, (112, bits, k))
+    offsets = np.concatenate([[0], np.cumsum([per_expert] * e)]).astype(np.int32)
+    p = int(offsets[-1])
+    x = inputs.rng_for(113, bits, k).integers(0, 3, size=(4, k)).astype(np.float16)
+    x_rows = inputs.rng_for(114, bits, k).integers(0, 4, size=p).astype(np.int32)
+    g_ref, _ = oracle.moe(gs["w"], gs["scales"], gs["mins"], x, x_rows, offsets, e, n, k, bits, 64)
+    u_ref, _ = oracle.moe(us["w"], us["scales"], us["mins"], x, x_rows, offsets, e, n, k, bits, 64)
+    assert g_ref.min() >= 32
+    announce("moe-swiglu-exact", bits, k, per_expert)
+    h = torch.full((p, n), float("nan"), dtype=torch.float32, device="cuda")
+    tensors.moe_swiglu(tensors.upload_matrix(gs), tensors.upload_matrix(us), tensors.device_tensor(x),
+                       tensors.device_tensor(x_rows), tensors.device_tensor(offsets), p, h=h)
+    torch.cuda.synchronize()
+    assert np.array_equal(h.cpu().numpy(), (g_ref * u_ref).astype(np.float32))
