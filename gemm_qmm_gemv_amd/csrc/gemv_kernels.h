@@ -73,6 +73,18 @@ constexpr bool xunits_in_lds() {
     return XC == 3 || B < 16;
 }
 
+// Work-group barrier for LDS data only: waits for this wave's LDS traffic,
+// not for its vector-memory loads in flight (a __syncthreads also drains
+// those).  The wait is the builtin, so the compiler's own bookkeeping knows
+// of it; the barrier is an asm statement with a memory clobber, so no load
+// or store moves across it.
+__device__ __forceinline__ void lds_barrier() {
+    // s_waitcnt fields: vmcnt bits 3:0 and 15:14 (63: no wait), expcnt 6:4
+    // (7: no wait), lgkmcnt 11:8 (0).
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (7 << 4));
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // a / group for the group size, a wave-uniform kernel argument: a shift for
 // the usual power-of-two sizes (a uniform branch), a division otherwise.
 // The division's set-up had put dozens of instructions between the
@@ -341,7 +353,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
 
     if constexpr (XL) {
         // Unit u (< LPR * XC) built by thread u; units past the row are
-        // zero.  Every wave reaches the barrier before any exits.
+        // zero.  Every wave reaches the barrier before any exits.  (Issuing
+        // the first weight loads before this, as the fused gate/up kernel
+        // does, measured slower here: 3072 x 1024 3.45 -> 3.58 us, 8192 x
+        // 2048 Q2 4.67 -> 5.30; 3072 x 8192 6.05 -> 5.85.)
         const int u = threadIdx.x;
         if (u < LPR * XC) {
             XUnit<B, UNIT> t;
@@ -489,33 +504,45 @@ __global__ __launch_bounds__(256) void gemv_glu_kernel(
     }
     XUnit<B, UNIT> xu[XC];
     // Activation units in LDS, built once per work-group, where the single
-    // GEMV keeps them there (the same layouts).  Every wave reaches the
-    // barrier before any exits.  Measured (Q4 unless named, two matrices,
+    // GEMV keeps them there (the same layouts; one spare unit, see below).
+    // Every wave reaches the barrier before any exits.  Measured (Q4 unless named, two matrices,
     // cache-busted): 3072 x 1024 4.60 -> 4.00 us, 8192 x 2048 7.22 -> 6.67,
     // 3072 x 8192 10.71 -> 8.73, 14336 x 4096 15.00 -> 14.64; 8192 x 3072 on
     // 16 x 3 rows instead of 64 x 1, Q4 9.27 -> 8.75, Q2 8.81 -> 6.94.
     constexpr bool XL = xunits_in_lds<B, LPR, XC>();
-    __shared__ __attribute__((aligned(16))) u32 xl_all[XL ? LPR * XC * XUNIT_LDS_WORDS : 4];
-    if constexpr (XL) {
-        const int u = threadIdx.x;
-        if (u < LPR * XC) {
-            XUnit<B, UNIT> t;
-            prep_xunit<B, UNIT>(xr, u < nu ? (uint32_t)(u * UNIT * 2) : (uint32_t)k * 2u, t);
-            store_xunit_lds<B, UNIT>(t, xl_all + u * XUNIT_LDS_WORDS);
-        }
-        __syncthreads();
-    }
+    __shared__ __attribute__((aligned(16))) u32 xl_all[XL ? (LPR * XC + 1) * XUNIT_LDS_WORDS : 4];
 
     auto body = [&](auto wide_c) {
         constexpr bool WIDE = decltype(wide_c)::value;
         using RB = RowBatch<B, UNIT, XC, 1>;
         int rb = wave * SLOTS;
-        if (rb >= n) return;
+        if (!XL && rb >= n) return;
+        // Activation words first, then the weights; the units are built and
+        // shared behind an LDS-only barrier while the weights are in flight
+        // (loads complete in order, so waiting on the activation words does
+        // not wait on the weights).  Every thread builds one unit, those
+        // past LPR * XC (zeros, no memory traffic) into a spare slot, so no
+        // branch holds a load.  Measured against building the units before
+        // any weight load (Q4): 3072 x 1024 3.99 -> 3.77 us, 8192 x 2048 6.72
+        // -> 6.44, 8192 x 3072 8.82 -> 8.48, 3072 x 8192 8.80 -> 8.45.
+        const int xb = (int)threadIdx.x < LPR * XC ? (int)threadIdx.x : LPR * XC;
+        u32 xw[XL ? UNIT / 2 : 1];
+        if constexpr (XL) {
+            buffer_words<UNIT / 2, 16>(xr, xb < nu ? (uint32_t)(xb * UNIT * 2) : (uint32_t)k * 2u, xw);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         RB ga, ua, gb, ub;
-        load_batch<B, UNIT, LPR, XC, 1, WIDE>(ga, mg, rb, true, wpr, gpr, slot, unit, gidx, nu, lane);
-        load_batch<B, UNIT, LPR, XC, 1, WIDE>(ua, mu, rb, true, wpr, gpr, slot, unit, gidx, nu, lane);
+        load_batch<B, UNIT, LPR, XC, 1, WIDE>(ga, mg, rb, rb < n, wpr, gpr, slot, unit, gidx, nu, lane);
+        load_batch<B, UNIT, LPR, XC, 1, WIDE>(ua, mu, rb, rb < n, wpr, gpr, slot, unit, gidx, nu, lane);
         // The first batch's weight loads go out before the activation set-up.
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (XL) {
+            XUnit<B, UNIT> t;
+            xunit_from_words<B, UNIT>(xw, t);
+            store_xunit_lds<B, UNIT>(t, xl_all + xb * XUNIT_LDS_WORDS);
+            lds_barrier();
+            if (rb >= n) return;
+        }
         if constexpr (!XL) {
 #pragma unroll
             for (int c = 0; c < XC; ++c)

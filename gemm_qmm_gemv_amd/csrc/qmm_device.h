@@ -328,11 +328,20 @@ struct XUnit {
 
 // Build an XUnit from the UNIT fp16 activations at byte offset off of the
 // activation buffer (16-byte aligned).
+// (Split in two below: xunit_from_words converts words already loaded.)
+template <int B, int UNIT>
+__device__ __forceinline__ void xunit_from_words(const u32 (&xw)[UNIT / 2], XUnit<B, UNIT>& xu);
+
 template <int B, int UNIT>
 __device__ __forceinline__ void prep_xunit(rsrc_t xr, uint32_t off, XUnit<B, UNIT>& xu) {
-    using F = PairFmt<B>;
     u32 xw[UNIT / 2];
     buffer_words<UNIT / 2, 16>(xr, off, xw);
+    xunit_from_words<B, UNIT>(xw, xu);
+}
+
+template <int B, int UNIT>
+__device__ __forceinline__ void xunit_from_words(const u32 (&xw)[UNIT / 2], XUnit<B, UNIT>& xu) {
+    using F = PairFmt<B>;
     // Both constants come from packed dot products on the pairs themselves:
     // corr += x_a * c + x_b * c with c = 1024 * 2^-f (exact in fp16), and
     // xsum += x_a + x_b.  No per-element conversions, few live registers.
