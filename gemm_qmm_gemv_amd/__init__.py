@@ -355,4 +355,5 @@ def qmm_get_plan(op, m, n, k, bits, group_size, cu_count=0, workspace_bytes=0) -
                                int(cu_count), int(workspace_bytes), ctypes.byref(plan)),
            "qmm_get_plan")
     return {f: getattr(plan, f) for f, _ in _Plan._fields_ if f != "reserved"} | {
-        "multipass": bool(plan.reserved[0]), "staged": bool(plan.reserved[1])}
+        "multipass": bool(plan.reserved[0]), "staged": bool(plan.reserved[1]),
+        "late": bool(plan.reserved[2])}

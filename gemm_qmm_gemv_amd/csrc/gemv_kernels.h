@@ -312,7 +312,7 @@ using out_ptr = std::conditional_t<RES, float*, float* __restrict__>;
 // may be y itself: each row's residual is read, by the lanes of that row's
 // slot, before the row is written.  Without RES, R is ignored and the
 // kernel issues no residual loads.
-template <int B, int UNIT, int LPR, int XC, int U, bool MP, bool RES = false, bool STG = false>
+template <int B, int UNIT, int LPR, int XC, int U, bool MP, bool RES = false, bool STG = false, bool LATE = false>
 __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
                                                    const uint16_t* __restrict__ S,
                                                    const uint16_t* __restrict__ Mn,
@@ -323,6 +323,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
     // once per work-group, instead of each unit's pairs in every lane's
     // registers.
     constexpr bool XL = xunits_in_lds<B, LPR, XC>() && !MP;
+    static_assert(!LATE || (XL && !STG), "the late unit build is for the single-pass store-per-batch loop");
     __shared__ __attribute__((aligned(16))) u32 xl_all[XL ? LPR * XC * XUNIT_LDS_WORDS : 4];
     constexpr int SLOTS = 64 / LPR;
     const int lane = threadIdx.x & 63;
@@ -351,12 +352,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
         }
     };
 
-    if constexpr (XL) {
+    if constexpr (XL && !LATE) {
         // Unit u (< LPR * XC) built by thread u; units past the row are
         // zero.  Every wave reaches the barrier before any exits.  (Issuing
         // the first weight loads before this, as the fused gate/up kernel
-        // does, measured slower here: 3072 x 1024 3.45 -> 3.58 us, 8192 x
-        // 2048 Q2 4.67 -> 5.30; 3072 x 8192 6.05 -> 5.85.)
+        // does, measured slower here but for small Q4 launches, see LATE:
+        // 8192 x 3072 5.62 -> 6.24 us, 8192 x 2048 Q2 4.66 -> 4.96, 65536 x
+        // 1024 Q8 14.75 -> 15.38.)
         const int u = threadIdx.x;
         if (u < LPR * XC) {
             XUnit<B, UNIT> t;
@@ -406,15 +408,40 @@ __global__ __launch_bounds__(256) void gemv_kernel(const u32* __restrict__ W,
         } else if constexpr (!STG) {
             units_of_pass(0);
             int rb = wave * SLOTS * U;
-            if (rb >= n) return;
+            if (!LATE && rb >= n) return;
+            // LATE (small Q4 launches, one unit per lane): the activation
+            // words first, then the first batch's weights; the units are
+            // built and shared behind an LDS-only barrier while the weights
+            // are in flight, as in the fused gate/up kernel.  Every wave
+            // reaches that barrier before any exits.  Measured (Q4): 3072 x
+            // 1024 3.47 -> 3.21 us, 1024 x 1024 3.33 -> 3.06, 4096 x 1024
+            // 3.53 -> 3.34, 1024 x 2048 3.41 -> 3.16, 151936 x 1024 17.8 ->
+            // 17.1.
+            const int xb = (int)threadIdx.x < LPR * XC ? (int)threadIdx.x : LPR * XC;
+            u32 xw[LATE ? UNIT / 2 : 1];
+            if constexpr (LATE) {
+                buffer_words<UNIT / 2, 16>(xr, xb < nu ? (uint32_t)(xb * UNIT * 2) : (uint32_t)k * 2u, xw);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             RowBatch<B, UNIT, XC, U> ba, bb;
             float ra[U], rb_res[U];
-            load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, rb, true, wpr, gpr, slot, unit, gidx, nu, lane);
-            load_res(rb, true, ra);
+            load_batch<B, UNIT, LPR, XC, U, WIDE>(ba, mr, rb, LATE ? rb < n : true, wpr, gpr, slot, unit, gidx, nu,
+                                                  lane);
+            load_res(rb, LATE ? rb < n : true, ra);
             // The first batch's weight loads go out before the activation
-            // loads and their set-up arithmetic.
+            // set-up arithmetic.
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (!XL) prep();
+            if constexpr (LATE) {
+                if (xb < LPR * XC) {
+                    XUnit<B, UNIT> t;
+                    xunit_from_words<B, UNIT>(xw, t);
+                    store_xunit_lds<B, UNIT>(t, xl_all + xb * XUNIT_LDS_WORDS);
+                }
+                lds_barrier();
+                if (rb >= n) return;
+            } else if constexpr (!XL) {
+                prep();
+            }
             while (true) {
                 float yacc[U];
                 int nxt = rb + stride;
@@ -1217,6 +1244,12 @@ hipError_t launch_gemv_t(const GemvArgs& a, const GemvShape& sh, hipStream_t st)
         if (sh.staged) {
             if (a.r) return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, false, true, true>>(a, sh, st);
             return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, false, false, true>>(a, sh, st);
+        }
+    }
+    if constexpr (B == 4 && LPR <= 32 && XC == 1 && xunits_in_lds<B, LPR, XC>()) {
+        if (sh.late) {
+            if (a.r) return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, false, true, false, true>>(a, sh, st);
+            return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, false, false, false, true>>(a, sh, st);
         }
     }
     if (a.r) return launch_gemv_k<gemv_kernel<B, UNIT, LPR, XC, U, false, true>>(a, sh, st);

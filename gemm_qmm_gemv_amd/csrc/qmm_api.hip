@@ -153,12 +153,13 @@ qmm_status device_cus(int* cus) {
 enum OverrideId {
     OV_UNIT, OV_GEMV_LPR, OV_GEMV_XC, OV_GEMV_U, OV_GEMV_WAVES_PER_CU, OV_BATCH_U, OV_ROWS_MR,
     OV_ROWS_WAVES_PER_CU, OV_GEMM_TILE_M, OV_GEMM_TILE_N, OV_GEMM_SPLIT, OV_GEMM_WIDE_SCALES,
-    OV_GEMM_ORDER, OV_GEMM_GROUPED, OV_GEMM_KERNEL, OV_GEMV_STAGED, OV_COUNT
+    OV_GEMM_ORDER, OV_GEMM_GROUPED, OV_GEMM_KERNEL, OV_GEMV_STAGED, OV_GEMV_LATE, OV_COUNT
 };
 const char* const OVERRIDE_NAMES[OV_COUNT] = {
     "QMM_UNIT", "QMM_GEMV_LPR", "QMM_GEMV_XC", "QMM_GEMV_U", "QMM_GEMV_WAVES_PER_CU", "QMM_BATCH_U",
     "QMM_ROWS_MR", "QMM_ROWS_WAVES_PER_CU", "QMM_GEMM_TILE_M", "QMM_GEMM_TILE_N", "QMM_GEMM_SPLIT",
-    "QMM_GEMM_WIDE_SCALES", "QMM_GEMM_ORDER", "QMM_GEMM_GROUPED", "QMM_GEMM_KERNEL", "QMM_GEMV_STAGED"};
+    "QMM_GEMM_WIDE_SCALES", "QMM_GEMM_ORDER", "QMM_GEMM_GROUPED", "QMM_GEMM_KERNEL", "QMM_GEMV_STAGED",
+    "QMM_GEMV_LATE"};
 std::atomic<int> g_override[OV_COUNT];
 
 struct OverridesFromEnvironment {
@@ -263,6 +264,16 @@ GemvShape plan_gemv(int64_t n, int64_t k, int bits, int group, int cus) {
     sh.staged = !sh.multipass && stageable && batches >= (int64_t)16 * cus;
     const int es = override_or(OV_GEMV_STAGED, -1);
     if (es >= 0) sh.staged = es == 1 && !sh.multipass && stageable;
+    // Q4 rows of one unit per lane on at most 32 lanes (K up to 2048) build
+    // their activation units after the first batch's weight loads, so the
+    // two latencies overlap: 3072 x 1024 3.47 -> 3.21 us, 4096 x 1024 3.53
+    // -> 3.34, 1024 x 2048 3.41 -> 3.16, 151936 x 1024 17.8 -> 17.1.  The
+    // other shapes lost by it (8192 x 3072 5.62 -> 6.24, 1024 x 3072 3.86 ->
+    // 4.17, 8192 x 2048 Q2 4.66 -> 4.96, 65536 x 1024 Q8 14.75 -> 15.38).
+    const bool lateable = !sh.multipass && !sh.staged && bits == 4 && sh.lpr <= 32 && sh.xc == 1;
+    sh.late = lateable;
+    const int ol = override_or(OV_GEMV_LATE, -1);
+    if (ol >= 0) sh.late = ol == 1 && lateable;
     sh.waves_per_cu = override_or(OV_GEMV_WAVES_PER_CU, wpc_default);
     // Reported grid: the cap assumes 16 resident waves per CU; the launch
     // uses the kernel's real occupancy.
@@ -1141,6 +1152,7 @@ qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits, int g
         plan->grid = sh.grid;
         plan->reserved[0] = sh.multipass;
         plan->reserved[1] = sh.staged;
+        plan->reserved[2] = sh.late;
         return ok();
     }
     if (op == 3) {

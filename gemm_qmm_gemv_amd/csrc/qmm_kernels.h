@@ -24,6 +24,7 @@ struct GemvShape {
     int u;              // rows per slot per iteration
     bool multipass;     // k > lpr * xc * unit
     bool staged;        // single pass, row sums staged in LDS (64-lane rows only)
+    bool late;          // single pass, activation units built after the first weight loads
     int64_t work;       // row batches (waves that have work)
     int cus;            // compute units of the device
     int waves_per_cu;   // > 0: cap resident waves per CU; 0: the kernel's occupancy

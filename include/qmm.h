@@ -354,7 +354,8 @@ typedef struct qmm_plan {
     int64_t grid;          /* work-groups launched                          */
     int32_t block;         /* threads per work-group                        */
     int32_t reserved[5];   /* GEMV: [0] multi-pass rows, [1] row sums staged
-                              in LDS; the rest zero                          */
+                              in LDS, [2] activation units built after the
+                              first weight loads; the rest zero              */
 } qmm_plan;
 
 QMM_API qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bits,
@@ -370,7 +371,9 @@ QMM_API qmm_status qmm_get_plan(int op, int64_t m, int64_t n, int64_t k, int bit
  * QMM_GEMM_WIDE_SCALES, QMM_GEMM_ORDER, QMM_GEMM_GROUPED, QMM_GEMM_KERNEL
  * (1: the prefill GEMM that dequantizes into LDS, 2: the one that
  * dequantizes into registers), QMM_GEMV_STAGED (1/0: single GEMVs with
- * 64-lane rows do / do not stage their row sums in LDS); value < 0 removes
+ * 64-lane rows do / do not stage their row sums in LDS), QMM_GEMV_LATE
+ * (1/0: single Q4 GEMVs of one unit per lane on at most 32 lanes do / do
+ * not build their activation units after the first weight loads); value < 0 removes
  * the override.  The same names are read from the environment once, when
  * the library is loaded.  Unknown name: QMM_ERR_INVALID_ARGUMENT.          */
 QMM_API qmm_status qmm_set_override(const char *name, int value);

@@ -246,3 +246,43 @@ def test_gemv_16x3_staged_and_unstaged_exact(qmm_override, bits, staged):
     yq = _run_gemv(q, x)
     y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, 64)
     assert_within(yq, y_ref, a_ref, "gemv 16x3 staged=%d b%d" % (staged, bits))
+
+
+@pytest.mark.parametrize("late", (0, 1))
+@pytest.mark.parametrize("n,k", ((5, 1024), (777, 128), (3075, 1024), (1029, 2048), (20011, 1024)))
+def test_gemv_q4_late_unit_build_exact(qmm_override, late, n, k):
+    """Q4 rows of one unit per lane (K up to 2048) with the activation units
+    built before or after the first weight loads, including launches where
+    most waves have no rows (every wave still reaches the LDS barrier) and
+    two rows per slot: exact integers bit for bit on NaN-prefilled outputs,
+    the residual added in place, and seeded inputs within tolerance."""
+    import gemm_qmm_gemv_amd as qmm
+    torch = _torch()
+    from gemm_qmm_gemv_amd import tensors
+    bits = 4
+    qmm_override("QMM_GEMV_LATE", late)
+    pl = qmm.qmm_get_plan(0, 1, n, k, bits, 64)
+    assert pl["units_per_lane"] == 1 and pl["lanes_per_row"] <= 32 and not pl["multipass"]
+    assert pl["late"] == bool(late)
+    rng = inputs.rng_for(61, n, k, bits)
+    w = inputs.packed_words(rng, n, k, bits)
+    s = np.ones((n, k // 64), dtype=np.float16)
+    mn = np.zeros((n, k // 64), dtype=np.float16)
+    xi = rng.integers(-2, 3, size=k).astype(np.float16)
+    qe = {"w": w, "scales": s, "mins": mn, "n": n, "k": k, "bits": bits, "group": 64}
+    announce("gemv-q4-late", late, n, k)
+    dq, xd = tensors.upload_matrix(qe), tensors.device_tensor(xi)
+    y = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    tensors.gemv(dq, xd, y)
+    r = rng.integers(-1000, 1000, size=n).astype(np.float32)
+    rd = tensors.device_tensor(r)
+    tensors.gemv_residual(dq, xd, rd, rd)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.qmm(w, s, mn, xi, n, k, bits, 64)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), y_ref.reshape(-1))
+    assert np.array_equal(rd.cpu().numpy().astype(np.float64), y_ref.reshape(-1) + r.astype(np.float64))
+    q = inputs.quantized_matrix(n, k, bits, 64, key=(62, n, k))
+    x = inputs.activation_rows(1, k, key=(62, n, k))[0]
+    yq = _run_gemv(q, x)
+    y_ref, a_ref = oracle.qmm(q["w"], q["scales"], q["mins"], x, n, k, bits, 64)
+    assert_within(yq, y_ref, a_ref, "gemv q4 late=%d %dx%d" % (late, n, k))
